@@ -1,0 +1,217 @@
+"""fp64 CPU oracle of the MoE layer forward pass (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never calls it.
+
+Thin ctypes wrapper over ``colibri_oracle.cpp``: numpy arrays in, numpy
+arrays out.  Inputs are the stored tensors (float32, or bf16 bit patterns as
+uint16); results are float64 (values) or int32 (indices).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "colibri_oracle.cpp")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+DT_F32, DT_BF16 = 0, 1
+ACT = {"relu": 0, "gelu": 1, "swiglu": 2}
+
+# -ffp-contract=off: no fused multiply-add, so every product and sum is rounded
+# exactly as written; no fast-math.
+CFLAGS = ["-O3", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c++17"]
+
+
+def build(extra_flags=()) -> str:
+    cmd = ["g++", *CFLAGS, *extra_flags, _SRC, "-o", _SO + ".tmp"]
+    subprocess.check_call(cmd)
+    os.replace(_SO + ".tmp", _SO)
+    return _SO
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def load_library(path: Optional[str] = None):
+    """Load the oracle (building it if absent).  A path loads a separate build."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    so = path or _SO
+    if path is None and not os.path.exists(so):
+        build()
+    lib = ctypes.CDLL(so)
+    i, d, z = ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+    lib.oracle_set_threads.argtypes = [i]
+    lib.oracle_max_threads.restype = i
+    lib.oracle_logits.argtypes = [i, i, i, i, _P, _P, _P, _P]
+    lib.oracle_top2.argtypes = [i, i, _P, _P]
+    lib.oracle_gates.argtypes = [i, i, _P, _P, _P]
+    lib.oracle_dispatch.argtypes = [i, i, _P, _P, _P, _P, _P]
+    lib.oracle_ffn_rows.argtypes = [i, i, i, i, i, _P, i, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.oracle_combine.argtypes = [i, i, i, _P, _P, _P, _P]
+    lib.oracle_layer.argtypes = [i, i, i, i, i, i, i] + [_P] * 8 + [_P] * 9
+    lib.oracle_round.argtypes = [_P, _P, z, i]
+    for f in ("oracle_set_threads", "oracle_logits", "oracle_top2", "oracle_gates", "oracle_dispatch",
+              "oracle_ffn_rows", "oracle_combine", "oracle_layer", "oracle_round"):
+        getattr(lib, f).restype = None
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.uint16:
+        return DT_BF16
+    raise TypeError(f"oracle inputs are float32 or bf16 bits (uint16), got {a.dtype}")
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype) if dtype is not None else np.ascontiguousarray(a)
+
+
+def set_threads(n: int, lib=None):
+    (lib or load_library()).oracle_set_threads(int(n))
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or load_library()).oracle_max_threads())
+
+
+def logits(x, w_r, b_r=None, lib=None) -> np.ndarray:
+    lib = lib or load_library()
+    x, w_r = _c(x), _c(w_r)
+    T, d = x.shape
+    E = w_r.shape[1]
+    b_r = _c(b_r, np.float32)
+    out = np.empty((T, E), np.float64)
+    lib.oracle_logits(T, d, E, _dt(x), _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(out))
+    return out
+
+
+def top2(lg: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load_library()
+    lg = _c(lg, np.float64)
+    T, E = lg.shape
+    idx = np.empty((T, 2), np.int32)
+    lib.oracle_top2(T, E, _ptr(lg), _ptr(idx))
+    return idx
+
+
+def gates(lg: np.ndarray, idx: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load_library()
+    lg = _c(lg, np.float64)
+    idx = _c(idx, np.int32)
+    T, E = lg.shape
+    g = np.empty((T, 2), np.float64)
+    lib.oracle_gates(T, E, _ptr(lg), _ptr(idx), _ptr(g))
+    return g
+
+
+def dispatch(idx: np.ndarray, E: int, lib=None) -> Dict[str, np.ndarray]:
+    lib = lib or load_library()
+    idx = _c(idx, np.int32)
+    T = idx.shape[0]
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    sa = np.empty(2 * T, np.int32)
+    ap = np.empty(2 * T, np.int32)
+    lib.oracle_dispatch(T, E, _ptr(idx), _ptr(counts), _ptr(offsets), _ptr(sa), _ptr(ap))
+    return {"counts": counts, "offsets": offsets, "sorted_assign": sa, "assign_pos": ap}
+
+
+def ffn_rows(x, rows_token, rows_expert, w1, w2, act: str, w3=None, b1=None, b2=None, mirror=True,
+             lib=None) -> np.ndarray:
+    lib = lib or load_library()
+    x, w1, w2, w3, b1, b2 = (_c(a) for a in (x, w1, w2, w3, b1, b2))
+    dt = _dt(x)
+    for a in (w1, w2, w3, b1, b2):
+        if a is not None and _dt(a) != dt:
+            raise TypeError("all layer tensors share one dtype")
+    E, d, h = w1.shape
+    rt = _c(rows_token, np.int32)
+    re = _c(rows_expert, np.int32)
+    n = rt.shape[0]
+    if act == "swiglu" and w3 is None:
+        raise ValueError("swiglu needs w3")
+    y = np.empty((n, d), np.float64)
+    lib.oracle_ffn_rows(d, h, dt, ACT[act], int(bool(mirror)), _ptr(x), n, _ptr(rt), _ptr(re), _ptr(w1),
+                        _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2), _ptr(y))
+    return y
+
+
+def combine(y_sorted, assign_pos, gate, dtype: int, lib=None) -> np.ndarray:
+    lib = lib or load_library()
+    y = _c(y_sorted, np.float64)
+    ap = _c(assign_pos, np.int32)
+    g = _c(gate, np.float64)
+    T = ap.shape[0] // 2
+    d = y.shape[1]
+    out = np.empty((T, d), np.float64)
+    lib.oracle_combine(T, d, dtype, _ptr(y), _ptr(ap), _ptr(g), _ptr(out))
+    return out
+
+
+def layer(x, w_r, w1, w2, act: str, b_r=None, w3=None, b1=None, b2=None, mirror=True,
+          lib=None) -> Dict[str, np.ndarray]:
+    lib = lib or load_library()
+    x, w_r, w1, w2, w3, b1, b2 = (_c(a) for a in (x, w_r, w1, w2, w3, b1, b2))
+    b_r = _c(b_r, np.float32)
+    T, d = x.shape
+    E, _, h = w1.shape
+    dt = _dt(x)
+    r = {
+        "logits": np.empty((T, E), np.float64), "idx": np.empty((T, 2), np.int32),
+        "gate": np.empty((T, 2), np.float64), "counts": np.empty(E, np.int32),
+        "offsets": np.empty(E + 1, np.int32), "sorted_assign": np.empty(2 * T, np.int32),
+        "assign_pos": np.empty(2 * T, np.int32), "y_sorted": np.empty((2 * T, d), np.float64),
+        "out": np.empty((T, d), np.float64),
+    }
+    lib.oracle_layer(T, d, h, E, dt, ACT[act], int(bool(mirror)), _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(w1),
+                     _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2), *(_ptr(r[k]) for k in (
+                         "logits", "idx", "gate", "counts", "offsets", "sorted_assign", "assign_pos",
+                         "y_sorted", "out")))
+    return r
+
+
+def layer_tokens(x, w_r, w1, w2, act: str, tokens, b_r=None, w3=None, b1=None, b2=None, mirror=True,
+                 idx_override=None, lib=None) -> Dict[str, np.ndarray]:
+    """Layer outputs for a sample of tokens only (each token's row depends only on
+    that token).  ``idx_override`` [len(tokens), 2] forces the chosen experts
+    (gates are then taken from the oracle's own logits for that pair)."""
+    lib = lib or load_library()
+    tokens = np.asarray(tokens, np.int64)
+    xs = _c(np.asarray(x)[tokens])
+    lg = logits(xs, w_r, b_r, lib=lib)
+    idx = top2(lg, lib=lib) if idx_override is None else _c(idx_override, np.int32)
+    g = gates(lg, idx, lib=lib)
+    n = len(tokens)
+    rt = np.repeat(np.arange(n, dtype=np.int32), 2)
+    re = idx.reshape(-1)
+    y = ffn_rows(xs, rt, re, w1, w2, act, w3=w3, b1=b1, b2=b2, mirror=mirror, lib=lib)
+    ap = np.arange(2 * n, dtype=np.int32)
+    out = combine(y, ap, g, _dt(xs), lib=lib)
+    return {"logits": lg, "idx": idx, "gate": g, "y": y.reshape(n, 2, -1), "out": out}
+
+
+def round_to(a: np.ndarray, dtype: int, lib=None) -> np.ndarray:
+    lib = lib or load_library()
+    a = _c(a, np.float64)
+    o = np.empty_like(a)
+    lib.oracle_round(_ptr(a), _ptr(o), a.size, dtype)
+    return o

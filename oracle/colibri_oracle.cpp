@@ -1,0 +1,281 @@
+// Plain fp64 CPU oracle of the Colibri MoE layer forward pass.
+//
+// TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously correct
+// reference that the GPU path is checked against.  Only the test suite, the
+// smoke check and the benchmark's CPU-baseline leg may load it; the product
+// library never links or calls it, and it shares no code, header or table
+// with the HIP path.
+//
+// Pages cited (Colibri write-ups; each page is named by its address):
+//   [zskr]  http://www.zskr.cn/news/2272131   "Colibri: a lightweight C MoE inference engine for edge devices"
+//   [rkmt]  http://news.rkmt.cn/news/2271114
+//   [hnwysp] https://www.hnwysp.cn/news/30485
+//   [nxbn]  http://m.nxbn.cn/news/48047
+//
+// Every value is widened exactly to double (fp32 and bf16 are subsets of
+// fp64) and every sum is taken in double, in the order stated at each step.
+// Conversions to fp32/bf16 round to nearest, ties to even.
+//
+// Readings of points the pages leave open (listed in full in the design notes):
+//  * gate weights are the softmax over all E renormalised over the chosen two
+//    ([hnwysp] section 3.1 takes softmax then the top-k; the verbose log in
+//    [hnwysp] section 4.3 prints gate pairs that sum to one);
+//  * selection ranks the raw logits (softmax is monotone; [zskr] section 2.3
+//    LINEAR_SCORE mode ranks logits) under the total order
+//    (logit descending, expert index ascending); NaN ranks below -inf;
+//  * tokens inside an expert's segment keep ascending assignment order
+//    a = 2t + s, the order of the counting loop in [zskr] section 3.2;
+//  * expert = two-layer FFN (ReLU / exact-erf GELU, or SwiGLU with W1, W3, W2).
+//
+// Parity is pinned by the CPU tests (brute-force top-2, exhaustive tie
+// patterns, the page's printed gate pairs, a hand-worked dispatch, library
+// matmuls, and whole-layer invariants).
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2 };
+
+inline double widen_bf16(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+inline double load(const void *p, int dt, size_t i) {
+    if (dt == DT_F32) return (double)((const float *)p)[i];
+    return widen_bf16(((const uint16_t *)p)[i]);
+}
+
+// Round a double to the nearest value with `mant` explicit mantissa bits and
+// the fp32 exponent range (fp32: 23, bf16: 7), ties to even.  Subnormals keep
+// a fixed quantum of 2^(-126-mant).  Overflow goes to +-inf.
+double round_to_format(double v, int mant) {
+    if (!std::isfinite(v) || v == 0.0) return v;
+    int e = std::ilogb(v);
+    if (e < -126) e = -126;
+    double q = std::ldexp(1.0, e - mant);
+    double r = std::nearbyint(v / q) * q;  // default rounding mode: nearest-even
+    if (std::fabs(r) >= std::ldexp(1.0, 128)) r = std::copysign(INFINITY, v);
+    return r;
+}
+
+double round_to_dtype(double v, int dt) { return round_to_format(v, dt == DT_F32 ? 23 : 7); }
+
+// Total order used for expert selection: a beats b when its logit is larger,
+// or equal with a smaller index.  NaN ranks below every number.
+bool beats(double la, int a, double lb, int b) {
+    bool na = std::isnan(la), nb = std::isnan(lb);
+    if (na != nb) return nb;          // the non-NaN one wins
+    if (!na && la != lb) return la > lb;
+    return a < b;
+}
+
+double act_relu(double z) { return z > 0.0 ? z : 0.0; }
+double act_gelu(double z) { return 0.5 * z * (1.0 + std::erf(z / std::sqrt(2.0))); }
+double act_silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+}  // namespace
+
+extern "C" {
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+// Step 1, router logits ([zskr] section 3.2, first step of the routing chain:
+// logits = input x routing weights, no softmax yet; [rkmt] section 3.1 stores a
+// router bias [E] beside the router weight):
+//   logits[t,e] = (sum_{j ascending} x[t,j] * w_r[j,e]) + b_r[e]
+// x [T,d], w_r [d,E] row-major in dtype `dt`; b_r [E] fp32 or NULL (= 0).
+void oracle_logits(int T, int d, int E, int dt, const void *x, const void *w_r, const float *b_r,
+                   double *logits) {
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int j = 0; j < d; ++j)
+                s += load(x, dt, (size_t)t * d + j) * load(w_r, dt, (size_t)j * E + e);
+            logits[(size_t)t * E + e] = s + (b_r ? (double)b_r[e] : 0.0);
+        }
+    }
+}
+
+// Step 2, deterministic top-2 ([zskr] section 3.2: a fixed comparison network,
+// so the selected sequence is deterministic; [hnwysp] section 3.1: the top-k
+// indices come out strictly descending by score).  Slot 0 holds the winner of
+// the total order, slot 1 the winner among the rest.
+void oracle_top2(int T, int E, const double *logits, int32_t *idx) {
+    for (int t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        int i0 = 0;
+        for (int e = 1; e < E; ++e)
+            if (beats(l[e], e, l[i0], i0)) i0 = e;
+        int i1 = -1;
+        for (int e = 0; e < E; ++e) {
+            if (e == i0) continue;
+            if (i1 < 0 || beats(l[e], e, l[i1], i1)) i1 = e;
+        }
+        idx[2 * t] = i0;
+        idx[2 * t + 1] = i1;
+    }
+}
+
+// Step 3, gate weights: softmax over all E experts ([hnwysp] section 3.1),
+// then the two chosen probabilities renormalised to sum to one (the gate pairs
+// printed in [hnwysp] section 4.3 sum to one).
+void oracle_gates(int T, int E, const double *logits, const int32_t *idx, double *gate) {
+    std::vector<double> p(E);
+    for (int t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        double m = -INFINITY;
+        for (int e = 0; e < E; ++e) m = std::max(m, l[e]);
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) {
+            p[e] = std::exp(l[e] - m);
+            z += p[e];
+        }
+        for (int e = 0; e < E; ++e) p[e] /= z;
+        double p0 = p[idx[2 * t]], p1 = p[idx[2 * t + 1]];
+        gate[2 * t] = p0 / (p0 + p1);
+        gate[2 * t + 1] = p1 / (p0 + p1);
+    }
+}
+
+// Step 4, dispatch ([zskr] section 3.2: count assignments per expert over
+// i = t*k + s, then build dispatch offsets; [zskr] section 3.3: one contiguous
+// region per expert).  Assignment a = 2t + s.
+//   counts[e]   = #{a : idx[a] = e}
+//   offsets[0]  = 0, offsets[e+1] = offsets[e] + counts[e]
+//   sorted_assign lists the assignments of expert 0, then expert 1, ..., each
+//   group in ascending a;  assign_pos[sorted_assign[p]] = p.
+void oracle_dispatch(int T, int E, const int32_t *idx, int32_t *counts, int32_t *offsets,
+                     int32_t *sorted_assign, int32_t *assign_pos) {
+    const int A = 2 * T;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int a = 0; a < A; ++a) counts[idx[a]] += 1;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int p = 0;
+    for (int e = 0; e < E; ++e)
+        for (int a = 0; a < A; ++a)
+            if (idx[a] == e) sorted_assign[p++] = a;
+    for (int q = 0; q < A; ++q) assign_pos[sorted_assign[q]] = q;
+}
+
+// Step 5, one expert applied to one token row ([zskr] section 1 and [nxbn]
+// section 3.1: each expert is a two-layer FFN stored W1 | b1 | W2 | b2;
+// [hnwysp] section 3.2: each layer is an affine map):
+//   relu/gelu: u = x W1[e] + b1[e];  H = act(u);        y = H W2[e] + b2[e]
+//   swiglu:    u = x W1[e];  v = x W3[e];  H = silu(u) * v;  y = H W2[e]
+// W1, W3 [E][d][h], W2 [E][h][d], b1 [E][h], b2 [E][d] (NULL = zero).
+// Each sum runs over the contraction index in ascending order, then adds the
+// bias.  mirror != 0: H is rounded to `dt` before the second product and y is
+// rounded to `dt` (the GPU stores both in that type); mirror == 0: no rounding.
+// Rows: for r in [0, nrows): token row_token[r] of x [*, d], expert row_expert[r].
+// y_out [nrows, d] in double.
+void oracle_ffn_rows(int d, int h, int dt, int act, int mirror, const void *x, int nrows,
+                     const int32_t *row_token, const int32_t *row_expert, const void *w1,
+                     const void *w3, const void *w2, const void *b1, const void *b2, double *y_out) {
+#pragma omp parallel
+    {
+        std::vector<double> xr(d), u(h), v(h), H(h), y(d);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; ++r) {
+            const int t = row_token[r], e = row_expert[r];
+            const size_t wdh = (size_t)e * d * h;
+            for (int k = 0; k < d; ++k) xr[k] = load(x, dt, (size_t)t * d + k);
+            std::fill(u.begin(), u.end(), 0.0);
+            std::fill(v.begin(), v.end(), 0.0);
+            for (int k = 0; k < d; ++k) {
+                const double xk = xr[k];
+                for (int j = 0; j < h; ++j) u[j] += xk * load(w1, dt, wdh + (size_t)k * h + j);
+                if (act == ACT_SWIGLU)
+                    for (int j = 0; j < h; ++j) v[j] += xk * load(w3, dt, wdh + (size_t)k * h + j);
+            }
+            for (int j = 0; j < h; ++j) {
+                double hv;
+                if (act == ACT_SWIGLU) {
+                    hv = act_silu(u[j]) * v[j];
+                } else {
+                    double z = u[j] + (b1 ? load(b1, dt, (size_t)e * h + j) : 0.0);
+                    hv = (act == ACT_RELU) ? act_relu(z) : act_gelu(z);
+                }
+                H[j] = mirror ? round_to_dtype(hv, dt) : hv;
+            }
+            std::fill(y.begin(), y.end(), 0.0);
+            const size_t whd = (size_t)e * h * d;
+            for (int j = 0; j < h; ++j) {
+                const double hj = H[j];
+                for (int c = 0; c < d; ++c) y[c] += hj * load(w2, dt, whd + (size_t)j * d + c);
+            }
+            double *yo = y_out + (size_t)r * d;
+            for (int c = 0; c < d; ++c) {
+                double yv = y[c] + ((act != ACT_SWIGLU && b2) ? load(b2, dt, (size_t)e * d + c) : 0.0);
+                yo[c] = mirror ? round_to_dtype(yv, dt) : yv;
+            }
+        }
+    }
+}
+
+// Step 6, combine ([nxbn] section 3.3: the expert outputs are summed weighted by
+// their gating scores):  out[t] = g[2t] * y[assign_pos[2t]] + g[2t+1] * y[assign_pos[2t+1]],
+// in double, then rounded to `dt`.  y_sorted [2T, d] double, out [T, d] double.
+void oracle_combine(int T, int d, int dt, const double *y_sorted, const int32_t *assign_pos,
+                    const double *gate, double *out) {
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const double *y0 = y_sorted + (size_t)assign_pos[2 * t] * d;
+        const double *y1 = y_sorted + (size_t)assign_pos[2 * t + 1] * d;
+        for (int c = 0; c < d; ++c)
+            out[(size_t)t * d + c] = round_to_dtype(gate[2 * t] * y0[c] + gate[2 * t + 1] * y1[c], dt);
+    }
+}
+
+// The whole layer, steps 1-6 in order.  Every output array is required.
+void oracle_layer(int T, int d, int h, int E, int dt, int act, int mirror, const void *x,
+                  const void *w_r, const float *b_r, const void *w1, const void *w3, const void *w2,
+                  const void *b1, const void *b2, double *logits, int32_t *idx, double *gate,
+                  int32_t *counts, int32_t *offsets, int32_t *sorted_assign, int32_t *assign_pos,
+                  double *y_sorted, double *out) {
+    oracle_logits(T, d, E, dt, x, w_r, b_r, logits);
+    oracle_top2(T, E, logits, idx);
+    oracle_gates(T, E, logits, idx, gate);
+    oracle_dispatch(T, E, idx, counts, offsets, sorted_assign, assign_pos);
+    std::vector<int32_t> rt(2 * (size_t)T), re(2 * (size_t)T);
+    for (int p = 0; p < 2 * T; ++p) {
+        rt[p] = sorted_assign[p] / 2;
+        re[p] = idx[sorted_assign[p]];
+    }
+    oracle_ffn_rows(d, h, dt, act, mirror, x, 2 * T, rt.data(), re.data(), w1, w3, w2, b1, b2, y_sorted);
+    oracle_combine(T, d, dt, y_sorted, assign_pos, gate, out);
+}
+
+// Round doubles to a storage type (for comparing against stored GPU values).
+void oracle_round(const double *in, double *out, size_t n, int dt) {
+    for (size_t i = 0; i < n; ++i) out[i] = round_to_dtype(in[i], dt);
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+"""Mutation check of the pins: each planted mistake in a copy of the oracle
+must make at least one pin fail.  The mistakes are planted in the oracle's
+source text (CPU only); the real oracle is untouched."""
+import os
+import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "colibri_oracle.cpp")
+
+# name -> (text in the oracle, planted replacement)
+MUTANTS = {
+    "tie_break_reversed": ("return a < b;", "return a > b;"),
+    "nan_ranks_high": ("if (na != nb) return nb;", "if (na != nb) return na;"),
+    "slot_order_swapped": ("idx[2 * t] = i0;\n        idx[2 * t + 1] = i1;",
+                           "idx[2 * t] = i1;\n        idx[2 * t + 1] = i0;"),
+    "gates_not_renormalised": ("gate[2 * t] = p0 / (p0 + p1);", "gate[2 * t] = p0;"),
+    "dispatch_unstable": ("for (int a = 0; a < A; ++a)\n            if (idx[a] == e)",
+                          "for (int a = A - 1; a >= 0; --a)\n            if (idx[a] == e)"),
+    "router_bias_dropped": ("s + (b_r ? (double)b_r[e] : 0.0)", "s"),
+    "router_weight_transposed": ("load(w_r, dt, (size_t)j * E + e)", "load(w_r, dt, (size_t)e * d + j)"),
+    "b1_dropped": ("double z = u[j] + (b1 ? load(b1, dt, (size_t)e * h + j) : 0.0);", "double z = u[j];"),
+    "gelu_tanh_approx": ("0.5 * z * (1.0 + std::erf(z / std::sqrt(2.0)))",
+                         "0.5 * z * (1.0 + std::tanh(0.7978845608028654 * (z + 0.044715 * z * z * z)))"),
+    "swiglu_operands_swapped": ("hv = act_silu(u[j]) * v[j];", "hv = u[j] * act_silu(v[j]);"),
+    "w2_transposed": ("load(w2, dt, whd + (size_t)j * d + c)", "load(w2, dt, whd + (size_t)c * h + j)"),
+    "h_not_rounded": ("H[j] = mirror ? round_to_dtype(hv, dt) : hv;", "H[j] = hv;"),
+    "y_not_rounded": ("yo[c] = mirror ? round_to_dtype(yv, dt) : yv;", "yo[c] = yv;"),
+    "combine_gates_swapped": ("gate[2 * t] * y0[c] + gate[2 * t + 1] * y1[c]",
+                              "gate[2 * t + 1] * y0[c] + gate[2 * t] * y1[c]"),
+    "b2_dropped": ("yv = y[c] + ((act != ACT_SWIGLU && b2) ? load(b2, dt, (size_t)e * d + c) : 0.0);",
+                   "yv = y[c];"),
+    "rounding_via_fp32": ("double round_to_dtype(double v, int dt) { return round_to_format(v, dt == DT_F32 ? 23 : 7); }",
+                          "double round_to_dtype(double v, int dt) { return round_to_format(dt == DT_F32 ? v : (double)(float)v, dt == DT_F32 ? 23 : 7); }"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_libs():
+    src = open(SRC).read()
+    tmp = tempfile.mkdtemp(prefix="oracle_mutants_")
+
+    def build(item):
+        name, (old, new) = item
+        assert src.count(old) == 1, f"mutant {name}: target text not found exactly once"
+        path = os.path.join(tmp, f"{name}.cpp")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        so = os.path.join(tmp, f"lib{name}.so")
+        flags = [f for f in oracle.CFLAGS if f != "-O3"] + ["-O1"]
+        subprocess.check_call(["g++", *flags, path, "-o", so])
+        return name, so
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        built = dict(ex.map(build, MUTANTS.items()))
+    return built
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_libs):
+    lib = oracle.load_library(mutant_libs[name])
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake '{name}'"
