@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward pass on one MI355X.
+
+Default workload: the 8-expert 1.3B-class layer (E=8, d=2048, h=5632, GELU
+experts with biases, bf16 storage, fp32 accumulation) on a T=512-token batch;
+one step = one colibri_moe_layer_forward (route, dispatch, grouped expert FFN,
+combine) over the batch.  Inputs are seeded synthetic tensors already resident
+in HBM.  Expert weights rotate over enough identical copies (>= 2 GB) that the
+256 MB MALL cannot serve them from cache.
+
+Prints one JSON line: whole-layer tokens/s plus the FFN stage's roofline
+fraction (HIP events around the stage on the stream it runs on), decode
+microseconds per step at T=1 and T=64, and the fp64 CPU oracle timed on the
+host cores as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="e8", help="workload key in gen.CONFIGS")
+    ap.add_argument("--T", type=int, default=None, help="tokens per step (default: the config's largest T)")
+    ap.add_argument("--rotate-gb", type=float, default=2.0, help="total bytes of rotated weight copies")
+    ap.add_argument("--decode-T", default="1,64", help="extra decode batch sizes timed (comma list, '' = none)")
+    ap.add_argument("--decode-iters", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the layer on one GPU only; this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import mixture_experts_layer_12_amd as moe
+
+    moe.load(build_if_missing=True)
+    cfg = gen.CONFIGS[args.config]
+    T = args.T or max(cfg.Ts)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    t0 = time.time()
+    hw = gen.make_experts(cfg)
+    x_np = gen.make_x(cfg, T)
+    w_r_np = gen.make_router(cfg)
+    b_r_np = gen.router_bias(cfg)
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    dw0 = {k: to_dev(v) for k, v in hw.items()}
+    x = to_dev(x_np)
+    w_r = to_dev(w_r_np)
+    b_r = to_dev(b_r_np)
+    el = 4 if cfg.dtype == gen.F32 else 2
+    per_expert = {k: (v[0].numel() * el if v is not None else 0) for k, v in dw0.items()}
+    layer_w_bytes = sum(v.numel() * el for v in dw0.values() if v is not None)
+    R = max(1, math.ceil(args.rotate_gb * 1e9 / layer_w_bytes))
+    copies = [dw0] + [{k: (v.clone() if v is not None else None) for k, v in dw0.items()} for _ in range(R - 1)]
+    del hw
+    log(f"{R} weight copies x {layer_w_bytes / 1e6:.1f} MB")
+
+    act = gen.ACT_CODE[cfg.act]
+    sh = moe.Shape(T, cfg.d, cfg.h, cfg.E, cfg.dtype, act)
+    ws_bytes = moe.workspace_size(sh)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    tdt = torch.float32 if cfg.dtype == gen.F32 else torch.bfloat16
+    out = torch.empty((T, cfg.d), dtype=tdt, device=dev)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+
+    def step(i, xx=x, s=sh, o=out):
+        w = copies[i % R]
+        moe.layer_forward(s, xx, w_r, b_r, w["w1"], w["w2"], o, ws, ws_bytes, w3=w["w3"], b1=w["b1"], b2=w["b2"],
+                          counts=counts)
+
+    # ---------------------------------------------------------------- whole layer
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    tok_s = T / (ms_per_step * 1e-3)
+    cnt = counts.cpu().numpy()
+    hit = int((cnt > 0).sum())
+    log(f"layer: {ms_per_step * 1e3:.1f} us/step, {tok_s / 1e6:.3f} M tokens/s, experts hit {hit}/{cfg.E}")
+
+    # ---------------------------------------------------------------- per-stage loop
+    A = 2 * T
+    idx = torch.empty((T, 2), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, 2), dtype=torch.float32, device=dev)
+    offs = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+    sa = torch.empty(A, dtype=torch.int32, device=dev)
+    ap_ = torch.empty(A, dtype=torch.int32, device=dev)
+    y = torch.empty((A, cfg.d), dtype=tdt, device=dev)
+    n_ev = 5
+    stage_ms = np.zeros(4)
+    iters = max(args.steps, 20)
+    for it in range(args.warmup + iters):
+        w = copies[it % R]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        evs[0].record(stream)
+        moe.route(sh, x, w_r, b_r, idx, gate)
+        evs[1].record(stream)
+        moe.dispatch(sh, idx, counts, offs, sa, ap_)
+        evs[2].record(stream)
+        moe.expert_ffn(sh, x, sa, offs, w["w1"], w["w2"], y, ws, ws_bytes, w3=w["w3"], b1=w["b1"], b2=w["b2"])
+        evs[3].record(stream)
+        moe.combine(sh, y, ap_, gate, out)
+        evs[4].record(stream)
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            stage_ms += np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(4)])
+    stage_ms /= iters
+    stages_us = dict(zip(("route", "dispatch", "expert_ffn", "combine"), (stage_ms * 1e3).round(2).tolist()))
+    log(f"stages (us): {stages_us}")
+
+    # algorithmic work (SURVEY-style accounting: weights of hit experts once, X in, Y out)
+    m = 2 if cfg.act == "swiglu" else 1
+    hit_w = hit * sum(per_expert.values())
+    ffn_bytes = hit_w + T * cfg.d * el + A * cfg.d * el
+    ffn_flops = 2.0 * A * cfg.d * cfg.h * (m + 1)
+    ffn_s = stage_ms[2] * 1e-3
+    ffn_gbs = ffn_bytes / ffn_s / 1e9
+    ffn_tfs = ffn_flops / ffn_s / 1e12
+    ai = ffn_flops / ffn_bytes
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ffn_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(ffn_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(ffn_tfs / MFMA_BF16_PEAK_TFS, 4)}
+    roof.update({"traffic": None, "kernel": "expert_ffn (gemm1 + gemm2 launches)",
+                 "algorithmic_bytes_per_launch": int(ffn_bytes), "algorithmic_flops_per_launch": ffn_flops,
+                 "avg_launch_us": round(ffn_s * 1e6, 2), "mfma_frac": round(ffn_tfs / MFMA_BF16_PEAK_TFS, 4),
+                 "hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4)})
+
+    # ---------------------------------------------------------------- decode sizes
+    decode = {}
+    for tok in [int(v) for v in args.decode_T.split(",") if v.strip()]:
+        if tok > T:
+            continue
+        s2 = sh.with_T(tok)
+        xd = x[:tok]
+        od = out[:tok]
+        times = []
+        for it in range(20 + args.decode_iters):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(it, xx=xd, s=s2, o=od)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if it >= 20:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        c2 = counts.cpu().numpy()
+        hit2 = int((c2 > 0).sum())
+        byt = hit2 * sum(per_expert.values()) + tok * cfg.d * el * 2 + cfg.d * cfg.E * el
+        med = float(np.median(times))
+        decode[f"T={tok}"] = {"us_per_step_median": round(med, 2), "us_min": round(float(np.min(times)), 2),
+                              "us_p90": round(float(np.percentile(times, 90)), 2), "experts_hit": hit2,
+                              "hbm_frac": round(byt / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"decode T={tok}: {decode[f'T={tok}']}")
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = args.cpu_sample or T
+        toks = np.arange(min(n, T))
+        w_host = gen.make_experts(cfg)
+        c0 = time.perf_counter()
+        oracle.layer_tokens(x_np, w_r_np, w_host["w1"], w_host["w2"], cfg.act, toks, b_r=b_r_np, w3=w_host["w3"],
+                            b1=w_host["b1"], b2=w_host["b2"], mirror=True)
+        el_s = time.perf_counter() - c0
+        cpu = {"value": round(len(toks) / el_s, 2), "unit": "tokens/s", "cores": oracle.max_threads(),
+               "kind": "oracle", "seconds": round(el_s, 2),
+               "sample": f"{len(toks)} of the {T} tokens of the timed batch, whole layer (fp64 logits, top-2, gates, "
+                         f"two expert FFN rows per token, combine)"}
+        log(f"cpu oracle: {cpu}")
+
+    rec = {
+        "metric": "MoE-layer tokens/s (prefill) + us/step (decode); % of MFMA / HBM peak",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == gen.BF16 else "f32", "data": "synthetic (seeded Philox normals)",
+        "config": {"workload": f"{cfg.title}: E={cfg.E}, top-2, d={cfg.d}, h={cfg.h}, {cfg.act}, T={T}",
+                   "T": T, "E": cfg.E, "d": cfg.d, "h": cfg.h, "act": cfg.act, "weight_copies": R},
+        "roofline": roof, "cpu_baseline": cpu, "stages_us": stages_us, "decode": decode,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+/*
+ * colibri_moe.h -- C ABI of the MI355X (gfx950) forward pass of one
+ * Mixture-of-Experts layer, as described by the Colibri write-ups:
+ *
+ *   [zskr]   http://www.zskr.cn/news/2272131  "Colibri: a lightweight C MoE
+ *            inference engine for edge devices"
+ *   [rkmt]   http://news.rkmt.cn/news/2271114
+ *   [hnwysp] https://www.hnwysp.cn/news/30485
+ *   [nxbn]   http://m.nxbn.cn/news/48047
+ *
+ * The layer maps tokens X [T, d] to out [T, d]:
+ *   1. router logits   l = X W_r + b_r                       ([zskr] section 3.2, step 1)
+ *   2. top-2 experts per token, ties to the lower index, and gates
+ *      g = softmax over all experts renormalised over the chosen two
+ *                                                             ([zskr] 3.2; [hnwysp] 3.1, 4.3)
+ *   3. dispatch: per-expert counts, offsets and a stable expert-sorted
+ *      permutation of the 2T assignments                      ([zskr] 3.2, 3.3)
+ *   4. per expert, a two-layer FFN on its rows                ([zskr] 1; [nxbn] 3.1; [hnwysp] 3.2)
+ *        ReLU / GELU : y = act(x W1 + b1) W2 + b2
+ *        SwiGLU      : y = (silu(x W1) * (x W3)) W2
+ *   5. combine: out[t] = g0 y(t, slot 0) + g1 y(t, slot 1)   ([nxbn] 3.3, output aggregation)
+ *
+ * Conventions for every entry point
+ *   - Tensor arguments are HIP device pointers, row-major, owned by the
+ *     caller; nothing is allocated, freed or synchronised inside a call.
+ *     Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without waiting for it.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call launches nothing and returns a negative status.
+ *   - Tensors marked "16-byte aligned" must start on a 16-byte boundary.
+ *   - Assignment a = 2t + s is token t's slot s (slot 0 = the larger logit).
+ *   - topk_idx entries must lie in [0, E) (the router never produces
+ *     anything else).  Entries outside that range are skipped by dispatch:
+ *     they are not counted, their assign_pos is -1, and the unused tail of
+ *     sorted_assign is -1; the FFN and combine skip such rows.
+ *   - Calls are reentrant: there is no global state.  Concurrent calls need
+ *     separate workspaces (the pages' one-context-per-thread rule, [nxbn] 3.3).
+ *   - Status codes: 0 = success, negative = error ([nxbn] 3.3 and 5.1 use the
+ *     same convention).
+ */
+#ifndef COLIBRI_MOE_H
+#define COLIBRI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    COLIBRI_OK = 0,
+    COLIBRI_ERR_INVALID_ARG = -1,  /* null required pointer, T < 0, misaligned pointer */
+    COLIBRI_ERR_WORKSPACE = -2,    /* ws_bytes smaller than the call needs */
+    COLIBRI_ERR_UNSUPPORTED = -3,  /* k != 2, E outside [2, 64], d or h not a multiple of 64,
+                                      unknown dtype / activation, act/weights mismatch */
+    COLIBRI_ERR_HIP = -4           /* a HIP launch failed */
+} colibri_status_t;
+
+/* Storage type of X, W_r, W1, W3, W2, b1, b2, Y and out.  Router bias,
+ * logits and gates are always fp32; arithmetic accumulates in fp32. */
+typedef enum { COLIBRI_F32 = 0, COLIBRI_BF16 = 1 } colibri_dtype_t;
+
+typedef enum {
+    COLIBRI_ACT_RELU = 0,   /* H = max(x W1 + b1, 0) */
+    COLIBRI_ACT_GELU = 1,   /* H = z * Phi(z), exact erf form, z = x W1 + b1 */
+    COLIBRI_ACT_SWIGLU = 2  /* H = silu(x W1) * (x W3); no biases */
+} colibri_act_t;
+
+/* Problem shape.  k must be 2; 2 <= E <= 64; d and h multiples of 64; T >= 0. */
+typedef struct {
+    int32_t T, d, h, E, k;
+    colibri_dtype_t dtype;
+    colibri_act_t act;
+} colibri_moe_shape_t;
+
+/* Expert parameters, all experts packed contiguously ([zskr] 2.2: one
+ * contiguous block per expert set; [nxbn] 3.1: W1 | b1 | W2 | b2 per expert).
+ *   w1 [E][d][h]  16-byte aligned
+ *   w3 [E][d][h]  16-byte aligned, SwiGLU only (NULL otherwise)
+ *   w2 [E][h][d]  16-byte aligned
+ *   b1 [E][h], b2 [E][d]  ReLU/GELU only; NULL means zero.  Must be NULL for SwiGLU. */
+typedef struct {
+    const void *w1, *w3, *w2;
+    const void *b1, *b2;
+} colibri_moe_experts_t;
+
+/* Bytes of device workspace that colibri_moe_layer_forward needs for this
+ * shape (every other entry point needs no more).  Returns 0 for an invalid
+ * shape or T = 0. */
+size_t colibri_moe_workspace_size(const colibri_moe_shape_t *s);
+
+/* Steps 1-2: router logits, deterministic top-2 and gates
+ * ([zskr] 3.2 routing chain; [hnwysp] 3.1 colibri_route_topk).
+ *   x         [T, d] dtype, 16-byte aligned
+ *   w_r       [d, E] dtype, 16-byte aligned
+ *   b_r       [E] fp32, or NULL (zero)
+ *   topk_idx  [T, 2] int32 out: slot 0 = best expert, slot 1 = second best under
+ *             (logit descending, index ascending); NaN ranks below -inf
+ *   topk_gate [T, 2] fp32 out: g0 = 1 / (1 + exp(l1 - l0)), g1 = 1 - g0
+ *   logits    [T, E] fp32 out, or NULL: the fp32 logits the selection used */
+int colibri_moe_route(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                      int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t stream);
+
+/* Step 3: dispatch ([zskr] 3.2: count per expert, then build offsets;
+ * [zskr] 3.3: one contiguous region per expert; [hnwysp] 2.2: pass row
+ * offsets instead of copying rows).
+ *   topk_idx       [T, 2] int32 in
+ *   expert_counts  [E] int32 out
+ *   expert_offsets [E + 1] int32 out, offsets[0] = 0, offsets[E] = 2T
+ *   sorted_assign  [2T] int32 out: assignments grouped by expert, ascending a
+ *                  inside a group
+ *   assign_pos     [2T] int32 out: inverse permutation
+ *   x, x_sorted    optional pair: when both are non-NULL, x_sorted[p] =
+ *                  x[sorted_assign[p] / 2] ([T, d] -> [2T, d], dtype, 16-byte aligned)
+ *   ws, ws_bytes   unused (may be NULL / 0) */
+int colibri_moe_dispatch(const colibri_moe_shape_t *s, const int32_t *topk_idx, int32_t *expert_counts,
+                         int32_t *expert_offsets, int32_t *sorted_assign, int32_t *assign_pos,
+                         const void *x, void *x_sorted, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 4: the grouped expert FFN over the expert-sorted rows
+ * ([zskr] 2.1 grouped GEMM; [nxbn] 2.1 fused matmul + activation kernel).
+ *   x_rows         if sorted_assign != NULL: X [T, d] and row p reads token
+ *                  sorted_assign[p] / 2; else already sorted rows [2T, d]
+ *   expert_offsets [E + 1] int32: rows [offsets[e], offsets[e+1]) use expert e
+ *   w              expert weights (layout above)
+ *   y_sorted       [2T, d] dtype out, 16-byte aligned
+ *   ws, ws_bytes   device workspace for the hidden activations H [2T, h]
+ *                  (stored in dtype, i.e. bf16 for bf16 layers) */
+int colibri_moe_expert_ffn(const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                           const int32_t *expert_offsets, const colibri_moe_experts_t *w, void *y_sorted,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 5: gate-weighted combine fused with the un-permute ([nxbn] 3.3).
+ *   out[t] = g[t,0] * y_sorted[assign_pos[2t]] + g[t,1] * y_sorted[assign_pos[2t+1]],
+ *   summed in fp32 and stored in dtype.  out [T, d], 16-byte aligned. */
+int colibri_moe_combine(const colibri_moe_shape_t *s, const void *y_sorted, const int32_t *assign_pos,
+                        const float *topk_gate, void *out, hipStream_t stream);
+
+/* Steps 1-5 in one call ([nxbn] 3.3: one call is one complete MoE forward).
+ * topk_idx_out [T, 2], topk_gate_out [T, 2] and expert_counts_out [E] are
+ * optional copies of the routing results (NULL = not wanted).  ws must hold
+ * colibri_moe_workspace_size(s) bytes, 256-byte aligned. */
+int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                              const colibri_moe_experts_t *w, void *out, int32_t *topk_idx_out,
+                              float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *colibri_moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLIBRI_MOE_H */

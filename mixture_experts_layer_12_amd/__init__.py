@@ -1,0 +1,194 @@
+"""Python binding of libcolibri_moe.so, the gfx950 MoE layer forward pass.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/colibri_moe.h``.  torch tensors are
+used for device memory and streams; their data pointers and the current HIP
+stream are handed to the library unchanged.  There is no fallback: if the
+library is not built, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcolibri_moe.so")
+
+COLIBRI_OK, COLIBRI_ERR_INVALID_ARG, COLIBRI_ERR_WORKSPACE, COLIBRI_ERR_UNSUPPORTED, COLIBRI_ERR_HIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+RELU, GELU, SWIGLU = 0, 1, 2
+ACT_CODES = {"relu": RELU, "gelu": GELU, "swiglu": SWIGLU}
+
+EXPORTED = [
+    "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn",
+    "colibri_moe_combine", "colibri_moe_layer_forward", "colibri_moe_status_string",
+]
+
+
+class ColibriError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("h", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
+
+
+@dataclass(frozen=True)
+class Shape:
+    T: int
+    d: int
+    h: int
+    E: int
+    dtype: int = BF16
+    act: int = SWIGLU
+    k: int = 2
+
+    def c(self) -> _Shape:
+        return _Shape(self.T, self.d, self.h, self.E, self.k, self.dtype, self.act)
+
+    def with_T(self, T: int) -> "Shape":
+        return Shape(T, self.d, self.h, self.E, self.dtype, self.act, self.k)
+
+
+_lib = None
+
+
+def build() -> str:
+    from . import _build
+    return _build.build()
+
+
+def load(build_if_missing: bool = False):
+    """Load the HIP library.  Raises if it is not built (unless asked to build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise ImportError(f"{LIB_PATH} is not built; run mixture_experts_layer_12_amd.build() "
+                              "(or __graft_entry__.build()) first")
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    SP = ctypes.POINTER(_Shape)
+    lib.colibri_moe_workspace_size.argtypes = [SP]
+    lib.colibri_moe_workspace_size.restype = Z
+    lib.colibri_moe_route.argtypes = [SP, P, P, P, P, P, P, P]
+    lib.colibri_moe_dispatch.argtypes = [SP, P, P, P, P, P, P, P, P, Z, P]
+    lib.colibri_moe_expert_ffn.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, Z, P]
+    lib.colibri_moe_combine.argtypes = [SP, P, P, P, P, P]
+    lib.colibri_moe_layer_forward.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, P, P, P, Z, P]
+    for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_combine",
+              "colibri_moe_layer_forward"):
+        getattr(lib, f).restype = I
+    lib.colibri_moe_status_string.argtypes = [I]
+    lib.colibri_moe_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().colibri_moe_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------------------ marshalling
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (or None).  Accepts raw integers for tests."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != COLIBRI_OK:
+        raise ColibriError(status, where)
+
+
+def _experts(w1, w2, w3=None, b1=None, b2=None) -> _Experts:
+    return _Experts(_ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2))
+
+
+def workspace_size(shape: Shape) -> int:
+    s = shape.c()
+    return int(load().colibri_moe_workspace_size(ctypes.byref(s)))
+
+
+def route(shape: Shape, x, w_r, b_r, topk_idx, topk_gate, logits=None, stream=None):
+    s = shape.c()
+    _check(load().colibri_moe_route(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(topk_idx),
+                                    _ptr(topk_gate), _ptr(logits), _stream(stream)), "colibri_moe_route")
+
+
+def dispatch(shape: Shape, topk_idx, counts, offsets, sorted_assign, assign_pos, x=None, x_sorted=None,
+             ws=None, ws_bytes: int = 0, stream=None):
+    s = shape.c()
+    _check(load().colibri_moe_dispatch(ctypes.byref(s), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                                       _ptr(sorted_assign), _ptr(assign_pos), _ptr(x), _ptr(x_sorted), _ptr(ws),
+                                       ws_bytes, _stream(stream)), "colibri_moe_dispatch")
+
+
+def expert_ffn(shape: Shape, x_rows, sorted_assign, offsets, w1, w2, y_sorted, ws, ws_bytes: int, w3=None, b1=None,
+               b2=None, stream=None):
+    s = shape.c()
+    e = _experts(w1, w2, w3, b1, b2)
+    _check(load().colibri_moe_expert_ffn(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
+                                         ctypes.byref(e), _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
+           "colibri_moe_expert_ffn")
+
+
+def combine(shape: Shape, y_sorted, assign_pos, topk_gate, out, stream=None):
+    s = shape.c()
+    _check(load().colibri_moe_combine(ctypes.byref(s), _ptr(y_sorted), _ptr(assign_pos), _ptr(topk_gate),
+                                      _ptr(out), _stream(stream)), "colibri_moe_combine")
+
+
+def layer_forward(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: int, w3=None, b1=None, b2=None,
+                  topk_idx=None, topk_gate=None, counts=None, stream=None):
+    s = shape.c()
+    e = _experts(w1, w2, w3, b1, b2)
+    _check(load().colibri_moe_layer_forward(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
+                                            _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
+                                            ws_bytes, _stream(stream)), "colibri_moe_layer_forward")
+
+
+class MoELayer:
+    """Device-resident layer: weights and a workspace sized for up to max_T tokens.
+
+    Holds torch tensors (memory only) and calls colibri_moe_layer_forward."""
+
+    def __init__(self, shape: Shape, w_r, w1, w2, w3=None, b1=None, b2=None, b_r=None):
+        import torch
+        self.shape = shape
+        self.w_r, self.w1, self.w2, self.w3, self.b1, self.b2, self.b_r = w_r, w1, w2, w3, b1, b2, b_r
+        self.ws_bytes = workspace_size(shape)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=w1.device)
+
+    def forward(self, x, out, topk_idx=None, topk_gate=None, counts=None, stream=None):
+        T = x.shape[0]
+        if T > self.shape.T:
+            raise ValueError(f"T={T} exceeds the workspace's T={self.shape.T}")
+        sh = self.shape.with_T(T)
+        layer_forward(sh, x, self.w_r, self.b_r, self.w1, self.w2, out, self.ws, self.ws_bytes, w3=self.w3,
+                      b1=self.b1, b2=self.b2, topk_idx=topk_idx, topk_gate=topk_gate, counts=counts, stream=stream)
+        return out

@@ -1,0 +1,197 @@
+// C ABI of the MoE layer: host-side validation, workspace carving and the
+// launch sequence.  Every argument is checked before anything is launched;
+// nothing here allocates, frees or waits on the device.
+//
+// Error convention follows the Colibri write-up [nxbn] http://m.nxbn.cn/news/48047
+// sections 3.3 and 5.1 (0 = success, negative codes for errors), failing
+// loudly instead of the silent zero output that [zskr]
+// http://www.zskr.cn/news/2272131 section 5.2 reports for a wrong pointer.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "colibri_moe.h"
+#include "launchers.h"
+
+using namespace colibri;
+
+namespace {
+
+constexpr int32_t kMaxTokens = 1 << 28;  // keeps assignment ids 2t+s and row counts in int32
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_shape(const colibri_moe_shape_t *s) {
+    if (!s) return COLIBRI_ERR_INVALID_ARG;
+    if (s->k != 2) return COLIBRI_ERR_UNSUPPORTED;
+    if (s->E < 2 || s->E > 64) return COLIBRI_ERR_UNSUPPORTED;
+    if (s->d <= 0 || s->h <= 0 || s->d % 64 || s->h % 64) return COLIBRI_ERR_UNSUPPORTED;
+    if (s->d > (1 << 20) || s->h > (1 << 20)) return COLIBRI_ERR_UNSUPPORTED;
+    if (s->dtype != COLIBRI_F32 && s->dtype != COLIBRI_BF16) return COLIBRI_ERR_UNSUPPORTED;
+    if (s->act != COLIBRI_ACT_RELU && s->act != COLIBRI_ACT_GELU && s->act != COLIBRI_ACT_SWIGLU)
+        return COLIBRI_ERR_UNSUPPORTED;
+    if (s->T < 0) return COLIBRI_ERR_INVALID_ARG;
+    if (s->T > kMaxTokens) return COLIBRI_ERR_UNSUPPORTED;
+    return COLIBRI_OK;
+}
+
+size_t elem_size(const colibri_moe_shape_t *s) { return s->dtype == COLIBRI_F32 ? 4 : 2; }
+
+int check_experts(const colibri_moe_shape_t *s, const colibri_moe_experts_t *w) {
+    if (!w || !w->w1 || !w->w2) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(w->w1, 16) || !aligned(w->w2, 16)) return COLIBRI_ERR_INVALID_ARG;
+    if (s->act == COLIBRI_ACT_SWIGLU) {
+        if (!w->w3) return COLIBRI_ERR_INVALID_ARG;
+        if (!aligned(w->w3, 16)) return COLIBRI_ERR_INVALID_ARG;
+        if (w->b1 || w->b2) return COLIBRI_ERR_UNSUPPORTED;
+    } else {
+        if (w->w3) return COLIBRI_ERR_UNSUPPORTED;
+        const size_t es = elem_size(s);
+        if ((w->b1 && !aligned(w->b1, es)) || (w->b2 && !aligned(w->b2, es))) return COLIBRI_ERR_INVALID_ARG;
+    }
+    return COLIBRI_OK;
+}
+
+struct LayerWorkspace {
+    size_t idx, gate, counts, offsets, sorted, pos, y, ffn, total;
+};
+
+LayerWorkspace layer_workspace(const colibri_moe_shape_t *s) {
+    LayerWorkspace L;
+    const size_t A = 2 * (size_t)s->T;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    L.idx = take(A * 4);
+    L.gate = take(A * 4);
+    L.counts = take((size_t)s->E * 4);
+    L.offsets = take((size_t)(s->E + 1) * 4);
+    L.sorted = take(A * 4);
+    L.pos = take(A * 4);
+    L.y = take(A * s->d * elem_size(s));
+    L.ffn = take(ffn_workspace_bytes(*s));
+    L.total = off;
+    return L;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? COLIBRI_OK : COLIBRI_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t colibri_moe_workspace_size(const colibri_moe_shape_t *s) {
+    if (check_shape(s) != COLIBRI_OK || s->T == 0) return 0;
+    return layer_workspace(s).total;
+}
+
+int colibri_moe_route(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                      int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    if (!x || !w_r || !topk_idx || !topk_gate) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(topk_idx, 4) || !aligned(topk_gate, 4) ||
+        (b_r && !aligned(b_r, 4)) || (logits && !aligned(logits, 4)))
+        return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_route(*s, x, w_r, b_r, topk_idx, topk_gate, logits, stream));
+}
+
+int colibri_moe_dispatch(const colibri_moe_shape_t *s, const int32_t *topk_idx, int32_t *expert_counts,
+                         int32_t *expert_offsets, int32_t *sorted_assign, int32_t *assign_pos, const void *x,
+                         void *x_sorted, void *ws, size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    if (!topk_idx || !expert_counts || !expert_offsets || !sorted_assign || !assign_pos)
+        return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(expert_counts, 4) || !aligned(expert_offsets, 4) ||
+        !aligned(sorted_assign, 4) || !aligned(assign_pos, 4))
+        return COLIBRI_ERR_INVALID_ARG;
+    if ((x == nullptr) != (x_sorted == nullptr)) return COLIBRI_ERR_INVALID_ARG;
+    if (x && (!aligned(x, 16) || !aligned(x_sorted, 16))) return COLIBRI_ERR_INVALID_ARG;
+    hipError_t e = launch_dispatch(*s, topk_idx, expert_counts, expert_offsets, sorted_assign, assign_pos, stream);
+    if (e == hipSuccess && x) e = launch_gather_rows(*s, x, sorted_assign, x_sorted, stream);
+    return hip_status(e);
+}
+
+int colibri_moe_expert_ffn(const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                           const int32_t *expert_offsets, const colibri_moe_experts_t *w, void *y_sorted, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts(s, w);
+    if (st != COLIBRI_OK) return st;
+    if (!x_rows || !expert_offsets || !y_sorted) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(x_rows, 16) || !aligned(y_sorted, 16) || !aligned(expert_offsets, 4) ||
+        (sorted_assign && !aligned(sorted_assign, 4)))
+        return COLIBRI_ERR_INVALID_ARG;
+    const size_t need = ffn_workspace_bytes(*s);
+    if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_expert_ffn(*s, x_rows, sorted_assign, expert_offsets, *w, y_sorted, ws, stream));
+}
+
+int colibri_moe_combine(const colibri_moe_shape_t *s, const void *y_sorted, const int32_t *assign_pos,
+                        const float *topk_gate, void *out, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    if (!y_sorted || !assign_pos || !topk_gate || !out) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(y_sorted, 16) || !aligned(out, 16) || !aligned(assign_pos, 4) || !aligned(topk_gate, 4))
+        return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_combine(*s, y_sorted, assign_pos, topk_gate, out, stream));
+}
+
+int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                              const colibri_moe_experts_t *w, void *out, int32_t *topk_idx_out, float *topk_gate_out,
+                              int32_t *expert_counts_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts(s, w);
+    if (st != COLIBRI_OK) return st;
+    if (!x || !w_r || !out) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(out, 16) || (b_r && !aligned(b_r, 4)) ||
+        (topk_idx_out && !aligned(topk_idx_out, 4)) || (topk_gate_out && !aligned(topk_gate_out, 4)) ||
+        (expert_counts_out && !aligned(expert_counts_out, 4)))
+        return COLIBRI_ERR_INVALID_ARG;
+    const LayerWorkspace L = layer_workspace(s);
+    if (ws_bytes < L.total) return COLIBRI_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+
+    char *base = static_cast<char *>(ws);
+    int32_t *idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t *>(base + L.idx);
+    float *gate = topk_gate_out ? topk_gate_out : reinterpret_cast<float *>(base + L.gate);
+    int32_t *counts = expert_counts_out ? expert_counts_out : reinterpret_cast<int32_t *>(base + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *sorted = reinterpret_cast<int32_t *>(base + L.sorted);
+    int32_t *pos = reinterpret_cast<int32_t *>(base + L.pos);
+    void *y = base + L.y;
+    void *ffn_ws = base + L.ffn;
+
+    hipError_t e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream);
+    if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
+    if (e == hipSuccess) e = launch_expert_ffn(*s, x, sorted, offsets, *w, y, ffn_ws, stream);
+    if (e == hipSuccess) e = launch_combine(*s, y, pos, gate, out, stream);
+    return hip_status(e);
+}
+
+const char *colibri_moe_status_string(int status) {
+    switch (status) {
+        case COLIBRI_OK: return "ok";
+        case COLIBRI_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, negative T)";
+        case COLIBRI_ERR_WORKSPACE: return "workspace too small";
+        case COLIBRI_ERR_UNSUPPORTED: return "unsupported shape or configuration";
+        case COLIBRI_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

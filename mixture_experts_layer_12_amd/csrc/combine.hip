@@ -1,0 +1,73 @@
+// Combine: gate-weighted sum of each token's two expert outputs, fused with
+// the un-permute from expert-sorted order back to token order.
+//
+// Colibri write-up [nxbn] http://m.nxbn.cn/news/48047 section 3.3 (output
+// aggregation: the expert outputs are summed weighted by their gating scores).
+//
+//   out[t] = g[t,0] * Y[assign_pos[2t]] + g[t,1] * Y[assign_pos[2t+1]]
+//
+// Design: a pure streaming kernel (reads 2 rows, writes 1 row per token).
+// Each thread handles one 16-byte vector of a token row; rows are read with
+// 16-byte loads and the sum is formed in fp32, then rounded once to the
+// storage type.  A slot whose assign_pos is negative (an out-of-range expert
+// index upstream) contributes nothing.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace colibri {
+namespace {
+
+template <typename TE>
+__global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, const int32_t *__restrict__ pos,
+                                                      const float *__restrict__ gate, TE *__restrict__ out, int T,
+                                                      int d) {
+    constexpr int VEC = 16 / sizeof(TE);
+    const int vpr = d / VEC;  // vectors per row
+    const size_t total = (size_t)T * vpr;
+    const int A = 2 * T;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+        const int t = (int)(i / vpr);
+        const int c = (int)(i % vpr) * VEC;
+        const int p0 = pos[2 * t], p1 = pos[2 * t + 1];
+        const float g0 = gate[2 * t], g1 = gate[2 * t + 1];
+        float y0[VEC], y1[VEC];
+        if (p0 >= 0 && p0 < A) Vec16<TE>::load(y + (size_t)p0 * d + c, y0);
+        else
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) y0[q] = 0.0f;
+        if (p1 >= 0 && p1 < A) Vec16<TE>::load(y + (size_t)p1 * d + c, y1);
+        else
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) y1[q] = 0.0f;
+        if constexpr (sizeof(TE) == 4) {
+            f32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = fmaf(g1, y1[q], g0 * y0[q]);
+            *reinterpret_cast<f32x4 *>(out + (size_t)t * d + c) = o;
+        } else {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = pack_bf16x2(fmaf(g1, y1[2 * q], g0 * y0[2 * q]), fmaf(g1, y1[2 * q + 1], g0 * y0[2 * q + 1]));
+            *reinterpret_cast<u32x4 *>(out + (size_t)t * d + c) = o;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, const int32_t *assign_pos,
+                          const float *topk_gate, void *out, hipStream_t st) {
+    const int vec = s.dtype == COLIBRI_F32 ? 4 : 8;
+    const size_t total = (size_t)s.T * (s.d / vec);
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
+    if (s.dtype == COLIBRI_F32)
+        combine_kernel<float><<<blocks, 256, 0, st>>>((const float *)y_sorted, assign_pos, topk_gate, (float *)out,
+                                                      s.T, s.d);
+    else
+        combine_kernel<uint16_t><<<blocks, 256, 0, st>>>((const uint16_t *)y_sorted, assign_pos, topk_gate,
+                                                         (uint16_t *)out, s.T, s.d);
+    return hipGetLastError();
+}
+
+}  // namespace colibri

@@ -1,0 +1,76 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace colibri {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest, ties to even.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element load/store for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float *p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(float *p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t *p, size_t i) { return bf16_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(uint16_t *p, size_t i, float v) {
+        p[i] = (uint16_t)f32_to_bf16_bits(v);
+    }
+};
+
+// 16-byte vector of a row: 4 fp32 or 8 bf16, widened to fp32.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ void load(const float *p, float (&o)[4]) {
+        f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+    }
+};
+template <> struct Vec16<uint16_t> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&o)[8]) {
+        u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { o[2 * i] = bf16_lo(v[i]); o[2 * i + 1] = bf16_hi(v[i]); }
+    }
+};
+
+enum Act { ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2 };
+
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+template <int ACT>
+__device__ __forceinline__ float apply_act(float z) {
+    if (ACT == ACT_RELU) return z > 0.0f ? z : 0.0f;
+    return gelu_erf(z);
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace colibri

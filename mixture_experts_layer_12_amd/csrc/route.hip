@@ -1,0 +1,192 @@
+// Router: logits, deterministic top-2 and gates, one launch.
+//
+// Colibri write-ups: [zskr] http://www.zskr.cn/news/2272131 section 3.2 (logits
+// = input x routing weights, then a fixed-sequence top-k that is
+// deterministic), [hnwysp] https://www.hnwysp.cn/news/30485 section 3.1
+// (softmax over experts, top-k indices strictly descending by score) and 4.3
+// (printed gate pairs sum to one), [rkmt] http://news.rkmt.cn/news/2271114
+// section 3.1 (router bias [E]).
+//
+// Design (gfx950): one wavefront handles TPW = 64 / EP tokens, EP = E rounded
+// up to a power of two.  Each lane streams 16-byte slices of the tokens' rows
+// of X and the matching rows of W_r and accumulates TPW * EP = 64 partial dot
+// products in fp32.  A six-step butterfly reduce-scatter (fixed order, so the
+// result is reproducible) leaves lane l holding the full logit of token
+// l / EP, expert l % EP.  The top-2 is then an argmax over the EP lanes of a
+// token under the total order (logit desc, index asc; NaN below -inf),
+// taken twice with xor-shuffles, which is deterministic by construction.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace colibri {
+namespace {
+
+constexpr int kRouteThreads = 128;  // 2 waves per block
+
+// rank class: 2 = a number, 1 = NaN, 0 = padding lane / already chosen
+__device__ __forceinline__ bool route_beats(int ca, float va, int ia, int cb, float vb, int ib) {
+    if (ca != cb) return ca > cb;
+    if (ca == 2 && va != vb) return va > vb;
+    return ia < ib;
+}
+
+template <int EP>
+__device__ __forceinline__ void segment_argmax(int &c, float &v, int &i) {
+#pragma unroll
+    for (int s = 1; s < EP; s <<= 1) {
+        int oc = __shfl_xor(c, s);
+        float ov = __shfl_xor(v, s);
+        int oi = __shfl_xor(i, s);
+        if (route_beats(oc, ov, oi, c, v, i)) { c = oc; v = ov; i = oi; }
+    }
+}
+
+template <typename TI, int EP, bool FULL>
+__device__ __forceinline__ void load_router_row(const TI *row, int E, float (&wv)[EP]) {
+    if constexpr (FULL && EP * sizeof(TI) >= 16) {
+#pragma unroll
+        for (int q = 0; q < EP; q += Vec16<TI>::N) {
+            float tmp[Vec16<TI>::N];
+            Vec16<TI>::load(row + q, tmp);
+#pragma unroll
+            for (int r = 0; r < Vec16<TI>::N; ++r) wv[q + r] = tmp[r];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EP; ++e) wv[e] = (FULL || e < E) ? Elem<TI>::load(row, e) : 0.0f;
+    }
+}
+
+template <typename TI, int EP, bool FULL>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const TI *__restrict__ x, const TI *__restrict__ w_r,
+                                                              const float *__restrict__ b_r, int T, int d, int E,
+                                                              int32_t *__restrict__ topk_idx,
+                                                              float *__restrict__ topk_gate,
+                                                              float *__restrict__ logits) {
+    constexpr int TPW = kWave / EP;
+    constexpr int VEC = Vec16<TI>::N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = (blockIdx.x * kRouteThreads + threadIdx.x) / kWave;
+    const int t0 = wave * TPW;
+    if (t0 >= T) return;  // uniform per wave
+
+    float acc[TPW * EP];
+#pragma unroll
+    for (int i = 0; i < TPW * EP; ++i) acc[i] = 0.0f;
+
+    for (int j0 = lane * VEC; j0 < d; j0 += kWave * VEC) {
+        if constexpr (EP <= 8) {
+            // few experts: keep the VEC router rows in registers, stream the tokens
+            float wv[VEC][EP];
+#pragma unroll
+            for (int jj = 0; jj < VEC; ++jj) load_router_row<TI, EP, FULL>(w_r + (size_t)(j0 + jj) * E, E, wv[jj]);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                if (t0 + tt >= T) break;
+                float xv[VEC];
+                Vec16<TI>::load(x + (size_t)(t0 + tt) * d + j0, xv);
+#pragma unroll
+                for (int jj = 0; jj < VEC; ++jj)
+#pragma unroll
+                    for (int e = 0; e < EP; ++e) acc[tt * EP + e] += xv[jj] * wv[jj][e];
+            }
+        } else {
+            // many experts: keep the tokens' slices in registers, stream the router rows
+            float xv[TPW][VEC];
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                if (t0 + tt < T) {
+                    Vec16<TI>::load(x + (size_t)(t0 + tt) * d + j0, xv[tt]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) xv[tt][q] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < VEC; ++jj) {
+                float wv[EP];
+                load_router_row<TI, EP, FULL>(w_r + (size_t)(j0 + jj) * E, E, wv);
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                    for (int e = 0; e < EP; ++e) acc[tt * EP + e] += xv[tt][jj] * wv[e];
+            }
+        }
+    }
+
+    // Butterfly reduce-scatter over the 64 lanes: after the step on lane bit b
+    // a lane keeps the half of its values selected by that bit, so at the end
+    // lane l holds the complete sum for value index l.
+#pragma unroll
+    for (int b = 5; b >= 0; --b) {
+        const int half = 1 << b;
+        const bool up = (lane >> b) & 1;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            float send = up ? acc[i] : acc[i + half];
+            float keep = up ? acc[i + half] : acc[i];
+            acc[i] = keep + __shfl_xor(send, half);
+        }
+    }
+
+    const int tt = lane / EP;
+    const int e = lane % EP;
+    const int t = t0 + tt;
+    const bool valid = (e < E) && (t < T);
+    float lg = acc[0];
+    if (b_r != nullptr && e < E) lg += b_r[e];
+    if (valid && logits != nullptr) logits[(size_t)t * E + e] = lg;
+
+    int c1 = valid ? (__builtin_isnan(lg) ? 1 : 2) : 0;
+    float v1 = lg;
+    int i1 = e;
+    segment_argmax<EP>(c1, v1, i1);
+    int c2 = (valid && e != i1) ? (__builtin_isnan(lg) ? 1 : 2) : 0;
+    float v2 = lg;
+    int i2 = e;
+    segment_argmax<EP>(c2, v2, i2);
+
+    if (e == 0 && t < T) {
+        const float g0 = 1.0f / (1.0f + expf(v2 - v1));
+        topk_idx[2 * t] = i1;
+        topk_idx[2 * t + 1] = i2;
+        topk_gate[2 * t] = g0;
+        topk_gate[2 * t + 1] = 1.0f - g0;
+    }
+}
+
+template <typename TI, int EP>
+hipError_t launch_ep(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r, int32_t *idx,
+                     float *gate, float *logits, hipStream_t st) {
+    constexpr int TPW = kWave / EP;
+    const int waves = ceil_div(s.T, TPW);
+    const int blocks = ceil_div(waves, kRouteThreads / kWave);
+    if (s.E == EP)
+        route_kernel<TI, EP, true><<<blocks, kRouteThreads, 0, st>>>(
+            (const TI *)x, (const TI *)w_r, b_r, s.T, s.d, s.E, idx, gate, logits);
+    else
+        route_kernel<TI, EP, false><<<blocks, kRouteThreads, 0, st>>>(
+            (const TI *)x, (const TI *)w_r, b_r, s.T, s.d, s.E, idx, gate, logits);
+    return hipGetLastError();
+}
+
+template <typename TI>
+hipError_t launch_t(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r, int32_t *idx,
+                    float *gate, float *logits, hipStream_t st) {
+    if (s.E <= 2) return launch_ep<TI, 2>(s, x, w_r, b_r, idx, gate, logits, st);
+    if (s.E <= 4) return launch_ep<TI, 4>(s, x, w_r, b_r, idx, gate, logits, st);
+    if (s.E <= 8) return launch_ep<TI, 8>(s, x, w_r, b_r, idx, gate, logits, st);
+    if (s.E <= 16) return launch_ep<TI, 16>(s, x, w_r, b_r, idx, gate, logits, st);
+    if (s.E <= 32) return launch_ep<TI, 32>(s, x, w_r, b_r, idx, gate, logits, st);
+    return launch_ep<TI, 64>(s, x, w_r, b_r, idx, gate, logits, st);
+}
+
+}  // namespace
+
+hipError_t launch_route(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
+                        int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t st) {
+    if (s.dtype == COLIBRI_F32) return launch_t<float>(s, x, w_r, b_r, topk_idx, topk_gate, logits, st);
+    return launch_t<uint16_t>(s, x, w_r, b_r, topk_idx, topk_gate, logits, st);
+}
+
+}  // namespace colibri

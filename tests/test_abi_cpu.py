@@ -1,0 +1,149 @@
+"""C-ABI library: loads, exports what the header declares, and rejects bad
+calls on the host before launching anything (CPU only: no call here reaches a
+kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_12_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "colibri_moe.h")
+
+A16 = 0x7F0000100000  # fake, 256-byte aligned device addresses (never dereferenced)
+
+
+def fake(i):
+    return A16 + i * 0x100000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load(build_if_missing=True)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(colibri_moe_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert moe.status_string(code) != "unknown status"
+    assert moe.status_string(-99) == "unknown status"
+
+
+GOOD = moe.Shape(T=16, d=128, h=256, E=8, dtype=moe.BF16, act=moe.SWIGLU)
+
+
+def shape_c(**kw):
+    base = dict(T=GOOD.T, d=GOOD.d, h=GOOD.h, E=GOOD.E, k=2, dtype=GOOD.dtype, act=GOOD.act)
+    base.update(kw)
+    return moe._Shape(base["T"], base["d"], base["h"], base["E"], base["k"], base["dtype"], base["act"])
+
+
+def route_call(lib, s, x=fake(0), w_r=fake(1), b_r=None, idx=fake(2), gate=fake(3), logits=None):
+    return lib.colibri_moe_route(ctypes.byref(s), x, w_r, b_r, idx, gate, logits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=1), moe.COLIBRI_ERR_UNSUPPORTED), (dict(k=3), moe.COLIBRI_ERR_UNSUPPORTED),
+    (dict(E=1), moe.COLIBRI_ERR_UNSUPPORTED), (dict(E=65), moe.COLIBRI_ERR_UNSUPPORTED),
+    (dict(d=100), moe.COLIBRI_ERR_UNSUPPORTED), (dict(h=32), moe.COLIBRI_ERR_UNSUPPORTED),
+    (dict(d=0), moe.COLIBRI_ERR_UNSUPPORTED), (dict(dtype=7), moe.COLIBRI_ERR_UNSUPPORTED),
+    (dict(act=9), moe.COLIBRI_ERR_UNSUPPORTED), (dict(T=-1), moe.COLIBRI_ERR_INVALID_ARG),
+    (dict(T=(1 << 28) + 1), moe.COLIBRI_ERR_UNSUPPORTED),
+])
+def test_shape_validation(lib, kw, code):
+    s = shape_c(**kw)
+    assert route_call(lib, s) == code
+    assert lib.colibri_moe_workspace_size(ctypes.byref(s)) == 0
+
+
+def test_empty_batch_is_a_no_op(lib):
+    s = shape_c(T=0)
+    # T = 0: success with no work, even with null pointers
+    assert route_call(lib, s, x=None, w_r=None, idx=None, gate=None) == 0
+    e = moe._Experts(None, None, None, None, None)
+    assert lib.colibri_moe_layer_forward(ctypes.byref(s), None, None, None, ctypes.byref(e), None, None, None,
+                                         None, None, 0, None) == 0
+    assert lib.colibri_moe_workspace_size(ctypes.byref(s)) == 0
+
+
+def test_route_pointer_checks(lib):
+    s = shape_c()
+    assert route_call(lib, s, x=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert route_call(lib, s, idx=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert route_call(lib, s, x=fake(0) + 8) == moe.COLIBRI_ERR_INVALID_ARG     # not 16-byte aligned
+    assert route_call(lib, s, b_r=fake(5) + 2) == moe.COLIBRI_ERR_INVALID_ARG   # fp32 bias misaligned
+
+
+def test_dispatch_checks(lib):
+    s = shape_c()
+    args = [fake(0), fake(1), fake(2), fake(3), fake(4)]
+    for i in range(5):
+        a = list(args)
+        a[i] = None
+        assert lib.colibri_moe_dispatch(ctypes.byref(s), *a, None, None, None, 0, None) == moe.COLIBRI_ERR_INVALID_ARG
+    # x without x_sorted (or the reverse) is an error
+    assert lib.colibri_moe_dispatch(ctypes.byref(s), *args, fake(6), None, None, 0, None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert lib.colibri_moe_dispatch(ctypes.byref(s), *args, None, fake(6), None, 0, None) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+def ffn_call(lib, s, e, ws_bytes=1 << 40, ws=fake(9), y=fake(8)):
+    return lib.colibri_moe_expert_ffn(ctypes.byref(s), fake(0), fake(1), fake(2), ctypes.byref(e), y, ws,
+                                      ws_bytes, None)
+
+
+def test_ffn_checks(lib):
+    s = shape_c()
+    sw = moe._Experts(fake(10), fake(11), fake(12), None, None)
+    # workspace too small
+    assert ffn_call(lib, s, sw, ws_bytes=1024) == moe.COLIBRI_ERR_WORKSPACE
+    # SwiGLU needs W3 and takes no biases
+    assert ffn_call(lib, s, moe._Experts(fake(10), None, fake(12), None, None)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert ffn_call(lib, s, moe._Experts(fake(10), fake(11), fake(12), fake(13), None)) == moe.COLIBRI_ERR_UNSUPPORTED
+    # ReLU / GELU take no W3
+    sr = shape_c(act=moe.RELU)
+    assert ffn_call(lib, sr, moe._Experts(fake(10), fake(11), fake(12), None, None)) == moe.COLIBRI_ERR_UNSUPPORTED
+    # misaligned weights / output / workspace
+    assert ffn_call(lib, s, moe._Experts(fake(10) + 4, fake(11), fake(12), None, None)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert ffn_call(lib, s, sw, y=fake(8) + 2) == moe.COLIBRI_ERR_INVALID_ARG
+    assert ffn_call(lib, s, sw, ws=fake(9) + 16) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+def test_layer_checks(lib):
+    s = shape_c()
+    e = moe._Experts(fake(10), fake(11), fake(12), None, None)
+    need = lib.colibri_moe_workspace_size(ctypes.byref(s))
+
+    def call(ws=fake(20), ws_bytes=need, x=fake(0), out=fake(3)):
+        return lib.colibri_moe_layer_forward(ctypes.byref(s), x, fake(1), None, ctypes.byref(e), out, None, None,
+                                             None, ws, ws_bytes, None)
+
+    assert call(ws_bytes=need - 1) == moe.COLIBRI_ERR_WORKSPACE
+    assert call(ws=fake(20) + 128) == moe.COLIBRI_ERR_INVALID_ARG  # layer workspace must be 256-byte aligned
+    assert call(x=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(out=fake(3) + 8) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+def test_workspace_size_covers_buffers(lib):
+    for dt, el in ((moe.F32, 4), (moe.BF16, 2)):
+        prev = 0
+        for T in (1, 7, 64, 4096):
+            s = shape_c(T=T, dtype=dt)
+            ws = lib.colibri_moe_workspace_size(ctypes.byref(s))
+            # at least H [2T, h] and Y [2T, d] plus the routing arrays
+            assert ws >= 2 * T * (GOOD.h + GOOD.d) * el + 4 * (2 * T) * 4
+            assert ws % 256 == 0 and ws > prev
+            prev = ws

@@ -1,0 +1,388 @@
+"""GPU parity: every C-ABI entry point and the whole layer against the fp64
+oracle on seeded inputs.
+
+Bar (per the method's reading):
+  * expert indices, counts, offsets and the dispatch permutation: bit-exact,
+    except that tokens whose oracle logit margin (1st/2nd or 2nd/3rd) is below
+    1e-6 are counted, reported and exempt from the index comparison only;
+    the oracle's top-2 of the GPU's own fp32 logits must equal the GPU's
+    indices, and the oracle's dispatch of the GPU's indices must equal the
+    GPU's dispatch, with no exemption;
+  * fp32 values: max relative error <= 1e-4 (floor 1e-3 * max |ref|);
+  * bf16 values: |a - b| <= 1e-2 + 2e-2 |b| for every element.
+"""
+import numpy as np
+import pytest
+
+import gen
+import mixture_experts_layer_12_amd as moe
+import oracle
+from tests import gpu_util as G
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    return moe.load(build_if_missing=True)
+
+
+# ------------------------------------------------------------------ router
+def run_route(layer):
+    sh = layer.shape
+    x = G.dev(layer.x)
+    idx = G.empty((sh.T, 2), torch.int32)
+    gate = G.empty((sh.T, 2), torch.float32)
+    lg = G.empty((sh.T, sh.E), torch.float32)
+    r = G.device_router(layer.key)
+    moe.route(sh, x, r["w_r"], r["b_r"], idx, gate, lg)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), gate.cpu().numpy(), lg.cpu().numpy()
+
+
+def check_route(layer, idx, gate, lg_gpu, tag):
+    w = G.host_router(layer.key)
+    lg_ref = oracle.logits(layer.x, w["w_r"], w["b_r"])
+    G.assert_fp32_close(lg_gpu, lg_ref, f"{tag} logits")
+    # the GPU's selection is exactly the oracle's top-2 of the GPU's own logits
+    assert np.array_equal(oracle.top2(lg_gpu.astype(np.float64)), idx), f"{tag}: top-2 of own logits"
+    idx_ref = oracle.top2(lg_ref)
+    near = G.near_tie_mask(lg_ref)
+    diff = np.any(idx != idx_ref, axis=1)
+    assert not np.any(diff & ~near), f"{tag}: {int((diff & ~near).sum())} non-near-tie tokens routed differently"
+    # gates: fp32 rule against the oracle's gates for the GPU's chosen pair
+    g_ref = oracle.gates(lg_ref, idx)
+    G.assert_fp32_close(gate, g_ref, f"{tag} gates")
+    assert np.all(gate[:, 0] + gate[:, 1] == np.float32(1.0)), f"{tag}: gates must sum to exactly 1 in fp32"
+    assert np.all(gate[:, 0] >= 0.5)
+    G.report({"check": "route", "case": tag, "tokens": int(layer.T), "near_tie_tokens": int(near.sum()),
+              "index_mismatches_on_near_ties": int(diff.sum())})
+
+
+ROUTE_CASES = [("tiny", 32), ("e8", 1), ("e8", 64), ("e8", 512), ("mixtral_decode", 1), ("mixtral_decode", 4),
+               ("mixtral_decode", 16), ("mixtral_decode", 32), ("mixtral_prefill", 4096), ("skew16", 8192)]
+
+
+@pytest.mark.parametrize("key,T", ROUTE_CASES, ids=[f"{k}-T{t}" for k, t in ROUTE_CASES])
+def test_route_parity(key, T):
+    layer = G.seeded_layer(key, T)
+    idx, gate, lg = run_route(layer)
+    check_route(layer, idx, gate, lg, f"{key}/T={T}")
+
+
+@pytest.mark.parametrize("E", [2, 3, 5, 16, 33, 64])
+@pytest.mark.parametrize("dt", [gen.F32, gen.BF16])
+def test_route_expert_counts_and_ties(E, dt):
+    """Every padded expert width, ragged token counts, and exact ties."""
+    rng = np.random.default_rng(E * 10 + dt)
+    T, d = 77, 192
+    x = rng.integers(-2, 3, size=(T, d)).astype(np.float32)       # integer data: exact sums, many ties
+    w_r = rng.integers(-1, 2, size=(d, E)).astype(np.float32)
+    x[5] = 0.0                                                      # all-zero token: every logit ties
+    if dt == gen.BF16:
+        x, w_r = gen.f32_to_bf16_bits(x), gen.f32_to_bf16_bits(w_r)
+    sh = moe.Shape(T, d, 64, E, dt, moe.RELU)
+    idx = G.empty((T, 2), torch.int32)
+    gate = G.empty((T, 2), torch.float32)
+    lg = G.empty((T, E), torch.float32)
+    moe.route(sh, G.dev(x), G.dev(w_r), None, idx, gate, lg)
+    torch.cuda.synchronize()
+    idx, gate, lg = idx.cpu().numpy(), gate.cpu().numpy(), lg.cpu().numpy()
+    lg_ref = oracle.logits(x, w_r)
+    assert np.array_equal(lg.astype(np.float64), lg_ref)           # integer sums are exact in fp32
+    assert np.array_equal(idx, oracle.top2(lg_ref))                # ties resolved to the lower index
+    assert tuple(idx[5]) == (0, 1) and gate[5].tolist() == [0.5, 0.5]
+    G.assert_fp32_close(gate, oracle.gates(lg_ref, idx), f"gates E={E}")
+
+
+def test_route_bias_and_nan_ranking():
+    T, d, E = 8, 64, 6
+    x = np.zeros((T, d), np.float32)
+    w_r = np.zeros((d, E), np.float32)
+    b_r = np.array([0.5, 2.0, -1.0, 2.0, 1.0, -np.inf], np.float32)
+    sh = moe.Shape(T, d, 64, E, gen.F32, moe.RELU)
+    idx = G.empty((T, 2), torch.int32)
+    gate = G.empty((T, 2), torch.float32)
+    moe.route(sh, G.dev(x), G.dev(w_r), G.dev(b_r), idx, gate)
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy().tolist() == [[1, 3]] * T               # bias only; tie 2.0/2.0 -> lower index first
+    b_r[1] = np.nan
+    moe.route(sh, G.dev(x), G.dev(w_r), G.dev(b_r), idx, gate)
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy().tolist() == [[3, 4]] * T               # NaN ranks below every number
+
+
+# ------------------------------------------------------------------ dispatch
+def run_dispatch(idx: np.ndarray, E: int, x=None, dt=gen.BF16):
+    T = idx.shape[0]
+    sh = moe.Shape(T, 64 if x is None else x.shape[1], 64, E, dt, moe.RELU)
+    counts = G.empty((E,), torch.int32)
+    offsets = G.empty((E + 1,), torch.int32)
+    sa = G.empty((2 * T,), torch.int32)
+    ap = G.empty((2 * T,), torch.int32)
+    xd = G.dev(x) if x is not None else None
+    xs = G.empty((2 * T, x.shape[1]), G.tdtype(dt)) if x is not None else None
+    moe.dispatch(sh, G.dev(idx.astype(np.int32)), counts, offsets, sa, ap, xd, xs)
+    torch.cuda.synchronize()
+    r = {"counts": counts.cpu().numpy(), "offsets": offsets.cpu().numpy(), "sorted_assign": sa.cpu().numpy(),
+         "assign_pos": ap.cpu().numpy()}
+    if xs is not None:
+        r["x_sorted"] = G.host(xs)
+    return r
+
+
+def _pairs(rng, T, E, p=None):
+    a = rng.choice(E, size=T, p=p)
+    b = (a + rng.integers(1, E, size=T)) % E
+    return np.stack([a, b], 1).astype(np.int32)
+
+
+DISPATCH_CASES = [(1, 8), (31, 4), (32, 4), (33, 4), (1000, 8), (4096, 8), (8192, 16), (50000, 64), (3, 2),
+                  (70001, 16)]
+
+
+@pytest.mark.parametrize("T,E", DISPATCH_CASES, ids=[f"T{t}-E{e}" for t, e in DISPATCH_CASES])
+def test_dispatch_bit_exact(T, E):
+    rng = np.random.default_rng(T + E)
+    idx = _pairs(rng, T, E)
+    r = run_dispatch(idx, E)
+    ref = oracle.dispatch(idx, E)
+    for k in ("counts", "offsets", "sorted_assign", "assign_pos"):
+        assert np.array_equal(r[k], ref[k]), k
+
+
+def test_dispatch_degenerate_routings():
+    # every token to the same pair (other experts empty), and a Zipf-like skew
+    for idx, E in ((np.tile([[6, 1]], (5000, 1)).astype(np.int32), 8),
+                   (np.tile([[0, 63]], (129, 1)).astype(np.int32), 64),
+                   (_pairs(np.random.default_rng(9), 20000, 16,
+                           p=(np.arange(1, 17) ** -1.2) / (np.arange(1, 17) ** -1.2).sum()), 16)):
+        r = run_dispatch(idx, E)
+        ref = oracle.dispatch(idx, E)
+        for k in ("counts", "offsets", "sorted_assign", "assign_pos"):
+            assert np.array_equal(r[k], ref[k]), k
+
+
+def test_dispatch_row_gather():
+    rng = np.random.default_rng(3)
+    T, E, d = 300, 8, 192
+    idx = _pairs(rng, T, E)
+    x = gen.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    r = run_dispatch(idx, E, x=x)
+    xf = gen.bf16_bits_to_f32(x)
+    assert np.array_equal(r["x_sorted"], xf[r["sorted_assign"] // 2])
+
+
+def test_dispatch_skips_out_of_range_indices():
+    idx = np.array([[1, 2], [9, 0], [1, -3], [3, 3]], np.int32)   # 9 and -3 are outside [0, 4)
+    r = run_dispatch(idx, 4)
+    valid = (idx.reshape(-1) >= 0) & (idx.reshape(-1) < 4)
+    assert r["counts"].tolist() == np.bincount(idx.reshape(-1)[valid], minlength=4).tolist()
+    assert r["offsets"][-1] == valid.sum()
+    assert np.all(r["assign_pos"][~valid] == -1)
+    assert np.all(r["sorted_assign"][valid.sum():] == -1)
+    order = np.flatnonzero(valid)[np.argsort(idx.reshape(-1)[valid], kind="stable")]
+    assert np.array_equal(r["sorted_assign"][:valid.sum()], order)
+
+
+# ------------------------------------------------------------------ expert FFN
+def small_ffn_case(act, dt, T=300, E=8, d=256, h=384, skew=None, seed=0):
+    rng = np.random.default_rng(seed)
+    cvt = (lambda a: a) if dt == gen.F32 else gen.f32_to_bf16_bits
+    f = lambda s, sc: cvt((rng.standard_normal(s) * sc).astype(np.float32))
+    w = {"x": f((T, d), 1.0), "w1": f((E, d, h), d ** -0.5), "w2": f((E, h, d), h ** -0.5),
+         "w3": f((E, d, h), d ** -0.5) if act == "swiglu" else None,
+         "b1": f((E, h), 0.1) if act != "swiglu" else None, "b2": f((E, d), 0.1) if act != "swiglu" else None}
+    idx = _pairs(rng, T, E, p=skew)
+    return w, idx
+
+
+def run_ffn(w, idx, act, dt, E, gather=True):
+    T, d = w["x"].shape
+    h = w["w1"].shape[2]
+    ref = oracle.dispatch(idx, E)
+    sh = moe.Shape(T, d, h, E, dt, moe.ACT_CODES[act])
+    ws_bytes = moe.workspace_size(sh)
+    ws = G.empty((ws_bytes,), torch.uint8)
+    y = G.empty((2 * T, d), G.tdtype(dt))
+    if gather:
+        x_rows, sa = G.dev(w["x"]), G.dev(ref["sorted_assign"])
+    else:
+        x_rows, sa = G.dev(np.ascontiguousarray(w["x"][ref["sorted_assign"] // 2])), None
+    moe.expert_ffn(sh, x_rows, sa, G.dev(ref["offsets"]), G.dev(w["w1"]), G.dev(w["w2"]), y, ws, ws_bytes,
+                   w3=G.dev(w["w3"]), b1=G.dev(w["b1"]), b2=G.dev(w["b2"]))
+    torch.cuda.synchronize()
+    rows_t = ref["sorted_assign"] // 2
+    rows_e = idx.reshape(-1)[ref["sorted_assign"]]
+    y_ref = oracle.ffn_rows(w["x"], rows_t, rows_e, w["w1"], w["w2"], act, w3=w["w3"], b1=w["b1"], b2=w["b2"],
+                            mirror=True)
+    return G.host(y), y_ref
+
+
+FFN_CASES = [(a, dt) for a in ("relu", "gelu", "swiglu") for dt in (gen.F32, gen.BF16)]
+
+
+@pytest.mark.parametrize("act,dt", FFN_CASES, ids=[f"{a}-{'f32' if d == 0 else 'bf16'}" for a, d in FFN_CASES])
+def test_ffn_parity_small(act, dt):
+    w, idx = small_ffn_case(act, dt)
+    y, y_ref = run_ffn(w, idx, act, dt, E=8)
+    G.assert_close(y, y_ref, dt, f"y_sorted {act}")
+
+
+@pytest.mark.parametrize("dt", [gen.F32, gen.BF16])
+def test_ffn_ragged_columns_and_presorted_rows(dt):
+    # h = 320 and d = 192: column counts that are not multiples of 128
+    w, idx = small_ffn_case("gelu", dt, T=173, E=5, d=192, h=320, seed=4)
+    for gather in (True, False):
+        y, y_ref = run_ffn(w, idx, "gelu", dt, E=5, gather=gather)
+        G.assert_close(y, y_ref, dt, f"y_sorted gather={gather}")
+
+
+def test_ffn_degenerate_routings():
+    E = 8
+    for seed, skew in ((1, [0.93] + [0.01] * 7), (2, [0.5, 0.5, 0, 0, 0, 0, 0, 0])):
+        w, idx = small_ffn_case("swiglu", gen.BF16, T=257, E=E, seed=seed, skew=skew)
+        if seed == 2:
+            idx[:, 1] = 1 - idx[:, 0]     # only experts 0 and 1 used; 6 empty experts
+        y, y_ref = run_ffn(w, idx, "swiglu", gen.BF16, E=E)
+        G.assert_bf16_close(y, y_ref, f"degenerate routing {seed}")
+
+
+def test_ffn_small_integers_bit_exact():
+    """bf16 ReLU path with small-integer operands: every MFMA product and fp32
+    sum is exact, so y must equal the oracle bit for bit (tests tiling and
+    indexing with no rounding noise)."""
+    rng = np.random.default_rng(11)
+    T, E, d, h = 200, 4, 256, 192
+    ints = lambda s, lo, hi: gen.f32_to_bf16_bits(rng.integers(lo, hi + 1, size=s).astype(np.float32))
+    w = {"x": ints((T, d), -3, 3), "w1": ints((E, d, h), -2, 2), "w2": ints((E, h, d), -2, 2), "w3": None,
+         "b1": ints((E, h), -4, 4), "b2": ints((E, d), -4, 4)}
+    idx = _pairs(rng, T, E)
+    y, y_ref = run_ffn(w, idx, "relu", gen.BF16, E=E)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+# ------------------------------------------------------------------ combine
+@pytest.mark.parametrize("dt", [gen.F32, gen.BF16])
+def test_combine_parity(dt):
+    rng = np.random.default_rng(5)
+    T, d = 333, 448
+    ap = rng.permutation(2 * T).astype(np.int32)
+    g0 = rng.uniform(0.5, 1.0, T).astype(np.float32)
+    gate = np.stack([g0, np.float32(1) - g0], 1)
+    yf = rng.standard_normal((2 * T, d)).astype(np.float32)
+    y = yf if dt == gen.F32 else gen.f32_to_bf16_bits(yf)
+    sh = moe.Shape(T, d, 64, 4, dt, moe.RELU)
+    out = G.empty((T, d), G.tdtype(dt))
+    moe.combine(sh, G.dev(y), G.dev(ap), G.dev(gate), out)
+    torch.cuda.synchronize()
+    y64 = yf.astype(np.float64) if dt == gen.F32 else gen.bf16_bits_to_f32(y).astype(np.float64)
+    ref = oracle.combine(y64, ap, gate.astype(np.float64), dt)
+    G.assert_close(G.host(out), ref, dt, "combine")
+
+
+# ------------------------------------------------------------------ whole layer
+def run_layer(layer, stream=None):
+    sh = layer.shape
+    ws_bytes = moe.workspace_size(sh)
+    ws = G.empty((ws_bytes,), torch.uint8)
+    out = G.empty((sh.T, sh.d), G.tdtype(sh.dtype))
+    idx = G.empty((sh.T, 2), torch.int32)
+    gate = G.empty((sh.T, 2), torch.float32)
+    counts = G.empty((sh.E,), torch.int32)
+    dw = layer.dw
+    moe.layer_forward(sh, G.dev(layer.x), dw["w_r"], dw["b_r"], dw["w1"], dw["w2"], out, ws, ws_bytes, w3=dw["w3"],
+                      b1=dw["b1"], b2=dw["b2"], topk_idx=idx, topk_gate=gate, counts=counts, stream=stream)
+    torch.cuda.synchronize()
+    return {"out": out, "idx": idx.cpu().numpy(), "gate": gate.cpu().numpy(), "counts": counts.cpu().numpy()}
+
+
+LAYER_CASES = [("tiny", 32, None), ("e8", 1, None), ("e8", 64, None), ("e8", 512, 48), ("mixtral_decode", 1, None),
+               ("mixtral_decode", 4, None), ("mixtral_decode", 16, 6), ("mixtral_decode", 32, 6),
+               ("mixtral_prefill", 4096, 12), ("skew16", 8192, 48)]
+
+
+@pytest.mark.parametrize("key,T,sample", LAYER_CASES, ids=[f"{k}-T{t}" for k, t, _ in LAYER_CASES])
+def test_layer_parity(key, T, sample):
+    layer = G.seeded_layer(key, T)
+    r = run_layer(layer)
+    w = layer.hw
+    # routing over all tokens
+    lg_ref = oracle.logits(layer.x, w["w_r"], w["b_r"])
+    idx_ref = oracle.top2(lg_ref)
+    near = G.near_tie_mask(lg_ref)
+    diff = np.any(r["idx"] != idx_ref, axis=1)
+    assert not np.any(diff & ~near), f"{int((diff & ~near).sum())} non-near-tie tokens routed differently"
+    assert np.array_equal(r["counts"], oracle.dispatch(r["idx"], layer.cfg.E)["counts"])
+    assert r["counts"].sum() == 2 * T
+    assert np.all(r["gate"].sum(1) == np.float32(1.0))
+    out = G.host(r["out"])
+    assert np.all(np.isfinite(out))
+    # outputs: every token at small sizes, a seeded sample at large ones, plus every exempt token
+    rng = np.random.default_rng(T)
+    toks = np.arange(T) if sample is None else np.sort(rng.choice(T, size=sample, replace=False))
+    toks = np.union1d(toks, np.flatnonzero(diff))
+    ref = layer.oracle_tokens(toks, idx_override=r["idx"][toks])
+    assert np.array_equal(ref["idx"], r["idx"][toks])
+    G.assert_close(out[toks], ref["out"], layer.cfg.dtype, f"{key}/T={T} out")
+    G.report({"check": "layer", "case": f"{key}/T={T}", "tokens_compared": int(len(toks)),
+              "near_tie_tokens": int(near.sum()), "index_mismatches_on_near_ties": int(diff.sum()),
+              "counts": r["counts"].tolist()})
+
+
+def test_layer_equals_composed_entry_points():
+    layer = G.seeded_layer("e8", 64)
+    r = run_layer(layer)
+    sh = layer.shape
+    idx, gate, _ = run_route(layer)
+    d = run_dispatch(idx, sh.E)
+    ws_bytes = moe.workspace_size(sh)
+    ws = G.empty((ws_bytes,), torch.uint8)
+    y = G.empty((2 * sh.T, sh.d), torch.bfloat16)
+    dw = layer.dw
+    moe.expert_ffn(sh, G.dev(layer.x), G.dev(d["sorted_assign"]), G.dev(d["offsets"]), dw["w1"], dw["w2"], y, ws,
+                   ws_bytes, b1=dw["b1"], b2=dw["b2"])
+    out = G.empty((sh.T, sh.d), torch.bfloat16)
+    moe.combine(sh, y, G.dev(d["assign_pos"]), G.dev(gate), out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, r["out"])
+
+
+def test_layer_deterministic_and_stream():
+    layer = G.seeded_layer("e8", 512)
+    a = run_layer(layer)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_layer(layer, stream=s)
+    assert torch.equal(a["out"], b["out"]) and np.array_equal(a["idx"], b["idx"])
+
+
+@pytest.mark.parametrize("E,d,h,act,dt", [(2, 64, 64, "relu", gen.F32), (64, 128, 192, "swiglu", gen.BF16),
+                                          (3, 64, 128, "gelu", gen.BF16), (64, 64, 64, "gelu", gen.F32)])
+def test_layer_shape_edges(E, d, h, act, dt):
+    """Smallest and largest expert counts and dims, T = 1 and ragged T."""
+    rng = np.random.default_rng(E + d + h)
+    cvt = (lambda a: a) if dt == gen.F32 else gen.f32_to_bf16_bits
+    f = lambda s, sc: cvt((rng.standard_normal(s) * sc).astype(np.float32))
+    for T in (1, 2, 97):
+        x, w_r = f((T, d), 1.0), f((d, E), d ** -0.5)
+        w = {"w1": f((E, d, h), d ** -0.5), "w2": f((E, h, d), h ** -0.5),
+             "w3": f((E, d, h), d ** -0.5) if act == "swiglu" else None,
+             "b1": f((E, h), 0.1) if act != "swiglu" else None, "b2": f((E, d), 0.1) if act != "swiglu" else None}
+        sh = moe.Shape(T, d, h, E, dt, moe.ACT_CODES[act])
+        ws_bytes = moe.workspace_size(sh)
+        ws = G.empty((ws_bytes,), torch.uint8)
+        out = G.empty((T, d), G.tdtype(dt))
+        idx = G.empty((T, 2), torch.int32)
+        moe.layer_forward(sh, G.dev(x), G.dev(w_r), None, G.dev(w["w1"]), G.dev(w["w2"]), out, ws, ws_bytes,
+                          w3=G.dev(w["w3"]), b1=G.dev(w["b1"]), b2=G.dev(w["b2"]), topk_idx=idx)
+        torch.cuda.synchronize()
+        gi = idx.cpu().numpy()
+        ref = oracle.layer_tokens(x, w_r, w["w1"], w["w2"], act, np.arange(T), w3=w["w3"], b1=w["b1"], b2=w["b2"],
+                                  idx_override=gi)
+        lg = ref["logits"]
+        near = G.near_tie_mask(lg)
+        assert not np.any(np.any(gi != oracle.top2(lg), axis=1) & ~near)
+        G.assert_close(G.host(out), ref["out"], dt, f"E={E} d={d} h={h} T={T}")
