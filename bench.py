@@ -5,13 +5,17 @@ Default workload: the 8-expert 1.3B-class layer (E=8, d=2048, h=5632, GELU
 experts with biases, bf16 storage, fp32 accumulation) on a T=512-token batch;
 one step = one colibri_moe_layer_forward (route, dispatch, grouped expert FFN,
 combine) over the batch.  Inputs are seeded synthetic tensors already resident
-in HBM.  Expert weights rotate over enough identical copies (>= 2 GB) that the
+in HBM; expert weights rotate over enough identical copies (>= 2 GB) that the
 256 MB MALL cannot serve them from cache.
 
-Prints one JSON line: whole-layer tokens/s plus the FFN stage's roofline
-fraction (HIP events around the stage on the stream it runs on), decode
-microseconds per step at T=1 and T=64, and the fp64 CPU oracle timed on the
-host cores as a baseline.
+Timing is GPU time from HIP events on the stream the kernels run on.  Before
+each timed region a spin kernel keeps the GPU busy while the host enqueues
+the work, so host launch latency does not show up as GPU idle time inside the
+region (decode steps are also reported host-inclusive, back to back).
+
+Prints one JSON line: whole-layer tokens/s, the roofline fraction of the
+dominant kernel, every kernel's time and fraction, decode microseconds per
+step at T=1 and T=64, and the fp64 CPU oracle timed on the host cores.
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+SLEEP_CYCLES = 3_000_000     # spin kernel in front of a timed region (~1.5 ms)
 
 
 def log(msg):
@@ -41,7 +46,7 @@ def parse():
     ap.add_argument("--config", default="e8", help="workload key in gen.CONFIGS")
     ap.add_argument("--T", type=int, default=None, help="tokens per step (default: the config's largest T)")
     ap.add_argument("--rotate-gb", type=float, default=2.0, help="total bytes of rotated weight copies")
-    ap.add_argument("--decode-T", default="1,64", help="extra decode batch sizes timed (comma list, '' = none)")
+    ap.add_argument("--decode-T", default="1,64", help="decode batch sizes also timed (comma list, '' = none)")
     ap.add_argument("--decode-iters", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
@@ -68,6 +73,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    can_sleep = hasattr(torch.cuda, "_sleep")
+
+    def prefill_queue():
+        if can_sleep:
+            torch.cuda._sleep(SLEEP_CYCLES)
 
     def to_dev(a):
         if a is None:
@@ -84,18 +94,21 @@ def main():
     b_r_np = gen.router_bias(cfg)
     log(f"generated inputs in {time.time() - t0:.1f}s")
     dw0 = {k: to_dev(v) for k, v in hw.items()}
+    del hw
     x = to_dev(x_np)
     w_r = to_dev(w_r_np)
     b_r = to_dev(b_r_np)
     el = 4 if cfg.dtype == gen.F32 else 2
     per_expert = {k: (v[0].numel() * el if v is not None else 0) for k, v in dw0.items()}
+    up_bytes_e = per_expert["w1"] + per_expert["w3"] + per_expert["b1"]
+    down_bytes_e = per_expert["w2"] + per_expert["b2"]
     layer_w_bytes = sum(v.numel() * el for v in dw0.values() if v is not None)
     R = max(1, math.ceil(args.rotate_gb * 1e9 / layer_w_bytes))
     copies = [dw0] + [{k: (v.clone() if v is not None else None) for k, v in dw0.items()} for _ in range(R - 1)]
-    del hw
     log(f"{R} weight copies x {layer_w_bytes / 1e6:.1f} MB")
 
     act = gen.ACT_CODE[cfg.act]
+    m = 2 if cfg.act == "swiglu" else 1
     sh = moe.Shape(T, cfg.d, cfg.h, cfg.E, cfg.dtype, act)
     ws_bytes = moe.workspace_size(sh)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -108,12 +121,13 @@ def main():
         moe.layer_forward(s, xx, w_r, b_r, w["w1"], w["w2"], o, ws, ws_bytes, w3=w["w3"], b1=w["b1"], b2=w["b2"],
                           counts=counts)
 
-    # ---------------------------------------------------------------- whole layer
+    # ---------------------------------------------------------------- whole layer (the timed region)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    prefill_queue()
     ev0.record(stream)
     for i in range(args.steps):
         step(i)
@@ -125,56 +139,68 @@ def main():
     hit = int((cnt > 0).sum())
     log(f"layer: {ms_per_step * 1e3:.1f} us/step, {tok_s / 1e6:.3f} M tokens/s, experts hit {hit}/{cfg.E}")
 
-    # ---------------------------------------------------------------- per-stage loop
+    # ---------------------------------------------------------------- per-kernel durations (same workload)
     A = 2 * T
     idx = torch.empty((T, 2), dtype=torch.int32, device=dev)
     gate = torch.empty((T, 2), dtype=torch.float32, device=dev)
     offs = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
     sa = torch.empty(A, dtype=torch.int32, device=dev)
     ap_ = torch.empty(A, dtype=torch.int32, device=dev)
+    H = torch.empty((A, cfg.h), dtype=tdt, device=dev)
     y = torch.empty((A, cfg.d), dtype=tdt, device=dev)
-    n_ev = 5
-    stage_ms = np.zeros(4)
+    names = ("route", "dispatch", "ffn_up", "ffn_down", "combine")
+    kern_ms = np.zeros(len(names))
     iters = max(args.steps, 20)
     for it in range(args.warmup + iters):
         w = copies[it % R]
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        prefill_queue()
         evs[0].record(stream)
         moe.route(sh, x, w_r, b_r, idx, gate)
         evs[1].record(stream)
         moe.dispatch(sh, idx, counts, offs, sa, ap_)
         evs[2].record(stream)
-        moe.expert_ffn(sh, x, sa, offs, w["w1"], w["w2"], y, ws, ws_bytes, w3=w["w3"], b1=w["b1"], b2=w["b2"])
+        moe.expert_ffn_up(sh, x, sa, offs, w["w1"], H, ws, ws_bytes, w3=w["w3"], b1=w["b1"])
         evs[3].record(stream)
-        moe.combine(sh, y, ap_, gate, out)
+        moe.expert_ffn_down(sh, H, offs, w["w2"], y, ws, ws_bytes, b2=w["b2"])
         evs[4].record(stream)
+        moe.combine(sh, y, ap_, gate, out)
+        evs[5].record(stream)
         torch.cuda.synchronize()
         if it >= args.warmup:
-            stage_ms += np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(4)])
-    stage_ms /= iters
-    stages_us = dict(zip(("route", "dispatch", "expert_ffn", "combine"), (stage_ms * 1e3).round(2).tolist()))
-    log(f"stages (us): {stages_us}")
+            kern_ms += np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(len(names))])
+    kern_ms /= iters
 
-    # algorithmic work (SURVEY-style accounting: weights of hit experts once, X in, Y out)
-    m = 2 if cfg.act == "swiglu" else 1
-    hit_w = hit * sum(per_expert.values())
-    ffn_bytes = hit_w + T * cfg.d * el + A * cfg.d * el
-    ffn_flops = 2.0 * A * cfg.d * cfg.h * (m + 1)
-    ffn_s = stage_ms[2] * 1e-3
-    ffn_gbs = ffn_bytes / ffn_s / 1e9
-    ffn_tfs = ffn_flops / ffn_s / 1e12
-    ai = ffn_flops / ffn_bytes
+    # algorithmic work per launch: weights of the experts hit, read once; each
+    # kernel's own inputs read once and outputs written once
+    s_ = el
+    work = {
+        "route": (T * cfg.d * s_ + cfg.d * cfg.E * s_ + T * 16, 2.0 * T * cfg.d * cfg.E),
+        "dispatch": (A * 4 + (cfg.E * 2 + 1) * 4 + A * 8, 0.0),
+        "ffn_up": (hit * up_bytes_e + T * cfg.d * s_ + A * cfg.h * s_, 2.0 * A * cfg.d * cfg.h * m),
+        "ffn_down": (hit * down_bytes_e + A * cfg.h * s_ + A * cfg.d * s_, 2.0 * A * cfg.h * cfg.d),
+        "combine": (A * cfg.d * s_ + T * cfg.d * s_ + A * 4 + A * 4, 3.0 * T * cfg.d),
+    }
     ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if ai < ridge:
-        roof = {"bound": "hbm", "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ffn_gbs / HBM_PEAK_GBS, 4)}
+    kernels = {}
+    for nme, ms_ in zip(names, kern_ms):
+        byt, flp = work[nme]
+        sec = ms_ * 1e-3
+        kernels[nme] = {"us": round(ms_ * 1e3, 2), "GB_s": round(byt / sec / 1e9, 1),
+                        "TFLOP_s": round(flp / sec / 1e12, 2), "hbm_frac": round(byt / sec / 1e9 / HBM_PEAK_GBS, 4),
+                        "mfma_frac": round(flp / sec / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+                        "bytes": int(byt), "flops": flp}
+    log(f"kernels: {json.dumps(kernels)}")
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    byt, flp = work[dom]
+    sec = kernels[dom]["us"] * 1e-6
+    if flp / byt < ridge:
+        roof = {"bound": "hbm", "achieved": round(byt / sec / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": round(ffn_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(ffn_tfs / MFMA_BF16_PEAK_TFS, 4)}
-    roof.update({"traffic": None, "kernel": "expert_ffn (gemm1 + gemm2 launches)",
-                 "algorithmic_bytes_per_launch": int(ffn_bytes), "algorithmic_flops_per_launch": ffn_flops,
-                 "avg_launch_us": round(ffn_s * 1e6, 2), "mfma_frac": round(ffn_tfs / MFMA_BF16_PEAK_TFS, 4),
-                 "hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4)})
+        roof = {"bound": "mfma", "achieved": round(flp / sec / 1e12, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof.update({"traffic": None, "kernel": dom, "avg_launch_us": kernels[dom]["us"],
+                 "algorithmic_bytes_per_launch": int(byt), "algorithmic_flops_per_launch": flp})
 
     # ---------------------------------------------------------------- decode sizes
     decode = {}
@@ -182,25 +208,37 @@ def main():
         if tok > T:
             continue
         s2 = sh.with_T(tok)
-        xd = x[:tok]
-        od = out[:tok]
+        xd, od = x[:tok], out[:tok]
         times = []
         for it in range(20 + args.decode_iters):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
+            if it % 10 == 0:
+                prefill_queue()
             e0.record(stream)
             step(it, xx=xd, s=s2, o=od)
             e1.record(stream)
-            torch.cuda.synchronize()
+            if it % 10 == 9:
+                torch.cuda.synchronize()
             if it >= 20:
-                times.append(e0.elapsed_time(e1) * 1e3)
+                times.append((e0, e1))
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in times])
+        # host-inclusive: back-to-back steps, no spin kernel in front
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for it in range(args.decode_iters):
+            step(it, xx=xd, s=s2, o=od)
+        torch.cuda.synchronize()
+        host_us = (time.perf_counter() - h0) / args.decode_iters * 1e6
         c2 = counts.cpu().numpy()
         hit2 = int((c2 > 0).sum())
-        byt = hit2 * sum(per_expert.values()) + tok * cfg.d * el * 2 + cfg.d * cfg.E * el
-        med = float(np.median(times))
-        decode[f"T={tok}"] = {"us_per_step_median": round(med, 2), "us_min": round(float(np.min(times)), 2),
-                              "us_p90": round(float(np.percentile(times, 90)), 2), "experts_hit": hit2,
-                              "hbm_frac": round(byt / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        byt2 = hit2 * (up_bytes_e + down_bytes_e) + tok * cfg.d * s_ * 2 + cfg.d * cfg.E * s_
+        med = float(np.median(us))
+        decode[f"T={tok}"] = {"us_per_step_median": round(med, 2), "us_min": round(float(us.min()), 2),
+                              "us_p90": round(float(np.percentile(us, 90)), 2),
+                              "us_per_step_host_inclusive": round(host_us, 2), "experts_hit": hit2,
+                              "hbm_frac": round(byt2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"decode T={tok}: {decode[f'T={tok}']}")
 
     # ---------------------------------------------------------------- CPU oracle baseline
@@ -216,8 +254,8 @@ def main():
         el_s = time.perf_counter() - c0
         cpu = {"value": round(len(toks) / el_s, 2), "unit": "tokens/s", "cores": oracle.max_threads(),
                "kind": "oracle", "seconds": round(el_s, 2),
-               "sample": f"{len(toks)} of the {T} tokens of the timed batch, whole layer (fp64 logits, top-2, gates, "
-                         f"two expert FFN rows per token, combine)"}
+               "sample": f"{len(toks)} of the {T} tokens of the timed batch, whole layer (fp64 logits, top-2, "
+                         f"gates, two expert FFN rows per token, combine)"}
         log(f"cpu oracle: {cpu}")
 
     rec = {
@@ -226,8 +264,10 @@ def main():
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == gen.BF16 else "f32", "data": "synthetic (seeded Philox normals)",
         "config": {"workload": f"{cfg.title}: E={cfg.E}, top-2, d={cfg.d}, h={cfg.h}, {cfg.act}, T={T}",
-                   "T": T, "E": cfg.E, "d": cfg.d, "h": cfg.h, "act": cfg.act, "weight_copies": R},
-        "roofline": roof, "cpu_baseline": cpu, "stages_us": stages_us, "decode": decode,
+                   "T": T, "E": cfg.E, "d": cfg.d, "h": cfg.h, "act": cfg.act, "weight_copies": R,
+                   "experts_hit": hit},
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode,
+        "timing": "GPU time (HIP events, queue pre-filled by a spin kernel)" if can_sleep else "GPU time (HIP events)",
     }
     print(json.dumps(rec), flush=True)
 

@@ -132,6 +132,21 @@ int colibri_moe_expert_ffn(const colibri_moe_shape_t *s, const void *x_rows, con
                            const int32_t *expert_offsets, const colibri_moe_experts_t *w, void *y_sorted,
                            void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Step 4, first layer alone: H = act(x W1[e] + b1[e]), or silu(x W1[e]) * (x W3[e])
+ * for SwiGLU, for every expert-sorted row ([zskr] section 1: the expert's
+ * first FFN layer).  Arguments as for colibri_moe_expert_ffn; h_rows [2T, h]
+ * dtype out, 16-byte aligned.  ws holds split-K scratch (see
+ * colibri_moe_workspace_size; the layer workspace is always enough). */
+int colibri_moe_expert_ffn_up(const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                              const int32_t *expert_offsets, const colibri_moe_experts_t *w, void *h_rows,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 4, second layer alone: Y[p] = H[p] W2[e] + b2[e] over the expert-sorted
+ * rows.  h_rows [2T, h] dtype in (16-byte aligned), y_sorted [2T, d] out. */
+int colibri_moe_expert_ffn_down(const colibri_moe_shape_t *s, const void *h_rows, const int32_t *expert_offsets,
+                                const colibri_moe_experts_t *w, void *y_sorted, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* Step 5: gate-weighted combine fused with the un-permute ([nxbn] 3.3).
  *   out[t] = g[t,0] * y_sorted[assign_pos[2t]] + g[t,1] * y_sorted[assign_pos[2t+1]],
  *   summed in fp32 and stored in dtype.  out [T, d], 16-byte aligned. */

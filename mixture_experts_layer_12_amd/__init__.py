@@ -23,7 +23,8 @@ ACT_CODES = {"relu": RELU, "gelu": GELU, "swiglu": SWIGLU}
 
 EXPORTED = [
     "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn",
-    "colibri_moe_combine", "colibri_moe_layer_forward", "colibri_moe_status_string",
+    "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
+    "colibri_moe_status_string",
 ]
 
 
@@ -86,10 +87,12 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_route.argtypes = [SP, P, P, P, P, P, P, P]
     lib.colibri_moe_dispatch.argtypes = [SP, P, P, P, P, P, P, P, P, Z, P]
     lib.colibri_moe_expert_ffn.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, Z, P]
+    lib.colibri_moe_expert_ffn_up.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, Z, P]
+    lib.colibri_moe_expert_ffn_down.argtypes = [SP, P, P, ctypes.POINTER(_Experts), P, P, Z, P]
     lib.colibri_moe_combine.argtypes = [SP, P, P, P, P, P]
     lib.colibri_moe_layer_forward.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, P, P, P, Z, P]
-    for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_combine",
-              "colibri_moe_layer_forward"):
+    for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up",
+              "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward"):
         getattr(lib, f).restype = I
     lib.colibri_moe_status_string.argtypes = [I]
     lib.colibri_moe_status_string.restype = ctypes.c_char_p
@@ -155,6 +158,23 @@ def expert_ffn(shape: Shape, x_rows, sorted_assign, offsets, w1, w2, y_sorted, w
     _check(load().colibri_moe_expert_ffn(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
                                          ctypes.byref(e), _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
            "colibri_moe_expert_ffn")
+
+
+def expert_ffn_up(shape: Shape, x_rows, sorted_assign, offsets, w1, h_rows, ws=None, ws_bytes: int = 0, w3=None,
+                  b1=None, stream=None):
+    s = shape.c()
+    e = _experts(w1, None, w3, b1, None)
+    _check(load().colibri_moe_expert_ffn_up(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
+                                            ctypes.byref(e), _ptr(h_rows), _ptr(ws), ws_bytes, _stream(stream)),
+           "colibri_moe_expert_ffn_up")
+
+
+def expert_ffn_down(shape: Shape, h_rows, offsets, w2, y_sorted, ws=None, ws_bytes: int = 0, b2=None, stream=None):
+    s = shape.c()
+    e = _experts(None, w2, None, None, b2)
+    _check(load().colibri_moe_expert_ffn_down(ctypes.byref(s), _ptr(h_rows), _ptr(offsets), ctypes.byref(e),
+                                              _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
+           "colibri_moe_expert_ffn_down")
 
 
 def combine(shape: Shape, y_sorted, assign_pos, topk_gate, out, stream=None):

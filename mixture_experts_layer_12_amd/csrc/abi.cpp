@@ -37,12 +37,15 @@ int check_shape(const colibri_moe_shape_t *s) {
 
 size_t elem_size(const colibri_moe_shape_t *s) { return s->dtype == COLIBRI_F32 ? 4 : 2; }
 
-int check_experts(const colibri_moe_shape_t *s, const colibri_moe_experts_t *w) {
-    if (!w || !w->w1 || !w->w2) return COLIBRI_ERR_INVALID_ARG;
-    if (!aligned(w->w1, 16) || !aligned(w->w2, 16)) return COLIBRI_ERR_INVALID_ARG;
+// Checks the expert parameters a call reads: the first layer (W1, W3, b1),
+// the second layer (W2, b2), or both.
+int check_experts(const colibri_moe_shape_t *s, const colibri_moe_experts_t *w, bool up = true, bool down = true) {
+    if (!w) return COLIBRI_ERR_INVALID_ARG;
+    if ((up && !w->w1) || (down && !w->w2)) return COLIBRI_ERR_INVALID_ARG;
+    if ((w->w1 && !aligned(w->w1, 16)) || (w->w2 && !aligned(w->w2, 16))) return COLIBRI_ERR_INVALID_ARG;
     if (s->act == COLIBRI_ACT_SWIGLU) {
-        if (!w->w3) return COLIBRI_ERR_INVALID_ARG;
-        if (!aligned(w->w3, 16)) return COLIBRI_ERR_INVALID_ARG;
+        if (up && !w->w3) return COLIBRI_ERR_INVALID_ARG;
+        if (w->w3 && !aligned(w->w3, 16)) return COLIBRI_ERR_INVALID_ARG;
         if (w->b1 || w->b2) return COLIBRI_ERR_UNSUPPORTED;
     } else {
         if (w->w3) return COLIBRI_ERR_UNSUPPORTED;
@@ -136,6 +139,40 @@ int colibri_moe_expert_ffn(const colibri_moe_shape_t *s, const void *x_rows, con
     if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
     return hip_status(launch_expert_ffn(*s, x_rows, sorted_assign, expert_offsets, *w, y_sorted, ws, stream));
+}
+
+int colibri_moe_expert_ffn_up(const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                              const int32_t *expert_offsets, const colibri_moe_experts_t *w, void *h_rows, void *ws,
+                              size_t ws_bytes, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts(s, w, true, false);
+    if (st != COLIBRI_OK) return st;
+    if (!x_rows || !expert_offsets || !h_rows) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(x_rows, 16) || !aligned(h_rows, 16) || !aligned(expert_offsets, 4) ||
+        (sorted_assign && !aligned(sorted_assign, 4)))
+        return COLIBRI_ERR_INVALID_ARG;
+    const size_t need = ffn_up_scratch_bytes(*s);
+    if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
+    if (need && (!ws || !aligned(ws, 256))) return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_ffn_up(*s, x_rows, sorted_assign, expert_offsets, *w, h_rows, ws, stream));
+}
+
+int colibri_moe_expert_ffn_down(const colibri_moe_shape_t *s, const void *h_rows, const int32_t *expert_offsets,
+                                const colibri_moe_experts_t *w, void *y_sorted, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts(s, w, false, true);
+    if (st != COLIBRI_OK) return st;
+    if (!h_rows || !expert_offsets || !y_sorted) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(h_rows, 16) || !aligned(y_sorted, 16) || !aligned(expert_offsets, 4)) return COLIBRI_ERR_INVALID_ARG;
+    const size_t need = ffn_down_scratch_bytes(*s);
+    if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
+    if (need && (!ws || !aligned(ws, 256))) return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_ffn_down(*s, h_rows, expert_offsets, *w, y_sorted, ws, stream));
 }
 
 int colibri_moe_combine(const colibri_moe_shape_t *s, const void *y_sorted, const int32_t *assign_pos,

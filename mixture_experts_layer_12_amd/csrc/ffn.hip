@@ -355,53 +355,65 @@ hipError_t launch_gemm_f32(bool gather, const void *Am, const int32_t *sa, int T
 
 }  // namespace
 
+size_t ffn_up_scratch_bytes(const colibri_moe_shape_t &) { return 0; }
+size_t ffn_down_scratch_bytes(const colibri_moe_shape_t &) { return 0; }
+
 size_t ffn_workspace_bytes(const colibri_moe_shape_t &s) {
     const size_t el = s.dtype == COLIBRI_F32 ? 4 : 2;
-    return align256((size_t)2 * s.T * s.h * el);
+    return align256((size_t)2 * s.T * s.h * el) + std::max(ffn_up_scratch_bytes(s), ffn_down_scratch_bytes(s));
+}
+
+hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                         const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *,
+                         hipStream_t st) {
+    const int A = 2 * s.T;
+    const bool gather = sorted_assign != nullptr;
+    if (s.dtype == COLIBRI_F32) {
+        switch (s.act) {
+            case COLIBRI_ACT_RELU:
+                return launch_gemm_f32<EPI_ACT_RELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E, w.w1,
+                                                     nullptr, w.b1, H, s.d, s.h, A, st);
+            case COLIBRI_ACT_GELU:
+                return launch_gemm_f32<EPI_ACT_GELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E, w.w1,
+                                                     nullptr, w.b1, H, s.d, s.h, A, st);
+            default:
+                return launch_gemm_f32<EPI_SWIGLU>(gather, x_rows, sorted_assign, s.T, offsets, s.E, w.w1, w.w3,
+                                                   nullptr, H, s.d, s.h, A, st);
+        }
+    }
+    switch (s.act) {
+        case COLIBRI_ACT_RELU:
+            return launch_gemm_bf16<128, 128, 2, 2, EPI_ACT_RELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
+                                                                  w.w1, nullptr, w.b1, H, s.d, s.h, A, st);
+        case COLIBRI_ACT_GELU:
+            return launch_gemm_bf16<128, 128, 2, 2, EPI_ACT_GELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
+                                                                  w.w1, nullptr, w.b1, H, s.d, s.h, A, st);
+        default:
+            return launch_gemm_bf16<128, 128, 2, 2, EPI_SWIGLU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
+                                                                w.w1, w.w3, nullptr, H, s.d, s.h, A, st);
+    }
+}
+
+hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
+                           const colibri_moe_experts_t &w, void *y_sorted, void *, hipStream_t st) {
+    const int A = 2 * s.T;
+    const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
+    if (s.dtype == COLIBRI_F32)
+        return launch_gemm_f32<EPI_BIAS_ONLY>(false, H, nullptr, s.T, offsets, s.E, w.w2, nullptr, b2, y_sorted, s.h,
+                                              s.d, A, st);
+    return launch_gemm_bf16<128, 128, 2, 2, EPI_BIAS_ONLY>(false, H, nullptr, s.T, offsets, s.E, w.w2, nullptr, b2,
+                                                           y_sorted, s.h, s.d, A, st);
 }
 
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
                              hipStream_t st) {
-    const int A = 2 * s.T;
-    const bool gather = sorted_assign != nullptr;
-    void *H = ws;
-    hipError_t err;
-    if (s.dtype == COLIBRI_F32) {
-        switch (s.act) {
-            case COLIBRI_ACT_RELU:
-                err = launch_gemm_f32<EPI_ACT_RELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E, w.w1, nullptr,
-                                                    w.b1, H, s.d, s.h, A, st);
-                break;
-            case COLIBRI_ACT_GELU:
-                err = launch_gemm_f32<EPI_ACT_GELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E, w.w1, nullptr,
-                                                    w.b1, H, s.d, s.h, A, st);
-                break;
-            default:
-                err = launch_gemm_f32<EPI_SWIGLU>(gather, x_rows, sorted_assign, s.T, offsets, s.E, w.w1, w.w3,
-                                                  nullptr, H, s.d, s.h, A, st);
-        }
-        if (err != hipSuccess) return err;
-        return launch_gemm_f32<EPI_BIAS_ONLY>(false, H, nullptr, s.T, offsets, s.E, w.w2, nullptr,
-                                              s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2, y_sorted, s.h, s.d, A, st);
-    }
-    switch (s.act) {
-        case COLIBRI_ACT_RELU:
-            err = launch_gemm_bf16<128, 128, 2, 2, EPI_ACT_RELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
-                                                                 w.w1, nullptr, w.b1, H, s.d, s.h, A, st);
-            break;
-        case COLIBRI_ACT_GELU:
-            err = launch_gemm_bf16<128, 128, 2, 2, EPI_ACT_GELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
-                                                                 w.w1, nullptr, w.b1, H, s.d, s.h, A, st);
-            break;
-        default:
-            err = launch_gemm_bf16<128, 128, 2, 2, EPI_SWIGLU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
-                                                               w.w1, w.w3, nullptr, H, s.d, s.h, A, st);
-    }
-    if (err != hipSuccess) return err;
-    return launch_gemm_bf16<128, 128, 2, 2, EPI_BIAS_ONLY>(false, H, nullptr, s.T, offsets, s.E, w.w2, nullptr,
-                                                           s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2, y_sorted,
-                                                           s.h, s.d, A, st);
+    const size_t el = s.dtype == COLIBRI_F32 ? 4 : 2;
+    char *H = static_cast<char *>(ws);
+    char *scratch = H + align256((size_t)2 * s.T * s.h * el);
+    hipError_t e = launch_ffn_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
+    if (e != hipSuccess) return e;
+    return launch_ffn_down(s, H, offsets, w, y_sorted, scratch, st);
 }
 
 }  // namespace colibri

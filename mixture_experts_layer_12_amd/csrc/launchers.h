@@ -20,9 +20,18 @@ hipError_t launch_dispatch(const colibri_moe_shape_t &s, const int32_t *topk_idx
 hipError_t launch_gather_rows(const colibri_moe_shape_t &s, const void *x, const int32_t *sorted_assign,
                               void *x_sorted, hipStream_t st);
 
-// Workspace the FFN needs (H [2T, h] plus any split-K scratch), 256-byte multiple.
+// Scratch the two FFN layers need besides their inputs and outputs (256-byte multiples).
+size_t ffn_up_scratch_bytes(const colibri_moe_shape_t &s);
+size_t ffn_down_scratch_bytes(const colibri_moe_shape_t &s);
+// Workspace of the whole FFN: H [2T, h] plus the larger of the two scratches.
 size_t ffn_workspace_bytes(const colibri_moe_shape_t &s);
 
+hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                         const int32_t *offsets, const colibri_moe_experts_t &w, void *h_rows, void *scratch,
+                         hipStream_t st);
+hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *h_rows, const int32_t *offsets,
+                           const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st);
+// H then Y, with H and the scratch carved from ws.
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
                              hipStream_t st);

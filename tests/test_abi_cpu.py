@@ -147,3 +147,24 @@ def test_workspace_size_covers_buffers(lib):
             assert ws >= 2 * T * (GOOD.h + GOOD.d) * el + 4 * (2 * T) * 4
             assert ws % 256 == 0 and ws > prev
             prev = ws
+
+
+def test_ffn_layer_entry_point_checks(lib):
+    s = shape_c()
+    up = lambda e: lib.colibri_moe_expert_ffn_up(ctypes.byref(s), fake(0), fake(1), fake(2), ctypes.byref(e),
+                                                 fake(3), None, 0, None)
+    down = lambda e, sh=s: lib.colibri_moe_expert_ffn_down(ctypes.byref(sh), fake(0), fake(2), ctypes.byref(e),
+                                                           fake(3), None, 0, None)
+    # the first layer needs W1 (and W3 for SwiGLU), the second needs W2
+    assert up(moe._Experts(None, fake(11), None, None, None)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert up(moe._Experts(fake(10), None, None, None, None)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert down(moe._Experts(None, None, None, None, None)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert down(moe._Experts(None, None, fake(12) + 2, None, None)) == moe.COLIBRI_ERR_INVALID_ARG
+    # SwiGLU takes no biases; ReLU takes no W3
+    assert down(moe._Experts(None, None, fake(12), None, fake(13))) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert down(moe._Experts(None, fake(11), fake(12), None, None), shape_c(act=moe.RELU)) == \
+        moe.COLIBRI_ERR_UNSUPPORTED
+    # misaligned hidden rows
+    e = moe._Experts(fake(10), fake(11), None, None, None)
+    assert lib.colibri_moe_expert_ffn_up(ctypes.byref(s), fake(0), fake(1), fake(2), ctypes.byref(e), fake(3) + 4,
+                                         None, 0, None) == moe.COLIBRI_ERR_INVALID_ARG
