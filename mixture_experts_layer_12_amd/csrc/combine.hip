@@ -12,6 +12,7 @@
 // storage type.  A slot whose assign_pos is negative (an out-of-range expert
 // index upstream) contributes nothing.
 #include "device_common.h"
+#include "ffn_common.h"
 #include "launchers.h"
 
 namespace colibri {
@@ -54,6 +55,45 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, 
     }
 }
 
+// Same combine, but each expert row Y[p] is first formed from the second
+// layer's S split partial sums: Y[p] = bf16(sum_{s=0..S-1} part[s][p] + b2[e]),
+// the value the separate reduce would have stored.
+__global__ __launch_bounds__(256) void combine_partials_kernel(const float *__restrict__ part, int S,
+                                                               const int32_t *__restrict__ pos,
+                                                               const int32_t *__restrict__ idx,
+                                                               const float *__restrict__ gate,
+                                                               const uint16_t *__restrict__ b2, int E,
+                                                               uint16_t *__restrict__ out, int T, int d) {
+    const int vpr = d / 4;
+    const size_t total = (size_t)T * vpr;
+    const int A = 2 * T;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+        const int t = (int)(i / vpr);
+        const int c = (int)(i % vpr) * 4;
+        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int p = pos[2 * t + sl];
+            const int e = idx[2 * t + sl];
+            if (p < 0 || p >= A || e < 0 || e >= E) continue;
+            float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int sp = 0; sp < S; ++sp) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(part + ((size_t)sp * A + p) * d + c);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) y[q] += a[q];
+            }
+            const float g = gate[2 * t + sl];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float yb = y[q] + (b2 ? bf16_to_f32(b2[(size_t)e * d + c + q]) : 0.0f);
+                const float yr = bf16_to_f32((uint16_t)f32_to_bf16_bits(yb));  // Y is a bf16 value
+                o[q] = sl == 0 ? g * yr : fmaf(g, yr, o[q]);
+            }
+        }
+        *reinterpret_cast<u32x2 *>(out + (size_t)t * d + c) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, const int32_t *assign_pos,
@@ -67,6 +107,16 @@ hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, co
     else
         combine_kernel<uint16_t><<<blocks, 256, 0, st>>>((const uint16_t *)y_sorted, assign_pos, topk_gate,
                                                          (uint16_t *)out, s.T, s.d);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
+                                   const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
+                                   hipStream_t st) {
+    const size_t total = (size_t)s.T * (s.d / 4);
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
+    combine_partials_kernel<<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate, (const uint16_t *)b2,
+                                                    s.E, (uint16_t *)out, s.T, s.d);
     return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@
 //
 // fp32 path: a plain LDS-tiled FMA GEMM (64 x 64 tiles, 4 x 4 per thread).
 #include "device_common.h"
+#include "ffn_common.h"
 #include "launchers.h"
 
 namespace colibri {
@@ -83,8 +84,6 @@ constexpr int kBK = 64;  // K per LDS stage (128-byte LDS rows)
 
 __device__ __forceinline__ int swz_a(int m) { return m & 7; }
 __device__ __forceinline__ int swz_b(int n) { return (n ^ (n >> 3)) & 7; }
-
-enum Epi { EPI_ACT_RELU = 0, EPI_ACT_GELU = 1, EPI_SWIGLU = 2, EPI_BIAS_ONLY = 3 };
 
 template <int BM, int BN, int WM, int WN, int EPI, bool GATHER>
 __global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(
@@ -355,8 +354,12 @@ hipError_t launch_gemm_f32(bool gather, const void *Am, const int32_t *sa, int T
 
 }  // namespace
 
-size_t ffn_up_scratch_bytes(const colibri_moe_shape_t &) { return 0; }
-size_t ffn_down_scratch_bytes(const colibri_moe_shape_t &) { return 0; }
+size_t ffn_up_scratch_bytes(const colibri_moe_shape_t &s) {
+    return ffn_decode_eligible(s) ? ffn_decode_scratch_bytes(s) : 0;
+}
+size_t ffn_down_scratch_bytes(const colibri_moe_shape_t &s) {
+    return ffn_decode_eligible(s) ? ffn_decode_scratch_bytes(s) : 0;
+}
 
 size_t ffn_workspace_bytes(const colibri_moe_shape_t &s) {
     const size_t el = s.dtype == COLIBRI_F32 ? 4 : 2;
@@ -364,8 +367,9 @@ size_t ffn_workspace_bytes(const colibri_moe_shape_t &s) {
 }
 
 hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
-                         const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *,
+                         const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
                          hipStream_t st) {
+    if (ffn_decode_eligible(s)) return launch_decode_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
     const int A = 2 * s.T;
     const bool gather = sorted_assign != nullptr;
     if (s.dtype == COLIBRI_F32) {
@@ -395,7 +399,8 @@ hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const
 }
 
 hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                           const colibri_moe_experts_t &w, void *y_sorted, void *, hipStream_t st) {
+                           const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st) {
+    if (ffn_decode_eligible(s)) return launch_decode_down(s, H, offsets, w, y_sorted, scratch, true, st);
     const int A = 2 * s.T;
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
     if (s.dtype == COLIBRI_F32)

@@ -1,0 +1,364 @@
+// Weight-streaming grouped expert GEMM for decode-sized batches (few rows per
+// expert), used for both FFN layers when T <= 64.
+//
+// Colibri write-ups: [zskr] http://www.zskr.cn/news/2272131 section 2.1 (the
+// Compute stage: a grouped GEMM over the experts' token groups), section 2.2
+// (top-2 activates 2 of the experts: only their weights need to move);
+// [nxbn] http://m.nxbn.cn/news/48047 section 2.1 (matmul + activation fused
+// in one kernel).
+//
+// At decode sizes the layer is a stream of expert weights: every weight
+// element of a live expert is used by only a handful of rows.  The design
+// keeps HBM busy and nothing else in the way:
+//   * a wave owns one (live expert, column block, K split) unit: 128 weight
+//     columns, or 64 W1 + 64 W3 columns for SwiGLU; only experts with rows
+//     get waves (found from the device-side offsets); the 4 waves of a
+//     workgroup take 4 adjacent column blocks over the same K range (waves
+//     of one workgroup that split K instead lose about a quarter of the
+//     stream bandwidth on this memory system: measured 5.2-5.7 against
+//     6.7-7.0 TB/s for the same read pattern);
+//   * each wave streams weights straight from HBM into registers: a lane loads an 8 (k) x 8 (n) bf16
+//     block with eight 16-byte non-temporal loads, transposes it in
+//     registers and feeds it as the B operand of eight
+//     v_mfma_f32_16x16x32_bf16 instructions (lane l's columns are
+//     n0 + 8(l%16) + j, j = 0..7, so MFMA j covers a strided set of 16
+//     columns and a lane owns 8 consecutive output columns); the few token
+//     rows (A operand) are read from L2; two k-steps (16 KB per wave) are
+//     always in flight;
+//   * with one K split, the epilogue (bias + activation, silu(u) * v, or bias
+//     only) runs on the accumulators and rounds once to bf16;
+//   * when the live experts' column blocks alone cannot fill the chip, the K
+//     range is split S ways: each wave writes its partial sums
+//     (fp32) to scratch, and the next kernel on the stream adds the S parts
+//     in order 0..S-1 and applies the epilogue (a separate reduce kernel, or
+//     the combine kernel for the second layer inside the layer call).
+#include "device_common.h"
+#include "ffn_common.h"
+#include "launchers.h"
+
+namespace colibri {
+namespace {
+
+constexpr int kDecWaves = 4;  // waves (adjacent column blocks) per workgroup
+
+// i-th set bit of a 64-bit mask (wave-uniform loop)
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int i) {
+    for (int q = 0; q < i; ++q) m &= m - 1;
+    return __ffsll((unsigned long long)m) - 1;
+}
+
+// The 8 x 8 bf16 block in rows r[0..7] (r[i] = columns c..c+7 of k-row i)
+// becomes eight B fragments: frag[j] = (k-rows 0..7 of column c + j).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], bf16x8 (&frag)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int q = j >> 1;
+        u32x4 o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t a = r[2 * p][q], b = r[2 * p + 1][q];
+            o[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        }
+        frag[j] = __builtin_bit_cast(bf16x8, o);
+    }
+}
+
+// Live expert `slot` (experts with rows, in index order): e, first row, row count.
+// Returns false when fewer experts are live.  Whole-wave call.
+__device__ __forceinline__ bool live_expert(const int32_t *__restrict__ offsets, int E, int A_total, int slot,
+                                            int &e, int &r0, int &count) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int lo_l = 0, cnt_l = 0;
+    if (lane < E) {
+        lo_l = min(max(offsets[lane], 0), A_total);
+        const int hi = min(max(offsets[lane + 1], lo_l), A_total);
+        cnt_l = hi - lo_l;
+    }
+    const uint64_t live = __ballot(cnt_l > 0);
+    if (__popcll(live) <= slot) return false;
+    e = nth_set_bit(live, slot);
+    r0 = __shfl(lo_l, e);
+    count = __shfl(cnt_l, e);
+    return true;
+}
+
+template <int MB, int EPI, bool GATHER>
+__global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
+    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NCB, int S,
+    float *__restrict__ part) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int WCOLS = DUAL ? 64 : 128;  // output columns per wave
+    constexpr int ROWS = MB * 16;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ncbg = (NCB + kDecWaves - 1) / kDecWaves;  // groups of 4 column blocks
+    const int cbg = blockIdx.x % ncbg;
+    const int rest = blockIdx.x / ncbg;
+    const int split = rest % S;
+    const int slot = rest / S;
+    const int cb = cbg * kDecWaves + (int)(threadIdx.x / kWave);
+    if (cb >= NCB) return;
+
+    const int A_total = 2 * T;
+    int e, r0, count;
+    if (!live_expert(offsets, E, A_total, slot, e, r0, count)) return;
+
+    const int n0 = cb * WCOLS;
+    const int c = lane & 15;  // column group of this lane
+    const int g = lane >> 4;  // k group: k 8g..8g+7 of a 32-deep step
+    // this lane's 8 consecutive weight columns and the matrix they come from;
+    // out-of-range columns load column block 0 instead (never stored)
+    const uint16_t *Bm = (DUAL && c >= 8) ? B1 : B0;
+    const int ccol = n0 + 8 * (DUAL ? (c & 7) : c);
+    const bool col_ok = ccol < N;
+    const uint16_t *b_base = Bm + (size_t)e * K * N + (size_t)(8 * g) * N + (col_ok ? ccol : 0);
+
+    // k-steps of this split
+    const int ksteps = K / 32;
+    const int s_begin = (int)((long)ksteps * split / S);
+    const int s_end = (int)((long)ksteps * (split + 1) / S);
+
+    for (int rc = 0; rc < count; rc += ROWS) {
+        const int rows = min(ROWS, count - rc);
+        // A rows of this lane: row (lane % 16) of each 16-row subtile; rows past
+        // the segment read row r0 instead (never stored)
+        const uint16_t *a_src[MB];
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi) {
+            const int r = mi * 16 + c;
+            const int p = r0 + rc + (r < rows ? r : 0);
+            long src = p;
+            if (GATHER) {
+                const int a = sorted_assign[p];
+                src = (a >= 0 && (a >> 1) < T) ? (a >> 1) : 0;
+            }
+            a_src[mi] = A + (size_t)src * K + 8 * g;
+        }
+
+        f32x4 acc[MB][8];
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[mi][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        // one k-step of operands: the lane's 8 x 8 weight block and its A fragments
+        struct Stage {
+            u32x4 b[8];
+            u32x4 a[MB];
+        };
+        auto load_stage = [&](Stage &sg, int step) {
+            const uint16_t *p = b_base + (size_t)step * 32 * N;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                sg.b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + (size_t)i * N));
+#pragma unroll
+            for (int mi = 0; mi < MB; ++mi) sg.a[mi] = *reinterpret_cast<const u32x4 *>(a_src[mi] + step * 32);
+        };
+        auto mma = [&](const Stage &sg) {
+            bf16x8 bfrag[8];
+            transpose8x8(sg.b, bfrag);
+#pragma unroll
+            for (int mi = 0; mi < MB; ++mi) {
+                const bf16x8 afrag = __builtin_bit_cast(bf16x8, sg.a[mi]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[mi][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[j], acc[mi][j], 0, 0, 0);
+            }
+        };
+
+        // two k-steps in flight: stage 0 holds even steps, stage 1 odd steps.
+        // The steady-state loop issues both prefetches unconditionally; the
+        // scheduling barriers keep each stage's loads together.
+        Stage sg0, sg1;
+        const int nsteps = s_end - s_begin;
+        if (nsteps > 0) load_stage(sg0, s_begin);
+        if (nsteps > 1) load_stage(sg1, s_begin + 1);
+        int st = s_begin;
+        for (; st + 3 < s_end; st += 2) {
+            mma(sg0);
+            load_stage(sg0, st + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(sg1);
+            load_stage(sg1, st + 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int left = s_end - st;  // 0 (no steps), 1, 2 or 3
+        if (left == 3) {
+            mma(sg0);
+            load_stage(sg0, st + 2);
+            mma(sg1);
+            mma(sg0);
+        } else if (left == 2) {
+            mma(sg0);
+            mma(sg1);
+        } else if (left == 1) {
+            mma(sg0);
+        }
+
+        // accumulator register r of MFMA j, subtile mi: row mi*16 + 4g + r,
+        // weight column ccol + j (for SwiGLU, lanes c >= 8 hold the W3 product)
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = mi * 16 + 4 * g + r;
+                float u[8], v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    u[j] = acc[mi][j][r];
+                    v[j] = DUAL ? __shfl_xor(u[j], 8) : 0.0f;
+                }
+                if (row >= rows || !col_ok) continue;
+                if (S == 1) {
+                    if (DUAL && c >= 8) continue;
+                    store_epilogue8<EPI>(C + (size_t)(r0 + rc + row) * N + ccol, u, v, bias, e, N, ccol);
+                } else {
+                    // partial sums of this split: [split][row][NC], W3 products at column N + n
+                    const int NC = DUAL ? 2 * N : N;
+                    const int pcol = (DUAL && c >= 8) ? N + ccol : ccol;
+                    float *dst = part + ((size_t)split * A_total + (r0 + rc + row)) * NC + pcol;
+                    *reinterpret_cast<f32x4 *>(dst) = f32x4{u[0], u[1], u[2], u[3]};
+                    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{u[4], u[5], u[6], u[7]};
+                }
+            }
+    }
+}
+
+// Adds the S split partials of every row in order 0..S-1 and applies the
+// epilogue: H (first layer) or Y (second layer) in bf16.  One thread per 4
+// output columns.
+template <int EPI>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ part, int S, int T,
+                                                           const int32_t *__restrict__ offsets, int E,
+                                                           const uint16_t *__restrict__ bias,
+                                                           uint16_t *__restrict__ C, int N) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    const int A_total = 2 * T;
+    const int NC = DUAL ? 2 * N : N;
+    const int q_per_row = N / 4;
+    const size_t total = (size_t)A_total * q_per_row;
+    const int rows_valid = min(max(offsets[E], 0), A_total);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+        const int row = (int)(i / q_per_row);
+        const int col = (int)(i % q_per_row) * 4;
+        if (row >= rows_valid) continue;
+        int e = 0;  // expert of this row: the last e with offsets[e] <= row
+        for (int k = 1; k < E; ++k)
+            if (offsets[k] <= row) e = k;
+        float u[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int sp = 0; sp < S; ++sp) {
+            const float *src = part + ((size_t)sp * A_total + row) * NC + col;
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) u[q] += a[q];
+            if (DUAL) {
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(src + N);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] += b[q];
+            }
+        }
+        store_epilogue<EPI, 4>(C + (size_t)row * N + col, u, v, bias, e, N, col);
+    }
+}
+
+}  // namespace
+
+bool ffn_decode_eligible(const colibri_moe_shape_t &s) { return s.dtype == COLIBRI_BF16 && s.T <= 64; }
+
+DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up) {
+    DecodePlan p;
+    const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
+    const int K = up ? s.d : s.h;
+    const int N = up ? s.h : s.d;
+    const int wcols = dual ? 64 : 128;
+    p.NCB = (N + wcols - 1) / wcols;
+    p.slots = std::min(s.E, 2 * s.T);
+    const int units = p.slots * p.NCB;
+    const int ksteps = K / 32;
+    // about 900 streaming waves fill the chip; keep at least two k-steps per split
+    p.S = std::max(1, std::min((896 + units - 1) / units, ksteps / 2));
+    p.W = kDecWaves;
+    // 16-row tiles when the expected rows per expert (2T/E) leave a 2x margin
+    p.MB = (2 * s.T <= 8 * s.E) ? 1 : 2;
+    p.part_bytes = p.S > 1 ? align256((size_t)p.S * 2 * s.T * (dual ? 2 : 1) * N * 4) : 0;
+    return p;
+}
+
+size_t ffn_decode_scratch_bytes(const colibri_moe_shape_t &s) {
+    return std::max(decode_plan(s, true).part_bytes, decode_plan(s, false).part_bytes);
+}
+
+namespace {
+template <int EPI>
+hipError_t launch_decode_t(const colibri_moe_shape_t &s, const DecodePlan &p, bool gather, const void *Am,
+                           const int32_t *sa, const int32_t *offsets, const void *B0, const void *B1, const void *bias,
+                           void *C, int K, int N, void *scratch, hipStream_t st) {
+    float *part = static_cast<float *>(scratch);
+    const int blocks = p.slots * p.S * ((p.NCB + kDecWaves - 1) / kDecWaves);
+#define COLIBRI_DEC_LAUNCH(MBV, G)                                                                              \
+    ffn_decode_kernel<MBV, EPI, G><<<blocks, kDecWaves * kWave, 0, st>>>(                                      \
+        (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,                \
+        (const uint16_t *)bias, (uint16_t *)C, K, N, p.NCB, p.S, part)
+    if (p.MB == 1) {
+        if (gather) COLIBRI_DEC_LAUNCH(1, true);
+        else COLIBRI_DEC_LAUNCH(1, false);
+    } else {
+        if (gather) COLIBRI_DEC_LAUNCH(2, true);
+        else COLIBRI_DEC_LAUNCH(2, false);
+    }
+#undef COLIBRI_DEC_LAUNCH
+    return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_reduce_t(const colibri_moe_shape_t &s, const DecodePlan &p, const int32_t *offsets,
+                           const void *bias, void *C, int N, const void *scratch, hipStream_t st) {
+    const size_t total = (size_t)2 * s.T * (N / 4);
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
+    split_reduce_kernel<EPI><<<blocks, 256, 0, st>>>((const float *)scratch, p.S, s.T, offsets, s.E,
+                                                     (const uint16_t *)bias, (uint16_t *)C, N);
+    return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t up_t(const colibri_moe_shape_t &s, const DecodePlan &p, bool gather, const void *x_rows,
+                const int32_t *sa, const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *H,
+                void *scratch, hipStream_t st) {
+    hipError_t err = launch_decode_t<EPI>(s, p, gather, x_rows, sa, offsets, B0, B1, bias, H, s.d, s.h, scratch, st);
+    if (err == hipSuccess && p.S > 1) err = launch_reduce_t<EPI>(s, p, offsets, bias, H, s.h, scratch, st);
+    return err;
+}
+}  // namespace
+
+hipError_t launch_decode_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                            const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
+                            hipStream_t st) {
+    const DecodePlan p = decode_plan(s, true);
+    const bool gather = sorted_assign != nullptr;
+    switch (s.act) {
+        case COLIBRI_ACT_RELU:
+            return up_t<EPI_ACT_RELU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, scratch,
+                                      st);
+        case COLIBRI_ACT_GELU:
+            return up_t<EPI_ACT_GELU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, scratch,
+                                      st);
+        default:
+            return up_t<EPI_SWIGLU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, scratch,
+                                    st);
+    }
+}
+
+hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
+                              const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st) {
+    const DecodePlan p = decode_plan(s, false);
+    const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
+    hipError_t err = launch_decode_t<EPI_BIAS_ONLY>(s, p, false, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d,
+                                                    scratch, st);
+    if (err == hipSuccess && p.S > 1 && reduce)
+        err = launch_reduce_t<EPI_BIAS_ONLY>(s, p, offsets, b2, y, s.d, scratch, st);
+    return err;
+}
+
+}  // namespace colibri

@@ -31,6 +31,28 @@ hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const
                          hipStream_t st);
 hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *h_rows, const int32_t *offsets,
                            const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st);
+// Decode-sized batches (bf16, T <= 64) use the weight-streaming kernel.
+struct DecodePlan {
+    int NCB;            // column blocks per expert
+    int slots;          // live-expert slots in the grid (min(E, 2T))
+    int W;              // waves per workgroup (split of each workgroup's K range)
+    int S;              // K splits across workgroups (partials reduced by the next kernel)
+    int MB;             // 16-row subtiles per row chunk
+    size_t part_bytes;  // fp32 partial-sum scratch when S > 1
+};
+bool ffn_decode_eligible(const colibri_moe_shape_t &s);
+DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up);
+size_t ffn_decode_scratch_bytes(const colibri_moe_shape_t &s);
+hipError_t launch_decode_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                            const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
+                            hipStream_t st);
+// reduce = false leaves the split partials in scratch for launch_combine_partials
+hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
+                              const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st);
+// combine straight from the second layer's S split partials (adds them, b2, rounds Y, then gates)
+hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
+                                   const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
+                                   hipStream_t st);
 // H then Y, with H and the scratch carved from ws.
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
