@@ -17,16 +17,10 @@
 // counts back: the grid is sized for the worst case and surplus workgroups
 // exit.  GEMM1 gathers its A rows through sorted_assign (no copy of X).
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Weights are
-// row-major [K, N] (N contiguous) while MFMA operands must be K-contiguous
-// per lane, so each thread loads a 4 x 8 (k x n) block with 16-byte loads and
-// transposes it in registers before writing it to LDS as [n][k].  LDS rows are
-// 128 bytes (BK = 64 bf16) with the 16-byte chunk index XOR-swizzled so that
-// both the transposing writes and the MFMA fragment reads spread over banks.
-// Two LDS stages: global loads of tile k+1 are in flight while tile k is
-// multiplied.
-//
-// fp32 path: a plain LDS-tiled FMA GEMM (64 x 64 tiles, 4 x 4 per thread).
+// bf16 layers run the MFMA kernels of ffn_gemm.hip (T > 64) and
+// ffn_decode.hip (T <= 64); this file holds the fp32 path -- a plain
+// LDS-tiled FMA GEMM (64 x 64 tiles, 4 x 4 per thread) -- and the entry
+// points that pick the kernel.
 #include "device_common.h"
 #include "ffn_common.h"
 #include "launchers.h"
@@ -77,166 +71,6 @@ __device__ __forceinline__ long a_source_row(const int32_t *__restrict__ sa, int
     const int a = sa[p];
     if (a < 0 || (a >> 1) >= T) return -1;
     return a >> 1;
-}
-
-// ------------------------------------------------------------------ bf16 MFMA GEMM
-constexpr int kBK = 64;  // K per LDS stage (128-byte LDS rows)
-
-__device__ __forceinline__ int swz_a(int m) { return m & 7; }
-__device__ __forceinline__ int swz_b(int n) { return (n ^ (n >> 3)) & 7; }
-
-template <int BM, int BN, int WM, int WN, int EPI, bool GATHER>
-__global__ __launch_bounds__(WM *WN *kWave) void gemm_bf16_kernel(
-    const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
-    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
-    const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int max_m_tiles) {
-    constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    constexpr int NB = DUAL ? 2 : 1;
-    constexpr int NT = WM * WN * kWave;
-    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-    constexpr int SM = WTM / 32, SN = WTN / 32;  // 32x32 MFMA sub-tiles per wave
-    constexpr int A_CHUNKS = BM * (kBK / 8) / NT;  // 16-byte chunks of A per thread
-    constexpr int B_UNITS = (kBK / 4) * (BN / 8);  // 4(k) x 8(n) blocks per B tile
-    static_assert(A_CHUNKS * NT == BM * (kBK / 8), "A tile split");
-    static_assert(B_UNITS == NT, "one 4x8 B block per thread");
-
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kBK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][NB][BN * kBK];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int wm = wave / WN, wn = wave % WN;
-
-    const int mt = blockIdx.x % max_m_tiles;
-    const int n0 = (blockIdx.x / max_m_tiles) * BN;
-    TileInfo ti;
-    if (!find_row_tile<BM>(offsets, E, 2 * T, mt, ti)) return;  // uniform across the block
-    const int e = ti.e;
-
-    // A rows handled by this thread
-    const int a_chunk = tid % 8;
-    const uint16_t *a_src[A_CHUNKS];
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-        const int r = tid / 8 + i * (NT / 8);
-        long src = -1;
-        if (r < ti.rows) src = a_source_row<GATHER>(sorted_assign, ti.row0 + r, T);
-        a_src[i] = (src >= 0) ? A + (size_t)src * K + a_chunk * 8 : nullptr;
-    }
-    // B block handled by this thread: rows kg*4..+3, columns ng*8..+7
-    const int kg = tid / (BN / 8), ng = tid % (BN / 8);
-    const bool b_ok = (n0 + ng * 8) < N;
-    const uint16_t *b_src[NB];
-    b_src[0] = B0 + (size_t)e * K * N + (size_t)(kg * 4) * N + n0 + ng * 8;
-    if (DUAL) b_src[NB - 1] = B1 + (size_t)e * K * N + (size_t)(kg * 4) * N + n0 + ng * 8;
-
-    u32x4 ra[A_CHUNKS];
-    u32x4 rb[NB][4];
-
-    auto load_global = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            if (a_src[i]) ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + k0);
-            else ra[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (b_ok) rb[b][i] = *reinterpret_cast<const u32x4 *>(b_src[b] + (size_t)(k0 + i) * N);
-                else rb[b][i] = u32x4{0u, 0u, 0u, 0u};
-            }
-    };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int r = tid / 8 + i * (NT / 8);
-            *reinterpret_cast<u32x4 *>(&As[buf][r * kBK + ((a_chunk ^ swz_a(r)) * 8)]) = ra[i];
-        }
-        const int kchunk = kg >> 1, khalf = (kg & 1) * 4;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int q = j >> 1;
-                uint32_t w0, w1;
-                if (j & 1) {
-                    w0 = (rb[b][0][q] >> 16) | (rb[b][1][q] & 0xffff0000u);
-                    w1 = (rb[b][2][q] >> 16) | (rb[b][3][q] & 0xffff0000u);
-                } else {
-                    w0 = (rb[b][0][q] & 0xffffu) | (rb[b][1][q] << 16);
-                    w1 = (rb[b][2][q] & 0xffffu) | (rb[b][3][q] << 16);
-                }
-                const int n = ng * 8 + j;
-                *reinterpret_cast<u32x2 *>(&Bs[buf][b][n * kBK + ((kchunk ^ swz_b(n)) * 8) + khalf]) = u32x2{w0, w1};
-            }
-    };
-
-    f32x16 acc[NB][SM][SN];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-#pragma unroll
-            for (int j = 0; j < SN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.0f;
-
-    const int KT = K / kBK;
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load_global((kt + 1) * kBK);
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            const int chunk = ks * 2 + (lane >> 5);
-            bf16x8 af[SM];
-#pragma unroll
-            for (int i = 0; i < SM; ++i) {
-                const int m = wm * WTM + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const bf16x8 *>(&As[cur][m * kBK + ((chunk ^ swz_a(m)) * 8)]);
-            }
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int j = 0; j < SN; ++j) {
-                    const int n = wn * WTN + j * 32 + (lane & 31);
-                    const bf16x8 bfr =
-                        *reinterpret_cast<const bf16x8 *>(&Bs[cur][b][n * kBK + ((chunk ^ swz_b(n)) * 8)]);
-#pragma unroll
-                    for (int i = 0; i < SM; ++i)
-                        acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr, acc[b][i][j], 0, 0, 0);
-                }
-        }
-        if (kt + 1 < KT) store_lds(cur ^ 1);
-        __syncthreads();
-    }
-
-    // epilogue: 32x32 accumulator layout, register r of lane l holds
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the sub-tile
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-        for (int j = 0; j < SN; ++j) {
-            const int n = n0 + wn * WTN + j * 32 + (lane & 31);
-            if (n >= N) continue;
-            float bv = 0.0f;
-            if (EPI != EPI_SWIGLU && bias != nullptr) bv = bf16_to_f32(bias[(size_t)e * N + n]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m >= ti.rows) continue;
-                float v;
-                if (EPI == EPI_SWIGLU) v = silu(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
-                else if (EPI == EPI_ACT_RELU) v = apply_act<ACT_RELU>(acc[0][i][j][r] + bv);
-                else if (EPI == EPI_ACT_GELU) v = apply_act<ACT_GELU>(acc[0][i][j][r] + bv);
-                else v = acc[0][i][j][r] + bv;
-                C[(size_t)(ti.row0 + m) * N + n] = (uint16_t)f32_to_bf16_bits(v);
-            }
-        }
 }
 
 // ------------------------------------------------------------------ fp32 FMA GEMM
@@ -316,25 +150,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
 // ------------------------------------------------------------------ launch
 inline int max_row_tiles(int A, int E, int BM) { return (A + BM - 1) / BM + std::min(E, A); }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-hipError_t launch_gemm_bf16(bool gather, const void *Am, const int32_t *sa, int T, const int32_t *offsets, int E,
-                            const void *B0, const void *B1, const void *bias, void *C, int K, int N, int A_rows,
-                            hipStream_t st) {
-    const int mtiles = max_row_tiles(A_rows, E, BM);
-    const int ntiles = (N + BN - 1) / BN;
-    const dim3 grid(mtiles * ntiles);
-    constexpr int threads = WM * WN * kWave;
-    if (gather)
-        gemm_bf16_kernel<BM, BN, WM, WN, EPI, true><<<grid, threads, 0, st>>>(
-            (const uint16_t *)Am, sa, T, offsets, E, (const uint16_t *)B0, (const uint16_t *)B1,
-            (const uint16_t *)bias, (uint16_t *)C, K, N, mtiles);
-    else
-        gemm_bf16_kernel<BM, BN, WM, WN, EPI, false><<<grid, threads, 0, st>>>(
-            (const uint16_t *)Am, sa, T, offsets, E, (const uint16_t *)B0, (const uint16_t *)B1,
-            (const uint16_t *)bias, (uint16_t *)C, K, N, mtiles);
-    return hipGetLastError();
-}
-
 template <int EPI>
 hipError_t launch_gemm_f32(bool gather, const void *Am, const int32_t *sa, int T, const int32_t *offsets, int E,
                            const void *B0, const void *B1, const void *bias, void *C, int K, int N, int A_rows,
@@ -385,17 +200,7 @@ hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const
                                                    nullptr, H, s.d, s.h, A, st);
         }
     }
-    switch (s.act) {
-        case COLIBRI_ACT_RELU:
-            return launch_gemm_bf16<128, 128, 2, 2, EPI_ACT_RELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
-                                                                  w.w1, nullptr, w.b1, H, s.d, s.h, A, st);
-        case COLIBRI_ACT_GELU:
-            return launch_gemm_bf16<128, 128, 2, 2, EPI_ACT_GELU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
-                                                                  w.w1, nullptr, w.b1, H, s.d, s.h, A, st);
-        default:
-            return launch_gemm_bf16<128, 128, 2, 2, EPI_SWIGLU>(gather, x_rows, sorted_assign, s.T, offsets, s.E,
-                                                                w.w1, w.w3, nullptr, H, s.d, s.h, A, st);
-    }
+    return launch_gemm_up(s, x_rows, sorted_assign, offsets, w, H, st);
 }
 
 hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
@@ -406,8 +211,7 @@ hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const in
     if (s.dtype == COLIBRI_F32)
         return launch_gemm_f32<EPI_BIAS_ONLY>(false, H, nullptr, s.T, offsets, s.E, w.w2, nullptr, b2, y_sorted, s.h,
                                               s.d, A, st);
-    return launch_gemm_bf16<128, 128, 2, 2, EPI_BIAS_ONLY>(false, H, nullptr, s.T, offsets, s.E, w.w2, nullptr, b2,
-                                                           y_sorted, s.h, s.d, A, st);
+    return launch_gemm_down(s, H, offsets, w, y_sorted, st);
 }
 
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,

@@ -1,0 +1,404 @@
+// Grouped expert GEMM for prefill and mid-sized batches (T > 64), bf16 MFMA.
+//
+// Colibri write-ups: [zskr] http://www.zskr.cn/news/2272131 section 2.1 (the
+// Compute stage: a grouped GEMM over token groups) and 3.3 (every expert's
+// weights share one stride so every tile's shared-memory load pattern is the
+// same); [nxbn] http://m.nxbn.cn/news/48047 section 2.1 (matmul + activation
+// fused in one kernel); [hnwysp] https://www.hnwysp.cn/news/30485 section 2.2
+// (feed the expert kernel row offsets instead of copying rows).
+//
+//   GEMM1: H[p] = act(X[tok(p)] W1[e] + b1[e])  or  silu(X W1[e]) * (X W3[e])
+//   GEMM2: Y[p] = H[p] W2[e] + b2[e]
+//
+// Structure (gfx950):
+//   * tiles: 256 rows of one expert x 256 weight columns (SwiGLU: 128 of W1
+//     and the same 128 of W3), 8 waves in a 2 x 4 grid, two per SIMD, each
+//     owning 128 x 64 of v_mfma_f32_32x32x16_bf16 accumulators; 32-row
+//     subtiles past the expert's last row are skipped;
+//   * tile order: row tiles are numbered expert by expert from the
+//     device-side offsets (the grid is sized for the worst case; surplus
+//     workgroups exit); inside an expert, column tiles go in groups of 8
+//     with all of the expert's row tiles, so tiles that share a weight panel
+//     or token rows run side by side; consecutive tiles are kept on one XCD
+//     (workgroups are dealt to the 8 XCDs round-robin) so they share its L2;
+//   * operands: both go global -> LDS with 16-byte-per-lane copies that skip
+//     the register file (global_load_lds_dwordx4); A rows are gathered
+//     through sorted_assign (GEMM1) or read in place (GEMM2) into
+//     XOR-swizzled rows; the row-major [K, N] weights land as 4 x 16 blocks
+//     that ds_read_b64_tr_b16 turns into k-contiguous MFMA B operands, so no
+//     transposes run in registers;
+//   * pipeline: a ring of two LDS stages; the operands of k-step ks+1 are
+//     read from LDS while k-step ks is multiplied, and the one workgroup
+//     barrier per k-tile sits before the tile's last k-step;
+//   * epilogue: bias + ReLU/GELU, silu(u)*v (the W1 and W3 tiles of a column
+//     block live in the same wave and lane), or bias only; the bf16 tile is
+//     staged through LDS and written back with 16-byte row stores.
+#include "device_common.h"
+#include "ffn_common.h"
+#include "launchers.h"
+
+#include <type_traits>
+
+namespace colibri {
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kGroupN = 8;  // column tiles per scheduling group
+
+struct Tile {
+    int e, row0, rows, n0;
+};
+
+// Logical tile `L` -> (expert, row range, first column).  Row tiles of expert
+// e: ceil(count_e / BM); column tiles: NT.  Whole-wave call; every lane gets
+// the same answer.  Returns the total number of tiles through `total`.
+template <int BM, int BN>
+__device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets, int E, int A, int NT, int b, int &total,
+                                            Tile &t) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int lo = 0, hi = 0;
+    if (lane < E) {
+        lo = min(max(offsets[lane], 0), A);
+        hi = min(max(offsets[lane + 1], lo), A);
+    }
+    const int mt = (hi - lo + BM - 1) / BM;  // row tiles of expert `lane`
+    const int tiles = mt * NT;
+    int incl = tiles;
+#pragma unroll
+    for (int s = 1; s < kWave; s <<= 1) {
+        const int o = __shfl_up(incl, s);
+        if (lane >= s) incl += o;
+    }
+    total = __shfl(incl, kWave - 1);
+    if (b >= total) return false;
+    // keep consecutive logical tiles on one XCD: block b runs on XCD b % 8
+    const int xcd = b % kXcds, i = b / kXcds;
+    const int q = total / kXcds, r = total % kXcds;
+    const int L = xcd * q + min(xcd, r) + i;
+    const int excl = incl - tiles;
+    const uint64_t m = __ballot(lane < E && L >= excl && L < incl);
+    const int e = __ffsll((unsigned long long)m) - 1;
+    const int mte = __shfl(mt, e);
+    const int local = L - __shfl(excl, e);
+    // inside the expert: groups of kGroupN column tiles, each with all row tiles
+    const int ng = local / (mte * kGroupN);
+    const int gs = min(kGroupN, NT - ng * kGroupN);
+    const int rr = local - ng * mte * kGroupN;
+    const int mi = rr / gs;
+    const int ni = ng * kGroupN + rr % gs;
+    t.e = e;
+    t.row0 = __shfl(lo, e) + mi * BM;
+    t.rows = min(BM, __shfl(hi, e) - t.row0);
+    t.n0 = ni * BN;
+    return true;
+}
+
+// 16-byte chunk swizzle inside an A row of BK bf16 (BK/8 chunks): the 16 rows
+// that one ds_read_b128 phase touches land on 16 distinct 16-byte bank slots
+// of the 256-byte bank window.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+    if (BK == 64) return (row ^ (row >> 3)) & 7;  // 128-byte rows: 2 per window
+    return (row >> 2) & 3;                        // 64-byte rows: 4 per window
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// Global -> LDS copy of 16 bytes per lane that bypasses registers
+// (global_load_lds_dwordx4): lane i fills LDS bytes [dst + 16 i, dst + 16 i + 16);
+// dst is wave-uniform and goes through M0 (nothing else in these kernels uses
+// M0).  Issued from inline assembly so that the waits for the copies are
+// placed by hand (wait_vmcnt) rather than before every LDS read.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 in the clobber list
+__device__ __forceinline__ void dma16(const void *src, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory", "m0");
+}
+// same, from a wave-uniform base plus a per-lane 32-bit byte offset
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void *sbase, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(dst)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One BM x BNC output tile of one expert.  NW = WM x WN waves, each owning a
+// (BM/WM) x (BNC/WN) block (for SwiGLU: that block of both W1 and W3).
+//
+// LDS stage (STAGES of them, a ring):
+//   A: BM rows x BK k, 16-byte chunks XOR-swizzled per row (swz);
+//   B: BK k x BN columns (SwiGLU: W1's BNC columns then W3's), stored as
+//      128-byte blocks of 4 k rows x 16 columns, block (kq, n16) at
+//      (kq * BN/16 + n16) * 128, row-major inside.  ds_read_b64_tr_b16 turns
+//      a block into 4 consecutive k of one column per lane, so two of them
+//      give a 32x32x16 MFMA B operand with no register transposes.
+// Both are filled with 1 KB global->LDS copies: an A copy is RPD whole rows,
+// a B copy is 4 k rows x 128 columns (16-byte runs of one weight row).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool GATHER>
+__global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
+    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NT) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int NB = DUAL ? 2 : 1;             // weight matrices per tile
+    constexpr int NW = WM * WN;
+    constexpr int BNC = DUAL ? BN / 2 : BN;      // output columns per tile
+    constexpr int WTM = BM / WM;                 // wave tile rows
+    constexpr int WNC = BNC / WN;                // wave tile columns (per matrix)
+    constexpr int SM = WTM / 32, SJ = WNC / 32;  // 32x32 subtiles per wave (per matrix)
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;  // 1 KB copies per wave per stage
+    constexpr int CPR = BK / 8;                  // 16-byte chunks per A row
+    constexpr int RPD = 64 / CPR;                // A rows per copy
+    constexpr int KQ_ROW = (BN / 16) * 128;      // bytes per 4-k-row band of the B tile
+    constexpr int HPB = BN / 128;                // B copies per band
+    static_assert(SM >= 1 && SJ >= 1, "wave tile too small");
+    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "whole copies per wave");
+    static_assert(NW % HPB == 0, "a wave's B copies share one column range");
+    static_assert(!DUAL || BNC % 128 == 0, "a B copy covers one matrix");
+    static_assert(STAGES >= 2 && (STAGES - 2) * (A_PW + B_PW) <= 63, "vmcnt range");
+    constexpr int LDS_MAIN = STAGES * STAGE_BYTES;
+    constexpr int LDS_EPI = BM * BNC * 2;  // bf16 output tile
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = w / WN, wn = w % WN;
+
+    int total;
+    Tile tl;
+    if (!locate_tile<BM, BNC>(offsets, E, 2 * T, NT, blockIdx.x, total, tl)) return;  // uniform per block
+    const int e = __builtin_amdgcn_readfirstlane(tl.e);
+    const int row0 = __builtin_amdgcn_readfirstlane(tl.row0);
+    const int rows = __builtin_amdgcn_readfirstlane(tl.rows);
+    const int n0 = __builtin_amdgcn_readfirstlane(tl.n0);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_byte *)lds;
+
+    // ---- copy sources.  Rows past the expert's segment read its first row and
+    // columns past N read column 0: they only feed accumulator rows and
+    // columns that are never stored, and every copy stays in bounds.
+    const uint16_t *a_src[A_PW];
+#pragma unroll
+    for (int q = 0; q < A_PW; ++q) {
+        const int m = (w + NW * q) * RPD + lane / CPR;  // tile row of this lane's chunk
+        const int c = (lane % CPR) ^ swz<BK>(m);        // logical chunk held by physical slot lane % CPR
+        long src = row0 + (m < rows ? m : 0);
+        if (GATHER) {
+            const int a = sorted_assign[src];
+            src = (a >= 0 && (a >> 1) < T) ? (a >> 1) : 0;
+        }
+        a_src[q] = A + (size_t)src * K + c * 8;
+    }
+    // B copy w + NW q: band kq = (w + NW q) / HPB, columns [(w % HPB) 128, +128) of the LDS tile;
+    // lane: 16-column block lane / 8, k row 4 kq + (lane % 8) / 2, 8 columns at 8 (lane % 2)
+    const int ncol = (w % HPB) * 128 + (lane >> 3) * 16 + (lane & 1) * 8;
+    const int mat = DUAL ? (w % HPB) * 128 / BNC : 0;  // uniform: one matrix per copy
+    int gcol = n0 + ncol - mat * BNC;
+    if (gcol >= N) gcol = 0;
+    const uint32_t b_voff = (uint32_t)((((lane & 7) >> 1) * N + gcol) * 2);
+    const uint16_t *b_base = (mat ? B1 : B0) + (size_t)e * K * N + (size_t)(w / HPB) * 4 * N;
+
+    auto issue = [&](int s, int kt) {
+        const int k0 = kt * BK;
+        const uint32_t sa = lds0 + s * STAGE_BYTES;
+#pragma unroll
+        for (int q = 0; q < A_PW; ++q) dma16(a_src[q] + k0, sa + (w + NW * q) * 1024);
+#pragma unroll
+        for (int q = 0; q < B_PW; ++q)
+            dma16_s(b_voff, b_base + (size_t)(k0 + 4 * (NW / HPB) * q) * N, sa + A_BYTES + (w + NW * q) * 1024);
+    };
+
+    f32x16 acc[NB][SM][SJ];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int j = 0; j < SJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.0f;
+
+    // 32-row subtiles that hold rows of this expert (the rest is padding)
+    const int live_sm = min(SM, max(0, (rows - wm * WTM + 31) / 32));
+
+    // per-lane LDS read offsets.  A operand (32 rows x 16 k): row lane % 32, chunk 2 ks + lane / 32.
+    int a_row[SM], a_swz[SM];
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+        const int m = wm * WTM + i * 32 + (lane & 31);
+        a_row[i] = m * BK * 2;
+        a_swz[i] = swz<BK>(m);
+    }
+    // B operand (16 k x 32 columns): 16-lane group g holds columns 16 (g % 2) + [0, 16) at k 8 (g / 2) + [0, 8),
+    // read as two transposing 4-k-row reads of blocks (kq, n16)
+    const int g = lane >> 4;
+    const int b_lane = (g >> 1) * 2 * KQ_ROW + (g & 1) * 128 + (lane & 15) * 8;
+
+    // MFMA operands of one 16-k step: SM A fragments, NB x SJ B fragments
+    struct Frags {
+        bf16x8 a[SM];
+        bf16x8 b[NB][SJ];
+    };
+    auto read_frags = [&](int s, int ks, Frags &f) {
+        const lds_byte *L = (const lds_byte *)lds + s * STAGE_BYTES;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < SJ; ++j) {
+                const int cb = b * BNC + wn * WNC + j * 32;  // LDS tile column of the subtile
+                const lds_byte *p = L + A_BYTES + b_lane + ks * 4 * KQ_ROW + (cb >> 4) * 128;
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + KQ_ROW));
+                f.b[b][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+            f.a[i] = *(const lds_bf16x8 *)(L + a_row[i] + (((2 * ks + (lane >> 5)) ^ a_swz[i]) << 4));
+    };
+    // FULL: every 32-row subtile of the wave holds rows of the expert
+    auto mma = [&](const Frags &f, auto full) {
+        constexpr bool FULL = decltype(full)::value;
+#pragma unroll
+        for (int i = 0; i < SM; ++i) {
+            if (!FULL && i >= live_sm) continue;  // uniform per wave
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < SJ; ++j)
+                    acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[b][j], acc[b][i][j], 0, 0, 0);
+        }
+    };
+
+    // ---- main loop over a ring of STAGES LDS stages.  The operands of k-step ks+1 are
+    // read while k-step ks is multiplied; the workgroup barrier sits before the last
+    // k-step of a tile, so the next tile's first reads overlap that step's MFMAs.
+    // After the barrier every wave has finished reading tile kt (the barrier waits for
+    // outstanding LDS reads), so tile kt + STAGES is copied into its stage.  Copies past
+    // the last k-tile re-read it, so every wait covers the same number of copies.
+    constexpr int KS = BK / 16;
+    constexpr int DPW = A_PW + B_PW;
+    const int KT = K / BK;
+    auto ktile = [&](int t) { return t < KT ? t : KT - 1; };
+    auto main_loop = [&](auto full) {
+        Frags f[2];
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) issue(s, ktile(s));
+        wait_vmcnt<(STAGES - 1) * DPW>();  // this wave's copies of k-tile 0 have landed
+        __syncthreads();                    // ... everyone's
+        read_frags(0, 0, f[0]);
+        for (int kt = 0; kt < KT; ++kt) {
+            const int s = kt % STAGES;
+#pragma unroll
+            for (int ks = 0; ks + 1 < KS; ++ks) {
+                read_frags(s, ks + 1, f[(ks + 1) & 1]);
+                mma(f[ks & 1], full);
+            }
+            wait_vmcnt<(STAGES - 2) * DPW>();  // k-tile kt+1 has landed (this wave's copies)
+            __syncthreads();                    // ... everyone's; and k-tile kt is fully read
+            issue(s, ktile(kt + STAGES));
+            if (kt + 1 < KT) read_frags((kt + 1) % STAGES, 0, f[0]);
+            mma(f[(KS - 1) & 1], full);
+        }
+    };
+    if (live_sm == SM) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // ---- epilogue: values -> bf16 tile in LDS -> 16-byte row stores
+    // 32x32 accumulator layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4, column l%32
+    uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
+    const uint16_t *bias_e = bias ? bias + (size_t)e * N : nullptr;
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SJ; ++j) {
+            const int cl = wn * WNC + j * 32 + (lane & 31);  // tile column
+            const int n = n0 + cl;
+            float bv = 0.0f;
+            if (EPI != EPI_SWIGLU && bias_e != nullptr && n < N) bv = bf16_to_f32(bias_e[n]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                float v;
+                if (EPI == EPI_SWIGLU) v = silu(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
+                else if (EPI == EPI_ACT_RELU) v = apply_act<ACT_RELU>(acc[0][i][j][r] + bv);
+                else if (EPI == EPI_ACT_GELU) v = apply_act<ACT_GELU>(acc[0][i][j][r] + bv);
+                else v = acc[0][i][j][r] + bv;
+                Cs[rl * BNC + cl] = (uint16_t)f32_to_bf16_bits(v);
+            }
+        }
+    __syncthreads();
+    constexpr int VPR = BNC / 8;  // 16-byte vectors per output row
+    for (int idx = tid; idx < BM * VPR; idx += NW * kWave) {
+        const int rl = idx / VPR, cv = idx % VPR;
+        const int n = n0 + cv * 8;
+        if (rl < rows && n < N)
+            *reinterpret_cast<u32x4 *>(C + (size_t)(row0 + rl) * N + n) =
+                *reinterpret_cast<const u32x4 *>(Cs + rl * BNC + cv * 8);
+    }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI>
+hipError_t launch_cfg(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
+                      const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
+                      hipStream_t st) {
+    constexpr int BNC = EPI == EPI_SWIGLU ? BN / 2 : BN;
+    const int A = 2 * s.T;
+    const int NT = (N + BNC - 1) / BNC;
+    const int mtiles = (A + BM - 1) / BM + std::min(s.E, A);
+    const dim3 grid(mtiles * NT);
+    constexpr int threads = WM * WN * kWave;
+    if (gather)
+        ffn_gemm_kernel<BM, BN, BK, WM, WN, STAGES, EPI, true><<<grid, threads, 0, st>>>(
+            (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
+            (const uint16_t *)bias, (uint16_t *)C, K, N, NT);
+    else
+        ffn_gemm_kernel<BM, BN, BK, WM, WN, STAGES, EPI, false><<<grid, threads, 0, st>>>(
+            (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
+            (const uint16_t *)bias, (uint16_t *)C, K, N, NT);
+    return hipGetLastError();
+}
+
+// 256 x 256 tiles (256 x 128 outputs of both W1 and W3 for SwiGLU), BK = 64,
+// two LDS stages (128 KB), 8 waves: one workgroup per CU, two waves per SIMD.
+template <int EPI>
+hipError_t launch_gemm(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
+                       const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
+                       hipStream_t st) {
+    return launch_cfg<256, 256, 64, 2, 4, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, st);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                          const int32_t *offsets, const colibri_moe_experts_t &w, void *H, hipStream_t st) {
+    const bool gather = sorted_assign != nullptr;
+    switch (s.act) {
+        case COLIBRI_ACT_RELU:
+            return launch_gemm<EPI_ACT_RELU>(gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d,
+                                             s.h, st);
+        case COLIBRI_ACT_GELU:
+            return launch_gemm<EPI_ACT_GELU>(gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d,
+                                             s.h, st);
+        default:
+            return launch_gemm<EPI_SWIGLU>(gather, s, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, s.d,
+                                           s.h, st);
+    }
+}
+
+hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
+                            const colibri_moe_experts_t &w, void *y, hipStream_t st) {
+    const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
+    return launch_gemm<EPI_BIAS_ONLY>(false, s, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d, st);
+}
+
+}  // namespace colibri

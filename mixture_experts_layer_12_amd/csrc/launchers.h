@@ -53,6 +53,11 @@ hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
                                    hipStream_t st);
+// bf16 grouped MFMA GEMMs for T > 64 (ffn_gemm.hip)
+hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                          const int32_t *offsets, const colibri_moe_experts_t &w, void *H, hipStream_t st);
+hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
+                            const colibri_moe_experts_t &w, void *y, hipStream_t st);
 // H then Y, with H and the scratch carved from ws.
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
