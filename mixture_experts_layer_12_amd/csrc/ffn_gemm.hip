@@ -11,15 +11,16 @@
 //   GEMM2: Y[p] = H[p] W2[e] + b2[e]
 //
 // Structure (gfx950):
-//   * tiles: 256 rows of one expert x 256 weight columns (SwiGLU: 128 of W1
-//     and the same 128 of W3), 8 waves in a 2 x 4 grid, two per SIMD, each
-//     owning 128 x 64 of v_mfma_f32_32x32x16_bf16 accumulators; 32-row
-//     subtiles past the expert's last row are skipped;
+//   * tiles: up to 320 rows of one expert x 256 weight columns (SwiGLU: 128
+//     of W1 and the same 128 of W3), 8 waves in a 2 x 4 grid, two per SIMD;
+//     the tile's 32-row subtiles are split evenly over the two wave rows,
+//     each wave owning up to 5 x 2 v_mfma_f32_32x32x16_bf16 accumulators;
 //   * tile order: row tiles are numbered expert by expert from the
 //     device-side offsets (the grid is sized for the worst case; surplus
-//     workgroups exit); inside an expert, column tiles go in groups of 8
-//     with all of the expert's row tiles, so tiles that share a weight panel
-//     or token rows run side by side; consecutive tiles are kept on one XCD
+//     workgroups exit); inside an expert, column tiles go in groups with all
+//     of the expert's row tiles, sized to fit one XCD's 32 CUs, so tiles that
+//     share a weight panel or token rows run side by side; consecutive tiles
+//     are kept on one XCD
 //     (workgroups are dealt to the 8 XCDs round-robin) so they share its L2;
 //   * operands: both go global -> LDS with 16-byte-per-lane copies that skip
 //     the register file (global_load_lds_dwordx4); A rows are gathered
@@ -43,16 +44,28 @@ namespace colibri {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kGroupN = 8;  // column tiles per scheduling group
+constexpr int kCusPerXcd = 32;  // a scheduling group fits the CUs of one XCD
 
 struct Tile {
     int e, row0, rows, n0;
 };
 
-// Logical tile `L` -> (expert, row range, first column).  Row tiles of expert
-// e: ceil(count_e / BM); column tiles: NT.  Whole-wave call; every lane gets
-// the same answer.  Returns the total number of tiles through `total`.
-template <int BM, int BN>
+// Row tiles of expert e: count_e rows are cut into ceil(count_e / BMB) row
+// tiles, except that a tail of at most BMB / 4 rows is spread over the other
+// tiles when they stay within BM rows (an expert of 1030 rows runs as 4 tiles
+// of ~258 rows, not 4 full tiles plus a 6-row tile that would stream the whole
+// weight panel for 6 rows); the tiles of an expert are of (nearly) equal size.
+__device__ __forceinline__ int row_tiles(int rows, int BMB, int BM) {
+    int mt = (rows + BMB - 1) / BMB;
+    const int tail = rows % BMB;
+    if (mt > 1 && tail != 0 && tail <= BMB / 4 && rows <= BM * (mt - 1)) mt -= 1;
+    return mt;
+}
+
+// Logical tile `L` -> (expert, row range, first column); column tiles: NT.
+// Whole-wave call; every lane gets the same answer.  Returns the total number
+// of tiles through `total`.
+template <int BMB, int BM, int BN>
 __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets, int E, int A, int NT, int b, int &total,
                                             Tile &t) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -61,7 +74,8 @@ __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets,
         lo = min(max(offsets[lane], 0), A);
         hi = min(max(offsets[lane + 1], lo), A);
     }
-    const int mt = (hi - lo + BM - 1) / BM;  // row tiles of expert `lane`
+    const int mt = row_tiles(hi - lo, BMB, BM);           // row tiles of expert `lane`
+    const int rt = mt > 0 ? (hi - lo + mt - 1) / mt : 0;  // rows per row tile (<= BM)
     const int tiles = mt * NT;
     int incl = tiles;
 #pragma unroll
@@ -80,15 +94,18 @@ __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets,
     const int e = __ffsll((unsigned long long)m) - 1;
     const int mte = __shfl(mt, e);
     const int local = L - __shfl(excl, e);
-    // inside the expert: groups of kGroupN column tiles, each with all row tiles
-    const int ng = local / (mte * kGroupN);
-    const int gs = min(kGroupN, NT - ng * kGroupN);
-    const int rr = local - ng * mte * kGroupN;
+    // inside the expert: groups of gn column tiles, each with all mte row tiles,
+    // gn * mte <= one XCD's CUs so that a group's tiles are resident together
+    const int gn = max(1, kCusPerXcd / mte);
+    const int ng = local / (mte * gn);
+    const int gs = min(gn, NT - ng * gn);
+    const int rr = local - ng * mte * gn;
     const int mi = rr / gs;
-    const int ni = ng * kGroupN + rr % gs;
+    const int ni = ng * gn + rr % gs;
     t.e = e;
-    t.row0 = __shfl(lo, e) + mi * BM;
-    t.rows = min(BM, __shfl(hi, e) - t.row0);
+    const int rte = __shfl(rt, e);
+    t.row0 = __shfl(lo, e) + mi * rte;
+    t.rows = min(rte, __shfl(hi, e) - t.row0);
     t.n0 = ni * BN;
     return true;
 }
@@ -140,7 +157,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 //      give a 32x32x16 MFMA B operand with no register transposes.
 // Both are filled with 1 KB global->LDS copies: an A copy is RPD whole rows,
 // a B copy is 4 k rows x 128 columns (16-byte runs of one weight row).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool GATHER>
+template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool GATHER>
 __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
@@ -175,7 +192,7 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
 
     int total;
     Tile tl;
-    if (!locate_tile<BM, BNC>(offsets, E, 2 * T, NT, blockIdx.x, total, tl)) return;  // uniform per block
+    if (!locate_tile<BMB, BM, BNC>(offsets, E, 2 * T, NT, blockIdx.x, total, tl)) return;  // uniform per block
     const int e = __builtin_amdgcn_readfirstlane(tl.e);
     const int row0 = __builtin_amdgcn_readfirstlane(tl.row0);
     const int rows = __builtin_amdgcn_readfirstlane(tl.rows);
@@ -185,12 +202,22 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     // ---- copy sources.  Rows past the expert's segment read its first row and
     // columns past N read column 0: they only feed accumulator rows and
     // columns that are never stored, and every copy stays in bounds.
+    // The tile's ceil(rows / 32) subtiles are split evenly over the WM wave rows:
+    // wave row wm owns tile rows [wm * per * 32, +live_sm * 32) (per <= SM since
+    // rows <= BM).  In LDS, wave row wm's rows always start at wm * WTM, so the
+    // operand reads have fixed offsets; the copies place the rows accordingly.
+    const int nsub = (rows + 31) / 32;
+    const int per = (nsub + WM - 1) / WM;
+    const int live_sm = min(per, max(0, nsub - wm * per));
+    const int wrow = wm * per * 32;  // first tile row of this wave
     const uint16_t *a_src[A_PW];
 #pragma unroll
     for (int q = 0; q < A_PW; ++q) {
-        const int m = (w + NW * q) * RPD + lane / CPR;  // tile row of this lane's chunk
+        const int m = (w + NW * q) * RPD + lane / CPR;  // LDS row of this lane's chunk
         const int c = (lane % CPR) ^ swz<BK>(m);        // logical chunk held by physical slot lane % CPR
-        long src = row0 + (m < rows ? m : 0);
+        const int reg = m / WTM, off = m % WTM;         // wave row region and row inside it
+        const int r = reg * per * 32 + off;             // tile row
+        long src = row0 + ((off < per * 32 && r < rows) ? r : 0);
         if (GATHER) {
             const int a = sorted_assign[src];
             src = (a >= 0 && (a >> 1) < T) ? (a >> 1) : 0;
@@ -226,8 +253,6 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.0f;
 
-    // 32-row subtiles that hold rows of this expert (the rest is padding)
-    const int live_sm = min(SM, max(0, (rows - wm * WTM + 31) / 32));
 
     // per-lane LDS read offsets.  A operand (32 rows x 16 k): row lane % 32, chunk 2 ks + lane / 32.
     int a_row[SM], a_swz[SM];
@@ -247,7 +272,11 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
         bf16x8 a[SM];
         bf16x8 b[NB][SJ];
     };
-    auto read_frags = [&](int s, int ks, Frags &f) {
+    // lv: compile-time count of live subtiles (LV >= 0) or LV = -1 for the runtime live_sm
+    auto read_frags = [&](int s, int ks, Frags &f, auto lv) {
+        constexpr int LV = decltype(lv)::value;
+        const int nl = LV >= 0 ? LV : live_sm;
+        if (nl == 0) return;  // this wave's rows are all padding
         const lds_byte *L = (const lds_byte *)lds + s * STAGE_BYTES;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -260,15 +289,17 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
                 f.b[b][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
 #pragma unroll
-        for (int i = 0; i < SM; ++i)
+        for (int i = 0; i < SM; ++i) {
+            if (i >= nl) break;  // uniform per wave
             f.a[i] = *(const lds_bf16x8 *)(L + a_row[i] + (((2 * ks + (lane >> 5)) ^ a_swz[i]) << 4));
+        }
     };
-    // FULL: every 32-row subtile of the wave holds rows of the expert
-    auto mma = [&](const Frags &f, auto full) {
-        constexpr bool FULL = decltype(full)::value;
+    auto mma = [&](const Frags &f, auto lv) {
+        constexpr int LV = decltype(lv)::value;
+        const int nl = LV >= 0 ? LV : live_sm;
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
-            if (!FULL && i >= live_sm) continue;  // uniform per wave
+            if (i >= nl) break;  // uniform per wave
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -287,29 +318,31 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     constexpr int DPW = A_PW + B_PW;
     const int KT = K / BK;
     auto ktile = [&](int t) { return t < KT ? t : KT - 1; };
-    auto main_loop = [&](auto full) {
+    auto main_loop = [&](auto lv) {
         Frags f[2];
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) issue(s, ktile(s));
         wait_vmcnt<(STAGES - 1) * DPW>();  // this wave's copies of k-tile 0 have landed
         __syncthreads();                    // ... everyone's
-        read_frags(0, 0, f[0]);
+        read_frags(0, 0, f[0], lv);
         for (int kt = 0; kt < KT; ++kt) {
             const int s = kt % STAGES;
 #pragma unroll
             for (int ks = 0; ks + 1 < KS; ++ks) {
-                read_frags(s, ks + 1, f[(ks + 1) & 1]);
-                mma(f[ks & 1], full);
+                read_frags(s, ks + 1, f[(ks + 1) & 1], lv);
+                mma(f[ks & 1], lv);
             }
             wait_vmcnt<(STAGES - 2) * DPW>();  // k-tile kt+1 has landed (this wave's copies)
             __syncthreads();                    // ... everyone's; and k-tile kt is fully read
             issue(s, ktile(kt + STAGES));
-            if (kt + 1 < KT) read_frags((kt + 1) % STAGES, 0, f[0]);
-            mma(f[(KS - 1) & 1], full);
+            if (kt + 1 < KT) read_frags((kt + 1) % STAGES, 0, f[0], lv);
+            mma(f[(KS - 1) & 1], lv);
         }
     };
-    if (live_sm == SM) main_loop(std::true_type{});
-    else main_loop(std::false_type{});
+    // the common live counts get their own copy of the loop, free of per-subtile tests
+    if (live_sm == SM) main_loop(std::integral_constant<int, SM>{});
+    else if (live_sm == SM - 1) main_loop(std::integral_constant<int, SM - 1>{});
+    else main_loop(std::integral_constant<int, -1>{});
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -318,7 +351,8 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
     const uint16_t *bias_e = bias ? bias + (size_t)e * N : nullptr;
 #pragma unroll
-    for (int i = 0; i < SM; ++i)
+    for (int i = 0; i < SM; ++i) {
+        if (i >= live_sm) break;  // padding subtiles may alias the next wave row's tile rows
 #pragma unroll
         for (int j = 0; j < SJ; ++j) {
             const int cl = wn * WNC + j * 32 + (lane & 31);  // tile column
@@ -327,7 +361,7 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
             if (EPI != EPI_SWIGLU && bias_e != nullptr && n < N) bv = bf16_to_f32(bias_e[n]);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int rl = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int rl = wrow + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 float v;
                 if (EPI == EPI_SWIGLU) v = silu(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
                 else if (EPI == EPI_ACT_RELU) v = apply_act<ACT_RELU>(acc[0][i][j][r] + bv);
@@ -336,6 +370,7 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
                 Cs[rl * BNC + cl] = (uint16_t)f32_to_bf16_bits(v);
             }
         }
+    }
     __syncthreads();
     constexpr int VPR = BNC / 8;  // 16-byte vectors per output row
     for (int idx = tid; idx < BM * VPR; idx += NW * kWave) {
@@ -347,34 +382,35 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI>
+template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI>
 hipError_t launch_cfg(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
                       const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
                       hipStream_t st) {
     constexpr int BNC = EPI == EPI_SWIGLU ? BN / 2 : BN;
     const int A = 2 * s.T;
     const int NT = (N + BNC - 1) / BNC;
-    const int mtiles = (A + BM - 1) / BM + std::min(s.E, A);
+    const int mtiles = (A + BMB - 1) / BMB + std::min(s.E, A);  // bound on the row tiles of all experts
     const dim3 grid(mtiles * NT);
     constexpr int threads = WM * WN * kWave;
     if (gather)
-        ffn_gemm_kernel<BM, BN, BK, WM, WN, STAGES, EPI, true><<<grid, threads, 0, st>>>(
+        ffn_gemm_kernel<BMB, BM, BN, BK, WM, WN, STAGES, EPI, true><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
             (const uint16_t *)bias, (uint16_t *)C, K, N, NT);
     else
-        ffn_gemm_kernel<BM, BN, BK, WM, WN, STAGES, EPI, false><<<grid, threads, 0, st>>>(
+        ffn_gemm_kernel<BMB, BM, BN, BK, WM, WN, STAGES, EPI, false><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
             (const uint16_t *)bias, (uint16_t *)C, K, N, NT);
     return hipGetLastError();
 }
 
-// 256 x 256 tiles (256 x 128 outputs of both W1 and W3 for SwiGLU), BK = 64,
-// two LDS stages (128 KB), 8 waves: one workgroup per CU, two waves per SIMD.
+// Row tiles of 256 rows (up to 320 when a small tail is spread over them) x
+// 256 weight columns (SwiGLU: 128 outputs of both W1 and W3), BK = 64, two LDS
+// stages (144 KB), 8 waves: one workgroup per CU, two waves per SIMD.
 template <int EPI>
 hipError_t launch_gemm(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
                        const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
                        hipStream_t st) {
-    return launch_cfg<256, 256, 64, 2, 4, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, st);
+    return launch_cfg<256, 320, 256, 64, 2, 4, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, st);
 }
 
 }  // namespace

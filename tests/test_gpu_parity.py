@@ -266,6 +266,25 @@ def test_ffn_decode_expert_over_32_rows():
     assert np.array_equal(y, y2)
 
 
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_ffn_row_tiles_split_evenly(act):
+    """Per-expert counts around multiples of the GEMM's 256-row tile: experts are
+    cut into equal row tiles (641 rows -> 3 x 214, 321 -> 2 x 161, 650 -> 3 x 217),
+    a tail of at most 64 rows is spread over the other tiles (320 -> 1 x 320,
+    1030 -> 4 x 258), and the 32-row subtiles split unevenly over the two wave
+    rows (4/3, 3/3, 5/5, 5/4) or leave one wave row empty (1 and 10 rows)."""
+    counts = [641, 321, 320, 33, 1, 0, 650, 10, 1030]
+    E = len(counts)
+    rng = np.random.default_rng(21)
+    slots = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts))
+    T = len(slots) // 2
+    w, _ = small_ffn_case(act, gen.BF16, T=T, E=E, d=128, h=256, seed=21)
+    idx = slots.reshape(T, 2)
+    for gather in (True, False):
+        y, y_ref = run_ffn(w, idx, act, gen.BF16, E=E, gather=gather)
+        G.assert_bf16_close(y, y_ref, f"row tiles {act} gather={gather}")
+
+
 def test_ffn_degenerate_routings():
     E = 8
     for seed, skew in ((1, [0.93] + [0.01] * 7), (2, [0.5, 0.5, 0, 0, 0, 0, 0, 0])):
