@@ -216,16 +216,17 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
     hipError_t e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream);
     if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
     if (e != hipSuccess) return hip_status(e);
-    if (ffn_decode_eligible(*s) && decode_plan(*s, false).S > 1) {
-        // decode sizes with a K-split second layer: the combine adds the split partials
+    const int Sd = ffn_down_splits(*s);
+    if (Sd > 1) {
+        // the second layer's K is split: the combine adds its partials (with b2) directly
         const size_t el = elem_size(s);
         char *H = static_cast<char *>(ffn_ws);
         void *scratch = H + align256((size_t)2 * s->T * s->h * el);
         e = launch_ffn_up(*s, x, sorted, offsets, *w, H, scratch, stream);
-        if (e == hipSuccess) e = launch_decode_down(*s, H, offsets, *w, nullptr, scratch, false, stream);
+        if (e == hipSuccess) e = launch_ffn_down(*s, H, offsets, *w, nullptr, scratch, stream, false);
         if (e == hipSuccess)
-            e = launch_combine_partials(*s, static_cast<const float *>(scratch), decode_plan(*s, false).S, pos, idx,
-                                        gate, s->act == COLIBRI_ACT_SWIGLU ? nullptr : w->b2, out, stream);
+            e = launch_combine_partials(*s, static_cast<const float *>(scratch), Sd, pos, idx, gate,
+                                        s->act == COLIBRI_ACT_SWIGLU ? nullptr : w->b2, out, stream);
         return hip_status(e);
     }
     e = launch_expert_ffn(*s, x, sorted, offsets, *w, y, ffn_ws, stream);

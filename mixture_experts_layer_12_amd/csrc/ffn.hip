@@ -170,10 +170,17 @@ hipError_t launch_gemm_f32(bool gather, const void *Am, const int32_t *sa, int T
 }  // namespace
 
 size_t ffn_up_scratch_bytes(const colibri_moe_shape_t &s) {
-    return ffn_decode_eligible(s) ? ffn_decode_scratch_bytes(s) : 0;
+    if (ffn_decode_eligible(s)) return ffn_decode_scratch_bytes(s);
+    return s.dtype == COLIBRI_BF16 ? gemm_scratch_bytes(s, true) : 0;
 }
 size_t ffn_down_scratch_bytes(const colibri_moe_shape_t &s) {
-    return ffn_decode_eligible(s) ? ffn_decode_scratch_bytes(s) : 0;
+    if (ffn_decode_eligible(s)) return ffn_decode_scratch_bytes(s);
+    return s.dtype == COLIBRI_BF16 ? gemm_scratch_bytes(s, false) : 0;
+}
+
+int ffn_down_splits(const colibri_moe_shape_t &s) {
+    if (ffn_decode_eligible(s)) return decode_plan(s, false).S;
+    return s.dtype == COLIBRI_BF16 ? gemm_splits(s, false) : 1;
 }
 
 size_t ffn_workspace_bytes(const colibri_moe_shape_t &s) {
@@ -200,18 +207,19 @@ hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const
                                                    nullptr, H, s.d, s.h, A, st);
         }
     }
-    return launch_gemm_up(s, x_rows, sorted_assign, offsets, w, H, st);
+    return launch_gemm_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
 }
 
 hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                           const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st) {
-    if (ffn_decode_eligible(s)) return launch_decode_down(s, H, offsets, w, y_sorted, scratch, true, st);
+                           const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st,
+                           bool reduce) {
+    if (ffn_decode_eligible(s)) return launch_decode_down(s, H, offsets, w, y_sorted, scratch, reduce, st);
     const int A = 2 * s.T;
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
     if (s.dtype == COLIBRI_F32)
         return launch_gemm_f32<EPI_BIAS_ONLY>(false, H, nullptr, s.T, offsets, s.E, w.w2, nullptr, b2, y_sorted, s.h,
                                               s.d, A, st);
-    return launch_gemm_down(s, H, offsets, w, y_sorted, st);
+    return launch_gemm_down(s, H, offsets, w, y_sorted, scratch, reduce, st);
 }
 
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,

@@ -313,11 +313,11 @@ hipError_t launch_decode_t(const colibri_moe_shape_t &s, const DecodePlan &p, bo
 }
 
 template <int EPI>
-hipError_t launch_reduce_t(const colibri_moe_shape_t &s, const DecodePlan &p, const int32_t *offsets,
-                           const void *bias, void *C, int N, const void *scratch, hipStream_t st) {
+hipError_t launch_reduce_t(const colibri_moe_shape_t &s, int S, const int32_t *offsets, const void *bias, void *C,
+                           int N, const void *scratch, hipStream_t st) {
     const size_t total = (size_t)2 * s.T * (N / 4);
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
-    split_reduce_kernel<EPI><<<blocks, 256, 0, st>>>((const float *)scratch, p.S, s.T, offsets, s.E,
+    split_reduce_kernel<EPI><<<blocks, 256, 0, st>>>((const float *)scratch, S, s.T, offsets, s.E,
                                                      (const uint16_t *)bias, (uint16_t *)C, N);
     return hipGetLastError();
 }
@@ -327,7 +327,7 @@ hipError_t up_t(const colibri_moe_shape_t &s, const DecodePlan &p, bool gather, 
                 const int32_t *sa, const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *H,
                 void *scratch, hipStream_t st) {
     hipError_t err = launch_decode_t<EPI>(s, p, gather, x_rows, sa, offsets, B0, B1, bias, H, s.d, s.h, scratch, st);
-    if (err == hipSuccess && p.S > 1) err = launch_reduce_t<EPI>(s, p, offsets, bias, H, s.h, scratch, st);
+    if (err == hipSuccess && p.S > 1) err = launch_reduce_t<EPI>(s, p.S, offsets, bias, H, s.h, scratch, st);
     return err;
 }
 }  // namespace
@@ -357,8 +357,20 @@ hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const
     hipError_t err = launch_decode_t<EPI_BIAS_ONLY>(s, p, false, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d,
                                                     scratch, st);
     if (err == hipSuccess && p.S > 1 && reduce)
-        err = launch_reduce_t<EPI_BIAS_ONLY>(s, p, offsets, b2, y, s.d, scratch, st);
+        err = launch_reduce_t<EPI_BIAS_ONLY>(s, p.S, offsets, b2, y, s.d, scratch, st);
     return err;
+}
+
+hipError_t launch_split_reduce(const colibri_moe_shape_t &s, bool up, int S, const int32_t *offsets,
+                               const colibri_moe_experts_t &w, void *C, const float *part, hipStream_t st) {
+    if (!up)
+        return launch_reduce_t<EPI_BIAS_ONLY>(s, S, offsets, s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2, C, s.d,
+                                              part, st);
+    switch (s.act) {
+        case COLIBRI_ACT_RELU: return launch_reduce_t<EPI_ACT_RELU>(s, S, offsets, w.b1, C, s.h, part, st);
+        case COLIBRI_ACT_GELU: return launch_reduce_t<EPI_ACT_GELU>(s, S, offsets, w.b1, C, s.h, part, st);
+        default: return launch_reduce_t<EPI_SWIGLU>(s, S, offsets, nullptr, C, s.h, part, st);
+    }
 }
 
 }  // namespace colibri

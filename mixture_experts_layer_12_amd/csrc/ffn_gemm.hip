@@ -47,7 +47,7 @@ constexpr int kXcds = 8;
 constexpr int kCusPerXcd = 32;  // a scheduling group fits the CUs of one XCD
 
 struct Tile {
-    int e, row0, rows, n0;
+    int e, row0, rows, n0, split;
 };
 
 // Row tiles of expert e: count_e rows are cut into ceil(count_e / BMB) row
@@ -62,11 +62,11 @@ __device__ __forceinline__ int row_tiles(int rows, int BMB, int BM) {
     return mt;
 }
 
-// Logical tile `L` -> (expert, row range, first column); column tiles: NT.
-// Whole-wave call; every lane gets the same answer.  Returns the total number
-// of tiles through `total`.
+// Block b -> (expert, row range, first column, K split); column tiles: NT,
+// K splits: S.  Whole-wave call; every lane gets the same answer.  Returns
+// false for surplus blocks (the grid is sized for the worst case).
 template <int BMB, int BM, int BN>
-__device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets, int E, int A, int NT, int b, int &total,
+__device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets, int E, int A, int NT, int S, int b,
                                             Tile &t) {
     const int lane = threadIdx.x & (kWave - 1);
     int lo = 0, hi = 0;
@@ -83,12 +83,15 @@ __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets,
         const int o = __shfl_up(incl, s);
         if (lane >= s) incl += o;
     }
-    total = __shfl(incl, kWave - 1);
-    if (b >= total) return false;
-    // keep consecutive logical tiles on one XCD: block b runs on XCD b % 8
+    const int total = __shfl(incl, kWave - 1);
+    if (b >= total * S) return false;
+    // keep consecutive logical indices on one XCD: block b runs on XCD b % 8;
+    // the index is split-major, so one XCD works on one K range of neighbouring tiles
     const int xcd = b % kXcds, i = b / kXcds;
-    const int q = total / kXcds, r = total % kXcds;
-    const int L = xcd * q + min(xcd, r) + i;
+    const int q = total * S / kXcds, r = total * S % kXcds;
+    const int LS = xcd * q + min(xcd, r) + i;
+    t.split = LS / total;
+    const int L = LS - t.split * total;
     const int excl = incl - tiles;
     const uint64_t m = __ballot(lane < E && L >= excl && L < incl);
     const int e = __ffsll((unsigned long long)m) - 1;
@@ -161,7 +164,8 @@ template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, 
 __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
-    const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NT) {
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NT, int S,
+    float *__restrict__ part) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr int NB = DUAL ? 2 : 1;             // weight matrices per tile
     constexpr int NW = WM * WN;
@@ -190,13 +194,13 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = w / WN, wn = w % WN;
 
-    int total;
     Tile tl;
-    if (!locate_tile<BMB, BM, BNC>(offsets, E, 2 * T, NT, blockIdx.x, total, tl)) return;  // uniform per block
+    if (!locate_tile<BMB, BM, BNC>(offsets, E, 2 * T, NT, S, blockIdx.x, tl)) return;  // uniform per block
     const int e = __builtin_amdgcn_readfirstlane(tl.e);
     const int row0 = __builtin_amdgcn_readfirstlane(tl.row0);
     const int rows = __builtin_amdgcn_readfirstlane(tl.rows);
     const int n0 = __builtin_amdgcn_readfirstlane(tl.n0);
+    const int split = __builtin_amdgcn_readfirstlane(tl.split);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_byte *)lds;
 
     // ---- copy sources.  Rows past the expert's segment read its first row and
@@ -316,8 +320,10 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     // the last k-tile re-read it, so every wait covers the same number of copies.
     constexpr int KS = BK / 16;
     constexpr int DPW = A_PW + B_PW;
-    const int KT = K / BK;
-    auto ktile = [&](int t) { return t < KT ? t : KT - 1; };
+    // this block's K range: k-tiles [kt0, kt0 + KT) of the K / BK
+    const int kt0 = split * (K / BK) / S;
+    const int KT = (split + 1) * (K / BK) / S - kt0;
+    auto ktile = [&](int t) { return kt0 + (t < KT ? t : KT - 1); };
     auto main_loop = [&](auto lv) {
         Frags f[2];
 #pragma unroll
@@ -346,8 +352,33 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     wait_vmcnt<0>();
     __syncthreads();
 
-    // ---- epilogue: values -> bf16 tile in LDS -> 16-byte row stores
+    // ---- K split: the fp32 partial sums go to part[split][row][col] (SwiGLU: the
+    // W3 products at col + N); a later kernel adds the splits and applies the epilogue
     // 32x32 accumulator layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4, column l%32
+    if (S > 1) {
+        constexpr int NC = DUAL ? 2 : 1;
+        float *pb = part + ((size_t)split * 2 * T + row0) * (size_t)(NC * N);
+#pragma unroll
+        for (int i = 0; i < SM; ++i) {
+            if (i >= live_sm) break;
+#pragma unroll
+            for (int j = 0; j < SJ; ++j) {
+                const int n = n0 + wn * WNC + j * 32 + (lane & 31);
+                if (n >= N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rl = wrow + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (rl >= rows) continue;
+                    float *dst = pb + (size_t)rl * (NC * N) + n;
+                    dst[0] = acc[0][i][j][r];
+                    if (DUAL) dst[N] = acc[NB - 1][i][j][r];
+                }
+            }
+        }
+        return;
+    }
+
+    // ---- epilogue: values -> bf16 tile in LDS -> 16-byte row stores
     uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
     const uint16_t *bias_e = bias ? bias + (size_t)e * N : nullptr;
 #pragma unroll
@@ -382,59 +413,103 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     }
 }
 
-template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI>
-hipError_t launch_cfg(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
-                      const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
-                      hipStream_t st) {
-    constexpr int BNC = EPI == EPI_SWIGLU ? BN / 2 : BN;
-    const int A = 2 * s.T;
-    const int NT = (N + BNC - 1) / BNC;
-    const int mtiles = (A + BMB - 1) / BMB + std::min(s.E, A);  // bound on the row tiles of all experts
-    const dim3 grid(mtiles * NT);
-    constexpr int threads = WM * WN * kWave;
-    if (gather)
-        ffn_gemm_kernel<BMB, BM, BN, BK, WM, WN, STAGES, EPI, true><<<grid, threads, 0, st>>>(
-            (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
-            (const uint16_t *)bias, (uint16_t *)C, K, N, NT);
-    else
-        ffn_gemm_kernel<BMB, BM, BN, BK, WM, WN, STAGES, EPI, false><<<grid, threads, 0, st>>>(
-            (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
-            (const uint16_t *)bias, (uint16_t *)C, K, N, NT);
-    return hipGetLastError();
-}
+// Tile shape of the launch: row tiles of 256 rows (up to 320 when a small tail
+// is spread over them) x 256 weight columns (SwiGLU: 128 outputs of both W1 and
+// W3), BK = 64, two LDS stages (144 KB), 8 waves: one workgroup per CU, two
+// waves per SIMD.
+constexpr int kBMB = 256, kBM = 320, kBN = 256, kBK = 64;
 
-// Row tiles of 256 rows (up to 320 when a small tail is spread over them) x
-// 256 weight columns (SwiGLU: 128 outputs of both W1 and W3), BK = 64, two LDS
-// stages (144 KB), 8 waves: one workgroup per CU, two waves per SIMD.
 template <int EPI>
 hipError_t launch_gemm(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
                        const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
-                       hipStream_t st) {
-    return launch_cfg<256, 320, 256, 64, 2, 4, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, st);
+                       int S, float *part, hipStream_t st) {
+    constexpr int BNC = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+    const int A = 2 * s.T;
+    const int NT = (N + BNC - 1) / BNC;
+    const int mtiles = (A + kBMB - 1) / kBMB + std::min(s.E, A);  // bound on the row tiles of all experts
+    const dim3 grid(mtiles * NT * S);
+    constexpr int threads = 2 * 4 * kWave;
+    if (gather)
+        ffn_gemm_kernel<kBMB, kBM, kBN, kBK, 2, 4, 2, EPI, true><<<grid, threads, 0, st>>>(
+            (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
+            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, part);
+    else
+        ffn_gemm_kernel<kBMB, kBM, kBN, kBK, 2, 4, 2, EPI, false><<<grid, threads, 0, st>>>(
+            (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
+            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, part);
+    return hipGetLastError();
 }
 
 }  // namespace
 
+// K splits of one layer.  Mid-sized batches (a few hundred rows per expert)
+// make too few tiles to fill 256 CUs; splitting K multiplies the blocks at the
+// cost of fp32 partials [S][2T][cols] written and read once more.  The split
+// minimises (rounds of 256 blocks) x (k-tiles per block + 2, a per-block
+// start-up cost) over the S whose partials stay within a quarter of the
+// layer's weight bytes, with at least 4 k-tiles per block; ties keep the
+// smaller S.  Expected row tiles: one per expert while experts hold at most
+// 320 rows, else one per 256 rows.
+int gemm_splits(const colibri_moe_shape_t &s, bool up) {
+    if (s.dtype != COLIBRI_BF16 || s.T <= 0) return 1;
+    const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
+    const long K = up ? s.d : s.h, N = up ? s.h : s.d;
+    const long A = 2L * s.T;
+    const long NT = (N + (dual ? kBN / 2 : kBN) - 1) / (dual ? kBN / 2 : kBN);
+    const long rt = std::max<long>(std::min<long>(s.E, A), (A + kBMB - 1) / kBMB);
+    const long tiles = rt * NT;
+    const long KT = K / kBK;
+    const double weight_bytes = (double)std::min<long>(s.E, A) * K * N * 2 * (dual ? 2 : 1);
+    int best = 1;
+    double best_cost = 1e300;
+    for (long S = 1; S <= KT / 4 || S == 1; ++S) {
+        const double part_bytes = (double)S * A * N * (dual ? 2 : 1) * 4;
+        if (S > 1 && part_bytes > 0.25 * weight_bytes) break;
+        const double cost = (double)((tiles * S + 255) / 256) * ((double)KT / S + 2.0);
+        if (cost < best_cost - 1e-9) best_cost = cost, best = (int)S;
+    }
+    return best;
+}
+
+size_t gemm_scratch_bytes(const colibri_moe_shape_t &s, bool up) {
+    const int S = gemm_splits(s, up);
+    if (S <= 1) return 0;
+    const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
+    return align256((size_t)S * 2 * s.T * (size_t)(up ? s.h : s.d) * (dual ? 2 : 1) * 4);
+}
+
 hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
-                          const int32_t *offsets, const colibri_moe_experts_t &w, void *H, hipStream_t st) {
+                          const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
+                          hipStream_t st) {
     const bool gather = sorted_assign != nullptr;
+    const int S = gemm_splits(s, true);
+    float *part = static_cast<float *>(scratch);
+    hipError_t e;
     switch (s.act) {
         case COLIBRI_ACT_RELU:
-            return launch_gemm<EPI_ACT_RELU>(gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d,
-                                             s.h, st);
+            e = launch_gemm<EPI_ACT_RELU>(gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d, s.h,
+                                          S, part, st);
+            break;
         case COLIBRI_ACT_GELU:
-            return launch_gemm<EPI_ACT_GELU>(gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d,
-                                             s.h, st);
+            e = launch_gemm<EPI_ACT_GELU>(gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d, s.h,
+                                          S, part, st);
+            break;
         default:
-            return launch_gemm<EPI_SWIGLU>(gather, s, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, s.d,
-                                           s.h, st);
+            e = launch_gemm<EPI_SWIGLU>(gather, s, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, s.d, s.h,
+                                        S, part, st);
     }
+    if (e == hipSuccess && S > 1) e = launch_split_reduce(s, true, S, offsets, w, H, part, st);
+    return e;
 }
 
 hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                            const colibri_moe_experts_t &w, void *y, hipStream_t st) {
+                            const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st) {
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
-    return launch_gemm<EPI_BIAS_ONLY>(false, s, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d, st);
+    const int S = gemm_splits(s, false);
+    float *part = static_cast<float *>(scratch);
+    hipError_t e = launch_gemm<EPI_BIAS_ONLY>(false, s, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d, S, part, st);
+    if (e == hipSuccess && S > 1 && reduce) e = launch_split_reduce(s, false, S, offsets, w, y, part, st);
+    return e;
 }
 
 }  // namespace colibri

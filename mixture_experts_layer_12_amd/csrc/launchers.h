@@ -29,8 +29,10 @@ size_t ffn_workspace_bytes(const colibri_moe_shape_t &s);
 hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                          const int32_t *offsets, const colibri_moe_experts_t &w, void *h_rows, void *scratch,
                          hipStream_t st);
+// reduce = false (when ffn_down_splits(s) > 1) leaves the split partials in scratch
 hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *h_rows, const int32_t *offsets,
-                           const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st);
+                           const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st,
+                           bool reduce = true);
 // Decode-sized batches (bf16, T <= 64) use the weight-streaming kernel.
 struct DecodePlan {
     int NCB;            // column blocks per expert
@@ -53,11 +55,23 @@ hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
                                    hipStream_t st);
-// bf16 grouped MFMA GEMMs for T > 64 (ffn_gemm.hip)
+// bf16 grouped MFMA GEMMs for T > 64 (ffn_gemm.hip).  A layer whose K is split
+// (gemm_splits > 1) writes fp32 partials [S][2T][cols] to scratch and then
+// reduces them (the second layer only when `reduce`; otherwise
+// launch_combine_partials adds them).
+int gemm_splits(const colibri_moe_shape_t &s, bool up);
+size_t gemm_scratch_bytes(const colibri_moe_shape_t &s, bool up);
 hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
-                          const int32_t *offsets, const colibri_moe_experts_t &w, void *H, hipStream_t st);
+                          const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
+                          hipStream_t st);
 hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                            const colibri_moe_experts_t &w, void *y, hipStream_t st);
+                            const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st);
+// Adds the S split partials of one layer and applies that layer's epilogue
+// (bias + activation, SwiGLU, or bias only), storing the dtype result.
+hipError_t launch_split_reduce(const colibri_moe_shape_t &s, bool up, int S, const int32_t *offsets,
+                               const colibri_moe_experts_t &w, void *C, const float *part, hipStream_t st);
+// K splits of the second layer as launch_ffn_down runs it (1: no partials).
+int ffn_down_splits(const colibri_moe_shape_t &s);
 // H then Y, with H and the scratch carved from ws.
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,

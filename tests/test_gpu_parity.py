@@ -285,6 +285,22 @@ def test_ffn_row_tiles_split_evenly(act):
         G.assert_bf16_close(y, y_ref, f"row tiles {act} gather={gather}")
 
 
+SPLIT_CASES = [(100, 8, 2048, 128, "swiglu"), (100, 8, 2048, 128, "gelu"), (300, 8, 128, 2048, "relu"),
+               (300, 8, 128, 2048, "swiglu")]
+
+
+@pytest.mark.parametrize("T,E,d,h,act", SPLIT_CASES, ids=[f"T{c[0]}-d{c[2]}-h{c[3]}-{c[4]}" for c in SPLIT_CASES])
+def test_ffn_gemm_k_split(T, E, d, h, act):
+    """Few tiles and a long K: the grouped GEMM splits K (d = 2048: the first
+    layer, h = 2048: the second), writes fp32 partials and a reduce applies the
+    epilogue; for the second layer the layer entry point instead lets the
+    combine add the partials (covered by the composed-equality test)."""
+    w, idx = small_ffn_case(act, gen.BF16, T=T, E=E, d=d, h=h, seed=T + d)
+    for gather in (True, False):
+        y, y_ref = run_ffn(w, idx, act, gen.BF16, E=E, gather=gather)
+        G.assert_bf16_close(y, y_ref, f"k split {act} gather={gather}")
+
+
 def test_ffn_degenerate_routings():
     E = 8
     for seed, skew in ((1, [0.93] + [0.01] * 7), (2, [0.5, 0.5, 0, 0, 0, 0, 0, 0])):
