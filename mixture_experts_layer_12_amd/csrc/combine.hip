@@ -57,40 +57,83 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, 
 
 // Same combine, but each expert row Y[p] is first formed from the second
 // layer's S split partial sums: Y[p] = bf16(sum_{s=0..S-1} part[s][p] + b2[e]),
-// the value the separate reduce would have stored.
+// the value the separate reduce would have stored.  The splits are added in
+// order s = 0, 1, ..., S-1 (the reduce uses the same order); their loads are
+// issued U at a time, both slots together, so a thread waits on memory about
+// S / U times rather than 2 S times.  VEC output columns per thread.
+template <int VEC, int U>
 __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__restrict__ part, int S,
                                                                const int32_t *__restrict__ pos,
                                                                const int32_t *__restrict__ idx,
                                                                const float *__restrict__ gate,
                                                                const uint16_t *__restrict__ b2, int E,
                                                                uint16_t *__restrict__ out, int T, int d) {
-    const int vpr = d / 4;
+    typedef float fv __attribute__((ext_vector_type(VEC)));
+    const int vpr = d / VEC;
     const size_t total = (size_t)T * vpr;
     const int A = 2 * T;
+    const size_t split_stride = (size_t)A * d;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
         const int t = (int)(i / vpr);
-        const int c = (int)(i % vpr) * 4;
-        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        const int c = (int)(i % vpr) * VEC;
+        int p[2], e[2];
+        bool live[2];
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
-            const int p = pos[2 * t + sl];
-            const int e = idx[2 * t + sl];
-            if (p < 0 || p >= A || e < 0 || e >= E) continue;
-            float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            for (int sp = 0; sp < S; ++sp) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(part + ((size_t)sp * A + p) * d + c);
+            p[sl] = pos[2 * t + sl];
+            e[sl] = idx[2 * t + sl];
+            live[sl] = p[sl] >= 0 && p[sl] < A && e[sl] >= 0 && e[sl] < E;
+        }
+        float y[2][VEC];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) y[q] += a[q];
-            }
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) y[sl][q] = 0.0f;
+        auto load = [&](int sp, int sl) {
+            return *reinterpret_cast<const fv *>(part + sp * split_stride + (size_t)p[sl] * d + c);
+        };
+        int sp = 0;
+        for (; sp + U <= S; sp += U) {
+            fv a[2][U];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int u = 0; u < U; ++u) a[sl][u] = live[sl] ? load(sp + u, sl) : fv{};
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) y[sl][q] += a[sl][u][q];
+        }
+        for (; sp < S; ++sp)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+                if (live[sl]) {
+                    const fv a = load(sp, sl);
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) y[sl][q] += a[q];
+                }
+        float o[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) o[q] = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            if (!live[sl]) continue;
             const float g = gate[2 * t + sl];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float yb = y[q] + (b2 ? bf16_to_f32(b2[(size_t)e * d + c + q]) : 0.0f);
+            for (int q = 0; q < VEC; ++q) {
+                const float yb = y[sl][q] + (b2 ? bf16_to_f32(b2[(size_t)e[sl] * d + c + q]) : 0.0f);
                 const float yr = bf16_to_f32((uint16_t)f32_to_bf16_bits(yb));  // Y is a bf16 value
                 o[q] = sl == 0 ? g * yr : fmaf(g, yr, o[q]);
             }
         }
-        *reinterpret_cast<u32x2 *>(out + (size_t)t * d + c) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        uint16_t *dst = out + (size_t)t * d + c;
+        if constexpr (VEC == 4) {
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        } else {
+            dst[0] = (uint16_t)f32_to_bf16_bits(o[0]);
+        }
     }
 }
 
@@ -115,8 +158,8 @@ hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *pa
                                    hipStream_t st) {
     const size_t total = (size_t)s.T * (s.d / 4);
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
-    combine_partials_kernel<<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate, (const uint16_t *)b2,
-                                                    s.E, (uint16_t *)out, s.T, s.d);
+    combine_partials_kernel<4, 8><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
+                                                          (const uint16_t *)b2, s.E, (uint16_t *)out, s.T, s.d);
     return hipGetLastError();
 }
 

@@ -247,9 +247,30 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
         int e = 0;  // expert of this row: the last e with offsets[e] <= row
         for (int k = 1; k < E; ++k)
             if (offsets[k] <= row) e = k;
+        // splits added in order s = 0 .. S-1 (the combine uses the same order); their
+        // loads are issued U at a time so a thread waits on memory about S / U times
+        constexpr int U = 8;
         float u[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int sp = 0; sp < S; ++sp) {
-            const float *src = part + ((size_t)sp * A_total + row) * NC + col;
+        const size_t split_stride = (size_t)A_total * NC;
+        const float *src0 = part + (size_t)row * NC + col;
+        int sp = 0;
+        for (; sp + U <= S; sp += U) {
+            f32x4 a[U], b[U];
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                a[k] = *reinterpret_cast<const f32x4 *>(src0 + (sp + k) * split_stride);
+                if (DUAL) b[k] = *reinterpret_cast<const f32x4 *>(src0 + (sp + k) * split_stride + N);
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u[q] += a[k][q];
+                    if (DUAL) v[q] += b[k][q];
+                }
+        }
+        for (; sp < S; ++sp) {
+            const float *src = src0 + sp * split_stride;
             const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
 #pragma unroll
             for (int q = 0; q < 4; ++q) u[q] += a[q];

@@ -15,6 +15,9 @@
 // l / EP, expert l % EP.  The top-2 is then an argmax over the EP lanes of a
 // token under the total order (logit desc, index asc; NaN below -inf),
 // taken twice with xor-shuffles, which is deterministic by construction.
+// Small batches (few token groups) split d over the W waves of a workgroup
+// instead: each wave reduce-scatters its slice's partial logits and wave 0
+// adds the W partials in wave order before the top-2.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -57,24 +60,32 @@ __device__ __forceinline__ void load_router_row(const TI *row, int E, float (&wv
     }
 }
 
-template <typename TI, int EP, bool FULL>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const TI *__restrict__ x, const TI *__restrict__ w_r,
-                                                              const float *__restrict__ b_r, int T, int d, int E,
-                                                              int32_t *__restrict__ topk_idx,
-                                                              float *__restrict__ topk_gate,
-                                                              float *__restrict__ logits) {
+constexpr int kRouteMaxW = 8;  // waves sharing one token group (split of d)
+
+// SPLITD: the block's W = blockDim.x / 64 waves share token group blockIdx.x
+// and take interleaved slices of d; else every wave owns its own token group.
+template <typename TI, int EP, bool FULL, bool SPLITD>
+__global__ __launch_bounds__(SPLITD ? kRouteMaxW * kWave : kRouteThreads) void route_kernel(const TI *__restrict__ x,
+                                                                   const TI *__restrict__ w_r,
+                                                                   const float *__restrict__ b_r, int T, int d, int E,
+                                                                   int32_t *__restrict__ topk_idx,
+                                                                   float *__restrict__ topk_gate,
+                                                                   float *__restrict__ logits) {
     constexpr int TPW = kWave / EP;
     constexpr int VEC = Vec16<TI>::N;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = (blockIdx.x * kRouteThreads + threadIdx.x) / kWave;
+    const int W = SPLITD ? (int)(blockDim.x / kWave) : 1;
+    const int wib = threadIdx.x / kWave;  // wave in block
+    const int wave = SPLITD ? (int)blockIdx.x : (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
     const int t0 = wave * TPW;
-    if (t0 >= T) return;  // uniform per wave
+    if (t0 >= T) return;  // uniform per wave (per block when SPLITD)
+    __shared__ float red[SPLITD ? kRouteMaxW : 1][kWave];
 
     float acc[TPW * EP];
 #pragma unroll
     for (int i = 0; i < TPW * EP; ++i) acc[i] = 0.0f;
 
-    for (int j0 = lane * VEC; j0 < d; j0 += kWave * VEC) {
+    for (int j0 = ((SPLITD ? wib : 0) * kWave + lane) * VEC; j0 < d; j0 += W * kWave * VEC) {
         if constexpr (EP <= 8) {
             // few experts: keep the VEC router rows in registers, stream the tokens
             float wv[VEC][EP];
@@ -129,6 +140,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const TI *__restri
         }
     }
 
+    if constexpr (SPLITD) {
+        red[wib][lane] = acc[0];
+        __syncthreads();
+        if (wib != 0) return;
+        float sum = red[0][lane];
+        for (int q = 1; q < W; ++q) sum += red[q][lane];
+        acc[0] = sum;
+    }
+
     const int tt = lane / EP;
     const int e = lane % EP;
     const int t = t0 + tt;
@@ -159,14 +179,24 @@ template <typename TI, int EP>
 hipError_t launch_ep(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r, int32_t *idx,
                      float *gate, float *logits, hipStream_t st) {
     constexpr int TPW = kWave / EP;
-    const int waves = ceil_div(s.T, TPW);
-    const int blocks = ceil_div(waves, kRouteThreads / kWave);
-    if (s.E == EP)
-        route_kernel<TI, EP, true><<<blocks, kRouteThreads, 0, st>>>(
-            (const TI *)x, (const TI *)w_r, b_r, s.T, s.d, s.E, idx, gate, logits);
-    else
-        route_kernel<TI, EP, false><<<blocks, kRouteThreads, 0, st>>>(
-            (const TI *)x, (const TI *)w_r, b_r, s.T, s.d, s.E, idx, gate, logits);
+    constexpr int VEC = Vec16<TI>::N;
+    const int groups = ceil_div(s.T, TPW);
+    // few token groups: split d over W waves per group (a power of two, one
+    // 16-byte slice of d per lane at most) so that about 256 waves run
+    int W = 1;
+    while (W < kRouteMaxW && groups * W * 2 <= 256 && (W * 2) * kWave * VEC <= s.d) W *= 2;
+#define COLIBRI_ROUTE_LAUNCH(FULLV, SPLITV, BLOCKS, THREADS)                                      \
+    route_kernel<TI, EP, FULLV, SPLITV><<<BLOCKS, THREADS, 0, st>>>((const TI *)x, (const TI *)w_r, b_r, s.T, s.d, \
+                                                                  s.E, idx, gate, logits)
+    if (W > 1) {
+        if (s.E == EP) COLIBRI_ROUTE_LAUNCH(true, true, groups, W * kWave);
+        else COLIBRI_ROUTE_LAUNCH(false, true, groups, W * kWave);
+    } else {
+        const int blocks = ceil_div(groups, kRouteThreads / kWave);
+        if (s.E == EP) COLIBRI_ROUTE_LAUNCH(true, false, blocks, kRouteThreads);
+        else COLIBRI_ROUTE_LAUNCH(false, false, blocks, kRouteThreads);
+    }
+#undef COLIBRI_ROUTE_LAUNCH
     return hipGetLastError();
 }
 
