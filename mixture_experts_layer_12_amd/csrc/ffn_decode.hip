@@ -296,10 +296,24 @@ DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up) {
     const int wcols = dual ? 64 : 128;
     p.NCB = (N + wcols - 1) / wcols;
     p.slots = std::min(s.E, 2 * s.T);
-    const int units = p.slots * p.NCB;
     const int ksteps = K / 32;
-    // about 900 streaming waves fill the chip; keep at least two k-steps per split
-    p.S = std::max(1, std::min((896 + units - 1) / units, ksteps / 2));
+    // S minimises an estimate of the layer's time.  The kernel runs one wave
+    // per SIMD, so 256 workgroups (one per CU) make one round; a wave streams
+    // one k-step per ~1.15 us (two k-steps in flight, measured) plus ~3 k-steps
+    // of start-up and epilogue; the stream cannot beat ~6.5 TB/s; S > 1 adds
+    // the partials' write and read (~5 TB/s) and a ~4 us reduce launch.  A larger
+    // S must win by 3% (the estimate is rough; fewer splits mean fewer partials).
+    const long wg_per_split = (long)p.slots * ((p.NCB + kDecWaves - 1) / kDecWaves);
+    const double cols = (double)N * (dual ? 2 : 1);
+    const double weight_bytes = (double)p.slots * K * cols * 2;
+    p.S = 1;
+    double best = 1e300;
+    for (int S = 1; S <= std::max(1, ksteps / 2); ++S) {
+        const double rounds = (double)((wg_per_split * S + 255) / 256);
+        double us = std::max(rounds * ((double)ksteps / S + 3.0) * 1.15, weight_bytes / 6.5e6);
+        if (S > 1) us += 4.0 + 2.0 * S * (2.0 * s.T) * cols * 4 / 5.0e6;
+        if (us < best * 0.97) best = us, p.S = S;
+    }
     p.W = kDecWaves;
     // 16-row tiles when the expected rows per expert (2T/E) leave a 2x margin
     p.MB = (2 * s.T <= 8 * s.E) ? 1 : 2;
