@@ -213,8 +213,13 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
     void *y = base + L.y;
     void *ffn_ws = base + L.ffn;
 
-    hipError_t e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream);
-    if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
+    hipError_t e;
+    if (route_dispatch_fusable(*s)) {
+        e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream);
+    } else {
+        e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream);
+        if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
+    }
     if (e != hipSuccess) return hip_status(e);
     const int Sd = ffn_down_splits(*s);
     if (Sd > 1) {

@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, 
 // layer's S split partial sums: Y[p] = bf16(sum_{s=0..S-1} part[s][p] + b2[e]),
 // the value the separate reduce would have stored.  The splits are added in
 // order s = 0, 1, ..., S-1 (the reduce uses the same order); their loads are
-// issued U at a time, both slots together, so a thread waits on memory about
-// S / U times rather than 2 S times.  VEC output columns per thread.
+// issued U at a time, both slots together, so a thread waits on memory
+// ceil(S / U) times rather than 2 S times.  VEC output columns per thread.
 template <int VEC, int U>
 __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__restrict__ part, int S,
                                                                const int32_t *__restrict__ pos,
@@ -89,31 +89,30 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
         for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
             for (int q = 0; q < VEC; ++q) y[sl][q] = 0.0f;
+        // loads are unconditional (a dead slot reads row 0, then contributes
+        // nothing), so no branch separates a load from its use
         auto load = [&](int sp, int sl) {
-            return *reinterpret_cast<const fv *>(part + sp * split_stride + (size_t)p[sl] * d + c);
+            const int row = live[sl] ? p[sl] : 0;
+            return *reinterpret_cast<const fv *>(part + sp * split_stride + (size_t)row * d + c);
         };
-        int sp = 0;
-        for (; sp + U <= S; sp += U) {
+        // batches of U splits; a last, partial batch loads split S-1 in its unused
+        // slots and skips their additions, so the order of additions is unchanged
+        for (int sp = 0; sp < S; sp += U) {
             fv a[2][U];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                for (int u = 0; u < U; ++u) a[sl][u] = live[sl] ? load(sp + u, sl) : fv{};
+                for (int u = 0; u < U; ++u) a[sl][u] = load(min(sp + u, S - 1), sl);
 #pragma unroll
-            for (int sl = 0; sl < 2; ++sl)
+            for (int u = 0; u < U; ++u) {
+                if (sp + u < S) {  // uniform; no break, so every index stays a constant
 #pragma unroll
-                for (int u = 0; u < U; ++u)
+                    for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                    for (int q = 0; q < VEC; ++q) y[sl][q] += a[sl][u][q];
-        }
-        for (; sp < S; ++sp)
-#pragma unroll
-            for (int sl = 0; sl < 2; ++sl)
-                if (live[sl]) {
-                    const fv a = load(sp, sl);
-#pragma unroll
-                    for (int q = 0; q < VEC; ++q) y[sl][q] += a[q];
+                        for (int q = 0; q < VEC; ++q) y[sl][q] += a[sl][u][q];
                 }
+            }
+        }
         float o[VEC];
 #pragma unroll
         for (int q = 0; q < VEC; ++q) o[q] = 0.0f;
@@ -158,7 +157,7 @@ hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *pa
                                    hipStream_t st) {
     const size_t total = (size_t)s.T * (s.d / 4);
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
-    combine_partials_kernel<4, 8><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
+    combine_partials_kernel<4, 16><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
                                                           (const uint16_t *)b2, s.E, (uint16_t *)out, s.T, s.d);
     return hipGetLastError();
 }

@@ -248,36 +248,30 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
         for (int k = 1; k < E; ++k)
             if (offsets[k] <= row) e = k;
         // splits added in order s = 0 .. S-1 (the combine uses the same order); their
-        // loads are issued U at a time so a thread waits on memory about S / U times
-        constexpr int U = 8;
+        // loads are issued U at a time so a thread waits on memory ceil(S / U) times
+        constexpr int U = 16;
         float u[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         const size_t split_stride = (size_t)A_total * NC;
         const float *src0 = part + (size_t)row * NC + col;
-        int sp = 0;
-        for (; sp + U <= S; sp += U) {
+        // batches of U splits; a last, partial batch loads split S-1 in its unused
+        // slots and skips their additions, so the order of additions is unchanged
+        for (int sp = 0; sp < S; sp += U) {
             f32x4 a[U], b[U];
 #pragma unroll
             for (int k = 0; k < U; ++k) {
-                a[k] = *reinterpret_cast<const f32x4 *>(src0 + (sp + k) * split_stride);
-                if (DUAL) b[k] = *reinterpret_cast<const f32x4 *>(src0 + (sp + k) * split_stride + N);
+                const float *src = src0 + min(sp + k, S - 1) * split_stride;
+                a[k] = *reinterpret_cast<const f32x4 *>(src);
+                if (DUAL) b[k] = *reinterpret_cast<const f32x4 *>(src + N);
             }
 #pragma unroll
-            for (int k = 0; k < U; ++k)
+            for (int k = 0; k < U; ++k) {
+                if (sp + k < S) {  // uniform; no break, so every index stays a constant
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    u[q] += a[k][q];
-                    if (DUAL) v[q] += b[k][q];
+                    for (int q = 0; q < 4; ++q) {
+                        u[q] += a[k][q];
+                        if (DUAL) v[q] += b[k][q];
+                    }
                 }
-        }
-        for (; sp < S; ++sp) {
-            const float *src = src0 + sp * split_stride;
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) u[q] += a[q];
-            if (DUAL) {
-                const f32x4 b = *reinterpret_cast<const f32x4 *>(src + N);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] += b[q];
             }
         }
         store_epilogue<EPI, 4>(C + (size_t)row * N + col, u, v, bias, e, N, col);

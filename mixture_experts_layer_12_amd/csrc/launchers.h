@@ -14,6 +14,14 @@ namespace colibri {
 hipError_t launch_route(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
                         int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t st);
 
+// route + dispatch in one launch for small batches (E <= 8, at most 2 token
+// groups of 64 / E rounded up to a power of two tokens); the results equal
+// launch_route followed by launch_dispatch bit for bit
+bool route_dispatch_fusable(const colibri_moe_shape_t &s);
+hipError_t launch_route_dispatch(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
+                                 int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
+                                 int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st);
+
 hipError_t launch_dispatch(const colibri_moe_shape_t &s, const int32_t *topk_idx, int32_t *counts,
                            int32_t *offsets, int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st);
 

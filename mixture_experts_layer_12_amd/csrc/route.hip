@@ -19,6 +19,7 @@
 // instead: each wave reduce-scatters its slice's partial logits and wave 0
 // adds the W partials in wave order before the top-2.
 #include "device_common.h"
+#include "dispatch_block.h"
 #include "launchers.h"
 
 namespace colibri {
@@ -60,32 +61,25 @@ __device__ __forceinline__ void load_router_row(const TI *row, int E, float (&wv
     }
 }
 
-constexpr int kRouteMaxW = 8;  // waves sharing one token group (split of d)
+constexpr int kRouteMaxW = 8;   // waves sharing one token group (split of d)
+constexpr int kFusedWaves = 8;  // waves of the fused route + dispatch workgroup
+constexpr int kFusedGroups = 2; // token groups up to which routing and dispatch are fused
 
-// SPLITD: the block's W = blockDim.x / 64 waves share token group blockIdx.x
-// and take interleaved slices of d; else every wave owns its own token group.
-template <typename TI, int EP, bool FULL, bool SPLITD>
-__global__ __launch_bounds__(SPLITD ? kRouteMaxW * kWave : kRouteThreads) void route_kernel(const TI *__restrict__ x,
-                                                                   const TI *__restrict__ w_r,
-                                                                   const float *__restrict__ b_r, int T, int d, int E,
-                                                                   int32_t *__restrict__ topk_idx,
-                                                                   float *__restrict__ topk_gate,
-                                                                   float *__restrict__ logits) {
+// One wave's partial logits of token group t0 over its slice of d (16-byte
+// chunks j_first + i * j_stride).  Returns, in lane l, the sum for value index l
+// (token t0 + l / EP, expert l % EP), reduced over the wave by a fixed
+// butterfly reduce-scatter.
+template <typename TI, int EP, bool FULL>
+__device__ __forceinline__ float route_wave_partial(const TI *__restrict__ x, const TI *__restrict__ w_r, int T, int d,
+                                                    int E, int t0, int j_first, int j_stride) {
     constexpr int TPW = kWave / EP;
     constexpr int VEC = Vec16<TI>::N;
     const int lane = threadIdx.x & (kWave - 1);
-    const int W = SPLITD ? (int)(blockDim.x / kWave) : 1;
-    const int wib = threadIdx.x / kWave;  // wave in block
-    const int wave = SPLITD ? (int)blockIdx.x : (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
-    const int t0 = wave * TPW;
-    if (t0 >= T) return;  // uniform per wave (per block when SPLITD)
-    __shared__ float red[SPLITD ? kRouteMaxW : 1][kWave];
-
     float acc[TPW * EP];
 #pragma unroll
     for (int i = 0; i < TPW * EP; ++i) acc[i] = 0.0f;
 
-    for (int j0 = ((SPLITD ? wib : 0) * kWave + lane) * VEC; j0 < d; j0 += W * kWave * VEC) {
+    for (int j0 = j_first + lane * VEC; j0 < d; j0 += j_stride) {
         if constexpr (EP <= 8) {
             // few experts: keep the VEC router rows in registers, stream the tokens
             float wv[VEC][EP];
@@ -139,21 +133,21 @@ __global__ __launch_bounds__(SPLITD ? kRouteMaxW * kWave : kRouteThreads) void r
             acc[i] = keep + __shfl_xor(send, half);
         }
     }
+    return acc[0];
+}
 
-    if constexpr (SPLITD) {
-        red[wib][lane] = acc[0];
-        __syncthreads();
-        if (wib != 0) return;
-        float sum = red[0][lane];
-        for (int q = 1; q < W; ++q) sum += red[q][lane];
-        acc[0] = sum;
-    }
-
+// Top-2 and gates of token group t0 from the full logits (lane l: token
+// t0 + l / EP, expert l % EP; bias not yet added).  sidx, when given, receives
+// the chosen experts at [2 (t - t_base)] (an LDS copy for a fused dispatch).
+template <int EP>
+__device__ __forceinline__ void route_select(float lg, const float *__restrict__ b_r, int T, int E, int t0,
+                                             int32_t *__restrict__ topk_idx, float *__restrict__ topk_gate,
+                                             float *__restrict__ logits, int32_t *sidx) {
+    const int lane = threadIdx.x & (kWave - 1);
     const int tt = lane / EP;
     const int e = lane % EP;
     const int t = t0 + tt;
     const bool valid = (e < E) && (t < T);
-    float lg = acc[0];
     if (b_r != nullptr && e < E) lg += b_r[e];
     if (valid && logits != nullptr) logits[(size_t)t * E + e] = lg;
 
@@ -172,7 +166,86 @@ __global__ __launch_bounds__(SPLITD ? kRouteMaxW * kWave : kRouteThreads) void r
         topk_idx[2 * t + 1] = i2;
         topk_gate[2 * t] = g0;
         topk_gate[2 * t + 1] = 1.0f - g0;
+        if (sidx != nullptr) {
+            sidx[2 * t] = i1;
+            sidx[2 * t + 1] = i2;
+        }
     }
+}
+
+// SPLITD: the block's W = blockDim.x / 64 waves share token group blockIdx.x
+// and take interleaved slices of d; else every wave owns its own token group.
+template <typename TI, int EP, bool FULL, bool SPLITD>
+__global__ __launch_bounds__(SPLITD ? kRouteMaxW * kWave : kRouteThreads) void route_kernel(
+    const TI *__restrict__ x, const TI *__restrict__ w_r, const float *__restrict__ b_r, int T, int d, int E,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_gate, float *__restrict__ logits) {
+    constexpr int TPW = kWave / EP;
+    constexpr int VEC = Vec16<TI>::N;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int W = SPLITD ? (int)(blockDim.x / kWave) : 1;
+    const int wib = threadIdx.x / kWave;  // wave in block
+    const int wave = SPLITD ? (int)blockIdx.x : (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
+    const int t0 = wave * TPW;
+    if (t0 >= T) return;  // uniform per wave (per block when SPLITD)
+    __shared__ float red[SPLITD ? kRouteMaxW : 1][kWave];
+
+    float lg = route_wave_partial<TI, EP, FULL>(x, w_r, T, d, E, t0, (SPLITD ? wib : 0) * kWave * VEC,
+                                                W * kWave * VEC);
+    if constexpr (SPLITD) {
+        red[wib][lane] = lg;
+        __syncthreads();
+        if (wib != 0) return;
+        float sum = red[0][lane];
+        for (int q = 1; q < W; ++q) sum += red[q][lane];
+        lg = sum;
+    }
+    route_select<EP>(lg, b_r, T, E, t0, topk_idx, topk_gate, logits, nullptr);
+}
+
+// Small batches: routing and dispatch in one workgroup of 8 waves.  The token
+// groups' logits are formed exactly as route_kernel forms them (W waves per
+// group split d and are added in wave order), the chosen experts stay in LDS,
+// and dispatch_block runs on them after a barrier: one launch instead of two.
+template <typename TI, int EP, bool FULL>
+__global__ __launch_bounds__(kFusedWaves *kWave) void route_dispatch_kernel(
+    const TI *__restrict__ x, const TI *__restrict__ w_r, const float *__restrict__ b_r, int T, int d, int E, int W,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_gate, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_assign, int32_t *__restrict__ assign_pos) {
+    constexpr int TPW = kWave / EP;
+    constexpr int VEC = Vec16<TI>::N;
+    constexpr int kMaxA = 2 * kFusedWaves * TPW;  // assignments of kFusedWaves token groups
+    __shared__ float red[kFusedWaves][kWave];
+    __shared__ int32_t sidx[kMaxA];
+    __shared__ DispatchShared<kFusedWaves> dsh;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int gi = w / W, wib = w % W;  // token group and wave within it
+    const int G = ceil_div(T, TPW);
+    if (gi < G)
+        red[w][lane] = route_wave_partial<TI, EP, FULL>(x, w_r, T, d, E, gi * TPW, wib * kWave * VEC, W * kWave * VEC);
+    __syncthreads();
+    if (gi < G && wib == 0) {
+        float sum = red[w][lane];
+        for (int q = 1; q < W; ++q) sum += red[w + q][lane];
+        route_select<EP>(sum, b_r, T, E, gi * TPW, topk_idx, topk_gate, nullptr, sidx);
+    }
+    __syncthreads();
+    dispatch_block<kFusedWaves>([&](int a) { return sidx[a]; }, 2 * T, E, counts, offsets, sorted_assign, assign_pos,
+                                dsh);
+}
+
+// Waves per token group: with few groups, split d over W (a power of two, one
+// 16-byte slice of d per lane at most) so that about 256 waves run; with at
+// most kFusedGroups groups, also G * W <= 8 so that one workgroup holds them
+// all (the fused route + dispatch kernel uses the same W, so both paths form
+// every logit identically).  With more groups, fusing would leave each group
+// too few waves: its d-stream costs more than the launch it saves.
+inline int route_waves(int T, int d, int EP, int VEC) {
+    const int G = ceil_div(T, kWave / EP);
+    int W = 1;
+    while (W < kRouteMaxW && G * W * 2 <= 256 && (W * 2) * kWave * VEC <= d && (G > kFusedGroups || G * W * 2 <= kFusedWaves))
+        W *= 2;
+    return W;
 }
 
 template <typename TI, int EP>
@@ -181,10 +254,7 @@ hipError_t launch_ep(const colibri_moe_shape_t &s, const void *x, const void *w_
     constexpr int TPW = kWave / EP;
     constexpr int VEC = Vec16<TI>::N;
     const int groups = ceil_div(s.T, TPW);
-    // few token groups: split d over W waves per group (a power of two, one
-    // 16-byte slice of d per lane at most) so that about 256 waves run
-    int W = 1;
-    while (W < kRouteMaxW && groups * W * 2 <= 256 && (W * 2) * kWave * VEC <= s.d) W *= 2;
+    const int W = route_waves(s.T, s.d, EP, VEC);
 #define COLIBRI_ROUTE_LAUNCH(FULLV, SPLITV, BLOCKS, THREADS)                                      \
     route_kernel<TI, EP, FULLV, SPLITV><<<BLOCKS, THREADS, 0, st>>>((const TI *)x, (const TI *)w_r, b_r, s.T, s.d, \
                                                                   s.E, idx, gate, logits)
@@ -200,6 +270,22 @@ hipError_t launch_ep(const colibri_moe_shape_t &s, const void *x, const void *w_
     return hipGetLastError();
 }
 
+template <typename TI, int EP>
+hipError_t launch_fused_ep(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
+                           int32_t *idx, float *gate, int32_t *counts, int32_t *offsets, int32_t *sorted,
+                           int32_t *pos, hipStream_t st) {
+    constexpr int VEC = Vec16<TI>::N;
+    const int W = route_waves(s.T, s.d, EP, VEC);
+#define COLIBRI_FUSED_LAUNCH(FULLV)                                                                          \
+    route_dispatch_kernel<TI, EP, FULLV><<<1, kFusedWaves * kWave, 0, st>>>((const TI *)x, (const TI *)w_r, b_r, s.T, \
+                                                                       s.d, s.E, W, idx, gate, counts, offsets,    \
+                                                                       sorted, pos)
+    if (s.E == EP) COLIBRI_FUSED_LAUNCH(true);
+    else COLIBRI_FUSED_LAUNCH(false);
+#undef COLIBRI_FUSED_LAUNCH
+    return hipGetLastError();
+}
+
 template <typename TI>
 hipError_t launch_t(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r, int32_t *idx,
                     float *gate, float *logits, hipStream_t st) {
@@ -211,12 +297,38 @@ hipError_t launch_t(const colibri_moe_shape_t &s, const void *x, const void *w_r
     return launch_ep<TI, 64>(s, x, w_r, b_r, idx, gate, logits, st);
 }
 
+template <typename TI>
+hipError_t launch_fused_t(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
+                          int32_t *idx, float *gate, int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *pos,
+                          hipStream_t st) {
+    if (s.E <= 2) return launch_fused_ep<TI, 2>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, st);
+    if (s.E <= 4) return launch_fused_ep<TI, 4>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, st);
+    return launch_fused_ep<TI, 8>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, st);
+}
+
 }  // namespace
 
 hipError_t launch_route(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
                         int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t st) {
     if (s.dtype == COLIBRI_F32) return launch_t<float>(s, x, w_r, b_r, topk_idx, topk_gate, logits, st);
     return launch_t<uint16_t>(s, x, w_r, b_r, topk_idx, topk_gate, logits, st);
+}
+
+// E <= 8 and at most kFusedGroups token groups (T <= 16 for E = 8)
+bool route_dispatch_fusable(const colibri_moe_shape_t &s) {
+    if (s.E > 8 || s.T <= 0) return false;
+    const int EP = s.E <= 2 ? 2 : s.E <= 4 ? 4 : 8;
+    return ceil_div(s.T, kWave / EP) <= kFusedGroups;
+}
+
+hipError_t launch_route_dispatch(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
+                                 int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
+                                 int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st) {
+    if (s.dtype == COLIBRI_F32)
+        return launch_fused_t<float>(s, x, w_r, b_r, topk_idx, topk_gate, counts, offsets, sorted_assign, assign_pos,
+                                     st);
+    return launch_fused_t<uint16_t>(s, x, w_r, b_r, topk_idx, topk_gate, counts, offsets, sorted_assign, assign_pos,
+                                    st);
 }
 
 }  // namespace colibri
