@@ -160,8 +160,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 //      give a 32x32x16 MFMA B operand with no register transposes.
 // Both are filled with 1 KB global->LDS copies: an A copy is RPD whole rows,
 // a B copy is 4 k rows x 128 columns (16-byte runs of one weight row).
-template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool GATHER>
-__global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
+template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool GATHER, int WPE>
+__global__ __launch_bounds__(WM *WN *kWave, WPE) void ffn_gemm_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NT, int S,
@@ -413,59 +413,89 @@ __global__ __launch_bounds__(WM *WN *kWave, 1) void ffn_gemm_kernel(
     }
 }
 
-// Tile shape of the launch: row tiles of 256 rows (up to 320 when a small tail
-// is spread over them) x 256 weight columns (SwiGLU: 128 outputs of both W1 and
-// W3), BK = 64, two LDS stages (144 KB), 8 waves: one workgroup per CU, two
-// waves per SIMD.
-constexpr int kBMB = 256, kBM = 320, kBN = 256, kBK = 64;
+// Two tile shapes, 8 waves per workgroup, BK = 64, two LDS stages:
+//   big: row tiles of 256 rows (up to 320 when a small tail is spread over
+//        them) x 256 weight columns (SwiGLU: 128 outputs of both W1 and W3);
+//        144 KB of LDS, one workgroup per CU, two waves per SIMD;
+//   mid: row tiles of 128 rows (up to 192) x 128 columns, no SwiGLU; 80 KB of
+//        LDS and <= 128 VGPRs, so two workgroups share a CU.  For a few
+//        hundred rows per expert the layer streams its weights; a second
+//        workgroup per CU overlaps its copies and barriers with the first's
+//        (measured: 8-expert T=512, first layer 57.8 -> 46.4 us).
+constexpr int kBK = 64;
+struct GemmCfg {
+    bool mid;
+    int BMB;      // base row-tile height
+    int BNC;      // output columns per tile
+    int per_cu;   // workgroups resident per CU
+};
+GemmCfg gemm_cfg(const colibri_moe_shape_t &s, bool up) {
+    const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
+    const bool mid = !dual && 2L * s.T <= 160L * s.E;  // <= 160 expected rows per expert
+    if (mid) return {true, 128, 128, 2};
+    return {false, 256, dual ? 128 : 256, 1};
+}
 
-template <int EPI>
-hipError_t launch_gemm(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
-                       const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
-                       int S, float *part, hipStream_t st) {
-    constexpr int BNC = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+template <int BMB, int BM, int BN, int WPE, int EPI>
+hipError_t launch_shape(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
+                        const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
+                        int S, float *part, hipStream_t st) {
+    constexpr int BNC = EPI == EPI_SWIGLU ? BN / 2 : BN;
     const int A = 2 * s.T;
     const int NT = (N + BNC - 1) / BNC;
-    const int mtiles = (A + kBMB - 1) / kBMB + std::min(s.E, A);  // bound on the row tiles of all experts
+    const int mtiles = (A + BMB - 1) / BMB + std::min(s.E, A);  // bound on the row tiles of all experts
     const dim3 grid(mtiles * NT * S);
     constexpr int threads = 2 * 4 * kWave;
     if (gather)
-        ffn_gemm_kernel<kBMB, kBM, kBN, kBK, 2, 4, 2, EPI, true><<<grid, threads, 0, st>>>(
+        ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, true, WPE><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
             (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, part);
     else
-        ffn_gemm_kernel<kBMB, kBM, kBN, kBK, 2, 4, 2, EPI, false><<<grid, threads, 0, st>>>(
+        ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, false, WPE><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
             (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, part);
     return hipGetLastError();
 }
 
+template <int EPI>
+hipError_t launch_gemm(bool up, bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
+                       const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
+                       int S, float *part, hipStream_t st) {
+    if constexpr (EPI != EPI_SWIGLU) {
+        if (gemm_cfg(s, up).mid)  // 2 workgroups per CU: 4 waves per SIMD
+            return launch_shape<128, 192, 128, 4, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, S, part, st);
+    }
+    return launch_shape<256, 320, 256, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, S, part, st);
+}
+
 }  // namespace
 
 // K splits of one layer.  Mid-sized batches (a few hundred rows per expert)
-// make too few tiles to fill 256 CUs; splitting K multiplies the blocks at the
+// make too few tiles to fill the chip; splitting K multiplies the blocks at the
 // cost of fp32 partials [S][2T][cols] written and read once more.  The split
-// minimises (rounds of 256 blocks) x (k-tiles per block + 2, a per-block
-// start-up cost) over the S whose partials stay within a quarter of the
-// layer's weight bytes, with at least 4 k-tiles per block; ties keep the
+// minimises (rounds of resident workgroups) x (k-tiles per block + 2, a
+// per-block start-up cost) over the S whose partials stay within a quarter of
+// the layer's weight bytes, with at least 4 k-tiles per block; ties keep the
 // smaller S.  Expected row tiles: one per expert while experts hold at most
-// 320 rows, else one per 256 rows.
+// a tile's rows, else one per base tile height.
 int gemm_splits(const colibri_moe_shape_t &s, bool up) {
     if (s.dtype != COLIBRI_BF16 || s.T <= 0) return 1;
+    const GemmCfg c = gemm_cfg(s, up);
     const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
     const long K = up ? s.d : s.h, N = up ? s.h : s.d;
     const long A = 2L * s.T;
-    const long NT = (N + (dual ? kBN / 2 : kBN) - 1) / (dual ? kBN / 2 : kBN);
-    const long rt = std::max<long>(std::min<long>(s.E, A), (A + kBMB - 1) / kBMB);
+    const long NT = (N + c.BNC - 1) / c.BNC;
+    const long rt = std::max<long>(std::min<long>(s.E, A), (A + c.BMB - 1) / c.BMB);
     const long tiles = rt * NT;
     const long KT = K / kBK;
+    const long slots = 256L * c.per_cu;
     const double weight_bytes = (double)std::min<long>(s.E, A) * K * N * 2 * (dual ? 2 : 1);
     int best = 1;
     double best_cost = 1e300;
     for (long S = 1; S <= KT / 4 || S == 1; ++S) {
         const double part_bytes = (double)S * A * N * (dual ? 2 : 1) * 4;
         if (S > 1 && part_bytes > 0.25 * weight_bytes) break;
-        const double cost = (double)((tiles * S + 255) / 256) * ((double)KT / S + 2.0);
+        const double cost = (double)((tiles * S + slots - 1) / slots) * ((double)KT / S + 2.0);
         if (cost < best_cost - 1e-9) best_cost = cost, best = (int)S;
     }
     return best;
@@ -487,15 +517,15 @@ hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, cons
     hipError_t e;
     switch (s.act) {
         case COLIBRI_ACT_RELU:
-            e = launch_gemm<EPI_ACT_RELU>(gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d, s.h,
+            e = launch_gemm<EPI_ACT_RELU>(true, gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d, s.h,
                                           S, part, st);
             break;
         case COLIBRI_ACT_GELU:
-            e = launch_gemm<EPI_ACT_GELU>(gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d, s.h,
+            e = launch_gemm<EPI_ACT_GELU>(true, gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d, s.h,
                                           S, part, st);
             break;
         default:
-            e = launch_gemm<EPI_SWIGLU>(gather, s, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, s.d, s.h,
+            e = launch_gemm<EPI_SWIGLU>(true, gather, s, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, s.d, s.h,
                                         S, part, st);
     }
     if (e == hipSuccess && S > 1) e = launch_split_reduce(s, true, S, offsets, w, H, part, st);
@@ -507,7 +537,7 @@ hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const i
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
     const int S = gemm_splits(s, false);
     float *part = static_cast<float *>(scratch);
-    hipError_t e = launch_gemm<EPI_BIAS_ONLY>(false, s, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d, S, part, st);
+    hipError_t e = launch_gemm<EPI_BIAS_ONLY>(false, false, s, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d, S, part, st);
     if (e == hipSuccess && S > 1 && reduce) e = launch_split_reduce(s, false, S, offsets, w, y, part, st);
     return e;
 }

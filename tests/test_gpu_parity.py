@@ -266,14 +266,23 @@ def test_ffn_decode_expert_over_32_rows():
     assert np.array_equal(y, y2)
 
 
+ROW_TILE_COUNTS = {
+    # large tiles (256 rows, up to 320): 641 -> 3 x 214, 321 -> 2 x 161, 650 -> 3 x 217, 320 -> 1 x 320,
+    # 1030 -> 4 x 258; subtiles split 4/3, 3/3, 5/5, 5/4 over the two wave rows, or leave one empty
+    "big": [641, 321, 320, 33, 1, 0, 650, 10, 1030],
+    # mid-size tiles (128 rows, up to 192; no more than 160 rows per expert on average):
+    # 129 -> 1 x 129, 160 -> 1 x 160, 192 -> 2 x 96, 193 -> 97 + 96, 255 -> 128 + 127
+    "mid": [129, 160, 192, 193, 255, 1, 0, 70],
+}
+
+
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
-def test_ffn_row_tiles_split_evenly(act):
-    """Per-expert counts around multiples of the GEMM's 256-row tile: experts are
-    cut into equal row tiles (641 rows -> 3 x 214, 321 -> 2 x 161, 650 -> 3 x 217),
-    a tail of at most 64 rows is spread over the other tiles (320 -> 1 x 320,
-    1030 -> 4 x 258), and the 32-row subtiles split unevenly over the two wave
-    rows (4/3, 3/3, 5/5, 5/4) or leave one wave row empty (1 and 10 rows)."""
-    counts = [641, 321, 320, 33, 1, 0, 650, 10, 1030]
+@pytest.mark.parametrize("which", ["big", "mid"])
+def test_ffn_row_tiles_split_evenly(act, which):
+    """Per-expert counts around the grouped GEMM's row-tile boundaries: experts are
+    cut into equal row tiles, a small tail is spread over the other tiles, and the
+    tiles' 32-row subtiles split unevenly over the two wave rows."""
+    counts = ROW_TILE_COUNTS[which]
     E = len(counts)
     rng = np.random.default_rng(21)
     slots = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts))
