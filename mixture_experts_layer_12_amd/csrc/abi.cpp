@@ -224,14 +224,11 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
     const int Sd = ffn_down_splits(*s);
     if (Sd > 1) {
         // the second layer's K is split: the combine adds its partials (with b2) directly
-        const size_t el = elem_size(s);
-        char *H = static_cast<char *>(ffn_ws);
-        void *scratch = H + align256((size_t)2 * s->T * s->h * el);
-        e = launch_ffn_up(*s, x, sorted, offsets, *w, H, scratch, stream);
-        if (e == hipSuccess) e = launch_ffn_down(*s, H, offsets, *w, nullptr, scratch, stream, false);
+        const float *part = nullptr;
+        e = launch_ffn_layers(*s, x, sorted, offsets, *w, nullptr, ffn_ws, false, stream, &part);
         if (e == hipSuccess)
-            e = launch_combine_partials(*s, static_cast<const float *>(scratch), Sd, pos, idx, gate,
-                                        s->act == COLIBRI_ACT_SWIGLU ? nullptr : w->b2, out, stream);
+            e = launch_combine_partials(*s, part, Sd, pos, idx, gate, s->act == COLIBRI_ACT_SWIGLU ? nullptr : w->b2,
+                                        out, stream);
         return hip_status(e);
     }
     e = launch_expert_ffn(*s, x, sorted, offsets, *w, y, ffn_ws, stream);

@@ -222,15 +222,31 @@ hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const in
     return launch_gemm_down(s, H, offsets, w, y_sorted, scratch, reduce, st);
 }
 
-hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
-                             hipStream_t st) {
+                             bool reduce, hipStream_t st, const float **down_partials) {
     const size_t el = s.dtype == COLIBRI_F32 ? 4 : 2;
     char *H = static_cast<char *>(ws);
     char *scratch = H + align256((size_t)2 * s.T * s.h * el);
+    if (decode_fuse_h(s)) {
+        // the first layer leaves its split partials; the second layer rebuilds H from them
+        char *down_scratch = scratch + align256(decode_plan(s, true).part_bytes);
+        if (down_partials) *down_partials = reinterpret_cast<const float *>(down_scratch);
+        hipError_t e = launch_decode_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st, false);
+        if (e != hipSuccess) return e;
+        return launch_decode_down(s, H, offsets, w, y_sorted, down_scratch, reduce, st,
+                                  reinterpret_cast<const float *>(scratch));
+    }
+    if (down_partials) *down_partials = reinterpret_cast<const float *>(scratch);
     hipError_t e = launch_ffn_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
     if (e != hipSuccess) return e;
-    return launch_ffn_down(s, H, offsets, w, y_sorted, scratch, st);
+    return launch_ffn_down(s, H, offsets, w, y_sorted, scratch, st, reduce);
+}
+
+hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                             const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
+                             hipStream_t st) {
+    return launch_ffn_layers(s, x_rows, sorted_assign, offsets, w, y_sorted, ws, true, st, nullptr);
 }
 
 }  // namespace colibri

@@ -82,15 +82,22 @@ __device__ __forceinline__ bool live_expert(const int32_t *__restrict__ offsets,
     return true;
 }
 
-template <int MB, int EPI, bool GATHER>
+// HEPI >= 0: second layer whose A rows (H) are rebuilt by the workgroup from
+// the first layer's hS split partials hpart [hS][2T][K or 2K], in split order
+// with the first layer's epilogue HEPI (bias hbias) and bf16 rounding, exactly
+// as the split reduce would store them; the slice for the workgroup's rows and
+// K range is staged in LDS (dynamic shared memory) before the weight stream.
+template <int MB, int EPI, bool GATHER, int HEPI>
 __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NCB, int S,
-    float *__restrict__ part) {
+    float *__restrict__ part, const float *__restrict__ hpart, int hS, const uint16_t *__restrict__ hbias) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr bool HFROMP = HEPI >= 0;
     constexpr int WCOLS = DUAL ? 64 : 128;  // output columns per wave
     constexpr int ROWS = MB * 16;
+    extern __shared__ __attribute__((aligned(16))) uint8_t hlds[];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int ncbg = (NCB + kDecWaves - 1) / kDecWaves;  // groups of 4 column blocks
@@ -99,7 +106,8 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
     const int split = rest % S;
     const int slot = rest / S;
     const int cb = cbg * kDecWaves + (int)(threadIdx.x / kWave);
-    if (cb >= NCB) return;
+    const bool active = cb < NCB;       // waves past the last column block only help stage H
+    if (!HFROMP && !active) return;
 
     const int A_total = 2 * T;
     int e, r0, count;
@@ -120,8 +128,54 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
     const int s_begin = (int)((long)ksteps * split / S);
     const int s_end = (int)((long)ksteps * (split + 1) / S);
 
+    // staged H slice (HFROMP): ROWS rows x klen k, rows padded by 16 bytes so the
+    // 16 rows one A-fragment read touches fall in different banks
+    const int klen = (s_end - s_begin) * 32;
+    const int hstride = klen * 2 + 16;
+
     for (int rc = 0; rc < count; rc += ROWS) {
         const int rows = min(ROWS, count - rc);
+        if constexpr (HFROMP) {
+            constexpr bool HDUAL = (HEPI == EPI_SWIGLU);
+            constexpr int U = 16;
+            const int NCU = HDUAL ? 2 * K : K;  // columns of a first-layer partial row
+            const size_t split_stride = (size_t)A_total * NCU;
+            __syncthreads();  // the previous chunk's H reads are done
+            const int vq = klen / 4;
+            for (int i = threadIdx.x; i < rows * vq; i += blockDim.x) {
+                const int r = i / vq;
+                const int kq = (i - r * vq) * 4;
+                const int col = s_begin * 32 + kq;  // first-layer output column
+                const float *src0 = hpart + (size_t)(r0 + rc + r) * NCU + col;
+                float u[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int sp = 0; sp < hS; sp += U) {
+                    f32x4 a[U], b[U];
+#pragma unroll
+                    for (int k = 0; k < U; ++k) {
+                        const float *p = src0 + min(sp + k, hS - 1) * split_stride;
+                        a[k] = *reinterpret_cast<const f32x4 *>(p);
+                        if (HDUAL) b[k] = *reinterpret_cast<const f32x4 *>(p + K);
+                    }
+#pragma unroll
+                    for (int k = 0; k < U; ++k) {
+                        if (sp + k < hS) {  // split order, as the reduce adds them
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                u[q] += a[k][q];
+                                if (HDUAL) v[q] += b[k][q];
+                            }
+                        }
+                    }
+                }
+                const uint32_t lo = pack_bf16x2(epi_value<HEPI>(u[0], v[0], hbias, e, K, col),
+                                                epi_value<HEPI>(u[1], v[1], hbias, e, K, col + 1));
+                const uint32_t hi = pack_bf16x2(epi_value<HEPI>(u[2], v[2], hbias, e, K, col + 2),
+                                                epi_value<HEPI>(u[3], v[3], hbias, e, K, col + 3));
+                *reinterpret_cast<u32x2 *>(hlds + (size_t)r * hstride + kq * 2) = u32x2{lo, hi};
+            }
+            __syncthreads();
+            if (!active) continue;
+        }
         // A rows of this lane: row (lane % 16) of each 16-row subtile; rows past
         // the segment read row r0 instead (never stored)
         const uint16_t *a_src[MB];
@@ -130,7 +184,7 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
             const int r = mi * 16 + c;
             const int p = r0 + rc + (r < rows ? r : 0);
             long src = p;
-            if (GATHER) {
+            if (GATHER && !HFROMP) {
                 const int a = sorted_assign[p];
                 src = (a >= 0 && (a >> 1) < T) ? (a >> 1) : 0;
             }
@@ -153,8 +207,16 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 sg.b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + (size_t)i * N));
+            if constexpr (!HFROMP) {
 #pragma unroll
-            for (int mi = 0; mi < MB; ++mi) sg.a[mi] = *reinterpret_cast<const u32x4 *>(a_src[mi] + step * 32);
+                for (int mi = 0; mi < MB; ++mi) sg.a[mi] = *reinterpret_cast<const u32x4 *>(a_src[mi] + step * 32);
+            } else {
+                // A fragment from the staged H slice: row mi*16 + c, k 8g..8g+7 of this step
+#pragma unroll
+                for (int mi = 0; mi < MB; ++mi)
+                    sg.a[mi] = *reinterpret_cast<const u32x4 *>(hlds + (size_t)(mi * 16 + c) * hstride +
+                                                                 ((step - s_begin) * 32 + 8 * g) * 2);
+            }
         };
         auto mma = [&](const Stage &sg) {
             bf16x8 bfrag[8];
@@ -315,21 +377,47 @@ DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up) {
     return p;
 }
 
+// The second layer rebuilds H from the first layer's split partials (instead
+// of a separate reduce launch) when the first layer is split, the staged H
+// slice fits in 64 KB of LDS, and the partial reads -- repeated once per column
+// group of the second layer -- stay within 5% of the second layer's weights.
+bool decode_fuse_h(const colibri_moe_shape_t &s) {
+    if (!ffn_decode_eligible(s)) return false;
+    const DecodePlan up = decode_plan(s, true), down = decode_plan(s, false);
+    if (up.S <= 1) return false;
+    const int ksteps = s.h / 32;
+    const size_t klen_max = (size_t)((ksteps + down.S - 1) / down.S) * 32;
+    if ((size_t)16 * down.MB * (klen_max * 2 + 16) > 64 * 1024) return false;
+    const double reads = (double)((down.NCB + kDecWaves - 1) / kDecWaves) * up.part_bytes;
+    const double down_weights = (double)down.slots * s.h * s.d * 2;
+    return reads <= 0.05 * down_weights;
+}
+
 size_t ffn_decode_scratch_bytes(const colibri_moe_shape_t &s) {
-    return std::max(decode_plan(s, true).part_bytes, decode_plan(s, false).part_bytes);
+    const size_t up = decode_plan(s, true).part_bytes, down = decode_plan(s, false).part_bytes;
+    return decode_fuse_h(s) ? align256(up) + down : std::max(up, down);
 }
 
 namespace {
-template <int EPI>
+// HEPI >= 0: A is not read from memory; each workgroup rebuilds its K slice of
+// the rows from the first layer's partials (hpart, hS splits) with activation
+// HEPI and bias hbias, in dynamic LDS.
+template <int EPI, int HEPI = -1>
 hipError_t launch_decode_t(const colibri_moe_shape_t &s, const DecodePlan &p, bool gather, const void *Am,
                            const int32_t *sa, const int32_t *offsets, const void *B0, const void *B1, const void *bias,
-                           void *C, int K, int N, void *scratch, hipStream_t st) {
+                           void *C, int K, int N, void *scratch, hipStream_t st, const float *hpart = nullptr,
+                           int hS = 0, const void *hbias = nullptr) {
     float *part = static_cast<float *>(scratch);
     const int blocks = p.slots * p.S * ((p.NCB + kDecWaves - 1) / kDecWaves);
+    size_t lds = 0;
+    if (HEPI >= 0) {
+        const int ksteps = K / 32;
+        lds = (size_t)16 * p.MB * ((size_t)((ksteps + p.S - 1) / p.S) * 32 * 2 + 16);
+    }
 #define COLIBRI_DEC_LAUNCH(MBV, G)                                                                              \
-    ffn_decode_kernel<MBV, EPI, G><<<blocks, kDecWaves * kWave, 0, st>>>(                                      \
+    ffn_decode_kernel<MBV, EPI, G, HEPI><<<blocks, kDecWaves * kWave, lds, st>>>(                              \
         (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,                \
-        (const uint16_t *)bias, (uint16_t *)C, K, N, p.NCB, p.S, part)
+        (const uint16_t *)bias, (uint16_t *)C, K, N, p.NCB, p.S, part, hpart, hS, (const uint16_t *)hbias)
     if (p.MB == 1) {
         if (gather) COLIBRI_DEC_LAUNCH(1, true);
         else COLIBRI_DEC_LAUNCH(1, false);
@@ -354,37 +442,59 @@ hipError_t launch_reduce_t(const colibri_moe_shape_t &s, int S, const int32_t *o
 template <int EPI>
 hipError_t up_t(const colibri_moe_shape_t &s, const DecodePlan &p, bool gather, const void *x_rows,
                 const int32_t *sa, const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *H,
-                void *scratch, hipStream_t st) {
+                void *scratch, bool reduce, hipStream_t st) {
     hipError_t err = launch_decode_t<EPI>(s, p, gather, x_rows, sa, offsets, B0, B1, bias, H, s.d, s.h, scratch, st);
-    if (err == hipSuccess && p.S > 1) err = launch_reduce_t<EPI>(s, p.S, offsets, bias, H, s.h, scratch, st);
+    if (err == hipSuccess && p.S > 1 && reduce) err = launch_reduce_t<EPI>(s, p.S, offsets, bias, H, s.h, scratch, st);
     return err;
+}
+
+template <int HEPI>
+hipError_t down_t(const colibri_moe_shape_t &s, const DecodePlan &p, const void *H, const int32_t *offsets,
+                  const void *w2, const void *b2, void *y, void *scratch, hipStream_t st, const float *hpart, int hS,
+                  const void *hbias) {
+    return launch_decode_t<EPI_BIAS_ONLY, HEPI>(s, p, false, H, nullptr, offsets, w2, nullptr, b2, y, s.h, s.d,
+                                                scratch, st, hpart, hS, hbias);
 }
 }  // namespace
 
 hipError_t launch_decode_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                             const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
-                            hipStream_t st) {
+                            hipStream_t st, bool reduce) {
     const DecodePlan p = decode_plan(s, true);
     const bool gather = sorted_assign != nullptr;
     switch (s.act) {
         case COLIBRI_ACT_RELU:
             return up_t<EPI_ACT_RELU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, scratch,
-                                      st);
+                                      reduce, st);
         case COLIBRI_ACT_GELU:
             return up_t<EPI_ACT_GELU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, scratch,
-                                      st);
+                                      reduce, st);
         default:
             return up_t<EPI_SWIGLU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, scratch,
-                                    st);
+                                    reduce, st);
     }
 }
 
 hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                              const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st) {
+                              const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st,
+                              const float *h_partials) {
     const DecodePlan p = decode_plan(s, false);
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
-    hipError_t err = launch_decode_t<EPI_BIAS_ONLY>(s, p, false, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d,
-                                                    scratch, st);
+    hipError_t err;
+    if (h_partials == nullptr) {
+        err = down_t<-1>(s, p, H, offsets, w.w2, b2, y, scratch, st, nullptr, 0, nullptr);
+    } else {
+        const int hS = decode_plan(s, true).S;
+        switch (s.act) {
+            case COLIBRI_ACT_RELU:
+                err = down_t<EPI_ACT_RELU>(s, p, H, offsets, w.w2, b2, y, scratch, st, h_partials, hS, w.b1);
+                break;
+            case COLIBRI_ACT_GELU:
+                err = down_t<EPI_ACT_GELU>(s, p, H, offsets, w.w2, b2, y, scratch, st, h_partials, hS, w.b1);
+                break;
+            default: err = down_t<EPI_SWIGLU>(s, p, H, offsets, w.w2, b2, y, scratch, st, h_partials, hS, nullptr);
+        }
+    }
     if (err == hipSuccess && p.S > 1 && reduce)
         err = launch_reduce_t<EPI_BIAS_ONLY>(s, p.S, offsets, b2, y, s.d, scratch, st);
     return err;

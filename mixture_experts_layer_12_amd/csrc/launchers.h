@@ -53,12 +53,19 @@ struct DecodePlan {
 bool ffn_decode_eligible(const colibri_moe_shape_t &s);
 DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up);
 size_t ffn_decode_scratch_bytes(const colibri_moe_shape_t &s);
+// reduce = false leaves the first layer's split partials in scratch (for decode_fuse_h)
 hipError_t launch_decode_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                             const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
-                            hipStream_t st);
-// reduce = false leaves the split partials in scratch for launch_combine_partials
+                            hipStream_t st, bool reduce = true);
+// reduce = false leaves the split partials in scratch for launch_combine_partials.
+// h_partials != nullptr: H is not read; each workgroup rebuilds its slice from
+// the first layer's split partials (decode_fuse_h).
 hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                              const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st);
+                              const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st,
+                              const float *h_partials = nullptr);
+// Decode sizes whose second layer rebuilds H from the first layer's partials;
+// the scratch then holds the first layer's partials, then (256-aligned) the second's.
+bool decode_fuse_h(const colibri_moe_shape_t &s);
 // combine straight from the second layer's S split partials (adds them, b2, rounds Y, then gates)
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
@@ -80,7 +87,13 @@ hipError_t launch_split_reduce(const colibri_moe_shape_t &s, bool up, int S, con
                                const colibri_moe_experts_t &w, void *C, const float *part, hipStream_t st);
 // K splits of the second layer as launch_ffn_down runs it (1: no partials).
 int ffn_down_splits(const colibri_moe_shape_t &s);
-// H then Y, with H and the scratch carved from ws.
+// Both layers with H and the scratch carved from ws (H first, then the scratch).
+// reduce = false (when ffn_down_splits(s) > 1) leaves the second layer's split
+// partials in the scratch, at *down_partials.
+hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                             const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
+                             bool reduce, hipStream_t st, const float **down_partials);
+// H then Y (launch_ffn_layers with the second layer reduced).
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
                              hipStream_t st);

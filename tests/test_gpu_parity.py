@@ -266,6 +266,42 @@ def test_ffn_decode_expert_over_32_rows():
     assert np.array_equal(y, y2)
 
 
+FUSED_H_CASES = [(5, 8, 192, 256, "relu", None), (3, 8, 512, 1024, "gelu", None), (4, 16, 512, 2048, "swiglu", None),
+                 (24, 16, 512, 2048, "swiglu", "two")]
+
+
+@pytest.mark.parametrize("T,E,d,h,act,skew", FUSED_H_CASES,
+                         ids=[f"T{c[0]}-E{c[1]}-d{c[2]}-h{c[3]}-{c[4]}" + ("-skew" if c[5] else "") for c in FUSED_H_CASES])
+def test_ffn_decode_h_from_partials(T, E, d, h, act, skew):
+    """Decode shapes whose first layer is K-split: inside expert_ffn the second
+    layer rebuilds H from the first layer's partials (no H store, no reduce
+    launch).  It must equal the single-layer entry points chained through H
+    (which reduce and store H) bit for bit.  "two": every token on experts 0
+    and 1, so 24 rows per expert run as a 16-row chunk and a ragged 8-row one."""
+    w, idx = small_ffn_case(act, gen.BF16, T=T, E=E, d=d, h=h, seed=T + E + d)
+    if skew == "two":
+        idx[:, 0], idx[:, 1] = 0, 1
+    ref = oracle.dispatch(idx, E)
+    sh = moe.Shape(T, d, h, E, gen.BF16, moe.ACT_CODES[act])
+    ws_bytes = moe.workspace_size(sh)
+    ws = G.empty((ws_bytes,), torch.uint8)
+    x, sa, off = G.dev(w["x"]), G.dev(ref["sorted_assign"]), G.dev(ref["offsets"])
+    dw = {k: G.dev(w[k]) for k in ("w1", "w2", "w3", "b1", "b2")}
+    y_full = G.empty((2 * T, d), torch.bfloat16)
+    H = G.empty((2 * T, h), torch.bfloat16)
+    y = G.empty((2 * T, d), torch.bfloat16)
+    for _ in range(2):  # the second call reuses a scratch that holds the first call's partials
+        moe.expert_ffn(sh, x, sa, off, dw["w1"], dw["w2"], y_full, ws, ws_bytes, w3=dw["w3"], b1=dw["b1"],
+                       b2=dw["b2"])
+        moe.expert_ffn_up(sh, x, sa, off, dw["w1"], H, ws, ws_bytes, w3=dw["w3"], b1=dw["b1"])
+        moe.expert_ffn_down(sh, H, off, dw["w2"], y, ws, ws_bytes, b2=dw["b2"])
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_full)
+    y_ref = oracle.ffn_rows(w["x"], ref["sorted_assign"] // 2, idx.reshape(-1)[ref["sorted_assign"]], w["w1"],
+                            w["w2"], act, w3=w["w3"], b1=w["b1"], b2=w["b2"], mirror=True)
+    G.assert_bf16_close(G.host(y_full), y_ref, f"fused-H decode T={T}")
+
+
 ROW_TILE_COUNTS = {
     # large tiles (256 rows, up to 320): 641 -> 3 x 214, 321 -> 2 x 161, 650 -> 3 x 217, 320 -> 1 x 320,
     # 1030 -> 4 x 258; subtiles split 4/3, 3/3, 5/5, 5/4 over the two wave rows, or leave one empty
