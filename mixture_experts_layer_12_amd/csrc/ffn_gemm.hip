@@ -148,6 +148,30 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// vmcnt(n * PER) for a runtime n in [0, MAXN] (larger n waits for MAXN * PER)
+template <int PER, int MAXN>
+__device__ __forceinline__ void wait_groups(int n) {
+    if constexpr (MAXN >= 0) {
+        if (n >= MAXN) {
+            wait_vmcnt<MAXN * PER>();
+            return;
+        }
+        if constexpr (MAXN > 0) wait_groups<PER, MAXN - 1>(n);
+    }
+}
+
+// vmcnt(n_a + NB) for a runtime count n_a of A copies per stage (0 .. NA)
+template <int NA, int NB>
+__device__ __forceinline__ void wait_live_stage(int n_a) {
+    if constexpr (NA >= 0) {
+        if (n_a >= NA) {
+            wait_vmcnt<NA + NB>();
+            return;
+        }
+        if constexpr (NA > 0) wait_live_stage<NA - 1, NB>(n_a);
+    }
+}
+
 // One BM x BNC output tile of one expert.  NW = WM x WN waves, each owning a
 // (BM/WM) x (BNC/WN) block (for SwiGLU: that block of both W1 and W3).
 //
@@ -160,8 +184,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 //      give a 32x32x16 MFMA B operand with no register transposes.
 // Both are filled with 1 KB global->LDS copies: an A copy is RPD whole rows,
 // a B copy is 4 k rows x 128 columns (16-byte runs of one weight row).
-template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool GATHER, int WPE>
-__global__ __launch_bounds__(WM *WN *kWave, WPE) void ffn_gemm_kernel(
+//
+// BLD > 0 (loader waves): BLD extra waves copy the weight tiles into a ring of
+// BST B stages of their own, and the NW compute waves copy only the A tiles
+// (two A stages).  A wave's copies retire in issue order, so when one wave
+// copies both operands, waiting for the next A tile also waits for every
+// weight tile issued before it, and the weight ring can be no deeper than the
+// A ring.  Split over waves, the weights run BST - 1 tiles ahead while A
+// (rows already in L2) runs one tile ahead.  All waves meet at the same
+// barriers; the loader waves leave after the last one.
+template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool GATHER, int WPE, int BLD = 0,
+          int BST = 2>
+__global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NT, int S,
@@ -173,19 +207,23 @@ __global__ __launch_bounds__(WM *WN *kWave, WPE) void ffn_gemm_kernel(
     constexpr int WTM = BM / WM;                 // wave tile rows
     constexpr int WNC = BNC / WN;                // wave tile columns (per matrix)
     constexpr int SM = WTM / 32, SJ = WNC / 32;  // 32x32 subtiles per wave (per matrix)
+    constexpr bool SPEC = BLD > 0;               // weight tiles copied by loader waves
+    constexpr int CW = SPEC ? BLD : NW;          // waves copying B
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE_BYTES = A_BYTES + B_BYTES;
-    constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;  // 1 KB copies per wave per stage
+    constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / CW;  // 1 KB copies per wave per stage
     constexpr int CPR = BK / 8;                  // 16-byte chunks per A row
     constexpr int RPD = 64 / CPR;                // A rows per copy
     constexpr int KQ_ROW = (BN / 16) * 128;      // bytes per 4-k-row band of the B tile
     constexpr int HPB = BN / 128;                // B copies per band
     static_assert(SM >= 1 && SJ >= 1, "wave tile too small");
     static_assert(BK == 32 || BK == 64, "BK");
-    static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "whole copies per wave");
-    static_assert(NW % HPB == 0, "a wave's B copies share one column range");
+    static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * CW * 1024 == B_BYTES, "whole copies per wave");
+    static_assert(CW % HPB == 0, "a wave's B copies share one column range");
+    static_assert(!SPEC || (STAGES == 2 && BST >= 3 && (BST - 1) * B_PW <= 63), "loader-wave ring");
     static_assert(!DUAL || BNC % 128 == 0, "a B copy covers one matrix");
     static_assert(STAGES >= 2 && (STAGES - 2) * (A_PW + B_PW) <= 63, "vmcnt range");
-    constexpr int LDS_MAIN = STAGES * STAGE_BYTES;
+    // LDS: the shared ring of STAGES (A, B) stages, or (SPEC) two A stages then BST B stages
+    constexpr int LDS_MAIN = SPEC ? 2 * A_BYTES + BST * B_BYTES : STAGES * STAGE_BYTES;
     constexpr int LDS_EPI = BM * BNC * 2;  // bf16 output tile
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI];
 
@@ -214,9 +252,17 @@ __global__ __launch_bounds__(WM *WN *kWave, WPE) void ffn_gemm_kernel(
     const int per = (nsub + WM - 1) / WM;
     const int live_sm = min(per, max(0, nsub - wm * per));
     const int wrow = wm * per * 32;  // first tile row of this wave
+    // With two stages every wait in the loop drains all of a wave's copies, so
+    // copies whose RPD rows all lie past the tile's live rows are skipped (live
+    // rows are a prefix of each wave row region, so the first row decides).
+    constexpr bool SKIP_DEAD = (STAGES == 2);
+    uint32_t a_live = 0;  // wave-uniform: bit q = A copy q carries live rows
     const uint16_t *a_src[A_PW];
 #pragma unroll
     for (int q = 0; q < A_PW; ++q) {
+        const int m0 = (w + NW * q) * RPD;  // first LDS row of copy q
+        const int reg0 = m0 / WTM, off0 = m0 % WTM;
+        if (!SKIP_DEAD || (off0 < per * 32 && reg0 * per * 32 + off0 < rows)) a_live |= 1u << q;
         const int m = (w + NW * q) * RPD + lane / CPR;  // LDS row of this lane's chunk
         const int c = (lane % CPR) ^ swz<BK>(m);        // logical chunk held by physical slot lane % CPR
         const int reg = m / WTM, off = m % WTM;         // wave row region and row inside it
@@ -228,23 +274,41 @@ __global__ __launch_bounds__(WM *WN *kWave, WPE) void ffn_gemm_kernel(
         }
         a_src[q] = A + (size_t)src * K + c * 8;
     }
-    // B copy w + NW q: band kq = (w + NW q) / HPB, columns [(w % HPB) 128, +128) of the LDS tile;
+    // B copy cw + CW q (cw: this wave's index among the CW copying waves): band
+    // kq = (cw + CW q) / HPB, columns [(cw % HPB) 128, +128) of the LDS tile;
     // lane: 16-column block lane / 8, k row 4 kq + (lane % 8) / 2, 8 columns at 8 (lane % 2)
-    const int ncol = (w % HPB) * 128 + (lane >> 3) * 16 + (lane & 1) * 8;
-    const int mat = DUAL ? (w % HPB) * 128 / BNC : 0;  // uniform: one matrix per copy
+    const int cw = SPEC ? max(w - NW, 0) : w;
+    const int ncol = (cw % HPB) * 128 + (lane >> 3) * 16 + (lane & 1) * 8;
+    const int mat = DUAL ? (cw % HPB) * 128 / BNC : 0;  // uniform: one matrix per copy
     int gcol = n0 + ncol - mat * BNC;
     if (gcol >= N) gcol = 0;
     const uint32_t b_voff = (uint32_t)((((lane & 7) >> 1) * N + gcol) * 2);
-    const uint16_t *b_base = (mat ? B1 : B0) + (size_t)e * K * N + (size_t)(w / HPB) * 4 * N;
+    const uint16_t *b_base = (mat ? B1 : B0) + (size_t)e * K * N + (size_t)(cw / HPB) * 4 * N;
 
     auto issue = [&](int s, int kt) {
         const int k0 = kt * BK;
         const uint32_t sa = lds0 + s * STAGE_BYTES;
 #pragma unroll
-        for (int q = 0; q < A_PW; ++q) dma16(a_src[q] + k0, sa + (w + NW * q) * 1024);
+        for (int q = 0; q < A_PW; ++q)
+            if ((a_live >> q) & 1) dma16(a_src[q] + k0, sa + (w + NW * q) * 1024);
 #pragma unroll
         for (int q = 0; q < B_PW; ++q)
             dma16_s(b_voff, b_base + (size_t)(k0 + 4 * (NW / HPB) * q) * N, sa + A_BYTES + (w + NW * q) * 1024);
+    };
+    // SPEC copies: A of k-tile kt into A stage s (compute waves), B of k-tile kt into B stage t (loader waves)
+    auto issue_a = [&](int s, int kt) {
+        const int k0 = kt * BK;
+        const uint32_t sa = lds0 + s * A_BYTES;
+#pragma unroll
+        for (int q = 0; q < A_PW; ++q)
+            if ((a_live >> q) & 1) dma16(a_src[q] + k0, sa + (w + NW * q) * 1024);
+    };
+    auto issue_b = [&](int t, int kt) {
+        const int k0 = kt * BK;
+        const uint32_t sb = lds0 + 2 * A_BYTES + t * B_BYTES;
+#pragma unroll
+        for (int q = 0; q < B_PW; ++q)
+            dma16_s(b_voff, b_base + (size_t)(k0 + 4 * (CW / HPB) * q) * N, sb + (cw + CW * q) * 1024);
     };
 
     f32x16 acc[NB][SM][SJ];
@@ -277,17 +341,19 @@ __global__ __launch_bounds__(WM *WN *kWave, WPE) void ffn_gemm_kernel(
         bf16x8 b[NB][SJ];
     };
     // lv: compile-time count of live subtiles (LV >= 0) or LV = -1 for the runtime live_sm
-    auto read_frags = [&](int s, int ks, Frags &f, auto lv) {
+    // ao, bo: byte offsets of the A and B stages in LDS
+    auto read_frags = [&](int ao, int bo, int ks, Frags &f, auto lv) {
         constexpr int LV = decltype(lv)::value;
         const int nl = LV >= 0 ? LV : live_sm;
         if (nl == 0) return;  // this wave's rows are all padding
-        const lds_byte *L = (const lds_byte *)lds + s * STAGE_BYTES;
+        const lds_byte *L = (const lds_byte *)lds + ao;
+        const lds_byte *LB = (const lds_byte *)lds + bo;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int j = 0; j < SJ; ++j) {
                 const int cb = b * BNC + wn * WNC + j * 32;  // LDS tile column of the subtile
-                const lds_byte *p = L + A_BYTES + b_lane + ks * 4 * KQ_ROW + (cb >> 4) * 128;
+                const lds_byte *p = LB + b_lane + ks * 4 * KQ_ROW + (cb >> 4) * 128;
                 const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
                 const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + KQ_ROW));
                 f.b[b][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -328,27 +394,86 @@ __global__ __launch_bounds__(WM *WN *kWave, WPE) void ffn_gemm_kernel(
         Frags f[2];
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) issue(s, ktile(s));
-        wait_vmcnt<(STAGES - 1) * DPW>();  // this wave's copies of k-tile 0 have landed
+        // this wave's copies of k-tile 0 have landed: at most one stage's copies remain
+        if constexpr (SKIP_DEAD) {
+            wait_live_stage<A_PW, B_PW>(__popc(a_live));
+        } else {
+            wait_vmcnt<(STAGES - 1) * DPW>();
+        }
         __syncthreads();                    // ... everyone's
-        read_frags(0, 0, f[0], lv);
+        read_frags(0, A_BYTES, 0, f[0], lv);
         for (int kt = 0; kt < KT; ++kt) {
             const int s = kt % STAGES;
+            const int so = s * STAGE_BYTES;
 #pragma unroll
             for (int ks = 0; ks + 1 < KS; ++ks) {
-                read_frags(s, ks + 1, f[(ks + 1) & 1], lv);
+                read_frags(so, so + A_BYTES, ks + 1, f[(ks + 1) & 1], lv);
                 mma(f[ks & 1], lv);
             }
             wait_vmcnt<(STAGES - 2) * DPW>();  // k-tile kt+1 has landed (this wave's copies)
             __syncthreads();                    // ... everyone's; and k-tile kt is fully read
             issue(s, ktile(kt + STAGES));
-            if (kt + 1 < KT) read_frags((kt + 1) % STAGES, 0, f[0], lv);
+            const int sn = ((kt + 1) % STAGES) * STAGE_BYTES;
+            if (kt + 1 < KT) read_frags(sn, sn + A_BYTES, 0, f[0], lv);
             mma(f[(KS - 1) & 1], lv);
         }
     };
+    // ---- SPEC: compute waves.  A stage kt & 1, B stage kt % BST.  Barrier P publishes
+    // k-tile 0, barrier kt publishes k-tile kt+1 (the loader waves wait for their copies
+    // of it before that barrier) and frees the stages of k-tile kt.
+    auto main_loop_spec = [&](auto lv) {
+        Frags f[2];
+        issue_a(0, kt0);
+        issue_a(1, ktile(1));
+        wait_live_stage<A_PW, 0>(__popc(a_live));  // A of k-tile 0 has landed
+        __syncthreads();                            // barrier P
+        read_frags(0, 2 * A_BYTES, 0, f[0], lv);
+        for (int kt = 0; kt < KT; ++kt) {
+            const int ao = (kt & 1) * A_BYTES, bo = 2 * A_BYTES + (kt % BST) * B_BYTES;
+#pragma unroll
+            for (int ks = 0; ks + 1 < KS; ++ks) {
+                read_frags(ao, bo, ks + 1, f[(ks + 1) & 1], lv);
+                mma(f[ks & 1], lv);
+            }
+            wait_vmcnt<0>();  // A of k-tile kt+1 has landed (this wave's copies)
+            __syncthreads();  // barrier kt
+            if (kt + 2 < KT) issue_a(kt & 1, kt0 + kt + 2);
+            if (kt + 1 < KT)
+                read_frags(((kt + 1) & 1) * A_BYTES, 2 * A_BYTES + ((kt + 1) % BST) * B_BYTES, 0, f[0], lv);
+            mma(f[(KS - 1) & 1], lv);
+        }
+    };
+    // ---- SPEC: loader waves.  B of k-tile t goes to stage t % BST, BST - 1 tiles ahead.
+    auto loader_loop = [&]() {
+#pragma unroll
+        for (int t = 0; t < BST; ++t)
+            if (t < KT) issue_b(t, kt0 + t);
+        wait_groups<B_PW, BST - 1>(min(BST, KT) - 1);  // k-tile 0 has landed
+        __syncthreads();                                 // barrier P
+        for (int kt = 0; kt < KT; ++kt) {
+            // k-tile kt+1 has landed: later tiles issued so far are kt+2 .. min(kt+BST-1, KT-1)
+            wait_groups<B_PW, BST - 2>(max(0, min(BST - 2, KT - 2 - kt)));
+            __syncthreads();  // barrier kt: k-tile kt is fully read, its stage is free
+            if (kt + BST < KT) issue_b(kt % BST, kt0 + kt + BST);
+        }
+    };
     // the common live counts get their own copy of the loop, free of per-subtile tests
-    if (live_sm == SM) main_loop(std::integral_constant<int, SM>{});
-    else if (live_sm == SM - 1) main_loop(std::integral_constant<int, SM - 1>{});
-    else main_loop(std::integral_constant<int, -1>{});
+    if constexpr (SPEC) {
+        if (w >= NW) {  // loader wave: the main loop's barriers, the one below, the epilogue's
+            loader_loop();
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (S == 1) __syncthreads();
+            return;
+        }
+        if (live_sm == SM) main_loop_spec(std::integral_constant<int, SM>{});
+        else if (live_sm == SM - 1) main_loop_spec(std::integral_constant<int, SM - 1>{});
+        else main_loop_spec(std::integral_constant<int, -1>{});
+    } else {
+        if (live_sm == SM) main_loop(std::integral_constant<int, SM>{});
+        else if (live_sm == SM - 1) main_loop(std::integral_constant<int, SM - 1>{});
+        else main_loop(std::integral_constant<int, -1>{});
+    }
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -413,30 +538,58 @@ __global__ __launch_bounds__(WM *WN *kWave, WPE) void ffn_gemm_kernel(
     }
 }
 
-// Two tile shapes, 8 waves per workgroup, BK = 64, two LDS stages:
+// Tile shapes, BK = 64, one workgroup per CU:
 //   big: row tiles of 256 rows (up to 320 when a small tail is spread over
 //        them) x 256 weight columns (SwiGLU: 128 outputs of both W1 and W3);
-//        144 KB of LDS, one workgroup per CU, two waves per SIMD;
-//   mid: row tiles of 128 rows (up to 192) x 128 columns, no SwiGLU; 80 KB of
-//        LDS and <= 128 VGPRs, so two workgroups share a CU.  For a few
-//        hundred rows per expert the layer streams its weights; a second
-//        workgroup per CU overlaps its copies and barriers with the first's
-//        (measured: 8-expert T=512, first layer 57.8 -> 46.4 us).
+//        8 waves copy both operands through two (A, B) stages, 144 KB of LDS;
+//   mid: no SwiGLU, at most 160 expected rows per expert, where the layer
+//        streams its weights: row tiles of 128 rows (up to 192) x 128 or 256
+//        columns; 8 compute waves copy A through two stages and 2 loader waves
+//        keep the weights 5 (128 columns) or 2 (256 columns) k-tiles ahead,
+//        144 KB of LDS.  Measured on the 8-expert layer at T = 512 (cold
+//        weights): first layer 60.1 -> 54.8 us with 256 columns; second layer
+//        with K split in 2 instead of 4, the same time and half the partials.
 constexpr int kBK = 64;
-struct GemmCfg {
-    bool mid;
-    int BMB;      // base row-tile height
-    int BNC;      // output columns per tile
-    int per_cu;   // workgroups resident per CU
-};
-GemmCfg gemm_cfg(const colibri_moe_shape_t &s, bool up) {
+
+}  // namespace
+
+GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up) {
     const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
     const bool mid = !dual && 2L * s.T <= 160L * s.E;  // <= 160 expected rows per expert
-    if (mid) return {true, 128, 128, 2};
-    return {false, 256, dual ? 128 : 256, 1};
+    const long K = up ? s.d : s.h, N = up ? s.h : s.d;
+    const long A = 2L * s.T;
+    const long KT = K / kBK;
+    const int BMB = mid ? 128 : 256;
+    GemmPlan best{mid, BMB, 0, 1};
+    double best_cost = 1e300;
+    // Expected row tiles: one per expert while experts hold at most a tile's
+    // rows, else one per base tile height.  Estimated time: (rounds of 256
+    // resident workgroups) x (k-tiles per block + 2, a per-block start-up cost)
+    // x the k-tile time (measured: ~0.85 us per 128 weight columns for the
+    // weight-streaming mid shapes, whose weight stream sets the pace; ~1.9 us
+    // for a big tile), plus, when K is split, the fp32 partials written and
+    // read once (~5 TB/s) and a ~4 us reduce launch.  Splits keep at least 4
+    // k-tiles per block.  Ties keep the wider tile and the smaller S.
+    const int widths[2] = {256, 128};
+    for (int wi = 0; wi < (mid ? 2 : 1); ++wi) {
+        const long BNC = mid ? widths[wi] : (dual ? 128 : 256);
+        const long NT = (N + BNC - 1) / BNC;
+        const long rt = std::max<long>(std::min<long>(s.E, A), (A + BMB - 1) / BMB);
+        const long tiles = rt * NT;
+        const double t_kt = mid ? 0.85 * (double)BNC / 128 : 1.9;
+        for (long S = 1; S <= KT / 4 || S == 1; ++S) {
+            const double part_bytes = (double)S * A * N * (dual ? 2 : 1) * 4;
+            double us = (double)((tiles * S + 255) / 256) * ((double)KT / S + 2.0) * t_kt;
+            if (S > 1) us += 2.0 * part_bytes / 5.0e6 + 4.0;
+            if (us < best_cost - 1e-9) best_cost = us, best = {mid, BMB, (int)BNC, (int)S};
+        }
+    }
+    return best;
 }
 
-template <int BMB, int BM, int BN, int WPE, int EPI>
+namespace {
+
+template <int BMB, int BM, int BN, int WPE, int BLD, int BST, int EPI>
 hipError_t launch_shape(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
                         const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
                         int S, float *part, hipStream_t st) {
@@ -445,60 +598,38 @@ hipError_t launch_shape(bool gather, const colibri_moe_shape_t &s, const void *A
     const int NT = (N + BNC - 1) / BNC;
     const int mtiles = (A + BMB - 1) / BMB + std::min(s.E, A);  // bound on the row tiles of all experts
     const dim3 grid(mtiles * NT * S);
-    constexpr int threads = 2 * 4 * kWave;
+    constexpr int threads = (2 * 4 + BLD) * kWave;
     if (gather)
-        ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, true, WPE><<<grid, threads, 0, st>>>(
+        ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, true, WPE, BLD, BST><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
             (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, part);
     else
-        ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, false, WPE><<<grid, threads, 0, st>>>(
+        ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, false, WPE, BLD, BST><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
             (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, part);
     return hipGetLastError();
 }
 
 template <int EPI>
-hipError_t launch_gemm(bool up, bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
+hipError_t launch_gemm(const GemmPlan &p, bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
                        const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
-                       int S, float *part, hipStream_t st) {
+                       float *part, hipStream_t st) {
     if constexpr (EPI != EPI_SWIGLU) {
-        if (gemm_cfg(s, up).mid)  // 2 workgroups per CU: 4 waves per SIMD
-            return launch_shape<128, 192, 128, 4, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, S, part, st);
+        if (p.mid && p.BNC == 256)
+            return launch_shape<128, 192, 256, 2, 2, 3, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S,
+                                                             part, st);
+        if (p.mid)
+            return launch_shape<128, 192, 128, 2, 2, 6, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S,
+                                                             part, st);
     }
-    return launch_shape<256, 320, 256, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, S, part, st);
+    return launch_shape<256, 320, 256, 2, 0, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S, part, st);
 }
 
 }  // namespace
 
-// K splits of one layer.  Mid-sized batches (a few hundred rows per expert)
-// make too few tiles to fill the chip; splitting K multiplies the blocks at the
-// cost of fp32 partials [S][2T][cols] written and read once more.  The split
-// minimises (rounds of resident workgroups) x (k-tiles per block + 2, a
-// per-block start-up cost) over the S whose partials stay within a quarter of
-// the layer's weight bytes, with at least 4 k-tiles per block; ties keep the
-// smaller S.  Expected row tiles: one per expert while experts hold at most
-// a tile's rows, else one per base tile height.
 int gemm_splits(const colibri_moe_shape_t &s, bool up) {
     if (s.dtype != COLIBRI_BF16 || s.T <= 0) return 1;
-    const GemmCfg c = gemm_cfg(s, up);
-    const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
-    const long K = up ? s.d : s.h, N = up ? s.h : s.d;
-    const long A = 2L * s.T;
-    const long NT = (N + c.BNC - 1) / c.BNC;
-    const long rt = std::max<long>(std::min<long>(s.E, A), (A + c.BMB - 1) / c.BMB);
-    const long tiles = rt * NT;
-    const long KT = K / kBK;
-    const long slots = 256L * c.per_cu;
-    const double weight_bytes = (double)std::min<long>(s.E, A) * K * N * 2 * (dual ? 2 : 1);
-    int best = 1;
-    double best_cost = 1e300;
-    for (long S = 1; S <= KT / 4 || S == 1; ++S) {
-        const double part_bytes = (double)S * A * N * (dual ? 2 : 1) * 4;
-        if (S > 1 && part_bytes > 0.25 * weight_bytes) break;
-        const double cost = (double)((tiles * S + slots - 1) / slots) * ((double)KT / S + 2.0);
-        if (cost < best_cost - 1e-9) best_cost = cost, best = (int)S;
-    }
-    return best;
+    return gemm_plan(s, up).S;
 }
 
 size_t gemm_scratch_bytes(const colibri_moe_shape_t &s, bool up) {
@@ -512,33 +643,34 @@ hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, cons
                           const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
                           hipStream_t st) {
     const bool gather = sorted_assign != nullptr;
-    const int S = gemm_splits(s, true);
+    const GemmPlan p = gemm_plan(s, true);
     float *part = static_cast<float *>(scratch);
     hipError_t e;
     switch (s.act) {
         case COLIBRI_ACT_RELU:
-            e = launch_gemm<EPI_ACT_RELU>(true, gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d, s.h,
-                                          S, part, st);
+            e = launch_gemm<EPI_ACT_RELU>(p, gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d,
+                                          s.h, part, st);
             break;
         case COLIBRI_ACT_GELU:
-            e = launch_gemm<EPI_ACT_GELU>(true, gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d, s.h,
-                                          S, part, st);
+            e = launch_gemm<EPI_ACT_GELU>(p, gather, s, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, s.d,
+                                          s.h, part, st);
             break;
         default:
-            e = launch_gemm<EPI_SWIGLU>(true, gather, s, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, s.d, s.h,
-                                        S, part, st);
+            e = launch_gemm<EPI_SWIGLU>(p, gather, s, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, s.d, s.h,
+                                        part, st);
     }
-    if (e == hipSuccess && S > 1) e = launch_split_reduce(s, true, S, offsets, w, H, part, st);
+    if (e == hipSuccess && p.S > 1) e = launch_split_reduce(s, true, p.S, offsets, w, H, part, st);
     return e;
 }
 
 hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
                             const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st) {
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
-    const int S = gemm_splits(s, false);
+    const GemmPlan p = gemm_plan(s, false);
     float *part = static_cast<float *>(scratch);
-    hipError_t e = launch_gemm<EPI_BIAS_ONLY>(false, false, s, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d, S, part, st);
-    if (e == hipSuccess && S > 1 && reduce) e = launch_split_reduce(s, false, S, offsets, w, y, part, st);
+    hipError_t e = launch_gemm<EPI_BIAS_ONLY>(p, false, s, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d, part,
+                                              st);
+    if (e == hipSuccess && p.S > 1 && reduce) e = launch_split_reduce(s, false, p.S, offsets, w, y, part, st);
     return e;
 }
 

@@ -74,6 +74,13 @@ hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *pa
 // (gemm_splits > 1) writes fp32 partials [S][2T][cols] to scratch and then
 // reduces them (the second layer only when `reduce`; otherwise
 // launch_combine_partials adds them).
+struct GemmPlan {
+    bool mid;  // weight-streaming tile shapes (no SwiGLU, <= 160 expected rows per expert)
+    int BMB;   // base row-tile height
+    int BNC;   // output columns per tile
+    int S;     // K splits
+};
+GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up);
 int gemm_splits(const colibri_moe_shape_t &s, bool up);
 size_t gemm_scratch_bytes(const colibri_moe_shape_t &s, bool up);
 hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
