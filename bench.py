@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--rotate-gb", type=float, default=2.0, help="total bytes of rotated weight copies")
     ap.add_argument("--decode-T", default="1,64", help="decode batch sizes also timed (comma list, '' = none)")
     ap.add_argument("--decode-iters", type=int, default=200)
+    ap.add_argument("--no-q8", action="store_true", help="skip the int8-weight decode lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle sample for about this long")
@@ -248,10 +249,9 @@ def main():
         log(f"calibration copy: {args.copy_mb} MiB")
 
     # ---------------------------------------------------------------- decode sizes
-    decode = {}
-    for tok in [int(v) for v in args.decode_T.split(",") if v.strip()]:
-        if tok > T:
-            continue
+    def time_decode(step_fn, tok):
+        """GPU-time median/min/p90 (spin kernel in front every 10 steps) and the
+        host-inclusive time of back-to-back steps, in us."""
         s2 = sh.with_T(tok)
         xd, od = x[:tok], out[:tok]
         times = []
@@ -261,7 +261,7 @@ def main():
             if it % 10 == 0:
                 prefill_queue()
             e0.record(stream)
-            step(it, xx=xd, s=s2, o=od)
+            step_fn(it, xx=xd, s=s2, o=od)
             e1.record(stream)
             if it % 10 == 9:
                 torch.cuda.synchronize()
@@ -269,22 +269,60 @@ def main():
                 times.append((e0, e1))
         torch.cuda.synchronize()
         us = np.array([a.elapsed_time(b) * 1e3 for a, b in times])
-        # host-inclusive: back-to-back steps, no spin kernel in front
         torch.cuda.synchronize()
         h0 = time.perf_counter()
         for it in range(args.decode_iters):
-            step(it, xx=xd, s=s2, o=od)
+            step_fn(it, xx=xd, s=s2, o=od)
         torch.cuda.synchronize()
         host_us = (time.perf_counter() - h0) / args.decode_iters * 1e6
-        c2 = counts.cpu().numpy()
-        hit2 = int((c2 > 0).sum())
-        byt2 = hit2 * (up_bytes_e + down_bytes_e) + tok * cfg.d * s_ * 2 + cfg.d * cfg.E * s_
-        med = float(np.median(us))
-        decode[f"T={tok}"] = {"us_per_step_median": round(med, 2), "us_min": round(float(us.min()), 2),
-                              "us_p90": round(float(np.percentile(us, 90)), 2),
-                              "us_per_step_host_inclusive": round(host_us, 2), "experts_hit": hit2,
-                              "hbm_frac": round(byt2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        return float(np.median(us)), float(us.min()), float(np.percentile(us, 90)), host_us
+
+    def decode_record(tok, med, umin, p90, host_us, up_e, down_e):
+        hit2 = int((counts.cpu().numpy() > 0).sum())
+        byt2 = hit2 * (up_e + down_e) + tok * cfg.d * s_ * 2 + cfg.d * cfg.E * s_
+        return {"us_per_step_median": round(med, 2), "us_min": round(umin, 2), "us_p90": round(p90, 2),
+                "us_per_step_host_inclusive": round(host_us, 2), "experts_hit": hit2,
+                "hbm_frac": round(byt2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    decode_ts = [int(v) for v in args.decode_T.split(",") if v.strip() and int(v) <= T]
+    decode = {}
+    for tok in decode_ts:
+        decode[f"T={tok}"] = decode_record(tok, *time_decode(step, tok), up_bytes_e, down_bytes_e)
         log(f"decode T={tok}: {decode[f'T={tok}']}")
+
+    # int8 expert weights (per-column scales), decode sizes only: quantized on the
+    # GPU by the library's own quantizer, rotated like the bf16 weights
+    decode_q8 = {}
+    q8_ts = [t for t in decode_ts if t <= 64]
+    if q8_ts and cfg.dtype == gen.BF16 and not args.no_q8:
+        q0 = {"b1": dw0["b1"], "b2": dw0["b2"]}
+        for name, qn, sn in (("w1", "q1", "s1"), ("w3", "q3", "s3"), ("w2", "q2", "s2")):
+            wt = dw0[name]
+            if wt is None:
+                q0[qn] = q0[sn] = None
+                continue
+            E_, K_, N_ = wt.shape
+            q0[qn] = torch.empty((E_, K_, N_), dtype=torch.int8, device=dev)
+            q0[sn] = torch.empty((E_, N_), dtype=torch.float32, device=dev)
+            moe.quantize_q8(wt, gen.BF16, E_, K_, N_, q0[qn], q0[sn])
+        torch.cuda.synchronize()
+        qb = {k: (v[0].numel() * v.element_size() if v is not None else 0) for k, v in q0.items()}
+        up_q8_e = qb["q1"] + qb["q3"] + qb["s1"] + qb["s3"] + qb["b1"]
+        down_q8_e = qb["q2"] + qb["s2"] + qb["b2"]
+        q8_layer_bytes = sum(v.numel() * v.element_size() for v in q0.values() if v is not None)
+        R8 = max(1, math.ceil(args.rotate_gb * 1e9 / q8_layer_bytes))
+        qcopies = [q0] + [{k: (v.clone() if v is not None else None) for k, v in q0.items()} for _ in range(R8 - 1)]
+        log(f"int8 weights: {R8} copies x {q8_layer_bytes / 1e6:.1f} MB")
+
+        def step_q8(i, xx=x, s=sh, o=out):
+            w = qcopies[i % R8]
+            moe.layer_forward_q8(s, xx, w_r, b_r, w["q1"], w["s1"], w["q2"], w["s2"], o, ws, ws_bytes, q3=w["q3"],
+                                 s3=w["s3"], b1=w["b1"], b2=w["b2"], counts=counts)
+
+        for tok in q8_ts:
+            decode_q8[f"T={tok}"] = decode_record(tok, *time_decode(step_q8, tok), up_q8_e, down_q8_e)
+            log(f"decode int8 weights T={tok}: {decode_q8[f'T={tok}']}")
+        del qcopies, q0
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -316,7 +354,7 @@ def main():
         "config": {"workload": f"{cfg.title}: E={cfg.E}, top-2, d={cfg.d}, h={cfg.h}, {cfg.act}, T={T}",
                    "T": T, "E": cfg.E, "d": cfg.d, "h": cfg.h, "act": cfg.act, "weight_copies": R,
                    "experts_hit": hit},
-        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode,
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode, "decode_int8_weights": decode_q8,
         "timing": "GPU time (HIP events, queue pre-filled by a spin kernel)" if can_sleep else "GPU time (HIP events)",
     }
     print(json.dumps(rec), flush=True)

@@ -162,6 +162,47 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
                               float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* ------------------------------------------------------------------ int8 expert weights
+ * Expert weights stored as int8 codes with one fp32 scale per output column
+ * ([zskr] section 5.3: per-channel INT8 quantization of the expert weights,
+ * scales kept beside them, halving the weight bytes):
+ *   W[e][k][n] = s[e][n] * q[e][k][n],  q in [-127, 127].
+ *   q1 [E][d][h], q3 [E][d][h] (SwiGLU only, else NULL), q2 [E][h][d]   int8, 16-byte aligned
+ *   s1 [E][h], s3 [E][h] (SwiGLU only, else NULL), s2 [E][d]             fp32, 4-byte aligned
+ *   b1 [E][h], b2 [E][d]   as in colibri_moe_experts_t (NULL = zero; NULL for SwiGLU)
+ * The layer computes exactly what it computes with the dequantized weights
+ * s * q stored in full precision (each column's sum is formed from the
+ * codes and multiplied by its scale).  These entry points stream weights at
+ * decode sizes: they take bf16 layers with T <= 64 and return
+ * COLIBRI_ERR_UNSUPPORTED for other shapes. */
+typedef struct {
+    const int8_t *q1, *q3, *q2;
+    const float *s1, *s3, *s2;
+    const void *b1, *b2;
+} colibri_moe_experts_q8_t;
+
+/* Per-column int8 quantization of one weight tensor (producing q1, q3 or q2
+ * and its scales).  For every expert e and column n, in fp32:
+ *   amax = max over k of |w[e][k][n]|,  s[e][n] = amax / 127  (1 when amax = 0),
+ *   q[e][k][n] = w[e][k][n] / s[e][n] rounded to nearest (ties to even),
+ *   clamped to [-127, 127].
+ *   w [E][K][N] dtype, 16-byte aligned; q [E][K][N] int8 out; s [E][N] fp32 out.
+ * E, K, N >= 1; N a multiple of 4. */
+int colibri_moe_quantize_q8(const void *w, colibri_dtype_t dtype, int32_t E, int32_t K, int32_t N, int8_t *q,
+                            float *s, hipStream_t stream);
+
+/* Step 4 with int8 expert weights; arguments as for colibri_moe_expert_ffn.
+ * ws must hold colibri_moe_workspace_size(s) bytes, 256-byte aligned. */
+int colibri_moe_expert_ffn_q8(const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                              const int32_t *expert_offsets, const colibri_moe_experts_q8_t *w, void *y_sorted,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps 1-5 with int8 expert weights; arguments as for colibri_moe_layer_forward. */
+int colibri_moe_layer_forward_q8(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                                 const colibri_moe_experts_q8_t *w, void *out, int32_t *topk_idx_out,
+                                 float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *colibri_moe_status_string(int status);
 

@@ -24,6 +24,7 @@ ACT_CODES = {"relu": RELU, "gelu": GELU, "swiglu": SWIGLU}
 EXPORTED = [
     "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn",
     "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
+    "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
     "colibri_moe_status_string",
 ]
 
@@ -41,6 +42,12 @@ class _Shape(ctypes.Structure):
 
 class _Experts(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
+
+
+class _ExpertsQ8(ctypes.Structure):
+    _fields_ = [("q1", ctypes.c_void_p), ("q3", ctypes.c_void_p), ("q2", ctypes.c_void_p),
+                ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
                 ("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
 
 
@@ -91,8 +98,13 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_expert_ffn_down.argtypes = [SP, P, P, ctypes.POINTER(_Experts), P, P, Z, P]
     lib.colibri_moe_combine.argtypes = [SP, P, P, P, P, P]
     lib.colibri_moe_layer_forward.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, P, P, P, Z, P]
+    i32 = ctypes.c_int32
+    lib.colibri_moe_quantize_q8.argtypes = [P, I, i32, i32, i32, P, P, P]
+    lib.colibri_moe_expert_ffn_q8.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ8), P, P, Z, P]
+    lib.colibri_moe_layer_forward_q8.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ8), P, P, P, P, P, Z, P]
     for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up",
-              "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward"):
+              "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
+              "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8"):
         getattr(lib, f).restype = I
     lib.colibri_moe_status_string.argtypes = [I]
     lib.colibri_moe_status_string.restype = ctypes.c_char_p
@@ -190,6 +202,35 @@ def layer_forward(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: int, w3=
     _check(load().colibri_moe_layer_forward(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
                                             _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
                                             ws_bytes, _stream(stream)), "colibri_moe_layer_forward")
+
+
+# ------------------------------------------------------------------ int8 expert weights
+def _experts_q8(q1, s1, q2, s2, q3=None, s3=None, b1=None, b2=None) -> _ExpertsQ8:
+    return _ExpertsQ8(_ptr(q1), _ptr(q3), _ptr(q2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(b1), _ptr(b2))
+
+
+def quantize_q8(w, dtype: int, E: int, K: int, N: int, q, scale, stream=None):
+    """Per-column int8 codes q [E, K, N] and fp32 scales [E, N] of w [E, K, N]."""
+    _check(load().colibri_moe_quantize_q8(_ptr(w), int(dtype), int(E), int(K), int(N), _ptr(q), _ptr(scale),
+                                          _stream(stream)), "colibri_moe_quantize_q8")
+
+
+def expert_ffn_q8(shape: Shape, x_rows, sorted_assign, offsets, q1, s1, q2, s2, y_sorted, ws, ws_bytes: int,
+                  q3=None, s3=None, b1=None, b2=None, stream=None):
+    s = shape.c()
+    e = _experts_q8(q1, s1, q2, s2, q3, s3, b1, b2)
+    _check(load().colibri_moe_expert_ffn_q8(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
+                                            ctypes.byref(e), _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
+           "colibri_moe_expert_ffn_q8")
+
+
+def layer_forward_q8(shape: Shape, x, w_r, b_r, q1, s1, q2, s2, out, ws, ws_bytes: int, q3=None, s3=None, b1=None,
+                     b2=None, topk_idx=None, topk_gate=None, counts=None, stream=None):
+    s = shape.c()
+    e = _experts_q8(q1, s1, q2, s2, q3, s3, b1, b2)
+    _check(load().colibri_moe_layer_forward_q8(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
+                                               _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
+                                               ws_bytes, _stream(stream)), "colibri_moe_layer_forward_q8")
 
 
 class MoELayer:

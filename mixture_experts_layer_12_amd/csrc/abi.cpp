@@ -55,6 +55,25 @@ int check_experts(const colibri_moe_shape_t *s, const colibri_moe_experts_t *w, 
     return COLIBRI_OK;
 }
 
+// int8 expert weights: decode-size bf16 layers only, codes and scales present
+// for the layers the call reads, no W3 outside SwiGLU and no biases inside it.
+int check_experts_q8(const colibri_moe_shape_t *s, const colibri_moe_experts_q8_t *w) {
+    if (!w) return COLIBRI_ERR_INVALID_ARG;
+    if (s->dtype != COLIBRI_BF16 || s->T > 64) return COLIBRI_ERR_UNSUPPORTED;
+    if (!w->q1 || !w->q2 || !w->s1 || !w->s2) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(w->q1, 16) || !aligned(w->q2, 16) || !aligned(w->s1, 4) || !aligned(w->s2, 4))
+        return COLIBRI_ERR_INVALID_ARG;
+    if (s->act == COLIBRI_ACT_SWIGLU) {
+        if (!w->q3 || !w->s3) return COLIBRI_ERR_INVALID_ARG;
+        if (!aligned(w->q3, 16) || !aligned(w->s3, 4)) return COLIBRI_ERR_INVALID_ARG;
+        if (w->b1 || w->b2) return COLIBRI_ERR_UNSUPPORTED;
+    } else {
+        if (w->q3 || w->s3) return COLIBRI_ERR_UNSUPPORTED;
+        if ((w->b1 && !aligned(w->b1, 2)) || (w->b2 && !aligned(w->b2, 2))) return COLIBRI_ERR_INVALID_ARG;
+    }
+    return COLIBRI_OK;
+}
+
 struct LayerWorkspace {
     size_t idx, gate, counts, offsets, sorted, pos, y, ffn, total;
 };
@@ -81,6 +100,53 @@ LayerWorkspace layer_workspace(const colibri_moe_shape_t *s) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? COLIBRI_OK : COLIBRI_ERR_HIP; }
+
+// Steps 1-5 after the shape and expert checks.  ffn(sorted, offsets, y, ffn_ws,
+// reduce, &partials) runs both FFN layers; with Sd > 1 second-layer K splits
+// the combine adds the splits' partials (with b2) instead of a separate reduce.
+template <class Ffn>
+int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r, void *out,
+                       int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
+                       size_t ws_bytes, hipStream_t stream, const void *b2, int Sd, Ffn ffn) {
+    if (!x || !w_r || !out) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(out, 16) || (b_r && !aligned(b_r, 4)) ||
+        (topk_idx_out && !aligned(topk_idx_out, 4)) || (topk_gate_out && !aligned(topk_gate_out, 4)) ||
+        (expert_counts_out && !aligned(expert_counts_out, 4)))
+        return COLIBRI_ERR_INVALID_ARG;
+    const LayerWorkspace L = layer_workspace(s);
+    if (ws_bytes < L.total) return COLIBRI_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+
+    char *base = static_cast<char *>(ws);
+    int32_t *idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t *>(base + L.idx);
+    float *gate = topk_gate_out ? topk_gate_out : reinterpret_cast<float *>(base + L.gate);
+    int32_t *counts = expert_counts_out ? expert_counts_out : reinterpret_cast<int32_t *>(base + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *sorted = reinterpret_cast<int32_t *>(base + L.sorted);
+    int32_t *pos = reinterpret_cast<int32_t *>(base + L.pos);
+    void *y = base + L.y;
+    void *ffn_ws = base + L.ffn;
+
+    hipError_t e;
+    if (route_dispatch_fusable(*s)) {
+        e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream);
+    } else {
+        e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream);
+        if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
+    }
+    if (e != hipSuccess) return hip_status(e);
+    if (Sd > 1) {
+        const float *part = nullptr;
+        e = ffn(sorted, offsets, nullptr, ffn_ws, false, &part);
+        if (e == hipSuccess)
+            e = launch_combine_partials(*s, part, Sd, pos, idx, gate, s->act == COLIBRI_ACT_SWIGLU ? nullptr : b2,
+                                        out, stream);
+        return hip_status(e);
+    }
+    e = ffn(sorted, offsets, y, ffn_ws, true, nullptr);
+    if (e == hipSuccess) e = launch_combine(*s, y, pos, gate, out, stream);
+    return hip_status(e);
+}
 
 }  // namespace
 
@@ -194,46 +260,60 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
     if (s->T == 0) return COLIBRI_OK;
     st = check_experts(s, w);
     if (st != COLIBRI_OK) return st;
-    if (!x || !w_r || !out) return COLIBRI_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(out, 16) || (b_r && !aligned(b_r, 4)) ||
-        (topk_idx_out && !aligned(topk_idx_out, 4)) || (topk_gate_out && !aligned(topk_gate_out, 4)) ||
-        (expert_counts_out && !aligned(expert_counts_out, 4)))
+    return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes,
+                              stream, w->b2, ffn_down_splits(*s),
+                              [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
+                                  const float **part) {
+                                  return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
+                                                           part);
+                              });
+}
+
+int colibri_moe_layer_forward_q8(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                                 const colibri_moe_experts_q8_t *w, void *out, int32_t *topk_idx_out,
+                                 float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts_q8(s, w);
+    if (st != COLIBRI_OK) return st;
+    return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes,
+                              stream, w->b2, ffn_down_splits(*s, true),
+                              [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
+                                  const float **part) {
+                                  return launch_ffn_layers_q8(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
+                                                              part);
+                              });
+}
+
+int colibri_moe_expert_ffn_q8(const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                              const int32_t *expert_offsets, const colibri_moe_experts_q8_t *w, void *y_sorted,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts_q8(s, w);
+    if (st != COLIBRI_OK) return st;
+    if (!x_rows || !expert_offsets || !y_sorted) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(x_rows, 16) || !aligned(y_sorted, 16) || !aligned(expert_offsets, 4) ||
+        (sorted_assign && !aligned(sorted_assign, 4)))
         return COLIBRI_ERR_INVALID_ARG;
-    const LayerWorkspace L = layer_workspace(s);
-    if (ws_bytes < L.total) return COLIBRI_ERR_WORKSPACE;
+    const size_t need = ffn_workspace_bytes(*s);
+    if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(
+        launch_ffn_layers_q8(*s, x_rows, sorted_assign, expert_offsets, *w, y_sorted, ws, true, stream, nullptr));
+}
 
-    char *base = static_cast<char *>(ws);
-    int32_t *idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t *>(base + L.idx);
-    float *gate = topk_gate_out ? topk_gate_out : reinterpret_cast<float *>(base + L.gate);
-    int32_t *counts = expert_counts_out ? expert_counts_out : reinterpret_cast<int32_t *>(base + L.counts);
-    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
-    int32_t *sorted = reinterpret_cast<int32_t *>(base + L.sorted);
-    int32_t *pos = reinterpret_cast<int32_t *>(base + L.pos);
-    void *y = base + L.y;
-    void *ffn_ws = base + L.ffn;
-
-    hipError_t e;
-    if (route_dispatch_fusable(*s)) {
-        e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream);
-    } else {
-        e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream);
-        if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
-    }
-    if (e != hipSuccess) return hip_status(e);
-    const int Sd = ffn_down_splits(*s);
-    if (Sd > 1) {
-        // the second layer's K is split: the combine adds its partials (with b2) directly
-        const float *part = nullptr;
-        e = launch_ffn_layers(*s, x, sorted, offsets, *w, nullptr, ffn_ws, false, stream, &part);
-        if (e == hipSuccess)
-            e = launch_combine_partials(*s, part, Sd, pos, idx, gate, s->act == COLIBRI_ACT_SWIGLU ? nullptr : w->b2,
-                                        out, stream);
-        return hip_status(e);
-    }
-    e = launch_expert_ffn(*s, x, sorted, offsets, *w, y, ffn_ws, stream);
-    if (e == hipSuccess) e = launch_combine(*s, y, pos, gate, out, stream);
-    return hip_status(e);
+int colibri_moe_quantize_q8(const void *w, colibri_dtype_t dtype, int32_t E, int32_t K, int32_t N, int8_t *q,
+                            float *scale, hipStream_t stream) {
+    if (!w || !q || !scale) return COLIBRI_ERR_INVALID_ARG;
+    if (dtype != COLIBRI_F32 && dtype != COLIBRI_BF16) return COLIBRI_ERR_UNSUPPORTED;
+    if (E < 1 || K < 1 || N < 1 || N % 4) return COLIBRI_ERR_UNSUPPORTED;
+    if ((int64_t)E * K * N > ((int64_t)1 << 40)) return COLIBRI_ERR_UNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(q, 4) || !aligned(scale, 4)) return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_quantize_q8(w, dtype, E, K, N, q, scale, stream));
 }
 
 const char *colibri_moe_status_string(int status) {

@@ -178,8 +178,8 @@ size_t ffn_down_scratch_bytes(const colibri_moe_shape_t &s) {
     return s.dtype == COLIBRI_BF16 ? gemm_scratch_bytes(s, false) : 0;
 }
 
-int ffn_down_splits(const colibri_moe_shape_t &s) {
-    if (ffn_decode_eligible(s)) return decode_plan(s, false).S;
+int ffn_down_splits(const colibri_moe_shape_t &s, bool q8) {
+    if (ffn_decode_eligible(s)) return decode_plan(s, false, q8).S;
     return s.dtype == COLIBRI_BF16 ? gemm_splits(s, false) : 1;
 }
 
@@ -191,7 +191,8 @@ size_t ffn_workspace_bytes(const colibri_moe_shape_t &s) {
 hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                          const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
                          hipStream_t st) {
-    if (ffn_decode_eligible(s)) return launch_decode_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
+    if (ffn_decode_eligible(s))
+        return launch_decode_up(s, x_rows, sorted_assign, offsets, decode_weights(w), H, scratch, st);
     const int A = 2 * s.T;
     const bool gather = sorted_assign != nullptr;
     if (s.dtype == COLIBRI_F32) {
@@ -213,7 +214,7 @@ hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const
 hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
                            const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st,
                            bool reduce) {
-    if (ffn_decode_eligible(s)) return launch_decode_down(s, H, offsets, w, y_sorted, scratch, reduce, st);
+    if (ffn_decode_eligible(s)) return launch_decode_down(s, H, offsets, decode_weights(w), y_sorted, scratch, reduce, st);
     const int A = 2 * s.T;
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
     if (s.dtype == COLIBRI_F32)
@@ -222,15 +223,16 @@ hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const in
     return launch_gemm_down(s, H, offsets, w, y_sorted, scratch, reduce, st);
 }
 
-hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
-                             const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
-                             bool reduce, hipStream_t st, const float **down_partials) {
-    const size_t el = s.dtype == COLIBRI_F32 ? 4 : 2;
+namespace {
+// Both decode-size layers (bf16 or int8 weights).  H first in ws, then the scratch.
+hipError_t decode_layers(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                         const int32_t *offsets, const DecodeWeights &w, void *y_sorted, void *ws, bool reduce,
+                         hipStream_t st, const float **down_partials) {
     char *H = static_cast<char *>(ws);
-    char *scratch = H + align256((size_t)2 * s.T * s.h * el);
-    if (decode_fuse_h(s)) {
+    char *scratch = H + align256((size_t)2 * s.T * s.h * 2);
+    if (decode_fuse_h(s, w.q8)) {
         // the first layer leaves its split partials; the second layer rebuilds H from them
-        char *down_scratch = scratch + align256(decode_plan(s, true).part_bytes);
+        char *down_scratch = scratch + align256(decode_plan(s, true, w.q8).part_bytes);
         if (down_partials) *down_partials = reinterpret_cast<const float *>(down_scratch);
         hipError_t e = launch_decode_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st, false);
         if (e != hipSuccess) return e;
@@ -238,9 +240,33 @@ hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, c
                                   reinterpret_cast<const float *>(scratch));
     }
     if (down_partials) *down_partials = reinterpret_cast<const float *>(scratch);
+    hipError_t e = launch_decode_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
+    if (e != hipSuccess) return e;
+    return launch_decode_down(s, H, offsets, w, y_sorted, scratch, reduce, st);
+}
+}  // namespace
+
+hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                             const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
+                             bool reduce, hipStream_t st, const float **down_partials) {
+    if (ffn_decode_eligible(s))
+        return decode_layers(s, x_rows, sorted_assign, offsets, decode_weights(w), y_sorted, ws, reduce, st,
+                             down_partials);
+    const size_t el = s.dtype == COLIBRI_F32 ? 4 : 2;
+    char *H = static_cast<char *>(ws);
+    char *scratch = H + align256((size_t)2 * s.T * s.h * el);
+    if (down_partials) *down_partials = reinterpret_cast<const float *>(scratch);
     hipError_t e = launch_ffn_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
     if (e != hipSuccess) return e;
     return launch_ffn_down(s, H, offsets, w, y_sorted, scratch, st, reduce);
+}
+
+hipError_t launch_ffn_layers_q8(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                                const int32_t *offsets, const colibri_moe_experts_q8_t &w, void *y_sorted, void *ws,
+                                bool reduce, hipStream_t st, const float **down_partials) {
+    if (!ffn_decode_eligible(s)) return hipErrorInvalidValue;  // the callers check the shape first
+    return decode_layers(s, x_rows, sorted_assign, offsets, decode_weights(w), y_sorted, ws, reduce, st,
+                         down_partials);
 }
 
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,

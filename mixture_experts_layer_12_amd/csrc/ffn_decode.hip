@@ -36,6 +36,8 @@
 #include "ffn_common.h"
 #include "launchers.h"
 
+#include <type_traits>
+
 namespace colibri {
 namespace {
 
@@ -59,6 +61,27 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], bf16x8 (&frag)
             const uint32_t a = r[2 * p][q], b = r[2 * p + 1][q];
             o[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
         }
+        frag[j] = __builtin_bit_cast(bf16x8, o);
+    }
+}
+
+// int8 weights: the 8 x 8 block in rows r[0..7] (r[i] = bytes of columns
+// c..c+7 of k-row i) becomes eight B fragments of exact bf16 values.  A byte
+// is sign-extended and converted exactly to fp32 (one conversion with a byte
+// select), and its bf16 pattern is the fp32 pattern's upper half (|q| < 2^8:
+// no bits are lost); two such halves are packed per 32-bit word.
+__device__ __forceinline__ uint32_t q8_f32_bits(uint32_t w, int b) {
+    return __builtin_bit_cast(uint32_t, (float)(int32_t)(int8_t)(w >> (8 * b)));
+}
+__device__ __forceinline__ void transpose8x8_q8(const u32x2 (&r)[8], bf16x8 (&frag)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        u32x4 o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            // bytes 2, 3 of the even row's fp32 bits, then bytes 2, 3 of the odd row's
+            o[p] = __builtin_amdgcn_perm(q8_f32_bits(r[2 * p + 1][j >> 2], j & 3),
+                                         q8_f32_bits(r[2 * p][j >> 2], j & 3), 0x07060302u);
         frag[j] = __builtin_bit_cast(bf16x8, o);
     }
 }
@@ -87,12 +110,20 @@ __device__ __forceinline__ bool live_expert(const int32_t *__restrict__ offsets,
 // with the first layer's epilogue HEPI (bias hbias) and bf16 rounding, exactly
 // as the split reduce would store them; the slice for the workgroup's rows and
 // K range is staged in LDS (dynamic shared memory) before the weight stream.
-template <int MB, int EPI, bool GATHER, int HEPI>
+//
+// QW: int8 weights (B0, B1 hold int8 codes) with one fp32 scale per output
+// column (Sc0 for B0's columns, Sc1 for B1's): the codes enter the MFMAs as
+// exact bf16 values and each column's sum is multiplied by its scale before
+// the epilogue (or before it is written as a partial).
+template <int MB, int EPI, bool GATHER, int HEPI, bool QW>
 __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
-    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
-    const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NCB, int S,
-    float *__restrict__ part, const float *__restrict__ hpart, int hS, const uint16_t *__restrict__ hbias) {
+    const int32_t *__restrict__ offsets, int E, const void *__restrict__ B0, const void *__restrict__ B1,
+    const float *__restrict__ Sc0, const float *__restrict__ Sc1, const uint16_t *__restrict__ bias,
+    uint16_t *__restrict__ C, int K, int N, int NCB, int S, float *__restrict__ part,
+    const float *__restrict__ hpart, int hS, const uint16_t *__restrict__ hbias) {
+    using WT = std::conditional_t<QW, int8_t, uint16_t>;  // weight element
+    using BRow = std::conditional_t<QW, u32x2, u32x4>;     // 8 weight columns of one k-row
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr bool HFROMP = HEPI >= 0;
     constexpr int WCOLS = DUAL ? 64 : 128;  // output columns per wave
@@ -118,10 +149,17 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
     const int g = lane >> 4;  // k group: k 8g..8g+7 of a 32-deep step
     // this lane's 8 consecutive weight columns and the matrix they come from;
     // out-of-range columns load column block 0 instead (never stored)
-    const uint16_t *Bm = (DUAL && c >= 8) ? B1 : B0;
+    const WT *Bm = static_cast<const WT *>((DUAL && c >= 8) ? B1 : B0);
     const int ccol = n0 + 8 * (DUAL ? (c & 7) : c);
     const bool col_ok = ccol < N;
-    const uint16_t *b_base = Bm + (size_t)e * K * N + (size_t)(8 * g) * N + (col_ok ? ccol : 0);
+    const WT *b_base = Bm + (size_t)e * K * N + (size_t)(8 * g) * N + (col_ok ? ccol : 0);
+    // QW: the scales of this lane's 8 columns (column block 0's for padding lanes)
+    float wscale[8];
+    if constexpr (QW) {
+        const float *sc = ((DUAL && c >= 8) ? Sc1 : Sc0) + (size_t)e * N + (col_ok ? ccol : 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wscale[j] = sc[j];
+    }
 
     // k-steps of this split
     const int ksteps = K / 32;
@@ -199,14 +237,14 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
 
         // one k-step of operands: the lane's 8 x 8 weight block and its A fragments
         struct Stage {
-            u32x4 b[8];
+            BRow b[8];
             u32x4 a[MB];
         };
         auto load_stage = [&](Stage &sg, int step) {
-            const uint16_t *p = b_base + (size_t)step * 32 * N;
+            const WT *p = b_base + (size_t)step * 32 * N;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                sg.b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + (size_t)i * N));
+                sg.b[i] = __builtin_nontemporal_load(reinterpret_cast<const BRow *>(p + (size_t)i * N));
             if constexpr (!HFROMP) {
 #pragma unroll
                 for (int mi = 0; mi < MB; ++mi) sg.a[mi] = *reinterpret_cast<const u32x4 *>(a_src[mi] + step * 32);
@@ -220,7 +258,8 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
         };
         auto mma = [&](const Stage &sg) {
             bf16x8 bfrag[8];
-            transpose8x8(sg.b, bfrag);
+            if constexpr (QW) transpose8x8_q8(sg.b, bfrag);
+            else transpose8x8(sg.b, bfrag);
 #pragma unroll
             for (int mi = 0; mi < MB; ++mi) {
                 const bf16x8 afrag = __builtin_bit_cast(bf16x8, sg.a[mi]);
@@ -230,33 +269,64 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
             }
         };
 
-        // two k-steps in flight: stage 0 holds even steps, stage 1 odd steps.
-        // The steady-state loop issues both prefetches unconditionally; the
-        // scheduling barriers keep each stage's loads together.
-        Stage sg0, sg1;
-        const int nsteps = s_end - s_begin;
-        if (nsteps > 0) load_stage(sg0, s_begin);
-        if (nsteps > 1) load_stage(sg1, s_begin + 1);
-        int st = s_begin;
-        for (; st + 3 < s_end; st += 2) {
-            mma(sg0);
-            load_stage(sg0, st + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(sg1);
-            load_stage(sg1, st + 3);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const int left = s_end - st;  // 0 (no steps), 1, 2 or 3
-        if (left == 3) {
-            mma(sg0);
-            load_stage(sg0, st + 2);
-            mma(sg1);
-            mma(sg0);
-        } else if (left == 2) {
-            mma(sg0);
-            mma(sg1);
-        } else if (left == 1) {
-            mma(sg0);
+        if constexpr (QW) {
+            // int8 weights: a k-step is half the bytes, so four k-steps stay in
+            // flight (the same bytes as two bf16 steps).  Stage i holds the steps
+            // st + i; the steady-state loop issues every prefetch unconditionally.
+            constexpr int NST = 4;
+            Stage sg[NST];
+#pragma unroll
+            for (int i = 0; i < NST; ++i)
+                if (s_begin + i < s_end) load_stage(sg[i], s_begin + i);
+            int st = s_begin;
+            for (; st + 2 * NST <= s_end; st += NST) {
+#pragma unroll
+                for (int i = 0; i < NST; ++i) {
+                    mma(sg[i]);
+                    load_stage(sg[i], st + NST + i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // fewer than 2 NST steps left: the stages hold st .. st + NST - 1 (those below s_end)
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                if (st + i < s_end) {
+                    mma(sg[i]);
+                    if (st + NST + i < s_end) load_stage(sg[i], st + NST + i);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NST; ++i)
+                if (st + NST + i < s_end) mma(sg[i]);
+        } else {
+            // two k-steps in flight: stage 0 holds even steps, stage 1 odd steps.
+            // The steady-state loop issues both prefetches unconditionally; the
+            // scheduling barriers keep each stage's loads together.
+            Stage sg0, sg1;
+            const int nsteps = s_end - s_begin;
+            if (nsteps > 0) load_stage(sg0, s_begin);
+            if (nsteps > 1) load_stage(sg1, s_begin + 1);
+            int st = s_begin;
+            for (; st + 3 < s_end; st += 2) {
+                mma(sg0);
+                load_stage(sg0, st + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                mma(sg1);
+                load_stage(sg1, st + 3);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const int left = s_end - st;  // 0 (no steps), 1, 2 or 3
+            if (left == 3) {
+                mma(sg0);
+                load_stage(sg0, st + 2);
+                mma(sg1);
+                mma(sg0);
+            } else if (left == 2) {
+                mma(sg0);
+                mma(sg1);
+            } else if (left == 1) {
+                mma(sg0);
+            }
         }
 
         // accumulator register r of MFMA j, subtile mi: row mi*16 + 4g + r,
@@ -269,7 +339,7 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
                 float u[8], v[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    u[j] = acc[mi][j][r];
+                    u[j] = QW ? acc[mi][j][r] * wscale[j] : acc[mi][j][r];
                     v[j] = DUAL ? __shfl_xor(u[j], 8) : 0.0f;
                 }
                 if (row >= rows || !col_ok) continue;
@@ -344,7 +414,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 
 bool ffn_decode_eligible(const colibri_moe_shape_t &s) { return s.dtype == COLIBRI_BF16 && s.T <= 64; }
 
-DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up) {
+DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up, bool q8) {
     DecodePlan p;
     const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
     const int K = up ? s.d : s.h;
@@ -355,18 +425,20 @@ DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up) {
     const int ksteps = K / 32;
     // S minimises an estimate of the layer's time.  The kernel runs one wave
     // per SIMD, so 256 workgroups (one per CU) make one round; a wave streams
-    // one k-step per ~1.15 us (two k-steps in flight, measured) plus ~3 k-steps
-    // of start-up and epilogue; the stream cannot beat ~6.5 TB/s; S > 1 adds
-    // the partials' write and read (~5 TB/s) and a ~4 us reduce launch.  A larger
+    // one k-step per ~1.15 us with bf16 weights (two k-steps in flight,
+    // measured; int8 weights: half the bytes, ~0.7 us) plus ~3 k-steps of
+    // start-up and epilogue; the stream cannot beat ~6.5 TB/s; S > 1 adds the
+    // partials' write and read (~5 TB/s) and a ~4 us reduce launch.  A larger
     // S must win by 3% (the estimate is rough; fewer splits mean fewer partials).
     const long wg_per_split = (long)p.slots * ((p.NCB + kDecWaves - 1) / kDecWaves);
     const double cols = (double)N * (dual ? 2 : 1);
-    const double weight_bytes = (double)p.slots * K * cols * 2;
+    const double weight_bytes = (double)p.slots * K * cols * (q8 ? 1 : 2);
+    const double step_us = q8 ? 0.7 : 1.15;
     p.S = 1;
     double best = 1e300;
     for (int S = 1; S <= std::max(1, ksteps / 2); ++S) {
         const double rounds = (double)((wg_per_split * S + 255) / 256);
-        double us = std::max(rounds * ((double)ksteps / S + 3.0) * 1.15, weight_bytes / 6.5e6);
+        double us = std::max(rounds * ((double)ksteps / S + 3.0) * step_us, weight_bytes / 6.5e6);
         if (S > 1) us += 4.0 + 2.0 * S * (2.0 * s.T) * cols * 4 / 5.0e6;
         if (us < best * 0.97) best = us, p.S = S;
     }
@@ -381,32 +453,36 @@ DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up) {
 // of a separate reduce launch) when the first layer is split, the staged H
 // slice fits in 64 KB of LDS, and the partial reads -- repeated once per column
 // group of the second layer -- stay within 5% of the second layer's weights.
-bool decode_fuse_h(const colibri_moe_shape_t &s) {
+bool decode_fuse_h(const colibri_moe_shape_t &s, bool q8) {
     if (!ffn_decode_eligible(s)) return false;
-    const DecodePlan up = decode_plan(s, true), down = decode_plan(s, false);
+    const DecodePlan up = decode_plan(s, true, q8), down = decode_plan(s, false, q8);
     if (up.S <= 1) return false;
     const int ksteps = s.h / 32;
     const size_t klen_max = (size_t)((ksteps + down.S - 1) / down.S) * 32;
     if ((size_t)16 * down.MB * (klen_max * 2 + 16) > 64 * 1024) return false;
     const double reads = (double)((down.NCB + kDecWaves - 1) / kDecWaves) * up.part_bytes;
-    const double down_weights = (double)down.slots * s.h * s.d * 2;
+    const double down_weights = (double)down.slots * s.h * s.d * (q8 ? 1 : 2);
     return reads <= 0.05 * down_weights;
 }
 
 size_t ffn_decode_scratch_bytes(const colibri_moe_shape_t &s) {
-    const size_t up = decode_plan(s, true).part_bytes, down = decode_plan(s, false).part_bytes;
-    return decode_fuse_h(s) ? align256(up) + down : std::max(up, down);
+    size_t need = 0;
+    for (int q8 = 0; q8 < 2; ++q8) {
+        const size_t up = decode_plan(s, true, q8).part_bytes, down = decode_plan(s, false, q8).part_bytes;
+        need = std::max(need, decode_fuse_h(s, q8) ? align256(up) + down : std::max(up, down));
+    }
+    return need;
 }
 
 namespace {
 // HEPI >= 0: A is not read from memory; each workgroup rebuilds its K slice of
 // the rows from the first layer's partials (hpart, hS splits) with activation
-// HEPI and bias hbias, in dynamic LDS.
-template <int EPI, int HEPI = -1>
+// HEPI and bias hbias, in dynamic LDS.  QW: int8 weights with scales Sc0, Sc1.
+template <int EPI, int HEPI, bool QW>
 hipError_t launch_decode_t(const colibri_moe_shape_t &s, const DecodePlan &p, bool gather, const void *Am,
-                           const int32_t *sa, const int32_t *offsets, const void *B0, const void *B1, const void *bias,
-                           void *C, int K, int N, void *scratch, hipStream_t st, const float *hpart = nullptr,
-                           int hS = 0, const void *hbias = nullptr) {
+                           const int32_t *sa, const int32_t *offsets, const void *B0, const void *B1,
+                           const float *Sc0, const float *Sc1, const void *bias, void *C, int K, int N, void *scratch,
+                           hipStream_t st, const float *hpart, int hS, const void *hbias) {
     float *part = static_cast<float *>(scratch);
     const int blocks = p.slots * p.S * ((p.NCB + kDecWaves - 1) / kDecWaves);
     size_t lds = 0;
@@ -415,9 +491,9 @@ hipError_t launch_decode_t(const colibri_moe_shape_t &s, const DecodePlan &p, bo
         lds = (size_t)16 * p.MB * ((size_t)((ksteps + p.S - 1) / p.S) * 32 * 2 + 16);
     }
 #define COLIBRI_DEC_LAUNCH(MBV, G)                                                                              \
-    ffn_decode_kernel<MBV, EPI, G, HEPI><<<blocks, kDecWaves * kWave, lds, st>>>(                              \
-        (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,                \
-        (const uint16_t *)bias, (uint16_t *)C, K, N, p.NCB, p.S, part, hpart, hS, (const uint16_t *)hbias)
+    ffn_decode_kernel<MBV, EPI, G, HEPI, QW><<<blocks, kDecWaves * kWave, lds, st>>>(                          \
+        (const uint16_t *)Am, sa, s.T, offsets, s.E, B0, B1, Sc0, Sc1, (const uint16_t *)bias, (uint16_t *)C, K, N, \
+        p.NCB, p.S, part, hpart, hS, (const uint16_t *)hbias)
     if (p.MB == 1) {
         if (gather) COLIBRI_DEC_LAUNCH(1, true);
         else COLIBRI_DEC_LAUNCH(1, false);
@@ -439,62 +515,73 @@ hipError_t launch_reduce_t(const colibri_moe_shape_t &s, int S, const int32_t *o
     return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool QW>
 hipError_t up_t(const colibri_moe_shape_t &s, const DecodePlan &p, bool gather, const void *x_rows,
-                const int32_t *sa, const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *H,
-                void *scratch, bool reduce, hipStream_t st) {
-    hipError_t err = launch_decode_t<EPI>(s, p, gather, x_rows, sa, offsets, B0, B1, bias, H, s.d, s.h, scratch, st);
+                const int32_t *sa, const int32_t *offsets, const DecodeWeights &w, const void *B1, const float *S1,
+                const void *bias, void *H, void *scratch, bool reduce, hipStream_t st) {
+    hipError_t err = launch_decode_t<EPI, -1, QW>(s, p, gather, x_rows, sa, offsets, w.w1, B1, w.s1, S1, bias, H, s.d,
+                                                  s.h, scratch, st, nullptr, 0, nullptr);
     if (err == hipSuccess && p.S > 1 && reduce) err = launch_reduce_t<EPI>(s, p.S, offsets, bias, H, s.h, scratch, st);
     return err;
 }
 
-template <int HEPI>
+template <bool QW>
+hipError_t up_q(const colibri_moe_shape_t &s, const DecodePlan &p, bool gather, const void *x_rows,
+                const int32_t *sa, const int32_t *offsets, const DecodeWeights &w, void *H, void *scratch,
+                bool reduce, hipStream_t st) {
+    switch (s.act) {
+        case COLIBRI_ACT_RELU:
+            return up_t<EPI_ACT_RELU, QW>(s, p, gather, x_rows, sa, offsets, w, nullptr, nullptr, w.b1, H, scratch,
+                                          reduce, st);
+        case COLIBRI_ACT_GELU:
+            return up_t<EPI_ACT_GELU, QW>(s, p, gather, x_rows, sa, offsets, w, nullptr, nullptr, w.b1, H, scratch,
+                                          reduce, st);
+        default:
+            return up_t<EPI_SWIGLU, QW>(s, p, gather, x_rows, sa, offsets, w, w.w3, w.s3, nullptr, H, scratch,
+                                        reduce, st);
+    }
+}
+
+template <int HEPI, bool QW>
 hipError_t down_t(const colibri_moe_shape_t &s, const DecodePlan &p, const void *H, const int32_t *offsets,
-                  const void *w2, const void *b2, void *y, void *scratch, hipStream_t st, const float *hpart, int hS,
-                  const void *hbias) {
-    return launch_decode_t<EPI_BIAS_ONLY, HEPI>(s, p, false, H, nullptr, offsets, w2, nullptr, b2, y, s.h, s.d,
-                                                scratch, st, hpart, hS, hbias);
+                  const DecodeWeights &w, const void *b2, void *y, void *scratch, hipStream_t st, const float *hpart,
+                  int hS, const void *hbias) {
+    return launch_decode_t<EPI_BIAS_ONLY, HEPI, QW>(s, p, false, H, nullptr, offsets, w.w2, nullptr, w.s2, nullptr,
+                                                     b2, y, s.h, s.d, scratch, st, hpart, hS, hbias);
+}
+
+template <bool QW>
+hipError_t down_q(const colibri_moe_shape_t &s, const DecodePlan &p, const void *H, const int32_t *offsets,
+                  const DecodeWeights &w, const void *b2, void *y, void *scratch, hipStream_t st,
+                  const float *h_partials) {
+    if (h_partials == nullptr) return down_t<-1, QW>(s, p, H, offsets, w, b2, y, scratch, st, nullptr, 0, nullptr);
+    const int hS = decode_plan(s, true, QW).S;
+    switch (s.act) {
+        case COLIBRI_ACT_RELU:
+            return down_t<EPI_ACT_RELU, QW>(s, p, H, offsets, w, b2, y, scratch, st, h_partials, hS, w.b1);
+        case COLIBRI_ACT_GELU:
+            return down_t<EPI_ACT_GELU, QW>(s, p, H, offsets, w, b2, y, scratch, st, h_partials, hS, w.b1);
+        default: return down_t<EPI_SWIGLU, QW>(s, p, H, offsets, w, b2, y, scratch, st, h_partials, hS, nullptr);
+    }
 }
 }  // namespace
 
 hipError_t launch_decode_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
-                            const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
-                            hipStream_t st, bool reduce) {
-    const DecodePlan p = decode_plan(s, true);
+                            const int32_t *offsets, const DecodeWeights &w, void *H, void *scratch, hipStream_t st,
+                            bool reduce) {
+    const DecodePlan p = decode_plan(s, true, w.q8);
     const bool gather = sorted_assign != nullptr;
-    switch (s.act) {
-        case COLIBRI_ACT_RELU:
-            return up_t<EPI_ACT_RELU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, scratch,
-                                      reduce, st);
-        case COLIBRI_ACT_GELU:
-            return up_t<EPI_ACT_GELU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, nullptr, w.b1, H, scratch,
-                                      reduce, st);
-        default:
-            return up_t<EPI_SWIGLU>(s, p, gather, x_rows, sorted_assign, offsets, w.w1, w.w3, nullptr, H, scratch,
-                                    reduce, st);
-    }
+    return w.q8 ? up_q<true>(s, p, gather, x_rows, sorted_assign, offsets, w, H, scratch, reduce, st)
+                : up_q<false>(s, p, gather, x_rows, sorted_assign, offsets, w, H, scratch, reduce, st);
 }
 
 hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                              const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st,
+                              const DecodeWeights &w, void *y, void *scratch, bool reduce, hipStream_t st,
                               const float *h_partials) {
-    const DecodePlan p = decode_plan(s, false);
+    const DecodePlan p = decode_plan(s, false, w.q8);
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
-    hipError_t err;
-    if (h_partials == nullptr) {
-        err = down_t<-1>(s, p, H, offsets, w.w2, b2, y, scratch, st, nullptr, 0, nullptr);
-    } else {
-        const int hS = decode_plan(s, true).S;
-        switch (s.act) {
-            case COLIBRI_ACT_RELU:
-                err = down_t<EPI_ACT_RELU>(s, p, H, offsets, w.w2, b2, y, scratch, st, h_partials, hS, w.b1);
-                break;
-            case COLIBRI_ACT_GELU:
-                err = down_t<EPI_ACT_GELU>(s, p, H, offsets, w.w2, b2, y, scratch, st, h_partials, hS, w.b1);
-                break;
-            default: err = down_t<EPI_SWIGLU>(s, p, H, offsets, w.w2, b2, y, scratch, st, h_partials, hS, nullptr);
-        }
-    }
+    hipError_t err = w.q8 ? down_q<true>(s, p, H, offsets, w, b2, y, scratch, st, h_partials)
+                          : down_q<false>(s, p, H, offsets, w, b2, y, scratch, st, h_partials);
     if (err == hipSuccess && p.S > 1 && reduce)
         err = launch_reduce_t<EPI_BIAS_ONLY>(s, p.S, offsets, b2, y, s.d, scratch, st);
     return err;

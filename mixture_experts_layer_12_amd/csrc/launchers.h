@@ -51,21 +51,37 @@ struct DecodePlan {
     size_t part_bytes;  // fp32 partial-sum scratch when S > 1
 };
 bool ffn_decode_eligible(const colibri_moe_shape_t &s);
-DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up);
+// q8: int8 weights (half the bytes per k-step)
+DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up, bool q8 = false);
+// scratch for any decode layout of this shape (bf16 or int8 weights, fused or not)
 size_t ffn_decode_scratch_bytes(const colibri_moe_shape_t &s);
+// The weights of the decode kernels: bf16 (q8 = false, scales null) or int8
+// codes with one fp32 scale per output column.
+struct DecodeWeights {
+    const void *w1, *w3, *w2;
+    const float *s1, *s3, *s2;
+    const void *b1, *b2;
+    bool q8;
+};
+inline DecodeWeights decode_weights(const colibri_moe_experts_t &w) {
+    return {w.w1, w.w3, w.w2, nullptr, nullptr, nullptr, w.b1, w.b2, false};
+}
+inline DecodeWeights decode_weights(const colibri_moe_experts_q8_t &w) {
+    return {w.q1, w.q3, w.q2, w.s1, w.s3, w.s2, w.b1, w.b2, true};
+}
 // reduce = false leaves the first layer's split partials in scratch (for decode_fuse_h)
 hipError_t launch_decode_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
-                            const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
+                            const int32_t *offsets, const DecodeWeights &w, void *H, void *scratch,
                             hipStream_t st, bool reduce = true);
 // reduce = false leaves the split partials in scratch for launch_combine_partials.
 // h_partials != nullptr: H is not read; each workgroup rebuilds its slice from
 // the first layer's split partials (decode_fuse_h).
 hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                              const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st,
+                              const DecodeWeights &w, void *y, void *scratch, bool reduce, hipStream_t st,
                               const float *h_partials = nullptr);
 // Decode sizes whose second layer rebuilds H from the first layer's partials;
 // the scratch then holds the first layer's partials, then (256-aligned) the second's.
-bool decode_fuse_h(const colibri_moe_shape_t &s);
+bool decode_fuse_h(const colibri_moe_shape_t &s, bool q8 = false);
 // combine straight from the second layer's S split partials (adds them, b2, rounds Y, then gates)
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
@@ -92,14 +108,22 @@ hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const i
 // (bias + activation, SwiGLU, or bias only), storing the dtype result.
 hipError_t launch_split_reduce(const colibri_moe_shape_t &s, bool up, int S, const int32_t *offsets,
                                const colibri_moe_experts_t &w, void *C, const float *part, hipStream_t st);
-// K splits of the second layer as launch_ffn_down runs it (1: no partials).
-int ffn_down_splits(const colibri_moe_shape_t &s);
+// K splits of the second layer as launch_ffn_down runs it (1: no partials);
+// q8: as the int8-weight decode layers run it.
+int ffn_down_splits(const colibri_moe_shape_t &s, bool q8 = false);
 // Both layers with H and the scratch carved from ws (H first, then the scratch).
 // reduce = false (when ffn_down_splits(s) > 1) leaves the second layer's split
 // partials in the scratch, at *down_partials.
 hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
                              bool reduce, hipStream_t st, const float **down_partials);
+// launch_ffn_layers with int8 expert weights: decode sizes only (bf16, T <= 64).
+hipError_t launch_ffn_layers_q8(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                                const int32_t *offsets, const colibri_moe_experts_q8_t &w, void *y_sorted, void *ws,
+                                bool reduce, hipStream_t st, const float **down_partials);
+// Per-column int8 quantization of a weight tensor [E][K][N] (colibri_moe_quantize_q8).
+hipError_t launch_quantize_q8(const void *w, colibri_dtype_t dtype, int E, int K, int N, int8_t *q, float *scale,
+                              hipStream_t st);
 // H then Y (launch_ffn_layers with the second layer reduced).
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,

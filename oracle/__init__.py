@@ -59,8 +59,11 @@ def load_library(path: Optional[str] = None):
     lib.oracle_combine.argtypes = [i, i, i, _P, _P, _P, _P]
     lib.oracle_layer.argtypes = [i, i, i, i, i, i, i] + [_P] * 8 + [_P] * 9
     lib.oracle_round.argtypes = [_P, _P, z, i]
+    lib.oracle_quantize_q8.argtypes = [_P, i, i, i, i, _P, _P]
+    lib.oracle_ffn_rows_q8.argtypes = [i, i, i, i, i, _P, i, _P, _P] + [_P] * 8 + [_P]
     for f in ("oracle_set_threads", "oracle_logits", "oracle_top2", "oracle_gates", "oracle_dispatch",
-              "oracle_ffn_rows", "oracle_combine", "oracle_layer", "oracle_round"):
+              "oracle_ffn_rows", "oracle_combine", "oracle_layer", "oracle_round", "oracle_quantize_q8",
+              "oracle_ffn_rows_q8"):
         getattr(lib, f).restype = None
     if path is None:
         _lib = lib
@@ -206,6 +209,58 @@ def layer_tokens(x, w_r, w1, w2, act: str, tokens, b_r=None, w3=None, b1=None, b
     y = ffn_rows(xs, rt, re, w1, w2, act, w3=w3, b1=b1, b2=b2, mirror=mirror, lib=lib)
     ap = np.arange(2 * n, dtype=np.int32)
     out = combine(y, ap, g, _dt(xs), lib=lib)
+    return {"logits": lg, "idx": idx, "gate": g, "y": y.reshape(n, 2, -1), "out": out}
+
+
+# ------------------------------------------------------------------ int8 expert weights
+def quantize_q8(w, lib=None):
+    """Per-column int8 codes and fp32 scales of w [E, K, N] (float32 or bf16 bits)."""
+    lib = lib or load_library()
+    w = _c(w)
+    E, K, N = w.shape
+    q = np.empty((E, K, N), np.int8)
+    s = np.empty((E, N), np.float32)
+    lib.oracle_quantize_q8(_ptr(w), _dt(w), E, K, N, _ptr(q), _ptr(s))
+    return q, s
+
+
+def ffn_rows_q8(x, rows_token, rows_expert, q1, s1, q2, s2, act: str, q3=None, s3=None, b1=None, b2=None,
+                mirror=True, lib=None) -> np.ndarray:
+    """ffn_rows with int8 weights q* and per-column scales s* (dequantized as s * q)."""
+    lib = lib or load_library()
+    x, b1, b2 = _c(x), _c(b1), _c(b2)
+    q1, q2, q3 = _c(q1, np.int8), _c(q2, np.int8), _c(q3, np.int8)
+    s1, s2, s3 = _c(s1, np.float32), _c(s2, np.float32), _c(s3, np.float32)
+    dt = _dt(x)
+    for a in (b1, b2):
+        if a is not None and _dt(a) != dt:
+            raise TypeError("x and the biases share one dtype")
+    E, d, h = q1.shape
+    rt = _c(rows_token, np.int32)
+    re = _c(rows_expert, np.int32)
+    n = rt.shape[0]
+    if act == "swiglu" and (q3 is None or s3 is None):
+        raise ValueError("swiglu needs q3 and s3")
+    y = np.empty((n, d), np.float64)
+    lib.oracle_ffn_rows_q8(d, h, dt, ACT[act], int(bool(mirror)), _ptr(x), n, _ptr(rt), _ptr(re), _ptr(q1),
+                           _ptr(s1), _ptr(q3), _ptr(s3), _ptr(q2), _ptr(s2), _ptr(b1), _ptr(b2), _ptr(y))
+    return y
+
+
+def layer_tokens_q8(x, w_r, q1, s1, q2, s2, act: str, tokens, b_r=None, q3=None, s3=None, b1=None, b2=None,
+                    mirror=True, idx_override=None, lib=None) -> Dict[str, np.ndarray]:
+    """layer_tokens with int8 expert weights."""
+    lib = lib or load_library()
+    tokens = np.asarray(tokens, np.int64)
+    xs = _c(np.asarray(x)[tokens])
+    lg = logits(xs, w_r, b_r, lib=lib)
+    idx = top2(lg, lib=lib) if idx_override is None else _c(idx_override, np.int32)
+    g = gates(lg, idx, lib=lib)
+    n = len(tokens)
+    rt = np.repeat(np.arange(n, dtype=np.int32), 2)
+    y = ffn_rows_q8(xs, rt, idx.reshape(-1), q1, s1, q2, s2, act, q3=q3, s3=s3, b1=b1, b2=b2, mirror=mirror,
+                    lib=lib)
+    out = combine(y, np.arange(2 * n, dtype=np.int32), g, _dt(xs), lib=lib)
     return {"logits": lg, "idx": idx, "gate": g, "y": y.reshape(n, 2, -1), "out": out}
 
 

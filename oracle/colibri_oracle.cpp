@@ -85,6 +85,37 @@ double act_relu(double z) { return z > 0.0 ? z : 0.0; }
 double act_gelu(double z) { return 0.5 * z * (1.0 + std::erf(z / std::sqrt(2.0))); }
 double act_silu(double z) { return z / (1.0 + std::exp(-z)); }
 
+// Step 5, shared by the bf16/fp32 and the int8-weight FFN: the hidden row
+// from the first layer's sums u (and v for SwiGLU), and the output row from H
+// and the second layer's weights w2at(j, c).
+void hidden_row(int h, int act, int mirror, int dt, int e, const std::vector<double> &u,
+                const std::vector<double> &v, const void *b1, std::vector<double> &H) {
+    for (int j = 0; j < h; ++j) {
+        double hv;
+        if (act == ACT_SWIGLU) {
+            hv = act_silu(u[j]) * v[j];
+        } else {
+            double z = u[j] + (b1 ? load(b1, dt, (size_t)e * h + j) : 0.0);
+            hv = (act == ACT_RELU) ? act_relu(z) : act_gelu(z);
+        }
+        H[j] = mirror ? round_to_dtype(hv, dt) : hv;
+    }
+}
+
+template <class W2At>
+void output_row(int h, int d, int act, int mirror, int dt, int e, const std::vector<double> &H, W2At w2at,
+                const void *b2, std::vector<double> &y, double *yo) {
+    std::fill(y.begin(), y.end(), 0.0);
+    for (int j = 0; j < h; ++j) {
+        const double hj = H[j];
+        for (int c = 0; c < d; ++c) y[c] += hj * w2at(j, c);
+    }
+    for (int c = 0; c < d; ++c) {
+        double yv = y[c] + ((act != ACT_SWIGLU && b2) ? load(b2, dt, (size_t)e * d + c) : 0.0);
+        yo[c] = mirror ? round_to_dtype(yv, dt) : yv;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,27 +246,10 @@ void oracle_ffn_rows(int d, int h, int dt, int act, int mirror, const void *x, i
                 if (act == ACT_SWIGLU)
                     for (int j = 0; j < h; ++j) v[j] += xk * load(w3, dt, wdh + (size_t)k * h + j);
             }
-            for (int j = 0; j < h; ++j) {
-                double hv;
-                if (act == ACT_SWIGLU) {
-                    hv = act_silu(u[j]) * v[j];
-                } else {
-                    double z = u[j] + (b1 ? load(b1, dt, (size_t)e * h + j) : 0.0);
-                    hv = (act == ACT_RELU) ? act_relu(z) : act_gelu(z);
-                }
-                H[j] = mirror ? round_to_dtype(hv, dt) : hv;
-            }
-            std::fill(y.begin(), y.end(), 0.0);
+            hidden_row(h, act, mirror, dt, e, u, v, b1, H);
             const size_t whd = (size_t)e * h * d;
-            for (int j = 0; j < h; ++j) {
-                const double hj = H[j];
-                for (int c = 0; c < d; ++c) y[c] += hj * load(w2, dt, whd + (size_t)j * d + c);
-            }
-            double *yo = y_out + (size_t)r * d;
-            for (int c = 0; c < d; ++c) {
-                double yv = y[c] + ((act != ACT_SWIGLU && b2) ? load(b2, dt, (size_t)e * d + c) : 0.0);
-                yo[c] = mirror ? round_to_dtype(yv, dt) : yv;
-            }
+            output_row(h, d, act, mirror, dt, e, H, [&](int j, int c) { return load(w2, dt, whd + (size_t)j * d + c); },
+                       b2, y, y_out + (size_t)r * d);
         }
     }
 }
@@ -271,6 +285,79 @@ void oracle_layer(int T, int d, int h, int E, int dt, int act, int mirror, const
     }
     oracle_ffn_rows(d, h, dt, act, mirror, x, 2 * T, rt.data(), re.data(), w1, w3, w2, b1, b2, y_sorted);
     oracle_combine(T, d, dt, y_sorted, assign_pos, gate, out);
+}
+
+// ---- int8 expert weights ([zskr] section 5.3: the expert weights are quantized
+// to INT8 per channel, with their scales stored beside them).  A channel is an
+// output column n of one expert; the scale is symmetric.
+
+// Quantization of w [E][K][N] (dt), in fp32 as defined:
+//   amax = max_k |w[e][k][n]|;  s[e][n] = amax / 127, or 1 when amax = 0;
+//   q[e][k][n] = w / s rounded to nearest, ties to even, clamped to [-127, 127].
+void oracle_quantize_q8(const void *w, int dt, int E, int K, int N, int8_t *q, float *scale) {
+    // Work is split over (expert, block of 256 columns); inside a block the
+    // rows are walked in order so that every read is contiguous.
+    constexpr int NB = 256;
+    const int nblk = (N + NB - 1) / NB;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long eb = 0; eb < (long)E * nblk; ++eb) {
+        const int e = (int)(eb / nblk), n0 = (int)(eb % nblk) * NB, n1 = std::min(N, n0 + NB);
+        const size_t base = (size_t)e * K * N;
+        float amax[NB], sc[NB];
+        for (int n = n0; n < n1; ++n) amax[n - n0] = 0.0f;
+        for (int k = 0; k < K; ++k)
+            for (int n = n0; n < n1; ++n) {
+                const float a = std::fabs((float)load(w, dt, base + (size_t)k * N + n));
+                if (a > amax[n - n0]) amax[n - n0] = a;
+            }
+        for (int n = n0; n < n1; ++n) {
+            sc[n - n0] = amax[n - n0] > 0.0f ? amax[n - n0] / 127.0f : 1.0f;
+            scale[(size_t)e * N + n] = sc[n - n0];
+        }
+        for (int k = 0; k < K; ++k)
+            for (int n = n0; n < n1; ++n) {
+                const size_t i = base + (size_t)k * N + n;
+                float r = std::nearbyint((float)load(w, dt, i) / sc[n - n0]);  // default mode: ties to even
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                q[i] = (int8_t)r;
+            }
+    }
+}
+
+// Step 5 with int8 expert weights: the same two-layer FFN on the dequantized
+// weights W[k][n] = s[n] * q[k][n], each formed exactly in double.
+//   q1, q3 [E][d][h] with s1, s3 [E][h];  q2 [E][h][d] with s2 [E][d];
+//   x, b1, b2 and the rounding of H and y in the storage type dt.
+void oracle_ffn_rows_q8(int d, int h, int dt, int act, int mirror, const void *x, int nrows,
+                        const int32_t *row_token, const int32_t *row_expert, const int8_t *q1, const float *s1,
+                        const int8_t *q3, const float *s3, const int8_t *q2, const float *s2, const void *b1,
+                        const void *b2, double *y_out) {
+#pragma omp parallel
+    {
+        std::vector<double> xr(d), u(h), v(h), H(h), y(d);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; ++r) {
+            const int t = row_token[r], e = row_expert[r];
+            const size_t wdh = (size_t)e * d * h;
+            for (int k = 0; k < d; ++k) xr[k] = load(x, dt, (size_t)t * d + k);
+            std::fill(u.begin(), u.end(), 0.0);
+            std::fill(v.begin(), v.end(), 0.0);
+            for (int k = 0; k < d; ++k) {
+                const double xk = xr[k];
+                for (int j = 0; j < h; ++j)
+                    u[j] += xk * ((double)s1[(size_t)e * h + j] * (double)q1[wdh + (size_t)k * h + j]);
+                if (act == ACT_SWIGLU)
+                    for (int j = 0; j < h; ++j)
+                        v[j] += xk * ((double)s3[(size_t)e * h + j] * (double)q3[wdh + (size_t)k * h + j]);
+            }
+            hidden_row(h, act, mirror, dt, e, u, v, b1, H);
+            const size_t whd = (size_t)e * h * d;
+            output_row(h, d, act, mirror, dt, e, H,
+                       [&](int j, int c) { return (double)s2[(size_t)e * d + c] * (double)q2[whd + (size_t)j * d + c]; },
+                       b2, y, y_out + (size_t)r * d);
+        }
+    }
 }
 
 // Round doubles to a storage type (for comparing against stored GPU values).

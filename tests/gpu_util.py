@@ -141,6 +141,24 @@ def _device_experts(wkey: str):
     return {k: dev(v) for k, v in _host_experts(wkey).items()}
 
 
+@functools.lru_cache(maxsize=1)
+def _host_experts_q8(wkey: str):
+    """int8 codes and per-column scales of the seeded weights, from the oracle's quantizer."""
+    w = _host_experts(wkey)
+    out = {"b1": w["b1"], "b2": w["b2"]}
+    for name, qn, sn in (("w1", "q1", "s1"), ("w3", "q3", "s3"), ("w2", "q2", "s2")):
+        if w[name] is None:
+            out[qn] = out[sn] = None
+        else:
+            out[qn], out[sn] = oracle.quantize_q8(w[name])
+    return out
+
+
+@functools.lru_cache(maxsize=1)
+def _device_experts_q8(wkey: str):
+    return {k: dev(v) for k, v in _host_experts_q8(wkey).items()}
+
+
 class Layer:
     """Seeded inputs of one config at T tokens; expert weights load on first use."""
 
@@ -171,6 +189,25 @@ class Layer:
         w = self.hw
         return oracle.layer_tokens(self.x, w["w_r"], w["w1"], w["w2"], self.cfg.act, tokens, b_r=w["b_r"],
                                    w3=w["w3"], b1=w["b1"], b2=w["b2"], mirror=True, idx_override=idx_override)
+
+
+    @property
+    def hq8(self) -> Dict:
+        w = dict(_host_experts_q8(weight_key(self.key)))
+        w.update(host_router(self.key))
+        return w
+
+    @property
+    def dq8(self) -> Dict:
+        w = dict(_device_experts_q8(weight_key(self.key)))
+        w.update(device_router(self.key))
+        return w
+
+    def oracle_tokens_q8(self, tokens, idx_override=None):
+        w = self.hq8
+        return oracle.layer_tokens_q8(self.x, w["w_r"], w["q1"], w["s1"], w["q2"], w["s2"], self.cfg.act, tokens,
+                                      b_r=w["b_r"], q3=w["q3"], s3=w["s3"], b1=w["b1"], b2=w["b2"], mirror=True,
+                                      idx_override=idx_override)
 
 
 def seeded_layer(key: str, T: int) -> Layer:

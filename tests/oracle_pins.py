@@ -407,4 +407,72 @@ def pin_layer_zero_padding(lib):
         assert np.all(rp["out"][:, 32:] == 0.0)
 
 
+# ----------------------------------------------------------------- int8 expert weights
+def pin_q8_quantize_hand_example(lib):
+    kv = _read_kv(os.path.join(GOLDEN, "q8_quantize_hand_example.txt"))
+    w = np.stack([np.array(kv[f"col{c}_w"], np.float32) for c in range(4)], axis=1)[None]  # [1, 8, 4]
+    for dt_w in (w, gen.f32_to_bf16_bits(w)):  # the values are bf16-exact too
+        q, sc = oracle.quantize_q8(dt_w, lib=lib)
+        for c in range(4):
+            assert q[0, :, c].tolist() == [int(v) for v in kv[f"col{c}_q"]], (c, q[0, :, c])
+            assert sc[0, c] == np.float32(kv[f"col{c}_s"][0]), (c, sc[0, c])
+
+
+def pin_q8_ffn_hand_example(lib):
+    kv = _read_kv(os.path.join(GOLDEN, "q8_ffn_hand_example.txt"))
+    f = lambda k, s, t=np.float32: np.array(kv[k], t).reshape(s)
+    x, b1, b2 = f("x", (1, 2)), f("b1", (1, 2)), f("b2", (1, 2))
+    q1, q2 = f("q1", (1, 2, 2), np.int8), f("q2", (1, 2, 2), np.int8)
+    s1, s2 = f("s1", (1, 2)), f("s2", (1, 2))
+    for mirror in (False, True):
+        y = oracle.ffn_rows_q8(x, [0], [0], q1, s1, q2, s2, "relu", b1=b1, b2=b2, mirror=mirror, lib=lib)
+        assert y[0].tolist() == kv["y"], y
+
+
+def pin_q8_ffn_unit_scales(lib):
+    """With every scale 1 the int8 path is the plain FFN on the integer weights."""
+    rng = np.random.default_rng(21)
+    d, h, E = 32, 48, 3
+    x = _rand_f32(rng, (5, d))
+    rows_t = np.array([0, 1, 2, 3, 4, 0], np.int32)
+    rows_e = np.array([0, 2, 1, 1, 0, 2], np.int32)
+    for act in ("relu", "gelu", "swiglu"):
+        q1, q3 = rng.integers(-127, 128, (E, d, h)), rng.integers(-127, 128, (E, d, h))
+        q2 = rng.integers(-127, 128, (E, h, d))
+        ones_h, ones_d = np.ones((E, h), np.float32), np.ones((E, d), np.float32)
+        b1 = _rand_f32(rng, (E, h)) if act != "swiglu" else None
+        b2 = _rand_f32(rng, (E, d)) if act != "swiglu" else None
+        sw = act == "swiglu"
+        y = oracle.ffn_rows_q8(x, rows_t, rows_e, q1, ones_h, q2, ones_d, act, q3=q3 if sw else None,
+                               s3=ones_h if sw else None, b1=b1, b2=b2, mirror=False, lib=lib)
+        ref = oracle.ffn_rows(x, rows_t, rows_e, q1.astype(np.float32), q2.astype(np.float32), act,
+                              w3=q3.astype(np.float32) if sw else None, b1=b1, b2=b2, mirror=False, lib=lib)
+        assert np.array_equal(y, ref), act
+
+
+def pin_q8_ffn_library(lib):
+    """Random codes and scales against numpy matmuls on s[None, :] * q (fp64)."""
+    rng = np.random.default_rng(22)
+    d, h, E = 40, 56, 2
+    x = _rand_f32(rng, (3, d))
+    for act in ("relu", "gelu", "swiglu"):
+        q1, q3, q2 = (rng.integers(-127, 128, s).astype(np.int8) for s in ((E, d, h), (E, d, h), (E, h, d)))
+        s1, s3 = (rng.uniform(0.5, 2.0, (E, h)).astype(np.float32) / 127 for _ in range(2))
+        s2 = rng.uniform(0.5, 2.0, (E, d)).astype(np.float32) / 127
+        b1 = _rand_f32(rng, (E, h), 0.1) if act != "swiglu" else None
+        b2 = _rand_f32(rng, (E, d), 0.1) if act != "swiglu" else None
+        sw = act == "swiglu"
+        rows_t = np.array([0, 1, 2, 1], np.int32)
+        rows_e = np.array([1, 0, 1, 1], np.int32)
+        y = oracle.ffn_rows_q8(x, rows_t, rows_e, q1, s1, q2, s2, act, q3=q3 if sw else None,
+                               s3=s3 if sw else None, b1=b1, b2=b2, mirror=False, lib=lib)
+        deq = lambda q, s: q.astype(np.float64) * s.astype(np.float64)[None, :]
+        for r, (t, e) in enumerate(zip(rows_t, rows_e)):
+            ref = _np_ffn(x[t].astype(np.float64), deq(q1[e], s1[e]),
+                          None if b1 is None else b1[e].astype(np.float64), deq(q2[e], s2[e]),
+                          None if b2 is None else b2[e].astype(np.float64), act,
+                          deq(q3[e], s3[e]) if sw else None)
+            np.testing.assert_allclose(y[r], ref, rtol=1e-11, atol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

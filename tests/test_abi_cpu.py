@@ -168,3 +168,67 @@ def test_ffn_layer_entry_point_checks(lib):
     e = moe._Experts(fake(10), fake(11), None, None, None)
     assert lib.colibri_moe_expert_ffn_up(ctypes.byref(s), fake(0), fake(1), fake(2), ctypes.byref(e), fake(3) + 4,
                                          None, 0, None) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ int8 expert weights
+def q8_experts(**kw):
+    base = dict(q1=fake(10), q3=fake(11), q2=fake(12), s1=fake(13), s3=fake(14), s2=fake(15), b1=None, b2=None)
+    base.update(kw)
+    return moe._ExpertsQ8(base["q1"], base["q3"], base["q2"], base["s1"], base["s3"], base["s2"], base["b1"],
+                          base["b2"])
+
+
+def ffn_q8_call(lib, s, e, ws_bytes=1 << 40, ws=fake(9), y=fake(8)):
+    return lib.colibri_moe_expert_ffn_q8(ctypes.byref(s), fake(0), fake(1), fake(2), ctypes.byref(e), y, ws,
+                                         ws_bytes, None)
+
+
+def test_q8_ffn_checks(lib):
+    s = shape_c()
+    e = q8_experts()
+    # decode sizes only: bf16 and T <= 64
+    assert ffn_q8_call(lib, shape_c(T=65), e) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert ffn_q8_call(lib, shape_c(dtype=moe.F32), e) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert ffn_q8_call(lib, s, e, ws_bytes=1024) == moe.COLIBRI_ERR_WORKSPACE
+    # codes and scales of both layers are required; SwiGLU needs q3/s3 and takes no biases
+    for k in ("q1", "q2", "s1", "s2", "q3", "s3"):
+        assert ffn_q8_call(lib, s, q8_experts(**{k: None})) == moe.COLIBRI_ERR_INVALID_ARG, k
+    assert ffn_q8_call(lib, s, q8_experts(b1=fake(16))) == moe.COLIBRI_ERR_UNSUPPORTED
+    # ReLU / GELU take no q3/s3
+    sr = shape_c(act=moe.GELU)
+    assert ffn_q8_call(lib, sr, q8_experts(s3=None)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert ffn_q8_call(lib, sr, q8_experts(q3=None)) == moe.COLIBRI_ERR_UNSUPPORTED
+    # alignment: codes 16 bytes, scales 4 bytes
+    assert ffn_q8_call(lib, s, q8_experts(q1=fake(10) + 8)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert ffn_q8_call(lib, s, q8_experts(s2=fake(15) + 2)) == moe.COLIBRI_ERR_INVALID_ARG
+    # T = 0 is a no-op even with null pointers
+    assert lib.colibri_moe_expert_ffn_q8(ctypes.byref(shape_c(T=0)), None, None, None, None, None, None, 0,
+                                         None) == 0
+
+
+def test_q8_layer_checks(lib):
+    s = shape_c()
+    need = lib.colibri_moe_workspace_size(ctypes.byref(s))
+
+    def call(sh=s, e=q8_experts(), ws_bytes=need, x=fake(0)):
+        return lib.colibri_moe_layer_forward_q8(ctypes.byref(sh), x, fake(1), None, ctypes.byref(e), fake(3), None,
+                                                None, None, fake(20), ws_bytes, None)
+
+    assert call(ws_bytes=need - 1) == moe.COLIBRI_ERR_WORKSPACE
+    assert call(x=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(sh=shape_c(T=100)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert call(e=q8_experts(q2=None)) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+def test_quantize_checks(lib):
+    def call(w=fake(0), dtype=moe.BF16, E=2, K=64, N=128, q=fake(1), sc=fake(2)):
+        return lib.colibri_moe_quantize_q8(w, dtype, E, K, N, q, sc, None)
+
+    assert call(w=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(q=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(sc=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(N=130) == moe.COLIBRI_ERR_UNSUPPORTED  # columns in groups of 4
+    assert call(K=0) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert call(dtype=5) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert call(w=fake(0) + 8) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(sc=fake(2) + 1) == moe.COLIBRI_ERR_INVALID_ARG

@@ -35,6 +35,18 @@ MUTANTS = {
                               "gate[2 * t + 1] * y0[c] + gate[2 * t] * y1[c]"),
     "b2_dropped": ("yv = y[c] + ((act != ACT_SWIGLU && b2) ? load(b2, dt, (size_t)e * d + c) : 0.0);",
                    "yv = y[c];"),
+    "q8_scale_along_k": ("u[j] += xk * ((double)s1[(size_t)e * h + j] * (double)q1[wdh + (size_t)k * h + j]);",
+                         "u[j] += xk * ((double)s1[(size_t)e * h + (k % h)] * (double)q1[wdh + (size_t)k * h + j]);"),
+    "q8_w3_takes_w1_scale": ("v[j] += xk * ((double)s3[(size_t)e * h + j]",
+                             "v[j] += xk * ((double)s1[(size_t)e * h + j]"),
+    "q8_second_scale_dropped": ("return (double)s2[(size_t)e * d + c] * (double)q2[whd + (size_t)j * d + c];",
+                                "return (double)q2[whd + (size_t)j * d + c];"),
+    "q8_ties_away_from_zero": ("float r = std::nearbyint((float)load(w, dt, i) / sc[n - n0]);",
+                               "float r = std::round((float)load(w, dt, i) / sc[n - n0]);"),
+    "q8_zero_column_unguarded": ("sc[n - n0] = amax[n - n0] > 0.0f ? amax[n - n0] / 127.0f : 1.0f;",
+                                 "sc[n - n0] = amax[n - n0] / 127.0f;"),
+    "q8_scale_over_128": ("sc[n - n0] = amax[n - n0] > 0.0f ? amax[n - n0] / 127.0f : 1.0f;",
+                          "sc[n - n0] = amax[n - n0] > 0.0f ? amax[n - n0] / 128.0f : 1.0f;"),
     "rounding_via_fp32": ("double round_to_dtype(double v, int dt) { return round_to_format(v, dt == DT_F32 ? 23 : 7); }",
                           "double round_to_dtype(double v, int dt) { return round_to_format(dt == DT_F32 ? v : (double)(float)v, dt == DT_F32 ? 23 : 7); }"),
 }
