@@ -25,6 +25,13 @@
 //     columns and a lane owns 8 consecutive output columns); the few token
 //     rows (A operand) are read from L2; two k-steps (16 KB per wave) are
 //     always in flight;
+//   * int8 weights (one fp32 scale per output column): with 16-row tiles a
+//     lane loads an 8 (k) x 16 (n) block of codes with eight 16-byte loads
+//     (256 columns per wave, the same 8 KB per k-step as bf16); with 32-row
+//     tiles an 8 x 8 block with 8-byte loads (128 columns, four k-steps in
+//     flight), which keeps the accumulators within the register budget.  The
+//     codes become exact bf16 values in registers and each column's sum is
+//     multiplied by its scale before the epilogue or the partial store;
 //   * with one K split, the epilogue (bias + activation, silu(u) * v, or bias
 //     only) runs on the accumulators and rounds once to bf16;
 //   * when the live experts' column blocks alone cannot fill the chip, the K
@@ -65,24 +72,39 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], bf16x8 (&frag)
     }
 }
 
-// int8 weights: the 8 x 8 block in rows r[0..7] (r[i] = bytes of columns
-// c..c+7 of k-row i) becomes eight B fragments of exact bf16 values.  A byte
+// int8 weights: the 8 x 16 block in rows r[0..7] (r[i] = bytes of columns
+// c..c+15 of k-row i) becomes sixteen B fragments of exact bf16 values.  A byte
 // is sign-extended and converted exactly to fp32 (one conversion with a byte
 // select), and its bf16 pattern is the fp32 pattern's upper half (|q| < 2^8:
 // no bits are lost); two such halves are packed per 32-bit word.
 __device__ __forceinline__ uint32_t q8_f32_bits(uint32_t w, int b) {
     return __builtin_bit_cast(uint32_t, (float)(int32_t)(int8_t)(w >> (8 * b)));
 }
+// The same for an 8 x 8 block (r[i] = bytes of columns c..c+7 of k-row i).
 __device__ __forceinline__ void transpose8x8_q8(const u32x2 (&r)[8], bf16x8 (&frag)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         u32x4 o;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            // bytes 2, 3 of the even row's fp32 bits, then bytes 2, 3 of the odd row's
             o[p] = __builtin_amdgcn_perm(q8_f32_bits(r[2 * p + 1][j >> 2], j & 3),
                                          q8_f32_bits(r[2 * p][j >> 2], j & 3), 0x07060302u);
         frag[j] = __builtin_bit_cast(bf16x8, o);
+    }
+}
+// (H selects columns 8H .. 8H+7: the fragments are built eight at a time.)
+template <int H>
+__device__ __forceinline__ void transpose8x16_q8(const u32x4 (&r)[8], bf16x8 (&frag)[8]) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        const int j = 8 * H + jj;
+        u32x4 o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            // bytes 2, 3 of the even row's fp32 bits, then bytes 2, 3 of the odd row's
+            o[p] = __builtin_amdgcn_perm(q8_f32_bits(r[2 * p + 1][j >> 2], j & 3),
+                                         q8_f32_bits(r[2 * p][j >> 2], j & 3), 0x07060302u);
+        frag[jj] = __builtin_bit_cast(bf16x8, o);
     }
 }
 
@@ -123,10 +145,13 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
     uint16_t *__restrict__ C, int K, int N, int NCB, int S, float *__restrict__ part,
     const float *__restrict__ hpart, int hS, const uint16_t *__restrict__ hbias) {
     using WT = std::conditional_t<QW, int8_t, uint16_t>;  // weight element
-    using BRow = std::conditional_t<QW, u32x2, u32x4>;     // 8 weight columns of one k-row
+    // weight columns per lane: 8 (bf16: one 16-byte run; int8 with 32-row tiles:
+    // one 8-byte run, which keeps the registers within budget) or 16 (int8, 16-row tiles)
+    constexpr int CPL = (QW && MB == 1) ? 16 : 8;
+    using BRow = std::conditional_t<QW && CPL == 8, u32x2, u32x4>;  // one k-row of the lane's columns
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr bool HFROMP = HEPI >= 0;
-    constexpr int WCOLS = DUAL ? 64 : 128;  // output columns per wave
+    constexpr int WCOLS = (DUAL ? 8 : 16) * CPL;  // output columns per wave
     constexpr int ROWS = MB * 16;
     extern __shared__ __attribute__((aligned(16))) uint8_t hlds[];
 
@@ -150,15 +175,15 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
     // this lane's 8 consecutive weight columns and the matrix they come from;
     // out-of-range columns load column block 0 instead (never stored)
     const WT *Bm = static_cast<const WT *>((DUAL && c >= 8) ? B1 : B0);
-    const int ccol = n0 + 8 * (DUAL ? (c & 7) : c);
+    const int ccol = n0 + CPL * (DUAL ? (c & 7) : c);
     const bool col_ok = ccol < N;
     const WT *b_base = Bm + (size_t)e * K * N + (size_t)(8 * g) * N + (col_ok ? ccol : 0);
     // QW: the scales of this lane's 8 columns (column block 0's for padding lanes)
-    float wscale[8];
+    float wscale[CPL];
     if constexpr (QW) {
         const float *sc = ((DUAL && c >= 8) ? Sc1 : Sc0) + (size_t)e * N + (col_ok ? ccol : 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) wscale[j] = sc[j];
+        for (int j = 0; j < CPL; ++j) wscale[j] = sc[j];
     }
 
     // k-steps of this split
@@ -229,11 +254,11 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
             a_src[mi] = A + (size_t)src * K + 8 * g;
         }
 
-        f32x4 acc[MB][8];
+        f32x4 acc[MB][CPL];
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[mi][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int j = 0; j < CPL; ++j) acc[mi][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
         // one k-step of operands: the lane's 8 x 8 weight block and its A fragments
         struct Stage {
@@ -256,23 +281,32 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
                                                                  ((step - s_begin) * 32 + 8 * g) * 2);
             }
         };
-        auto mma = [&](const Stage &sg) {
+        // MFMAs of one k-step, eight weight columns at a time (int8: two halves,
+        // so that only eight converted fragments are live at once)
+        auto mma_half = [&](const Stage &sg, auto hv) {
+            constexpr int H = decltype(hv)::value;
             bf16x8 bfrag[8];
-            if constexpr (QW) transpose8x8_q8(sg.b, bfrag);
+            if constexpr (QW && CPL == 16) transpose8x16_q8<H>(sg.b, bfrag);
+            else if constexpr (QW) transpose8x8_q8(sg.b, bfrag);
             else transpose8x8(sg.b, bfrag);
 #pragma unroll
             for (int mi = 0; mi < MB; ++mi) {
                 const bf16x8 afrag = __builtin_bit_cast(bf16x8, sg.a[mi]);
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    acc[mi][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[j], acc[mi][j], 0, 0, 0);
+                    acc[mi][8 * H + j] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[j], acc[mi][8 * H + j], 0, 0, 0);
             }
         };
+        auto mma = [&](const Stage &sg) {
+            mma_half(sg, std::integral_constant<int, 0>{});
+            if constexpr (CPL == 16) mma_half(sg, std::integral_constant<int, 1>{});
+        };
 
-        if constexpr (QW) {
-            // int8 weights: a k-step is half the bytes, so four k-steps stay in
-            // flight (the same bytes as two bf16 steps).  Stage i holds the steps
-            // st + i; the steady-state loop issues every prefetch unconditionally.
+        if constexpr (QW && CPL == 8) {
+            // narrow int8 layout: a k-step is 4 KB per wave, so four k-steps stay
+            // in flight.  Stage i holds the steps st + i; the steady-state loop
+            // issues every prefetch unconditionally.
             constexpr int NST = 4;
             Stage sg[NST];
 #pragma unroll
@@ -299,7 +333,8 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
             for (int i = 0; i < NST; ++i)
                 if (st + NST + i < s_end) mma(sg[i]);
         } else {
-            // two k-steps in flight: stage 0 holds even steps, stage 1 odd steps.
+            // two k-steps in flight (8 KB per wave: 8 k-rows x 16 bytes x 64 lanes):
+            // stage 0 holds even steps, stage 1 odd steps.
             // The steady-state loop issues both prefetches unconditionally; the
             // scheduling barriers keep each stage's loads together.
             Stage sg0, sg1;
@@ -336,23 +371,31 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = mi * 16 + 4 * g + r;
-                float u[8], v[8];
+                float u[CPL], v[CPL];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < CPL; ++j) {
                     u[j] = QW ? acc[mi][j][r] * wscale[j] : acc[mi][j][r];
                     v[j] = DUAL ? __shfl_xor(u[j], 8) : 0.0f;
                 }
                 if (row >= rows || !col_ok) continue;
                 if (S == 1) {
                     if (DUAL && c >= 8) continue;
-                    store_epilogue8<EPI>(C + (size_t)(r0 + rc + row) * N + ccol, u, v, bias, e, N, ccol);
+#pragma unroll
+                    for (int h8 = 0; h8 < CPL; h8 += 8) {
+                        float uh[8], vh[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) uh[j] = u[h8 + j], vh[j] = v[h8 + j];
+                        store_epilogue8<EPI>(C + (size_t)(r0 + rc + row) * N + ccol + h8, uh, vh, bias, e, N,
+                                             ccol + h8);
+                    }
                 } else {
                     // partial sums of this split: [split][row][NC], W3 products at column N + n
                     const int NC = DUAL ? 2 * N : N;
                     const int pcol = (DUAL && c >= 8) ? N + ccol : ccol;
                     float *dst = part + ((size_t)split * A_total + (r0 + rc + row)) * NC + pcol;
-                    *reinterpret_cast<f32x4 *>(dst) = f32x4{u[0], u[1], u[2], u[3]};
-                    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{u[4], u[5], u[6], u[7]};
+#pragma unroll
+                    for (int q = 0; q < CPL; q += 4)
+                        *reinterpret_cast<f32x4 *>(dst + q) = f32x4{u[q], u[q + 1], u[q + 2], u[q + 3]};
                 }
             }
     }
@@ -419,21 +462,25 @@ DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up, bool q8) {
     const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
     const int K = up ? s.d : s.h;
     const int N = up ? s.h : s.d;
-    const int wcols = dual ? 64 : 128;
+    // 16-row tiles when the expected rows per expert (2T/E) leave a 2x margin
+    p.MB = (2 * s.T <= 8 * s.E) ? 1 : 2;
+    // columns per wave: 128 (SwiGLU: 64 of W1 and W3); int8 weights with 16-row
+    // tiles take 16 columns per lane, twice that
+    const int wcols = (dual ? 64 : 128) * ((q8 && p.MB == 1) ? 2 : 1);
     p.NCB = (N + wcols - 1) / wcols;
     p.slots = std::min(s.E, 2 * s.T);
     const int ksteps = K / 32;
     // S minimises an estimate of the layer's time.  The kernel runs one wave
     // per SIMD, so 256 workgroups (one per CU) make one round; a wave streams
-    // one k-step per ~1.15 us with bf16 weights (two k-steps in flight,
-    // measured; int8 weights: half the bytes, ~0.7 us) plus ~3 k-steps of
+    // one k-step per ~1.15 us (two k-steps in flight, measured with bf16
+    // weights; an int8 k-step moves as many bytes over twice the columns) plus ~3 k-steps of
     // start-up and epilogue; the stream cannot beat ~6.5 TB/s; S > 1 adds the
     // partials' write and read (~5 TB/s) and a ~4 us reduce launch.  A larger
     // S must win by 3% (the estimate is rough; fewer splits mean fewer partials).
     const long wg_per_split = (long)p.slots * ((p.NCB + kDecWaves - 1) / kDecWaves);
     const double cols = (double)N * (dual ? 2 : 1);
     const double weight_bytes = (double)p.slots * K * cols * (q8 ? 1 : 2);
-    const double step_us = q8 ? 0.7 : 1.15;
+    const double step_us = 1.15;
     p.S = 1;
     double best = 1e300;
     for (int S = 1; S <= std::max(1, ksteps / 2); ++S) {
@@ -443,8 +490,6 @@ DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up, bool q8) {
         if (us < best * 0.97) best = us, p.S = S;
     }
     p.W = kDecWaves;
-    // 16-row tiles when the expected rows per expert (2T/E) leave a 2x margin
-    p.MB = (2 * s.T <= 8 * s.E) ? 1 : 2;
     p.part_bytes = p.S > 1 ? align256((size_t)p.S * 2 * s.T * (dual ? 2 : 1) * N * 4) : 0;
     return p;
 }
