@@ -15,7 +15,9 @@ region (decode steps are also reported host-inclusive, back to back).
 
 Prints one JSON line: whole-layer tokens/s, the roofline fraction of the
 dominant kernel, every kernel's time and fraction, decode microseconds per
-step at T=1 and T=64, and the fp64 CPU oracle timed on the host cores.
+step at T=1 and T=64 with bf16 expert weights and with per-column int8
+expert weights (colibri_moe_layer_forward_q8, quantized on the GPU by the
+library's own quantizer), and the fp64 CPU oracle timed on the host cores.
 """
 from __future__ import annotations
 
