@@ -22,6 +22,9 @@ _SO = os.path.join(_HERE, "liboracle.so")
 
 DT_F32, DT_BF16 = 0, 1
 ACT = {"relu": 0, "gelu": 1, "swiglu": 2}
+# gating of the chosen pair: pair softmax, softmax over all experts (unnormalised
+# pair), or the raw logits
+GATE = {"pair": 0, "softmax": 1, "linear": 2}
 
 # -ffp-contract=off: no fused multiply-add, so every product and sum is rounded
 # exactly as written; no fast-math.
@@ -54,6 +57,8 @@ def load_library(path: Optional[str] = None):
     lib.oracle_logits.argtypes = [i, i, i, i, _P, _P, _P, _P]
     lib.oracle_top2.argtypes = [i, i, _P, _P]
     lib.oracle_gates.argtypes = [i, i, _P, _P, _P]
+    lib.oracle_gates_mode.argtypes = [i, i, i, _P, _P, _P]
+    lib.oracle_combine_ex.argtypes = [i, i, i, _P, _P, _P, _P, _P, _P]
     lib.oracle_dispatch.argtypes = [i, i, _P, _P, _P, _P, _P]
     lib.oracle_ffn_rows.argtypes = [i, i, i, i, i, _P, i, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.oracle_combine.argtypes = [i, i, i, _P, _P, _P, _P]
@@ -63,7 +68,7 @@ def load_library(path: Optional[str] = None):
     lib.oracle_ffn_rows_q8.argtypes = [i, i, i, i, i, _P, i, _P, _P] + [_P] * 8 + [_P]
     for f in ("oracle_set_threads", "oracle_logits", "oracle_top2", "oracle_gates", "oracle_dispatch",
               "oracle_ffn_rows", "oracle_combine", "oracle_layer", "oracle_round", "oracle_quantize_q8",
-              "oracle_ffn_rows_q8"):
+              "oracle_ffn_rows_q8", "oracle_gates_mode", "oracle_combine_ex"):
         getattr(lib, f).restype = None
     if path is None:
         _lib = lib
@@ -116,13 +121,16 @@ def top2(lg: np.ndarray, lib=None) -> np.ndarray:
     return idx
 
 
-def gates(lg: np.ndarray, idx: np.ndarray, lib=None) -> np.ndarray:
+def gates(lg: np.ndarray, idx: np.ndarray, mode: str = "pair", lib=None) -> np.ndarray:
     lib = lib or load_library()
     lg = _c(lg, np.float64)
     idx = _c(idx, np.int32)
     T, E = lg.shape
     g = np.empty((T, 2), np.float64)
-    lib.oracle_gates(T, E, _ptr(lg), _ptr(idx), _ptr(g))
+    if mode == "pair":
+        lib.oracle_gates(T, E, _ptr(lg), _ptr(idx), _ptr(g))
+    else:
+        lib.oracle_gates_mode(T, E, GATE[mode], _ptr(lg), _ptr(idx), _ptr(g))
     return g
 
 
@@ -158,7 +166,9 @@ def ffn_rows(x, rows_token, rows_expert, w1, w2, act: str, w3=None, b1=None, b2=
     return y
 
 
-def combine(y_sorted, assign_pos, gate, dtype: int, lib=None) -> np.ndarray:
+def combine(y_sorted, assign_pos, gate, dtype: int, shared_y=None, residual=None, lib=None) -> np.ndarray:
+    """Gate-weighted pair; with ``shared_y`` [T, d] (float64) and/or ``residual``
+    [T, d] (stored dtype) added before the rounding."""
     lib = lib or load_library()
     y = _c(y_sorted, np.float64)
     ap = _c(assign_pos, np.int32)
@@ -166,7 +176,14 @@ def combine(y_sorted, assign_pos, gate, dtype: int, lib=None) -> np.ndarray:
     T = ap.shape[0] // 2
     d = y.shape[1]
     out = np.empty((T, d), np.float64)
-    lib.oracle_combine(T, d, dtype, _ptr(y), _ptr(ap), _ptr(g), _ptr(out))
+    if shared_y is None and residual is None:
+        lib.oracle_combine(T, d, dtype, _ptr(y), _ptr(ap), _ptr(g), _ptr(out))
+        return out
+    sh = _c(shared_y, np.float64)
+    res = _c(residual)
+    if res is not None and _dt(res) != dtype:
+        raise TypeError("residual must be stored in the layer dtype")
+    lib.oracle_combine_ex(T, d, dtype, _ptr(y), _ptr(ap), _ptr(g), _ptr(sh), _ptr(res), _ptr(out))
     return out
 
 
@@ -193,23 +210,36 @@ def layer(x, w_r, w1, w2, act: str, b_r=None, w3=None, b1=None, b2=None, mirror=
 
 
 def layer_tokens(x, w_r, w1, w2, act: str, tokens, b_r=None, w3=None, b1=None, b2=None, mirror=True,
-                 idx_override=None, lib=None) -> Dict[str, np.ndarray]:
+                 idx_override=None, gate="pair", shared=None, residual=None, lib=None) -> Dict[str, np.ndarray]:
     """Layer outputs for a sample of tokens only (each token's row depends only on
     that token).  ``idx_override`` [len(tokens), 2] forces the chosen experts
-    (gates are then taken from the oracle's own logits for that pair)."""
+    (gates are then taken from the oracle's own logits for that pair).
+
+    ``gate``: "pair" | "softmax" | "linear" (see ``gates``).  ``shared``: a dict
+    with the shared expert's w1, w2 (and w3, b1, b2), each with a leading expert
+    axis of 1; its output (rounded to the dtype when ``mirror``) is added with
+    weight one.  ``residual`` [T, d] (all tokens, stored dtype) is added last."""
     lib = lib or load_library()
     tokens = np.asarray(tokens, np.int64)
     xs = _c(np.asarray(x)[tokens])
     lg = logits(xs, w_r, b_r, lib=lib)
     idx = top2(lg, lib=lib) if idx_override is None else _c(idx_override, np.int32)
-    g = gates(lg, idx, lib=lib)
+    g = gates(lg, idx, mode=gate, lib=lib)
     n = len(tokens)
     rt = np.repeat(np.arange(n, dtype=np.int32), 2)
     re = idx.reshape(-1)
     y = ffn_rows(xs, rt, re, w1, w2, act, w3=w3, b1=b1, b2=b2, mirror=mirror, lib=lib)
     ap = np.arange(2 * n, dtype=np.int32)
-    out = combine(y, ap, g, _dt(xs), lib=lib)
-    return {"logits": lg, "idx": idx, "gate": g, "y": y.reshape(n, 2, -1), "out": out}
+    ysh = None
+    if shared is not None:
+        ysh = ffn_rows(xs, np.arange(n, dtype=np.int32), np.zeros(n, np.int32), shared["w1"], shared["w2"], act,
+                       w3=shared.get("w3"), b1=shared.get("b1"), b2=shared.get("b2"), mirror=mirror, lib=lib)
+    res = None if residual is None else _c(np.asarray(residual)[tokens])
+    out = combine(y, ap, g, _dt(xs), shared_y=ysh, residual=res, lib=lib)
+    r = {"logits": lg, "idx": idx, "gate": g, "y": y.reshape(n, 2, -1), "out": out}
+    if ysh is not None:
+        r["y_shared"] = ysh
+    return r
 
 
 # ------------------------------------------------------------------ int8 expert weights

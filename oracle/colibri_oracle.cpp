@@ -25,7 +25,12 @@
 //    (logit descending, expert index ascending); NaN ranks below -inf;
 //  * tokens inside an expert's segment keep ascending assignment order
 //    a = 2t + s, the order of the counting loop in [zskr] section 3.2;
-//  * expert = two-layer FFN (ReLU / exact-erf GELU, or SwiGLU with W1, W3, W2).
+//  * expert = two-layer FFN (ReLU / exact-erf GELU, or SwiGLU with W1, W3, W2);
+//  * the other gatings: DeepSeek-MoE's softmax top-2 ([rkmt] section 5.2)
+//    keeps the two softmax probabilities as they are; LINEAR_SCORE ([zskr]
+//    section 2.3) weights the outputs by the raw logits;
+//  * a shared expert ([rkmt] section 5.2) sees every token and adds its
+//    output with weight one; a residual row ([nxbn] section 2.1) is added last.
 //
 // Parity is pinned by the CPU tests (brute-force top-2, exhaustive tie
 // patterns, the page's printed gate pairs, a hand-worked dispatch, library
@@ -195,6 +200,36 @@ void oracle_gates(int T, int E, const double *logits, const int32_t *idx, double
     }
 }
 
+// Step 3 with a choice of gating (the selection of step 2 is the same in
+// every mode):
+//   mode 0: the pair softmax above;
+//   mode 1: softmax over all E experts, the chosen two taken as they are, not
+//           renormalised (the DeepSeek-MoE softmax top-2 router of [rkmt]
+//           section 5.2: softmax over every expert, then the top two):
+//           gate[s] = exp(l[idx_s]) / sum_e exp(l[e]);
+//   mode 2: no softmax, each chosen logit weights its expert's output
+//           (the LINEAR_SCORE mode of [zskr] section 2.3): gate[s] = l[idx_s].
+void oracle_gates_mode(int T, int E, int mode, const double *logits, const int32_t *idx, double *gate) {
+    if (mode == 0) {
+        oracle_gates(T, E, logits, idx, gate);
+        return;
+    }
+    for (int t = 0; t < T; ++t) {
+        const double *l = logits + (size_t)t * E;
+        if (mode == 2) {
+            gate[2 * t] = l[idx[2 * t]];
+            gate[2 * t + 1] = l[idx[2 * t + 1]];
+            continue;
+        }
+        double m = -INFINITY;
+        for (int e = 0; e < E; ++e) m = std::max(m, l[e]);
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) z += std::exp(l[e] - m);
+        gate[2 * t] = std::exp(l[idx[2 * t]] - m) / z;
+        gate[2 * t + 1] = std::exp(l[idx[2 * t + 1]] - m) / z;
+    }
+}
+
 // Step 4, dispatch ([zskr] section 3.2: count assignments per expert over
 // i = t*k + s, then build dispatch offsets; [zskr] section 3.3: one contiguous
 // region per expert).  Assignment a = 2t + s.
@@ -257,14 +292,34 @@ void oracle_ffn_rows(int d, int h, int dt, int act, int mirror, const void *x, i
 // Step 6, combine ([nxbn] section 3.3: the expert outputs are summed weighted by
 // their gating scores):  out[t] = g[2t] * y[assign_pos[2t]] + g[2t+1] * y[assign_pos[2t+1]],
 // in double, then rounded to `dt`.  y_sorted [2T, d] double, out [T, d] double.
+// (oracle_combine_ex below with neither addend.)
+void oracle_combine_ex(int T, int d, int dt, const double *y_sorted, const int32_t *assign_pos, const double *gate,
+                       const double *shared_y, const void *residual, double *out);
 void oracle_combine(int T, int d, int dt, const double *y_sorted, const int32_t *assign_pos,
                     const double *gate, double *out) {
+    oracle_combine_ex(T, d, dt, y_sorted, assign_pos, gate, nullptr, nullptr, out);
+}
+
+// Step 6 with two optional addends: the output of a shared expert applied to
+// every token with weight one ([rkmt] section 5.2: Qwen2-MoE runs one shared
+// expert beside its routed ones) and a residual row ([nxbn] section 2.1: the
+// residual add belongs to the expert computation):
+//   out[t] = g[2t] y[assign_pos[2t]] + g[2t+1] y[assign_pos[2t+1]] + shared_y[t] + residual[t]
+// in double, then rounded to `dt`.  shared_y [T, d] double or NULL;
+// residual [T, d] in `dt` or NULL.
+void oracle_combine_ex(int T, int d, int dt, const double *y_sorted, const int32_t *assign_pos, const double *gate,
+                       const double *shared_y, const void *residual, double *out) {
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         const double *y0 = y_sorted + (size_t)assign_pos[2 * t] * d;
         const double *y1 = y_sorted + (size_t)assign_pos[2 * t + 1] * d;
-        for (int c = 0; c < d; ++c)
-            out[(size_t)t * d + c] = round_to_dtype(gate[2 * t] * y0[c] + gate[2 * t + 1] * y1[c], dt);
+        for (int c = 0; c < d; ++c) {
+            const size_t i = (size_t)t * d + c;
+            double v = gate[2 * t] * y0[c] + gate[2 * t + 1] * y1[c];
+            if (shared_y) v += shared_y[i];
+            if (residual) v += load(residual, dt, i);
+            out[i] = round_to_dtype(v, dt);
+        }
     }
 }
 

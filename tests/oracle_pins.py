@@ -475,4 +475,130 @@ def pin_q8_ffn_library(lib):
             np.testing.assert_allclose(y[r], ref, rtol=1e-11, atol=1e-13)
 
 
+# ----------------------------------------------------------------- gating variants, shared expert, residual
+def pin_gate_modes_hand_example(lib):
+    kv = _read_kv(os.path.join(GOLDEN, "gate_modes_hand_example.txt"))
+    for case in ("a", "b"):
+        lg = np.log(np.array([kv[f"{case}_p"]]))
+        idx = oracle.top2(lg, lib=lib)
+        assert idx[0].tolist() == [int(v) for v in kv[f"{case}_idx"]], (case, idx)
+        for mode in ("softmax", "pair"):
+            g = oracle.gates(lg, idx, mode=mode, lib=lib)
+            np.testing.assert_allclose(g[0], kv[f"{case}_{mode}"], rtol=1e-14, err_msg=f"{case} {mode}")
+        g = oracle.gates(lg, idx, mode="linear", lib=lib)
+        assert g[0].tolist() == lg[0, idx[0]].tolist()
+
+
+def pin_gates_softmax_all_library(lib):
+    """Softmax over all experts (scipy), read at the chosen pair, unnormalised."""
+    rng = np.random.default_rng(31)
+    for E in (2, 3, 8, 16, 60, 64):
+        lg = rng.standard_normal((200, E)) * 3
+        idx = oracle.top2(lg, lib=lib)
+        g = oracle.gates(lg, idx, mode="softmax", lib=lib)
+        p = softmax(lg, axis=1)
+        rows = np.arange(200)
+        np.testing.assert_allclose(g[:, 0], p[rows, idx[:, 0]], rtol=1e-13)
+        np.testing.assert_allclose(g[:, 1], p[rows, idx[:, 1]], rtol=1e-13)
+        # the pair keeps the ratio of the pair softmax; with two experts the modes agree
+        gp = oracle.gates(lg, idx, lib=lib)
+        np.testing.assert_allclose(g[:, 0] / g.sum(1), gp[:, 0], rtol=1e-13)
+        if E == 2:
+            np.testing.assert_allclose(g, gp, rtol=1e-14)
+        else:
+            assert np.all(g.sum(1) < 1.0)
+
+
+def pin_gates_linear_are_logits(lib):
+    rng = np.random.default_rng(32)
+    for E in (2, 5, 64):
+        lg = rng.standard_normal((100, E)) * 4
+        idx = oracle.top2(lg, lib=lib)
+        g = oracle.gates(lg, idx, mode="linear", lib=lib)
+        rows = np.arange(100)
+        assert np.array_equal(g[:, 0], lg[rows, idx[:, 0]])
+        assert np.array_equal(g[:, 1], lg[rows, idx[:, 1]])
+
+
+def pin_combine_addends_hand_example(lib):
+    kv = _read_kv(os.path.join(GOLDEN, "combine_addends_hand_example.txt"))
+    y = np.array([kv["y0"], kv["y1"]])
+    ap = np.array([0, 1], np.int32)
+    g = np.array([kv["g"]])
+    sh = np.array([kv["shared"]])
+    res = np.array([kv["residual"]], np.float32)
+    for dt, cast in ((oracle.DT_F32, lambda a: a), (oracle.DT_BF16, gen.f32_to_bf16_bits)):
+        out = oracle.combine(y, ap, g, dt, shared_y=sh, residual=cast(res), lib=lib)
+        assert out[0].tolist() == kv["out"], out
+        assert oracle.combine(y, ap, g, dt, lib=lib)[0].tolist() == kv["out_plain"]
+        assert oracle.combine(y, ap, g, dt, shared_y=sh, lib=lib)[0].tolist() == kv["out_shared_only"]
+
+
+def pin_combine_addends_indexing(lib):
+    """Addend rows follow the token: row t of shared_y / residual holds t and
+    10 t in every column."""
+    rng = np.random.default_rng(33)
+    T, d = 30, 4
+    ap = rng.permutation(2 * T).astype(np.int32)
+    g = rng.random((T, 2))
+    y = np.repeat(np.arange(2 * T, dtype=np.float64)[:, None], d, 1)
+    sh = np.repeat(np.arange(T, dtype=np.float64)[:, None], d, 1)
+    res = np.repeat((10 * np.arange(T, dtype=np.float32))[:, None], d, 1)
+    out = oracle.combine(y, ap, g, oracle.DT_F32, shared_y=sh, residual=res, lib=lib)
+    ref = g[:, 0] * ap[0::2] + g[:, 1] * ap[1::2] + 11 * np.arange(T)
+    for c in range(d):
+        np.testing.assert_allclose(out[:, c], ref, rtol=1e-7)
+
+
+def _shared_expert(rng, act, d, h):
+    return {
+        "w1": _rand_f32(rng, (1, d, h), 1 / math.sqrt(d)), "w2": _rand_f32(rng, (1, h, d), 1 / math.sqrt(h)),
+        "w3": _rand_f32(rng, (1, d, h), 1 / math.sqrt(d)) if act == "swiglu" else None,
+        "b1": _rand_f32(rng, (1, h), 0.1) if act != "swiglu" else None,
+        "b2": _rand_f32(rng, (1, d), 0.1) if act != "swiglu" else None,
+    }
+
+
+def pin_layer_shared_expert_library(lib):
+    """The shared expert is a dense FFN over every token (numpy matmuls), added
+    with weight one beside the routed pair and the residual."""
+    rng = np.random.default_rng(34)
+    for act in ("relu", "gelu", "swiglu"):
+        w = _small_layer(rng, act)
+        T, d = w["x"].shape
+        sh = _shared_expert(rng, act, d, 80)
+        res = _rand_f32(rng, (T, d))
+        tokens = np.arange(T)
+        for gate in ("pair", "softmax", "linear"):
+            r = oracle.layer_tokens(w["x"], w["w_r"], w["w1"], w["w2"], act, tokens, b_r=w["b_r"], w3=w["w3"],
+                                    b1=w["b1"], b2=w["b2"], mirror=False, gate=gate, shared=sh, residual=res,
+                                    lib=lib)
+            x64 = w["x"].astype(np.float64)
+            f = lambda k: None if sh[k] is None else sh[k][0].astype(np.float64)
+            ysh = _np_ffn(x64, f("w1"), f("b1"), f("w2"), f("b2"), act, f("w3"))
+            np.testing.assert_allclose(r["y_shared"], ysh, rtol=1e-11, atol=1e-13)
+            routed = r["gate"][:, :1] * r["y"][:, 0] + r["gate"][:, 1:] * r["y"][:, 1]
+            ref = routed + ysh + res.astype(np.float64)
+            np.testing.assert_allclose(r["out"], ref, rtol=3e-7, atol=1e-6)
+
+
+def pin_layer_zero_addends_are_plain(lib):
+    """A shared expert of zero weights and a zero residual leave the layer as it was."""
+    rng = np.random.default_rng(35)
+    for act in ("relu", "swiglu"):
+        for dt in (gen.F32, gen.BF16):
+            w = _small_layer(rng, act, dt=dt)
+            T, d = w["x"].shape
+            zero = lambda shape: np.zeros(shape, w["x"].dtype)
+            sh = {"w1": zero((1, d, 64)), "w2": zero((1, 64, d)), "w3": zero((1, d, 64)) if act == "swiglu" else None}
+            tokens = np.arange(T)
+            kw = dict(b_r=w["b_r"], w3=w["w3"], b1=w["b1"], b2=w["b2"], mirror=True, lib=lib)
+            base = oracle.layer_tokens(w["x"], w["w_r"], w["w1"], w["w2"], act, tokens, **kw)
+            ex = oracle.layer_tokens(w["x"], w["w_r"], w["w1"], w["w2"], act, tokens, shared=sh,
+                                     residual=zero((T, d)), **kw)
+            assert np.array_equal(base["out"], ex["out"])
+            full = oracle.layer(w["x"], w["w_r"], w["w1"], w["w2"], act, **kw)
+            assert np.array_equal(full["out"], base["out"])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

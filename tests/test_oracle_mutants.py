@@ -47,6 +47,16 @@ MUTANTS = {
                                  "sc[n - n0] = amax[n - n0] / 127.0f;"),
     "q8_scale_over_128": ("sc[n - n0] = amax[n - n0] > 0.0f ? amax[n - n0] / 127.0f : 1.0f;",
                           "sc[n - n0] = amax[n - n0] > 0.0f ? amax[n - n0] / 128.0f : 1.0f;"),
+    "softmax_gates_renormalised": ("gate[2 * t] = std::exp(l[idx[2 * t]] - m) / z;",
+                                   "gate[2 * t] = std::exp(l[idx[2 * t]] - m) / (std::exp(l[idx[2 * t]] - m) + "
+                                   "std::exp(l[idx[2 * t + 1]] - m));"),
+    "softmax_gates_unscaled": ("gate[2 * t + 1] = std::exp(l[idx[2 * t + 1]] - m) / z;",
+                               "gate[2 * t + 1] = std::exp(l[idx[2 * t + 1]] - m);"),
+    "linear_gates_slots_swapped": ("gate[2 * t] = l[idx[2 * t]];", "gate[2 * t] = l[idx[2 * t + 1]];"),
+    "shared_expert_dropped": ("if (shared_y) v += shared_y[i];", "(void)shared_y;"),
+    "shared_expert_row_offset": ("if (shared_y) v += shared_y[i];", "if (shared_y) v += shared_y[c];"),
+    "residual_dropped": ("if (residual) v += load(residual, dt, i);", "(void)residual;"),
+    "residual_subtracted": ("if (residual) v += load(residual, dt, i);", "if (residual) v -= load(residual, dt, i);"),
     "rounding_via_fp32": ("double round_to_dtype(double v, int dt) { return round_to_format(v, dt == DT_F32 ? 23 : 7); }",
                           "double round_to_dtype(double v, int dt) { return round_to_format(dt == DT_F32 ? v : (double)(float)v, dt == DT_F32 ? 23 : 7); }"),
 }
