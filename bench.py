@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--decode-T", default="1,64", help="decode batch sizes also timed (comma list, '' = none)")
     ap.add_argument("--decode-iters", type=int, default=200)
     ap.add_argument("--no-q8", action="store_true", help="skip the int8-weight decode lines")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the shared-expert / softmax-gating / residual layer lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle sample for about this long")
@@ -326,6 +328,14 @@ def main():
             log(f"decode int8 weights T={tok}: {decode_q8[f'T={tok}']}")
         del qcopies, q0
 
+    # ---------------------------------------------------------------- layer variants
+    # 15 routed + 1 shared expert, softmax over all experts (unnormalised pair),
+    # residual added in the combine; beside it the same routed layer without the
+    # shared expert and residual, pair gating, to show what the options cost
+    variants = {}
+    if not args.no_variants:
+        variants = time_variants(args, moe, gen, torch, np, to_dev, stream, prefill_queue)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -357,9 +367,82 @@ def main():
                    "T": T, "E": cfg.E, "d": cfg.d, "h": cfg.h, "act": cfg.act, "weight_copies": R,
                    "experts_hit": hit},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode, "decode_int8_weights": decode_q8,
+        "variants": variants,
         "timing": "GPU time (HIP events, queue pre-filled by a spin kernel)" if can_sleep else "GPU time (HIP events)",
     }
     print(json.dumps(rec), flush=True)
+
+
+def time_variants(args, moe, gen, torch, np, to_dev, stream, prefill_queue):
+    """GPU time per step of the 15 + 1 shared-expert layer through
+    colibri_moe_layer_forward_ex (softmax gating, shared expert, residual) and of
+    the same routed layer through colibri_moe_layer_forward, at T = 1, 64, 512.
+    Weights rotate over copies (as in the main measurement) so that no step
+    finds them in the last-level cache."""
+    cfg = gen.CONFIGS["shared15"]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w0 = {k: to_dev(v) for k, v in gen.make_experts(cfg).items()}
+    s0 = {k: to_dev(v) for k, v in gen.make_shared_expert(cfg).items()}
+    Tmax = max(cfg.Ts)
+    x = to_dev(gen.make_x(cfg, Tmax))
+    res = to_dev(gen.make_residual(cfg, Tmax))
+    w_r = to_dev(gen.make_router(cfg))
+    el = 2
+    routed_bytes = sum(v.numel() * el for v in w0.values() if v is not None)
+    shared_bytes = sum(v.numel() * el for v in s0.values() if v is not None)
+    R = max(1, math.ceil(args.rotate_gb * 1e9 / (routed_bytes + shared_bytes)))
+    copies = [(w0, s0)] + [({k: (v.clone() if v is not None else None) for k, v in w0.items()},
+                            {k: (v.clone() if v is not None else None) for k, v in s0.items()}) for _ in range(R - 1)]
+    log(f"variants: shared15 inputs in {time.time() - t0:.1f}s, {R} weight copies")
+    act = gen.ACT_CODE[cfg.act]
+    up_e = 2 * cfg.d * cfg.h * el
+    down_e = cfg.h * cfg.d * el
+    out = torch.empty((Tmax, cfg.d), dtype=torch.bfloat16, device=dev)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    rec = {}
+    for T in cfg.Ts:
+        sh = moe.Shape(T, cfg.d, cfg.h, cfg.E, cfg.dtype, act)
+        ws_ex = moe.workspace_size_ex(sh, gate="softmax", shared=s0, shared_h=cfg.shared_h, residual=res)
+        ws_pl = moe.workspace_size(sh)
+        ws = torch.empty(max(ws_ex, ws_pl), dtype=torch.uint8, device=dev)
+
+        def step_ex(i):
+            w, sw = copies[i % R]
+            moe.layer_forward_ex(sh, x[:T], w_r, None, w["w1"], w["w2"], out[:T], ws, ws_ex, w3=w["w3"], gate="softmax",
+                                 shared=sw, shared_h=cfg.shared_h, residual=res[:T], counts=counts)
+
+        def step_plain(i):
+            w, _ = copies[i % R]
+            moe.layer_forward(sh, x[:T], w_r, None, w["w1"], w["w2"], out[:T], ws, ws_pl, w3=w["w3"], counts=counts)
+
+        for name, fn, extra in (("softmax+shared+residual", step_ex, shared_bytes + T * cfg.d * el),
+                                ("plain", step_plain, 0)):
+            iters = 200 if T <= 64 else 60
+            times = []
+            for it in range(10 + iters):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                if it % 10 == 0:
+                    prefill_queue()
+                e0.record(stream)
+                fn(it)
+                e1.record(stream)
+                if it % 10 == 9:
+                    torch.cuda.synchronize()
+                if it >= 10:
+                    times.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in times]))
+            hit = int((counts.cpu().numpy() > 0).sum())
+            byt = hit * (up_e + down_e) + extra + 2 * T * cfg.d * el
+            rec[f"{name} T={T}"] = {"us_per_step_median": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
+                                    "experts_hit": hit, "hbm_frac": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"variant {name} T={T}: {rec[f'{name} T={T}']}")
+    rec["workload"] = (f"{cfg.title}: E={cfg.E} routed + 1 shared (h_shared={cfg.shared_h}), top-2, d={cfg.d}, "
+                       f"h={cfg.h}, {cfg.act}, bf16")
+    del copies
+    return rec
 
 
 if __name__ == "__main__":

@@ -27,6 +27,8 @@ _SO = os.path.join(_HERE, "libgen.so")
 
 # tensor ids (Philox key word 1); the seed is key word 0
 TID_X, TID_WR, TID_W1, TID_B1, TID_W3, TID_W2, TID_B2 = 1, 2, 10, 11, 12, 13, 14
+TID_SH_W1, TID_SH_B1, TID_SH_W3, TID_SH_W2, TID_SH_B2 = 20, 21, 22, 23, 24  # shared expert
+TID_RES = 30  # residual rows
 
 F32, BF16 = 0, 1
 
@@ -104,6 +106,8 @@ class Config:
     router_bias: Optional[str] = None   # None | "zipf"
     zipf_s: float = 0.0
     seed: int = 0
+    shared_h: int = 0      # hidden width of an always-on shared expert (0: none)
+    gate: str = "pair"     # gating of the chosen pair: "pair" | "softmax" | "linear"
 
 
 CONFIGS: Dict[str, Config] = {
@@ -122,6 +126,11 @@ CONFIGS: Dict[str, Config] = {
     # 16 experts with Zipf(1.2) expert popularity set by a fitted router bias
     "skew16": Config("skew16", "16-expert Zipf-skewed layer", E=16, d=3584, h=2560, act="swiglu",
                      dtype=BF16, Ts=[8192], biases=False, router_bias="zipf", zipf_s=1.2),
+    # 1 shared + 15 routed experts (the Qwen2-MoE split), softmax over all
+    # experts without renormalising the pair; widths of a 2.7B-active layer
+    # (routed h 1408, shared h 4 x 1408)
+    "shared15": Config("shared15", "15 routed + 1 shared expert layer", E=15, d=2048, h=1408, act="swiglu",
+                       dtype=BF16, Ts=[1, 64, 512], biases=False, shared_h=5632, gate="softmax"),
 }
 
 ACT_CODE = {"relu": 0, "gelu": 1, "swiglu": 2}
@@ -165,6 +174,23 @@ def make_experts(cfg: Config) -> Dict[str, Optional[np.ndarray]]:
         "b2": normal(cfg.seed, TID_B2, (E, d), 0.1, dt) if cfg.biases else None,
     }
     return w
+
+
+def make_shared_expert(cfg: Config) -> Dict[str, Optional[np.ndarray]]:
+    """The shared expert's weights, laid out as one expert: w1 [1, d, shared_h] ..."""
+    d, h, dt = cfg.d, cfg.shared_h or cfg.h, cfg.dtype
+    return {
+        "w1": normal(cfg.seed, TID_SH_W1, (1, d, h), 1.0 / math.sqrt(d), dt),
+        "w3": normal(cfg.seed, TID_SH_W3, (1, d, h), 1.0 / math.sqrt(d), dt) if cfg.act == "swiglu" else None,
+        "w2": normal(cfg.seed, TID_SH_W2, (1, h, d), 1.0 / math.sqrt(h), dt),
+        "b1": normal(cfg.seed, TID_SH_B1, (1, h), 0.1, dt) if cfg.biases else None,
+        "b2": normal(cfg.seed, TID_SH_B2, (1, d), 0.1, dt) if cfg.biases else None,
+    }
+
+
+def make_residual(cfg: Config, T: int) -> np.ndarray:
+    """Residual rows [T, d] ~ N(0, 1), in the layer dtype."""
+    return normal(cfg.seed, TID_RES, (T, cfg.d), 1.0, cfg.dtype)
 
 
 def make_all(cfg: Config, T: int) -> Dict[str, Optional[np.ndarray]]:

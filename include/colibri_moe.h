@@ -162,6 +162,59 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
                               float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* ------------------------------------------------------------------ layer variants
+ * Gating of the chosen pair (the selection itself always ranks the logits
+ * under (logit descending, index ascending)):
+ *   COLIBRI_GATE_PAIR     g0 = 1 / (1 + exp(l1 - l0)), g1 = 1 - g0: softmax over
+ *                         the two chosen logits, i.e. softmax over all experts
+ *                         renormalised over the pair (Mixtral's top-2; the default)
+ *   COLIBRI_GATE_SOFTMAX  g_s = exp(l_s - l0) / sum_e exp(l_e - l0): softmax over
+ *                         all E experts, the chosen two taken unnormalised
+ *                         (DeepSeek-MoE's "softmax top-2", [rkmt] section 5.2)
+ *   COLIBRI_GATE_LINEAR   g_s = l_s: no softmax, the logits weight the outputs
+ *                         (LINEAR_SCORE, [zskr] section 2.3) */
+typedef enum { COLIBRI_GATE_PAIR = 0, COLIBRI_GATE_SOFTMAX = 1, COLIBRI_GATE_LINEAR = 2 } colibri_gate_t;
+
+/* Options of colibri_moe_layer_forward_ex:
+ *   gate      gating of the routed pair (above)
+ *   shared    an always-on shared expert applied to every token with weight 1
+ *             ([rkmt] section 5.2: Qwen2-MoE's shared expert beside the routed
+ *             ones), one expert in the layout of colibri_moe_experts_t
+ *             (w1 [1][d][shared_h] ...), same activation; or NULL
+ *   residual  [T, d] dtype, 16-byte aligned, added to the output ([nxbn]
+ *             section 2.1: residual add fused with the expert computation); or
+ *             NULL.  It may be the same buffer as out (an in-place update).
+ * out[t] = g0 y(t, slot 0) + g1 y(t, slot 1) + y_shared(t) + residual[t], summed
+ * in fp32 and rounded once; y_shared is stored in dtype like the routed rows. */
+typedef struct {
+    colibri_gate_t gate;
+    const colibri_moe_experts_t *shared;
+    int32_t shared_h; /* hidden width of the shared expert (0: h); a multiple of 64 */
+    const void *residual;
+} colibri_moe_layer_opts_t;
+
+/* Workspace of colibri_moe_layer_forward_ex for these options (NULL opts =
+ * the plain layer: equal to colibri_moe_workspace_size). */
+size_t colibri_moe_workspace_size_ex(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *opts);
+
+/* Steps 1-2 with a choice of gating; colibri_moe_route is gate = COLIBRI_GATE_PAIR. */
+int colibri_moe_route_ex(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                         colibri_gate_t gate, int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t stream);
+
+/* Step 5 with the optional addends: out[t] = g0 y0 + g1 y1 + shared_y[t] +
+ * residual[t].  shared_y [T, d] and residual [T, d] are dtype, 16-byte aligned,
+ * or NULL. */
+int colibri_moe_combine_ex(const colibri_moe_shape_t *s, const void *y_sorted, const int32_t *assign_pos,
+                           const float *topk_gate, const void *shared_y, const void *residual, void *out,
+                           hipStream_t stream);
+
+/* Steps 1-5 with the options above (NULL opts = colibri_moe_layer_forward).
+ * ws must hold colibri_moe_workspace_size_ex(s, opts) bytes, 256-byte aligned. */
+int colibri_moe_layer_forward_ex(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                                 const colibri_moe_experts_t *w, const colibri_moe_layer_opts_t *opts, void *out,
+                                 int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ int8 expert weights
  * Expert weights stored as int8 codes with one fp32 scale per output column
  * ([zskr] section 5.3: per-channel INT8 quantization of the expert weights,

@@ -20,12 +20,15 @@ COLIBRI_OK, COLIBRI_ERR_INVALID_ARG, COLIBRI_ERR_WORKSPACE, COLIBRI_ERR_UNSUPPOR
 F32, BF16 = 0, 1
 RELU, GELU, SWIGLU = 0, 1, 2
 ACT_CODES = {"relu": RELU, "gelu": GELU, "swiglu": SWIGLU}
+GATE_PAIR, GATE_SOFTMAX, GATE_LINEAR = 0, 1, 2
+GATE_CODES = {"pair": GATE_PAIR, "softmax": GATE_SOFTMAX, "linear": GATE_LINEAR}
 
 EXPORTED = [
     "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn",
     "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
     "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
-    "colibri_moe_status_string",
+    "colibri_moe_workspace_size_ex", "colibri_moe_route_ex", "colibri_moe_combine_ex",
+    "colibri_moe_layer_forward_ex", "colibri_moe_status_string",
 ]
 
 
@@ -49,6 +52,11 @@ class _ExpertsQ8(ctypes.Structure):
     _fields_ = [("q1", ctypes.c_void_p), ("q3", ctypes.c_void_p), ("q2", ctypes.c_void_p),
                 ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
                 ("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_int), ("shared", ctypes.POINTER(_Experts)), ("shared_h", ctypes.c_int32),
+                ("residual", ctypes.c_void_p)]
 
 
 @dataclass(frozen=True)
@@ -102,9 +110,16 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_quantize_q8.argtypes = [P, I, i32, i32, i32, P, P, P]
     lib.colibri_moe_expert_ffn_q8.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ8), P, P, Z, P]
     lib.colibri_moe_layer_forward_q8.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ8), P, P, P, P, P, Z, P]
+    OP = ctypes.POINTER(_Opts)
+    lib.colibri_moe_workspace_size_ex.argtypes = [SP, OP]
+    lib.colibri_moe_workspace_size_ex.restype = Z
+    lib.colibri_moe_route_ex.argtypes = [SP, P, P, P, I, P, P, P, P]
+    lib.colibri_moe_combine_ex.argtypes = [SP, P, P, P, P, P, P, P]
+    lib.colibri_moe_layer_forward_ex.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), OP, P, P, P, P, P, Z, P]
     for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up",
               "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
-              "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8"):
+              "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
+              "colibri_moe_route_ex", "colibri_moe_combine_ex", "colibri_moe_layer_forward_ex"):
         getattr(lib, f).restype = I
     lib.colibri_moe_status_string.argtypes = [I]
     lib.colibri_moe_status_string.restype = ctypes.c_char_p
@@ -202,6 +217,53 @@ def layer_forward(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: int, w3=
     _check(load().colibri_moe_layer_forward(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
                                             _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
                                             ws_bytes, _stream(stream)), "colibri_moe_layer_forward")
+
+
+# ------------------------------------------------------------------ gating variants, shared expert, residual
+def _gate_code(gate) -> int:
+    return GATE_CODES[gate] if isinstance(gate, str) else int(gate)
+
+
+def _opts(gate="pair", shared=None, shared_h: int = 0, residual=None):
+    """ctypes options and the experts struct it points to (keep both alive).
+    ``shared``: dict with the shared expert's w1, w2 (and w3, b1, b2)."""
+    sh = None
+    if shared is not None:
+        sh = _experts(shared["w1"], shared["w2"], shared.get("w3"), shared.get("b1"), shared.get("b2"))
+    o = _Opts(_gate_code(gate), ctypes.pointer(sh) if sh is not None else None, int(shared_h), _ptr(residual))
+    return o, sh
+
+
+def workspace_size_ex(shape: Shape, gate="pair", shared=None, shared_h: int = 0, residual=None) -> int:
+    s = shape.c()
+    o, keep = _opts(gate, shared, shared_h, residual)
+    return int(load().colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(o)))
+
+
+def route_ex(shape: Shape, x, w_r, b_r, gate, topk_idx, topk_gate, logits=None, stream=None):
+    s = shape.c()
+    _check(load().colibri_moe_route_ex(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), _gate_code(gate),
+                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(logits), _stream(stream)),
+           "colibri_moe_route_ex")
+
+
+def combine_ex(shape: Shape, y_sorted, assign_pos, topk_gate, out, shared_y=None, residual=None, stream=None):
+    s = shape.c()
+    _check(load().colibri_moe_combine_ex(ctypes.byref(s), _ptr(y_sorted), _ptr(assign_pos), _ptr(topk_gate),
+                                         _ptr(shared_y), _ptr(residual), _ptr(out), _stream(stream)),
+           "colibri_moe_combine_ex")
+
+
+def layer_forward_ex(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: int, w3=None, b1=None, b2=None,
+                     gate="pair", shared=None, shared_h: int = 0, residual=None, topk_idx=None, topk_gate=None,
+                     counts=None, stream=None):
+    s = shape.c()
+    e = _experts(w1, w2, w3, b1, b2)
+    o, keep = _opts(gate, shared, shared_h, residual)
+    _check(load().colibri_moe_layer_forward_ex(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
+                                               ctypes.byref(o), _ptr(out), _ptr(topk_idx), _ptr(topk_gate),
+                                               _ptr(counts), _ptr(ws), ws_bytes, _stream(stream)),
+           "colibri_moe_layer_forward_ex")
 
 
 # ------------------------------------------------------------------ int8 expert weights

@@ -8,6 +8,7 @@
 // http://www.zskr.cn/news/2272131 section 5.2 reports for a wrong pointer.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "colibri_moe.h"
@@ -74,12 +75,42 @@ int check_experts_q8(const colibri_moe_shape_t *s, const colibri_moe_experts_q8_
     return COLIBRI_OK;
 }
 
+// The shared expert runs as a one-expert group over the T token rows of x:
+// shape {ceil(T / 2), d, shared_h, E = 1} (the FFN kernels work on 2T rows
+// of a shape; its one expert gets rows [0, T), so x is read in place and its
+// outputs land in token order).
+colibri_moe_shape_t shared_shape(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o) {
+    colibri_moe_shape_t sh = *s;
+    sh.T = (s->T + 1) / 2;
+    sh.h = o->shared_h ? o->shared_h : s->h;
+    sh.E = 1;
+    return sh;
+}
+
+bool has_shared(const colibri_moe_layer_opts_t *o) { return o && o->shared; }
+
+int check_opts(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o) {
+    if (!o) return COLIBRI_OK;
+    if (o->gate != COLIBRI_GATE_PAIR && o->gate != COLIBRI_GATE_SOFTMAX && o->gate != COLIBRI_GATE_LINEAR)
+        return COLIBRI_ERR_UNSUPPORTED;
+    if (o->residual && !aligned(o->residual, 16)) return COLIBRI_ERR_INVALID_ARG;
+    if (o->shared_h < 0 || o->shared_h % 64 || o->shared_h > (1 << 20)) return COLIBRI_ERR_UNSUPPORTED;
+    if (o->shared) {
+        const colibri_moe_shape_t sh = shared_shape(s, o);
+        return check_experts(&sh, o->shared);
+    }
+    return COLIBRI_OK;
+}
+
 struct LayerWorkspace {
-    size_t idx, gate, counts, offsets, sorted, pos, y, ffn, total;
+    size_t idx, gate, counts, offsets, sorted, pos, y, sh_offsets, sh_y, ffn, total;
 };
 
-LayerWorkspace layer_workspace(const colibri_moe_shape_t *s) {
-    LayerWorkspace L;
+// The plain layer's regions, then (with a shared expert) its offsets and
+// output rows; the FFN region last, sized for the larger of the routed and the
+// shared FFN (the shared expert runs first and is done with it).
+LayerWorkspace layer_workspace(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o = nullptr) {
+    LayerWorkspace L{};
     const size_t A = 2 * (size_t)s->T;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -94,7 +125,14 @@ LayerWorkspace layer_workspace(const colibri_moe_shape_t *s) {
     L.sorted = take(A * 4);
     L.pos = take(A * 4);
     L.y = take(A * s->d * elem_size(s));
-    L.ffn = take(ffn_workspace_bytes(*s));
+    size_t ffn = ffn_workspace_bytes(*s);
+    if (has_shared(o)) {
+        const colibri_moe_shape_t sh = shared_shape(s, o);
+        L.sh_offsets = take(2 * 4);
+        L.sh_y = take(2 * (size_t)sh.T * s->d * elem_size(s));
+        ffn = std::max(ffn, ffn_workspace_bytes(sh));
+    }
+    L.ffn = take(ffn);
     L.total = off;
     return L;
 }
@@ -107,13 +145,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? COLIBRI_OK : COLIBRI_ERR
 template <class Ffn>
 int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r, void *out,
                        int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
-                       size_t ws_bytes, hipStream_t stream, const void *b2, int Sd, Ffn ffn) {
+                       size_t ws_bytes, hipStream_t stream, const void *b2, int Sd, Ffn ffn,
+                       const colibri_moe_layer_opts_t *opts = nullptr) {
     if (!x || !w_r || !out) return COLIBRI_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(out, 16) || (b_r && !aligned(b_r, 4)) ||
         (topk_idx_out && !aligned(topk_idx_out, 4)) || (topk_gate_out && !aligned(topk_gate_out, 4)) ||
         (expert_counts_out && !aligned(expert_counts_out, 4)))
         return COLIBRI_ERR_INVALID_ARG;
-    const LayerWorkspace L = layer_workspace(s);
+    const LayerWorkspace L = layer_workspace(s, opts);
     if (ws_bytes < L.total) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
 
@@ -127,12 +166,24 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
     void *y = base + L.y;
     void *ffn_ws = base + L.ffn;
 
+    const int gate_mode = opts ? opts->gate : COLIBRI_GATE_PAIR;
+    const void *residual = opts ? opts->residual : nullptr;
+    void *sh_y = has_shared(opts) ? base + L.sh_y : nullptr;
+
     hipError_t e;
     if (route_dispatch_fusable(*s)) {
-        e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream);
+        e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream, gate_mode);
     } else {
-        e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream);
+        e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream, gate_mode);
         if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
+    }
+    if (e == hipSuccess && sh_y) {
+        // the shared expert over all T rows of x, before the routed FFN takes the FFN region
+        const colibri_moe_shape_t sh = shared_shape(s, opts);
+        int32_t *sh_off = reinterpret_cast<int32_t *>(base + L.sh_offsets);
+        e = launch_pair_offsets(sh_off, s->T, stream);
+        if (e == hipSuccess)
+            e = launch_ffn_layers(sh, x, nullptr, sh_off, *opts->shared, sh_y, ffn_ws, true, stream, nullptr);
     }
     if (e != hipSuccess) return hip_status(e);
     if (Sd > 1) {
@@ -140,11 +191,11 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
         e = ffn(sorted, offsets, nullptr, ffn_ws, false, &part);
         if (e == hipSuccess)
             e = launch_combine_partials(*s, part, Sd, pos, idx, gate, s->act == COLIBRI_ACT_SWIGLU ? nullptr : b2,
-                                        out, stream);
+                                        out, stream, sh_y, residual);
         return hip_status(e);
     }
     e = ffn(sorted, offsets, y, ffn_ws, true, nullptr);
-    if (e == hipSuccess) e = launch_combine(*s, y, pos, gate, out, stream);
+    if (e == hipSuccess) e = launch_combine(*s, y, pos, gate, out, stream, sh_y, residual);
     return hip_status(e);
 }
 
@@ -314,6 +365,58 @@ int colibri_moe_quantize_q8(const void *w, colibri_dtype_t dtype, int32_t E, int
     if ((int64_t)E * K * N > ((int64_t)1 << 40)) return COLIBRI_ERR_UNSUPPORTED;
     if (!aligned(w, 16) || !aligned(q, 4) || !aligned(scale, 4)) return COLIBRI_ERR_INVALID_ARG;
     return hip_status(launch_quantize_q8(w, dtype, E, K, N, q, scale, stream));
+}
+
+size_t colibri_moe_workspace_size_ex(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *opts) {
+    if (check_shape(s) != COLIBRI_OK || s->T == 0 || check_opts(s, opts) != COLIBRI_OK) return 0;
+    return layer_workspace(s, opts).total;
+}
+
+int colibri_moe_route_ex(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                         colibri_gate_t gate, int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (gate != COLIBRI_GATE_PAIR && gate != COLIBRI_GATE_SOFTMAX && gate != COLIBRI_GATE_LINEAR)
+        return COLIBRI_ERR_UNSUPPORTED;
+    if (s->T == 0) return COLIBRI_OK;
+    if (!x || !w_r || !topk_idx || !topk_gate) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(topk_idx, 4) || !aligned(topk_gate, 4) ||
+        (b_r && !aligned(b_r, 4)) || (logits && !aligned(logits, 4)))
+        return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_route(*s, x, w_r, b_r, topk_idx, topk_gate, logits, stream, gate));
+}
+
+int colibri_moe_combine_ex(const colibri_moe_shape_t *s, const void *y_sorted, const int32_t *assign_pos,
+                           const float *topk_gate, const void *shared_y, const void *residual, void *out,
+                           hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    if (!y_sorted || !assign_pos || !topk_gate || !out) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(y_sorted, 16) || !aligned(out, 16) || !aligned(assign_pos, 4) || !aligned(topk_gate, 4) ||
+        (shared_y && !aligned(shared_y, 16)) || (residual && !aligned(residual, 16)))
+        return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_combine(*s, y_sorted, assign_pos, topk_gate, out, stream, shared_y, residual));
+}
+
+int colibri_moe_layer_forward_ex(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                                 const colibri_moe_experts_t *w, const colibri_moe_layer_opts_t *opts, void *out,
+                                 int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    st = check_opts(s, opts);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts(s, w);
+    if (st != COLIBRI_OK) return st;
+    return layer_forward_impl(
+        s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes, stream, w->b2,
+        ffn_down_splits(*s),
+        [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce, const float **part) {
+            return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream, part);
+        },
+        opts);
 }
 
 const char *colibri_moe_status_string(int status) {

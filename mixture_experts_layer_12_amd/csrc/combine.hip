@@ -5,6 +5,13 @@
 // aggregation: the expert outputs are summed weighted by their gating scores).
 //
 //   out[t] = g[t,0] * Y[assign_pos[2t]] + g[t,1] * Y[assign_pos[2t+1]]
+//            (+ shared[t], a shared expert's output, + residual[t], when given)
+//
+// The optional addends follow [rkmt] http://news.rkmt.cn/news/2271114 section
+// 5.2 (a shared expert applied to every token beside the routed ones) and
+// [nxbn] section 2.1 (residual add fused into the expert computation): both
+// are added in fp32 after the gated pair, in that order, before the one
+// rounding.
 //
 // Design: a pure streaming kernel (reads 2 rows, writes 1 row per token).
 // Each thread handles one 16-byte vector of a token row; rows are read with
@@ -18,10 +25,29 @@
 namespace colibri {
 namespace {
 
+// o[q] += shared[t][c + q], then residual[t][c + q] (each optional)
+template <typename TE, int VEC>
+__device__ __forceinline__ void add_addends(float (&o)[VEC], const TE *__restrict__ shared,
+                                            const TE *__restrict__ residual, size_t at) {
+    if (shared) {
+        float v[VEC];
+        Vec16<TE>::load(shared + at, v);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) o[q] += v[q];
+    }
+    if (residual) {
+        float v[VEC];
+        Vec16<TE>::load(residual + at, v);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) o[q] += v[q];
+    }
+}
+
 template <typename TE>
 __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, const int32_t *__restrict__ pos,
                                                       const float *__restrict__ gate, TE *__restrict__ out, int T,
-                                                      int d) {
+                                                      int d, const TE *__restrict__ shared,
+                                                      const TE *__restrict__ residual) {
     constexpr int VEC = 16 / sizeof(TE);
     const int vpr = d / VEC;  // vectors per row
     const size_t total = (size_t)T * vpr;
@@ -40,17 +66,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, 
         else
 #pragma unroll
             for (int q = 0; q < VEC; ++q) y1[q] = 0.0f;
+        float o[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) o[q] = fmaf(g1, y1[q], g0 * y0[q]);
+        add_addends<TE, VEC>(o, shared, residual, (size_t)t * d + c);
         if constexpr (sizeof(TE) == 4) {
-            f32x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = fmaf(g1, y1[q], g0 * y0[q]);
-            *reinterpret_cast<f32x4 *>(out + (size_t)t * d + c) = o;
+            *reinterpret_cast<f32x4 *>(out + (size_t)t * d + c) = f32x4{o[0], o[1], o[2], o[3]};
         } else {
-            u32x4 o;
+            u32x4 ov;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                o[q] = pack_bf16x2(fmaf(g1, y1[2 * q], g0 * y0[2 * q]), fmaf(g1, y1[2 * q + 1], g0 * y0[2 * q + 1]));
-            *reinterpret_cast<u32x4 *>(out + (size_t)t * d + c) = o;
+            for (int q = 0; q < 4; ++q) ov[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
+            *reinterpret_cast<u32x4 *>(out + (size_t)t * d + c) = ov;
         }
     }
 }
@@ -67,7 +93,9 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                                                                const int32_t *__restrict__ idx,
                                                                const float *__restrict__ gate,
                                                                const uint16_t *__restrict__ b2, int E,
-                                                               uint16_t *__restrict__ out, int T, int d) {
+                                                               uint16_t *__restrict__ out, int T, int d,
+                                                               const uint16_t *__restrict__ shared,
+                                                               const uint16_t *__restrict__ residual) {
     typedef float fv __attribute__((ext_vector_type(VEC)));
     const int vpr = d / VEC;
     const size_t total = (size_t)T * vpr;
@@ -127,6 +155,14 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                 o[q] = sl == 0 ? g * yr : fmaf(g, yr, o[q]);
             }
         }
+        if (shared || residual) {
+            const size_t at = (size_t)t * d + c;
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) {
+                if (shared) o[q] += bf16_to_f32(shared[at + q]);
+                if (residual) o[q] += bf16_to_f32(residual[at + q]);
+            }
+        }
         uint16_t *dst = out + (size_t)t * d + c;
         if constexpr (VEC == 4) {
             *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
@@ -139,26 +175,41 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
 }  // namespace
 
 hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, const int32_t *assign_pos,
-                          const float *topk_gate, void *out, hipStream_t st) {
+                          const float *topk_gate, void *out, hipStream_t st, const void *shared,
+                          const void *residual) {
     const int vec = s.dtype == COLIBRI_F32 ? 4 : 8;
     const size_t total = (size_t)s.T * (s.d / vec);
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
     if (s.dtype == COLIBRI_F32)
         combine_kernel<float><<<blocks, 256, 0, st>>>((const float *)y_sorted, assign_pos, topk_gate, (float *)out,
-                                                      s.T, s.d);
+                                                      s.T, s.d, (const float *)shared, (const float *)residual);
     else
         combine_kernel<uint16_t><<<blocks, 256, 0, st>>>((const uint16_t *)y_sorted, assign_pos, topk_gate,
-                                                         (uint16_t *)out, s.T, s.d);
+                                                         (uint16_t *)out, s.T, s.d, (const uint16_t *)shared,
+                                                         (const uint16_t *)residual);
     return hipGetLastError();
 }
 
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
-                                   hipStream_t st) {
+                                   hipStream_t st, const void *shared, const void *residual) {
     const size_t total = (size_t)s.T * (s.d / 4);
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
     combine_partials_kernel<4, 16><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
-                                                          (const uint16_t *)b2, s.E, (uint16_t *)out, s.T, s.d);
+                                                          (const uint16_t *)b2, s.E, (uint16_t *)out, s.T, s.d,
+                                                          (const uint16_t *)shared, (const uint16_t *)residual);
+    return hipGetLastError();
+}
+
+namespace {
+__global__ void pair_offsets_kernel(int32_t *o, int n) {
+    if (threadIdx.x == 0) o[0] = 0;
+    if (threadIdx.x == 1) o[1] = n;
+}
+}  // namespace
+
+hipError_t launch_pair_offsets(int32_t *offsets, int n, hipStream_t st) {
+    pair_offsets_kernel<<<1, 64, 0, st>>>(offsets, n);
     return hipGetLastError();
 }
 

@@ -11,8 +11,10 @@
 
 namespace colibri {
 
+// gate_mode: a colibri_gate_t
 hipError_t launch_route(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
-                        int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t st);
+                        int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t st,
+                        int gate_mode = COLIBRI_GATE_PAIR);
 
 // route + dispatch in one launch for small batches (E <= 8, at most 2 token
 // groups of 64 / E rounded up to a power of two tokens); the results equal
@@ -20,7 +22,8 @@ hipError_t launch_route(const colibri_moe_shape_t &s, const void *x, const void 
 bool route_dispatch_fusable(const colibri_moe_shape_t &s);
 hipError_t launch_route_dispatch(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
                                  int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
-                                 int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st);
+                                 int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st,
+                                 int gate_mode = COLIBRI_GATE_PAIR);
 
 hipError_t launch_dispatch(const colibri_moe_shape_t &s, const int32_t *topk_idx, int32_t *counts,
                            int32_t *offsets, int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st);
@@ -83,9 +86,10 @@ hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const
 // the scratch then holds the first layer's partials, then (256-aligned) the second's.
 bool decode_fuse_h(const colibri_moe_shape_t &s, bool q8 = false);
 // combine straight from the second layer's S split partials (adds them, b2, rounds Y, then gates)
+// shared, residual: optional [T, d] dtype addends (as in launch_combine)
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
-                                   hipStream_t st);
+                                   hipStream_t st, const void *shared = nullptr, const void *residual = nullptr);
 // bf16 grouped MFMA GEMMs for T > 64 (ffn_gemm.hip).  A layer whose K is split
 // (gemm_splits > 1) writes fp32 partials [S][2T][cols] to scratch and then
 // reduces them (the second layer only when `reduce`; otherwise
@@ -129,8 +133,13 @@ hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, c
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
                              hipStream_t st);
 
+// shared, residual: optional [T, d] dtype rows added after the gated pair
 hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, const int32_t *assign_pos,
-                          const float *topk_gate, void *out, hipStream_t st);
+                          const float *topk_gate, void *out, hipStream_t st, const void *shared = nullptr,
+                          const void *residual = nullptr);
+// offsets[0] = 0, offsets[1] = n (a one-expert group of n rows) by a kernel,
+// so the step can sit in a captured graph
+hipError_t launch_pair_offsets(int32_t *offsets, int n, hipStream_t st);
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 

@@ -139,10 +139,15 @@ __device__ __forceinline__ float route_wave_partial(const TI *__restrict__ x, co
 // Top-2 and gates of token group t0 from the full logits (lane l: token
 // t0 + l / EP, expert l % EP; bias not yet added).  sidx, when given, receives
 // the chosen experts at [2 (t - t_base)] (an LDS copy for a fused dispatch).
+// Gates (colibri_gate_t): softmax over the chosen pair, g0 = 1 / (1 + e^(l1 - l0))
+// and g1 = 1 - g0; softmax over all experts, the pair taken unnormalised
+// (DeepSeek-MoE, [rkmt] section 5.2): g = e^(l - l0) / sum_e e^(l_e - l0), the
+// sum formed by a fixed xor-shuffle tree over the expert lanes; or the two
+// logits themselves (LINEAR_SCORE, [zskr] section 2.3: no softmax).
 template <int EP>
 __device__ __forceinline__ void route_select(float lg, const float *__restrict__ b_r, int T, int E, int t0,
                                              int32_t *__restrict__ topk_idx, float *__restrict__ topk_gate,
-                                             float *__restrict__ logits, int32_t *sidx) {
+                                             float *__restrict__ logits, int32_t *sidx, int gate_mode) {
     const int lane = threadIdx.x & (kWave - 1);
     const int tt = lane / EP;
     const int e = lane % EP;
@@ -160,12 +165,25 @@ __device__ __forceinline__ void route_select(float lg, const float *__restrict__
     int i2 = e;
     segment_argmax<EP>(c2, v2, i2);
 
+    float g0, g1;
+    if (gate_mode == COLIBRI_GATE_SOFTMAX) {
+        float z = (valid && !__builtin_isnan(lg)) ? expf(lg - v1) : 0.0f;
+#pragma unroll
+        for (int s = 1; s < EP; s <<= 1) z += __shfl_xor(z, s);
+        g0 = 1.0f / z;
+        g1 = expf(v2 - v1) / z;
+    } else if (gate_mode == COLIBRI_GATE_LINEAR) {
+        g0 = v1;
+        g1 = v2;
+    } else {
+        g0 = 1.0f / (1.0f + expf(v2 - v1));
+        g1 = 1.0f - g0;
+    }
     if (e == 0 && t < T) {
-        const float g0 = 1.0f / (1.0f + expf(v2 - v1));
         topk_idx[2 * t] = i1;
         topk_idx[2 * t + 1] = i2;
         topk_gate[2 * t] = g0;
-        topk_gate[2 * t + 1] = 1.0f - g0;
+        topk_gate[2 * t + 1] = g1;
         if (sidx != nullptr) {
             sidx[2 * t] = i1;
             sidx[2 * t + 1] = i2;
@@ -178,7 +196,7 @@ __device__ __forceinline__ void route_select(float lg, const float *__restrict__
 template <typename TI, int EP, bool FULL, bool SPLITD>
 __global__ __launch_bounds__(SPLITD ? kRouteMaxW * kWave : kRouteThreads) void route_kernel(
     const TI *__restrict__ x, const TI *__restrict__ w_r, const float *__restrict__ b_r, int T, int d, int E,
-    int32_t *__restrict__ topk_idx, float *__restrict__ topk_gate, float *__restrict__ logits) {
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_gate, float *__restrict__ logits, int gate_mode) {
     constexpr int TPW = kWave / EP;
     constexpr int VEC = Vec16<TI>::N;
     const int lane = threadIdx.x & (kWave - 1);
@@ -199,7 +217,7 @@ __global__ __launch_bounds__(SPLITD ? kRouteMaxW * kWave : kRouteThreads) void r
         for (int q = 1; q < W; ++q) sum += red[q][lane];
         lg = sum;
     }
-    route_select<EP>(lg, b_r, T, E, t0, topk_idx, topk_gate, logits, nullptr);
+    route_select<EP>(lg, b_r, T, E, t0, topk_idx, topk_gate, logits, nullptr, gate_mode);
 }
 
 // Small batches: routing and dispatch in one workgroup of 8 waves.  The token
@@ -210,7 +228,8 @@ template <typename TI, int EP, bool FULL>
 __global__ __launch_bounds__(kFusedWaves *kWave) void route_dispatch_kernel(
     const TI *__restrict__ x, const TI *__restrict__ w_r, const float *__restrict__ b_r, int T, int d, int E, int W,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_gate, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_assign, int32_t *__restrict__ assign_pos) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_assign, int32_t *__restrict__ assign_pos,
+    int gate_mode) {
     constexpr int TPW = kWave / EP;
     constexpr int VEC = Vec16<TI>::N;
     constexpr int kMaxA = 2 * kFusedWaves * TPW;  // assignments of kFusedWaves token groups
@@ -227,7 +246,7 @@ __global__ __launch_bounds__(kFusedWaves *kWave) void route_dispatch_kernel(
     if (gi < G && wib == 0) {
         float sum = red[w][lane];
         for (int q = 1; q < W; ++q) sum += red[w + q][lane];
-        route_select<EP>(sum, b_r, T, E, gi * TPW, topk_idx, topk_gate, nullptr, sidx);
+        route_select<EP>(sum, b_r, T, E, gi * TPW, topk_idx, topk_gate, nullptr, sidx, gate_mode);
     }
     __syncthreads();
     dispatch_block<kFusedWaves>([&](int a) { return sidx[a]; }, 2 * T, E, counts, offsets, sorted_assign, assign_pos,
@@ -250,14 +269,14 @@ inline int route_waves(int T, int d, int EP, int VEC) {
 
 template <typename TI, int EP>
 hipError_t launch_ep(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r, int32_t *idx,
-                     float *gate, float *logits, hipStream_t st) {
+                     float *gate, float *logits, int gate_mode, hipStream_t st) {
     constexpr int TPW = kWave / EP;
     constexpr int VEC = Vec16<TI>::N;
     const int groups = ceil_div(s.T, TPW);
     const int W = route_waves(s.T, s.d, EP, VEC);
 #define COLIBRI_ROUTE_LAUNCH(FULLV, SPLITV, BLOCKS, THREADS)                                      \
     route_kernel<TI, EP, FULLV, SPLITV><<<BLOCKS, THREADS, 0, st>>>((const TI *)x, (const TI *)w_r, b_r, s.T, s.d, \
-                                                                  s.E, idx, gate, logits)
+                                                                  s.E, idx, gate, logits, gate_mode)
     if (W > 1) {
         if (s.E == EP) COLIBRI_ROUTE_LAUNCH(true, true, groups, W * kWave);
         else COLIBRI_ROUTE_LAUNCH(false, true, groups, W * kWave);
@@ -273,13 +292,13 @@ hipError_t launch_ep(const colibri_moe_shape_t &s, const void *x, const void *w_
 template <typename TI, int EP>
 hipError_t launch_fused_ep(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
                            int32_t *idx, float *gate, int32_t *counts, int32_t *offsets, int32_t *sorted,
-                           int32_t *pos, hipStream_t st) {
+                           int32_t *pos, int gate_mode, hipStream_t st) {
     constexpr int VEC = Vec16<TI>::N;
     const int W = route_waves(s.T, s.d, EP, VEC);
 #define COLIBRI_FUSED_LAUNCH(FULLV)                                                                          \
     route_dispatch_kernel<TI, EP, FULLV><<<1, kFusedWaves * kWave, 0, st>>>((const TI *)x, (const TI *)w_r, b_r, s.T, \
                                                                        s.d, s.E, W, idx, gate, counts, offsets,    \
-                                                                       sorted, pos)
+                                                                       sorted, pos, gate_mode)
     if (s.E == EP) COLIBRI_FUSED_LAUNCH(true);
     else COLIBRI_FUSED_LAUNCH(false);
 #undef COLIBRI_FUSED_LAUNCH
@@ -288,30 +307,30 @@ hipError_t launch_fused_ep(const colibri_moe_shape_t &s, const void *x, const vo
 
 template <typename TI>
 hipError_t launch_t(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r, int32_t *idx,
-                    float *gate, float *logits, hipStream_t st) {
-    if (s.E <= 2) return launch_ep<TI, 2>(s, x, w_r, b_r, idx, gate, logits, st);
-    if (s.E <= 4) return launch_ep<TI, 4>(s, x, w_r, b_r, idx, gate, logits, st);
-    if (s.E <= 8) return launch_ep<TI, 8>(s, x, w_r, b_r, idx, gate, logits, st);
-    if (s.E <= 16) return launch_ep<TI, 16>(s, x, w_r, b_r, idx, gate, logits, st);
-    if (s.E <= 32) return launch_ep<TI, 32>(s, x, w_r, b_r, idx, gate, logits, st);
-    return launch_ep<TI, 64>(s, x, w_r, b_r, idx, gate, logits, st);
+                    float *gate, float *logits, int gm, hipStream_t st) {
+    if (s.E <= 2) return launch_ep<TI, 2>(s, x, w_r, b_r, idx, gate, logits, gm, st);
+    if (s.E <= 4) return launch_ep<TI, 4>(s, x, w_r, b_r, idx, gate, logits, gm, st);
+    if (s.E <= 8) return launch_ep<TI, 8>(s, x, w_r, b_r, idx, gate, logits, gm, st);
+    if (s.E <= 16) return launch_ep<TI, 16>(s, x, w_r, b_r, idx, gate, logits, gm, st);
+    if (s.E <= 32) return launch_ep<TI, 32>(s, x, w_r, b_r, idx, gate, logits, gm, st);
+    return launch_ep<TI, 64>(s, x, w_r, b_r, idx, gate, logits, gm, st);
 }
 
 template <typename TI>
 hipError_t launch_fused_t(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
                           int32_t *idx, float *gate, int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *pos,
-                          hipStream_t st) {
-    if (s.E <= 2) return launch_fused_ep<TI, 2>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, st);
-    if (s.E <= 4) return launch_fused_ep<TI, 4>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, st);
-    return launch_fused_ep<TI, 8>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, st);
+                          int gm, hipStream_t st) {
+    if (s.E <= 2) return launch_fused_ep<TI, 2>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, gm, st);
+    if (s.E <= 4) return launch_fused_ep<TI, 4>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, gm, st);
+    return launch_fused_ep<TI, 8>(s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, gm, st);
 }
 
 }  // namespace
 
 hipError_t launch_route(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
-                        int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t st) {
-    if (s.dtype == COLIBRI_F32) return launch_t<float>(s, x, w_r, b_r, topk_idx, topk_gate, logits, st);
-    return launch_t<uint16_t>(s, x, w_r, b_r, topk_idx, topk_gate, logits, st);
+                        int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t st, int gate_mode) {
+    if (s.dtype == COLIBRI_F32) return launch_t<float>(s, x, w_r, b_r, topk_idx, topk_gate, logits, gate_mode, st);
+    return launch_t<uint16_t>(s, x, w_r, b_r, topk_idx, topk_gate, logits, gate_mode, st);
 }
 
 // E <= 8 and at most kFusedGroups token groups (T <= 16 for E = 8)
@@ -323,12 +342,12 @@ bool route_dispatch_fusable(const colibri_moe_shape_t &s) {
 
 hipError_t launch_route_dispatch(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
                                  int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
-                                 int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st) {
+                                 int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st, int gate_mode) {
     if (s.dtype == COLIBRI_F32)
         return launch_fused_t<float>(s, x, w_r, b_r, topk_idx, topk_gate, counts, offsets, sorted_assign, assign_pos,
-                                     st);
+                                     gate_mode, st);
     return launch_fused_t<uint16_t>(s, x, w_r, b_r, topk_idx, topk_gate, counts, offsets, sorted_assign, assign_pos,
-                                    st);
+                                    gate_mode, st);
 }
 
 }  // namespace colibri

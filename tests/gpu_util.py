@@ -210,5 +210,37 @@ class Layer:
                                       idx_override=idx_override)
 
 
+    # ---- gating variants, shared expert, residual
+    @property
+    def h_shared(self) -> Dict:
+        return _host_shared(self.key)
+
+    @property
+    def d_shared(self) -> Dict:
+        return _device_shared(self.key)
+
+    @property
+    def residual(self) -> np.ndarray:
+        return gen.make_residual(self.cfg, self.T)
+
+    def oracle_tokens_ex(self, tokens, idx_override=None, gate="pair", shared=False, residual=False):
+        w = self.hw
+        return oracle.layer_tokens(self.x, w["w_r"], w["w1"], w["w2"], self.cfg.act, tokens, b_r=w["b_r"],
+                                   w3=w["w3"], b1=w["b1"], b2=w["b2"], mirror=True, idx_override=idx_override,
+                                   gate=gate, shared=self.h_shared if shared else None,
+                                   residual=self.residual if residual else None)
+
+
+@functools.lru_cache(maxsize=2)
+def _host_shared(key: str):
+    cfg = gen.CONFIGS[key]
+    return gen.make_shared_expert(cfg)
+
+
+@functools.lru_cache(maxsize=2)
+def _device_shared(key: str):
+    return {k: dev(v) for k, v in _host_shared(key).items()}
+
+
 def seeded_layer(key: str, T: int) -> Layer:
     return Layer(key, T)

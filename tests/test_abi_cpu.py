@@ -232,3 +232,76 @@ def test_quantize_checks(lib):
     assert call(dtype=5) == moe.COLIBRI_ERR_UNSUPPORTED
     assert call(w=fake(0) + 8) == moe.COLIBRI_ERR_INVALID_ARG
     assert call(sc=fake(2) + 1) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ gating variants, shared expert, residual
+def opts_c(gate=moe.GATE_PAIR, shared=None, shared_h=0, residual=None):
+    return moe._Opts(gate, ctypes.pointer(shared) if shared is not None else None, shared_h, residual)
+
+
+def layer_ex_call(lib, s, o, ws_bytes=1 << 40, e=None):
+    e = e or moe._Experts(fake(4), fake(5), fake(6), None, None)
+    return lib.colibri_moe_layer_forward_ex(ctypes.byref(s), fake(0), fake(1), None, ctypes.byref(e),
+                                            ctypes.byref(o) if o is not None else None, fake(3), None, None, None,
+                                            fake(20), ws_bytes, None)
+
+
+def test_workspace_size_ex(lib):
+    s = shape_c()
+    plain = lib.colibri_moe_workspace_size(ctypes.byref(s))
+    assert lib.colibri_moe_workspace_size_ex(ctypes.byref(s), None) == plain
+    for gate in (moe.GATE_PAIR, moe.GATE_SOFTMAX, moe.GATE_LINEAR):
+        o = opts_c(gate=gate, residual=fake(30))
+        assert lib.colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(o)) == plain
+    sh = moe._Experts(fake(7), fake(8), fake(9), None, None)
+    with_shared = lib.colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(opts_c(shared=sh)))
+    wider = lib.colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(opts_c(shared=sh, shared_h=4096)))
+    assert plain < with_shared < wider
+    # invalid options size nothing
+    assert lib.colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(opts_c(gate=3))) == 0
+    assert lib.colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(opts_c(shared=sh, shared_h=96))) == 0
+
+
+def test_layer_ex_checks(lib):
+    s = shape_c()
+    sh = moe._Experts(fake(7), fake(8), fake(9), None, None)
+    need = lib.colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(opts_c(shared=sh)))
+    assert layer_ex_call(lib, s, opts_c(shared=sh), ws_bytes=need - 1) == moe.COLIBRI_ERR_WORKSPACE
+    assert layer_ex_call(lib, s, opts_c(gate=-1)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert layer_ex_call(lib, s, opts_c(gate=3)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert layer_ex_call(lib, s, opts_c(residual=fake(30) + 8)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert layer_ex_call(lib, s, opts_c(shared=sh, shared_h=-64)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert layer_ex_call(lib, s, opts_c(shared=sh, shared_h=100)) == moe.COLIBRI_ERR_UNSUPPORTED
+    # the shared expert is checked like the routed ones (SwiGLU: W1, W3, W2 and no biases)
+    for bad, code in ((moe._Experts(None, fake(8), fake(9), None, None), moe.COLIBRI_ERR_INVALID_ARG),
+                      (moe._Experts(fake(7), None, fake(9), None, None), moe.COLIBRI_ERR_INVALID_ARG),
+                      (moe._Experts(fake(7), fake(8), None, None, None), moe.COLIBRI_ERR_INVALID_ARG),
+                      (moe._Experts(fake(7) + 4, fake(8), fake(9), None, None), moe.COLIBRI_ERR_INVALID_ARG),
+                      (moe._Experts(fake(7), fake(8), fake(9), fake(10), None), moe.COLIBRI_ERR_UNSUPPORTED)):
+        assert layer_ex_call(lib, s, opts_c(shared=bad)) == code
+    # the routed experts are still checked
+    e = moe._Experts(fake(4), None, fake(6), None, None)
+    assert layer_ex_call(lib, s, None, e=e) == moe.COLIBRI_ERR_INVALID_ARG
+    # T = 0: a no-op with null pointers, but options are still validated
+    z = shape_c(T=0)
+    ez = moe._Experts(None, None, None, None, None)
+    assert lib.colibri_moe_layer_forward_ex(ctypes.byref(z), None, None, None, ctypes.byref(ez), None, None, None,
+                                            None, None, None, 0, None) == 0
+    assert lib.colibri_moe_layer_forward_ex(ctypes.byref(z), None, None, None, ctypes.byref(ez),
+                                            ctypes.byref(opts_c(gate=7)), None, None, None, None, None, 0,
+                                            None) == moe.COLIBRI_ERR_UNSUPPORTED
+
+
+def test_route_and_combine_ex_checks(lib):
+    s = shape_c()
+    r = lambda gate, x=fake(0): lib.colibri_moe_route_ex(ctypes.byref(s), x, fake(1), None, gate, fake(2), fake(3),
+                                                         None, None)
+    assert r(3) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert r(-1) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert r(moe.GATE_SOFTMAX, x=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert r(moe.GATE_LINEAR, x=fake(0) + 2) == moe.COLIBRI_ERR_INVALID_ARG
+    c = lambda sh=None, res=None, y=fake(0): lib.colibri_moe_combine_ex(ctypes.byref(s), y, fake(1), fake(2), sh,
+                                                                        res, fake(3), None)
+    assert c(sh=fake(4) + 8) == moe.COLIBRI_ERR_INVALID_ARG
+    assert c(res=fake(5) + 2) == moe.COLIBRI_ERR_INVALID_ARG
+    assert c(y=None) == moe.COLIBRI_ERR_INVALID_ARG

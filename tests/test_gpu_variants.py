@@ -1,0 +1,314 @@
+"""GPU parity of the layer variants against the fp64 oracle: the three gatings
+of the chosen pair (pair softmax, softmax over all experts, raw logits), an
+always-on shared expert, and the residual add fused into the combine.
+
+Same bar as the other parity tests: indices bit-exact outside near ties,
+fp32 values within a per-row relative error of 1e-4, bf16 values within
+|a - b| <= 1e-2 + 2e-2 |b|.
+"""
+import numpy as np
+import pytest
+
+import gen
+import mixture_experts_layer_12_amd as moe
+import oracle
+from tests import gpu_util as G
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+GATES = ("pair", "softmax", "linear")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    return moe.load(build_if_missing=True)
+
+
+# ------------------------------------------------------------------ router
+def run_route_ex(shape, x, w_r, b_r, gate):
+    idx = G.empty((shape.T, 2), torch.int32)
+    g = G.empty((shape.T, 2), torch.float32)
+    lg = G.empty((shape.T, shape.E), torch.float32)
+    moe.route_ex(shape, x, w_r, b_r, gate, idx, g, lg)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), g.cpu().numpy(), lg.cpu().numpy()
+
+
+def check_gates(gate_mode, idx, g, lg_gpu, lg_ref, tag):
+    rows = np.arange(idx.shape[0])
+    if gate_mode == "linear":
+        # the gates are the kernel's own logits of the chosen pair, exactly
+        assert np.array_equal(g[:, 0], lg_gpu[rows, idx[:, 0]]), f"{tag}: linear gate 0"
+        assert np.array_equal(g[:, 1], lg_gpu[rows, idx[:, 1]]), f"{tag}: linear gate 1"
+        return
+    G.assert_fp32_close(g, oracle.gates(lg_ref, idx, mode=gate_mode), f"{tag} gates")
+    assert np.all(g[:, 0] >= g[:, 1]), f"{tag}: slot 0 carries the larger gate"
+    if gate_mode == "softmax":
+        assert np.all(g.sum(1) <= 1.0 + 1e-6), f"{tag}: softmax gates are a part of one"
+    else:
+        assert np.all(g.sum(1) == np.float32(1.0))
+
+
+ROUTE_CASES = [("tiny", 32), ("e8", 64), ("e8", 512), ("shared15", 512), ("mixtral_decode", 4), ("skew16", 8192)]
+
+
+@pytest.mark.parametrize("gate", GATES)
+@pytest.mark.parametrize("key,T", ROUTE_CASES, ids=[f"{k}-T{t}" for k, t in ROUTE_CASES])
+def test_route_gate_modes(key, T, gate):
+    layer = G.seeded_layer(key, T)
+    r = G.device_router(key)
+    idx, g, lg = run_route_ex(layer.shape, G.dev(layer.x), r["w_r"], r["b_r"], gate)
+    w = G.host_router(key)
+    lg_ref = oracle.logits(layer.x, w["w_r"], w["b_r"])
+    G.assert_fp32_close(lg, lg_ref, f"{key}/T={T} logits")
+    # the selection does not depend on the gating
+    assert np.array_equal(oracle.top2(lg.astype(np.float64)), idx), "top-2 of own logits"
+    near = G.near_tie_mask(lg_ref)
+    diff = np.any(idx != oracle.top2(lg_ref), axis=1)
+    assert not np.any(diff & ~near)
+    check_gates(gate, idx, g, lg, lg_ref, f"{key}/T={T}/{gate}")
+    if gate == "pair":  # route_ex with the pair gating is route
+        idx2 = G.empty((T, 2), torch.int32)
+        g2 = G.empty((T, 2), torch.float32)
+        moe.route(layer.shape, G.dev(layer.x), r["w_r"], r["b_r"], idx2, g2)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx2.cpu().numpy(), idx) and np.array_equal(g2.cpu().numpy(), g)
+    G.report({"check": "route_ex", "case": f"{key}/T={T}/{gate}", "near_tie_tokens": int(near.sum())})
+
+
+@pytest.mark.parametrize("E", [2, 3, 16, 64])
+def test_route_gate_modes_ties(E):
+    """Integer data (exact logits, many ties) and an all-zero token."""
+    rng = np.random.default_rng(40 + E)
+    T, d = 77, 192
+    x = rng.integers(-2, 3, size=(T, d)).astype(np.float32)
+    w_r = rng.integers(-1, 2, size=(d, E)).astype(np.float32)
+    x[5] = 0.0
+    sh = moe.Shape(T, d, 64, E, gen.F32, moe.RELU)
+    lg_ref = oracle.logits(x, w_r)
+    for gate in GATES:
+        idx, g, lg = run_route_ex(sh, G.dev(x), G.dev(w_r), None, gate)
+        assert np.array_equal(lg.astype(np.float64), lg_ref)
+        assert np.array_equal(idx, oracle.top2(lg_ref))
+        check_gates(gate, idx, g, lg, lg_ref, f"ties E={E} {gate}")
+        zero = {"pair": [0.5, 0.5], "softmax": [1.0 / E, 1.0 / E], "linear": [0.0, 0.0]}[gate]
+        np.testing.assert_allclose(g[5], zero, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ combine with addends
+@pytest.mark.parametrize("addends", ["shared", "residual", "both"])
+@pytest.mark.parametrize("dt", [gen.F32, gen.BF16])
+def test_combine_ex_parity(dt, addends):
+    rng = np.random.default_rng(6)
+    T, d = 333, 448
+    ap = rng.permutation(2 * T).astype(np.int32)
+    g0 = rng.uniform(0.2, 0.7, T).astype(np.float32)
+    gate = np.stack([g0, rng.uniform(0.0, 0.3, T).astype(np.float32)], 1)
+    draw = lambda n: rng.standard_normal((n, d)).astype(np.float32)
+    cast = (lambda a: a) if dt == gen.F32 else gen.f32_to_bf16_bits
+    wide = (lambda a: a.astype(np.float64)) if dt == gen.F32 else (lambda a: gen.bf16_bits_to_f32(a).astype(np.float64))
+    y, shy, res = cast(draw(2 * T)), cast(draw(T)), cast(draw(T))
+    use_sh, use_res = addends in ("shared", "both"), addends in ("residual", "both")
+    sh = moe.Shape(T, d, 64, 4, dt, moe.RELU)
+    out = G.empty((T, d), G.tdtype(dt))
+    args = dict(shared_y=G.dev(shy) if use_sh else None, residual=G.dev(res) if use_res else None)
+    moe.combine_ex(sh, G.dev(y), G.dev(ap), G.dev(gate), out, **args)
+    # in place over the residual
+    inplace = args["residual"].clone() if use_res else None
+    if use_res:
+        moe.combine_ex(sh, G.dev(y), G.dev(ap), G.dev(gate), inplace, shared_y=args["shared_y"], residual=inplace)
+    torch.cuda.synchronize()
+    ref = oracle.combine(wide(y), ap, gate.astype(np.float64), dt, shared_y=wide(shy) if use_sh else None,
+                         residual=res if use_res else None)
+    G.assert_close(G.host(out), ref, dt, f"combine_ex {addends}")
+    if use_res:
+        assert torch.equal(inplace, out)
+
+
+# ------------------------------------------------------------------ whole layer
+def assert_bf16_close_gate_scaled(a, b, gate, what):
+    """The bf16 rule for outputs whose gates are not a convex pair (raw logits):
+    each token's bound is scaled by s = max(1, |g0| + |g1|).  The expert rows are
+    stored in bf16 on both sides; where the two round a row to neighbouring bf16
+    values, the output moves by up to |g| ulp(y), so the absolute bound of the
+    convex case (|g0| + |g1| = 1) grows with the gates' magnitude."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    s = np.maximum(1.0, np.abs(gate).sum(1))[:, None]
+    bad = np.abs(a - b) > (1e-2 + 2e-2 * np.abs(b)) * s
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} elements outside the gate-scaled bf16 bound"
+
+
+def run_layer_ex(layer, gate="pair", shared=False, residual=False, out=None, stream=None):
+    sh = layer.shape
+    dsh = layer.d_shared if shared else None
+    shared_h = layer.cfg.shared_h if shared else 0
+    res = G.dev(layer.residual) if residual else None
+    ws_bytes = moe.workspace_size_ex(sh, gate=gate, shared=dsh, shared_h=shared_h, residual=res)
+    assert ws_bytes > 0
+    ws = G.empty((ws_bytes,), torch.uint8)
+    out = G.empty((sh.T, sh.d), G.tdtype(sh.dtype)) if out is None else out
+    idx = G.empty((sh.T, 2), torch.int32)
+    g = G.empty((sh.T, 2), torch.float32)
+    counts = G.empty((sh.E,), torch.int32)
+    dw = layer.dw
+    moe.layer_forward_ex(sh, G.dev(layer.x), dw["w_r"], dw["b_r"], dw["w1"], dw["w2"], out, ws, ws_bytes,
+                         w3=dw["w3"], b1=dw["b1"], b2=dw["b2"], gate=gate, shared=dsh, shared_h=shared_h,
+                         residual=res, topk_idx=idx, topk_gate=g,
+                         counts=counts, stream=stream)
+    torch.cuda.synchronize()
+    return {"out": out, "idx": idx.cpu().numpy(), "gate": g.cpu().numpy(), "counts": counts.cpu().numpy()}
+
+
+# key, T, sampled tokens (None: all), gating, shared expert, residual
+LAYER_EX_CASES = [
+    ("tiny", 32, None, "softmax", True, True),
+    ("tiny", 32, None, "linear", False, True),
+    ("e8", 1, None, "softmax", True, True),
+    ("e8", 64, None, "linear", True, False),
+    ("e8", 512, 48, "pair", True, True),
+    ("shared15", 1, None, "softmax", True, False),
+    ("shared15", 64, None, "softmax", True, True),
+    ("shared15", 512, 48, "softmax", True, True),
+    ("mixtral_decode", 4, None, "pair", True, True),
+    ("mixtral_decode", 32, 6, "softmax", False, True),
+    ("mixtral_prefill", 4096, 10, "pair", True, True),
+    ("skew16", 8192, 24, "linear", False, True),
+]
+
+
+@pytest.mark.parametrize("key,T,sample,gate,shared,residual", LAYER_EX_CASES,
+                         ids=[f"{c[0]}-T{c[1]}-{c[3]}{'-shared' if c[4] else ''}{'-res' if c[5] else ''}"
+                              for c in LAYER_EX_CASES])
+def test_layer_ex_parity(key, T, sample, gate, shared, residual):
+    layer = G.seeded_layer(key, T)
+    r = run_layer_ex(layer, gate, shared, residual)
+    w = layer.hw
+    lg_ref = oracle.logits(layer.x, w["w_r"], w["b_r"])
+    near = G.near_tie_mask(lg_ref)
+    diff = np.any(r["idx"] != oracle.top2(lg_ref), axis=1)
+    assert not np.any(diff & ~near), f"{int((diff & ~near).sum())} non-near-tie tokens routed differently"
+    assert np.array_equal(r["counts"], oracle.dispatch(r["idx"], layer.cfg.E)["counts"])
+    out = G.host(r["out"])
+    assert np.all(np.isfinite(out))
+    rng = np.random.default_rng(T + 1)
+    toks = np.arange(T) if sample is None else np.sort(rng.choice(T, size=sample, replace=False))
+    toks = np.union1d(toks, np.flatnonzero(diff))
+    ref = layer.oracle_tokens_ex(toks, idx_override=r["idx"][toks], gate=gate, shared=shared, residual=residual)
+    if gate == "linear":
+        np.testing.assert_allclose(r["gate"][toks], ref["gate"], rtol=1e-4,
+                                   atol=1e-4 * np.abs(ref["logits"]).max())
+    else:
+        G.assert_fp32_close(r["gate"][toks], ref["gate"], f"{key}/T={T} gates")
+    if gate == "linear" and layer.cfg.dtype == gen.BF16:
+        assert_bf16_close_gate_scaled(out[toks], ref["out"], ref["gate"], f"{key}/T={T}/{gate} out")
+    else:
+        G.assert_close(out[toks], ref["out"], layer.cfg.dtype, f"{key}/T={T}/{gate} out")
+    G.report({"check": "layer_ex", "case": f"{key}/T={T}/{gate}/shared={shared}/residual={residual}",
+              "tokens_compared": int(len(toks)), "near_tie_tokens": int(near.sum()),
+              "index_mismatches_on_near_ties": int(diff.sum())})
+
+
+@pytest.mark.parametrize("key,T", [("e8", 1), ("e8", 64), ("mixtral_decode", 1), ("e8", 512), ("tiny", 32)])
+def test_layer_ex_plain_options_equal_layer(key, T):
+    """Pair gating with no shared expert and no residual is layer_forward, bit for bit."""
+    layer = G.seeded_layer(key, T)
+    sh = layer.shape
+    a = run_layer_ex(layer)
+    ws_bytes = moe.workspace_size(sh)
+    assert moe.workspace_size_ex(sh) == ws_bytes
+    ws = G.empty((ws_bytes,), torch.uint8)
+    out = G.empty((sh.T, sh.d), G.tdtype(sh.dtype))
+    dw = layer.dw
+    moe.layer_forward(sh, G.dev(layer.x), dw["w_r"], dw["b_r"], dw["w1"], dw["w2"], out, ws, ws_bytes, w3=dw["w3"],
+                      b1=dw["b1"], b2=dw["b2"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, a["out"])
+
+
+@pytest.mark.parametrize("key,T,gate", [("e8", 64, "softmax"), ("mixtral_decode", 1, "linear"),
+                                        ("e8", 512, "softmax"), ("shared15", 64, "linear")])
+def test_layer_ex_equals_composed_entry_points(key, T, gate):
+    """Without a shared expert, layer_forward_ex equals route_ex -> dispatch ->
+    expert_ffn -> combine_ex (with the residual) bit for bit."""
+    layer = G.seeded_layer(key, T)
+    r = run_layer_ex(layer, gate, residual=True)
+    sh = layer.shape
+    dr = G.device_router(key)
+    idx, g, _ = run_route_ex(sh, G.dev(layer.x), dr["w_r"], dr["b_r"], gate)
+    d = oracle.dispatch(idx, sh.E)
+    ws_bytes = moe.workspace_size(sh)
+    ws = G.empty((ws_bytes,), torch.uint8)
+    y = G.empty((2 * sh.T, sh.d), G.tdtype(sh.dtype))
+    dw = layer.dw
+    moe.expert_ffn(sh, G.dev(layer.x), G.dev(d["sorted_assign"]), G.dev(d["offsets"]), dw["w1"], dw["w2"], y, ws,
+                   ws_bytes, w3=dw["w3"], b1=dw["b1"], b2=dw["b2"])
+    out = G.empty((sh.T, sh.d), G.tdtype(sh.dtype))
+    moe.combine_ex(sh, y, G.dev(d["assign_pos"]), G.dev(g), out, residual=G.dev(layer.residual))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx, r["idx"]) and np.array_equal(g, r["gate"])
+    assert torch.equal(out, r["out"])
+
+
+@pytest.mark.parametrize("key,T", [("shared15", 64), ("mixtral_decode", 4), ("e8", 512)])
+def test_layer_ex_in_place_residual_and_deterministic(key, T):
+    """out may be the residual buffer; repeated calls (also on another stream) agree bit for bit."""
+    layer = G.seeded_layer(key, T)
+    a = run_layer_ex(layer, "softmax", shared=True, residual=True)
+    b = run_layer_ex(layer, "softmax", shared=True, residual=True)
+    assert torch.equal(a["out"], b["out"])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = run_layer_ex(layer, "softmax", shared=True, residual=True, stream=s)
+    assert torch.equal(a["out"], c["out"])
+    # in place: the residual rows are overwritten by the layer output
+    sh = layer.shape
+    buf = G.dev(layer.residual)
+    dsh = layer.d_shared
+    ws_bytes = moe.workspace_size_ex(sh, shared=dsh, shared_h=layer.cfg.shared_h, residual=buf)
+    ws = G.empty((ws_bytes,), torch.uint8)
+    dw = layer.dw
+    moe.layer_forward_ex(sh, G.dev(layer.x), dw["w_r"], dw["b_r"], dw["w1"], dw["w2"], buf, ws, ws_bytes,
+                         w3=dw["w3"], b1=dw["b1"], b2=dw["b2"], gate="softmax", shared=dsh,
+                         shared_h=layer.cfg.shared_h, residual=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, a["out"])
+
+
+def test_layer_ex_shared_expert_shapes():
+    """A shared expert wider or narrower than the routed ones, odd T (the
+    shared rows fill 2 ceil(T / 2) - 1 of the one-expert group), f32 and bf16."""
+    for dt, act, T, E, d, h, hs in ((gen.F32, "relu", 37, 5, 128, 192, 320), (gen.BF16, "gelu", 1, 8, 256, 384, 64),
+                                    (gen.BF16, "swiglu", 129, 6, 192, 256, 512),
+                                    (gen.BF16, "gelu", 63, 4, 256, 512, 1024)):
+        rng = np.random.default_rng(T + E + hs)
+        f = lambda shape, std: rng.standard_normal(shape).astype(np.float32) * std
+        w = {"x": f((T, d), 1.0), "w_r": f((d, E), d ** -0.5), "w1": f((E, d, h), d ** -0.5),
+             "w2": f((E, h, d), h ** -0.5), "w3": f((E, d, h), d ** -0.5) if act == "swiglu" else None,
+             "b1": f((E, h), 0.1) if act != "swiglu" else None, "b2": f((E, d), 0.1) if act != "swiglu" else None}
+        s = {"w1": f((1, d, hs), d ** -0.5), "w2": f((1, hs, d), hs ** -0.5),
+             "w3": f((1, d, hs), d ** -0.5) if act == "swiglu" else None,
+             "b1": f((1, hs), 0.1) if act != "swiglu" else None, "b2": f((1, d), 0.1) if act != "swiglu" else None}
+        res = f((T, d), 1.0)
+        if dt == gen.BF16:
+            w = {k: None if v is None else gen.f32_to_bf16_bits(v) for k, v in w.items()}
+            s = {k: None if v is None else gen.f32_to_bf16_bits(v) for k, v in s.items()}
+            res = gen.f32_to_bf16_bits(res)
+        shape = moe.Shape(T, d, h, E, dt, moe.ACT_CODES[act])
+        dw = {k: G.dev(v) for k, v in w.items()}
+        ds = {k: G.dev(v) for k, v in s.items()}
+        dres = G.dev(res)
+        ws_bytes = moe.workspace_size_ex(shape, shared=ds, shared_h=hs, residual=dres)
+        ws = G.empty((ws_bytes,), torch.uint8)
+        out = G.empty((T, d), G.tdtype(dt))
+        idx = G.empty((T, 2), torch.int32)
+        moe.layer_forward_ex(shape, dw["x"], dw["w_r"], None, dw["w1"], dw["w2"], out, ws, ws_bytes, w3=dw["w3"],
+                             b1=dw["b1"], b2=dw["b2"], gate="softmax", shared=ds, shared_h=hs, residual=dres,
+                             topk_idx=idx)
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy()
+        ref = oracle.layer_tokens(w["x"], w["w_r"], w["w1"], w["w2"], act, np.arange(T), w3=w["w3"], b1=w["b1"],
+                                  b2=w["b2"], mirror=True, idx_override=idx, gate="softmax", shared=s, residual=res)
+        G.assert_close(G.host(out), ref["out"], dt, f"shared expert {act} T={T} h_shared={hs}")
