@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-q8", action="store_true", help="skip the int8-weight decode lines")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the shared-expert / softmax-gating / residual layer lines")
+    ap.add_argument("--step-layers", type=int, default=8,
+                    help="layers of the multi-layer decode step timed eagerly and as a HIP graph (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle sample for about this long")
@@ -336,6 +338,11 @@ def main():
     if not args.no_variants:
         variants = time_variants(args, moe, gen, torch, np, to_dev, stream, prefill_queue)
 
+    # ---------------------------------------------------------------- multi-layer decode step
+    steps = {}
+    if args.step_layers > 0:
+        steps = time_steps(args, moe, gen, torch, np, to_dev, stream, prefill_queue)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -367,7 +374,7 @@ def main():
                    "T": T, "E": cfg.E, "d": cfg.d, "h": cfg.h, "act": cfg.act, "weight_copies": R,
                    "experts_hit": hit},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode, "decode_int8_weights": decode_q8,
-        "variants": variants,
+        "variants": variants, "multi_layer_step": steps,
         "timing": "GPU time (HIP events, queue pre-filled by a spin kernel)" if can_sleep else "GPU time (HIP events)",
     }
     print(json.dumps(rec), flush=True)
@@ -442,6 +449,80 @@ def time_variants(args, moe, gen, torch, np, to_dev, stream, prefill_queue):
     rec["workload"] = (f"{cfg.title}: E={cfg.E} routed + 1 shared (h_shared={cfg.shared_h}), top-2, d={cfg.d}, "
                        f"h={cfg.h}, {cfg.act}, bf16")
     del copies
+    return rec
+
+
+def time_steps(args, moe, gen, torch, np, to_dev, stream, prefill_queue):
+    """A decode step through L layers (x <- layer_l(x) + x, each layer with its
+    own weights), launched eagerly (colibri_moe_step_forward) and replayed as
+    one HIP graph (colibri_moe_graph_*): GPU time per step (median) and the
+    host-inclusive time of back-to-back steps.  L layers of distinct weights
+    (several GB) keep every step's weights out of the last-level cache."""
+    L = args.step_layers
+    rec = {}
+    for key, Ts, shared in (("e8", (1, 64), False), ("shared15", (1, 64), True)):
+        cfg = gen.CONFIGS[key]
+        layers, wbytes = [], []
+        for l in range(L):
+            c = gen.layer_of(cfg, l)
+            d = {k: to_dev(v) for k, v in gen.make_experts(c).items()}
+            d["w_r"] = to_dev(gen.make_router(c))
+            d["gate"] = "softmax" if shared else "pair"
+            eb = {k: (v[0].numel() * v.element_size() if v is not None else 0) for k, v in d.items()
+                  if k in ("w1", "w3", "w2", "b1", "b2")}
+            sb = 0
+            if shared:
+                d["shared"] = {k: to_dev(v) for k, v in gen.make_shared_expert(c).items()}
+                d["shared_h"] = cfg.shared_h
+                sb = sum(v.numel() * v.element_size() for v in d["shared"].values() if v is not None)
+            layers.append(d)
+            wbytes.append((sum(eb.values()), sb))
+        act = gen.ACT_CODE[cfg.act]
+        for T in Ts:
+            sh = moe.Shape(T, cfg.d, cfg.h, cfg.E, cfg.dtype, act)
+            ws_bytes = moe.step_workspace_size(sh, layers)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+            x0 = to_dev(gen.make_x(cfg, T))
+            x = x0.clone()
+            g = moe.Graph(sh, layers, x, ws, ws_bytes, residual=True)
+            out = {}
+            for name, fn in (("eager", lambda: moe.step_forward(sh, layers, x, ws, ws_bytes, residual=True)),
+                             ("graph", lambda: g.launch())):
+                times = []
+                iters = 100
+                for it in range(10 + iters):
+                    x.copy_(x0)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    if it % 10 == 0:
+                        prefill_queue()
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    if it % 10 == 9:
+                        torch.cuda.synchronize()
+                    if it >= 10:
+                        times.append((e0, e1))
+                torch.cuda.synchronize()
+                us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in times]))
+                h0 = time.perf_counter()
+                for it in range(iters):
+                    fn()
+                torch.cuda.synchronize()
+                host_us = (time.perf_counter() - h0) / iters * 1e6
+                out[name] = {"us_per_step_median": round(us, 1), "us_per_layer": round(us / L, 2),
+                             "us_per_step_host_inclusive": round(host_us, 1)}
+            g.destroy()
+            # weights of the experts a step reads: at T = 1 two per layer, at 64 every one (seeded routing)
+            routed_e = min(cfg.E, 2 * T)
+            byt = sum(routed_e * eb + sb for eb, sb in wbytes)
+            for v in out.values():
+                v["hbm_frac_weights"] = round(byt / (v["us_per_step_median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            rec[f"{key} L={L} T={T}"] = out
+            log(f"step {key} L={L} T={T}: {out}")
+    rec["workload"] = (f"{L} layers in place with residual, each with its own weights: the 8-expert 1.3B-class "
+                       f"layer (pair gating), and the 15 routed + 1 shared expert layer (softmax gating; in the "
+                       f"graph each layer's shared expert runs on a parallel branch)")
     return rec
 
 

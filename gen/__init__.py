@@ -193,6 +193,13 @@ def make_residual(cfg: Config, T: int) -> np.ndarray:
     return normal(cfg.seed, TID_RES, (T, cfg.d), 1.0, cfg.dtype)
 
 
+def layer_of(cfg: Config, l: int) -> Config:
+    """Layer l of a multi-layer stack of this shape: its own weights (seed
+    cfg.seed + 1000 l; layer 0 is the single-layer workload itself)."""
+    import dataclasses
+    return cfg if l == 0 else dataclasses.replace(cfg, seed=cfg.seed + 1000 * l)
+
+
 def make_all(cfg: Config, T: int) -> Dict[str, Optional[np.ndarray]]:
     out = {"x": make_x(cfg, T), "w_r": make_router(cfg), "b_r": router_bias(cfg)}
     out.update(make_experts(cfg))

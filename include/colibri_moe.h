@@ -22,7 +22,9 @@
  *
  * Conventions for every entry point
  *   - Tensor arguments are HIP device pointers, row-major, owned by the
- *     caller; nothing is allocated, freed or synchronised inside a call.
+ *     caller; nothing is allocated, freed or synchronised inside a call
+ *     (colibri_moe_graph_create / _destroy, which make and free a HIP graph,
+ *     aside).
  *     Work is enqueued on `stream` (0 = the null stream) and the call returns
  *     without waiting for it.
  *   - Arguments are validated on the host before anything is launched; an
@@ -214,6 +216,53 @@ int colibri_moe_layer_forward_ex(const colibri_moe_shape_t *s, const void *x, co
                                  const colibri_moe_experts_t *w, const colibri_moe_layer_opts_t *opts, void *out,
                                  int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
                                  size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ multi-layer step, graph replay
+ * A decode step through L MoE layers in sequence, each with its own weights,
+ * in place on x [T, d]:
+ *   for l = 0 .. L-1:  x <- layer_l(x) + x   (residual != 0)   or   x <- layer_l(x)
+ * where layer_l is colibri_moe_layer_forward_ex with that layer's parameters
+ * (the residual add is the fused one of [nxbn] section 2.1).  The pages keep
+ * the launches of a step few and run routing and the GEMMs on two streams so
+ * that they overlap ([zskr] section 5.3); here a step is captured once into a
+ * HIP graph and replayed as one launch, and each layer's shared expert (which
+ * reads only x) sits on a parallel branch of the graph beside routing and the
+ * routed FFN. */
+typedef struct {
+    const void *w_r;                     /* [d, E] dtype */
+    const float *b_r;                    /* [E] fp32 or NULL */
+    colibri_moe_experts_t experts;       /* the layer's routed experts */
+    colibri_gate_t gate;                 /* gating of the chosen pair */
+    const colibri_moe_experts_t *shared; /* shared expert or NULL (as colibri_moe_layer_opts_t) */
+    int32_t shared_h;                    /* its hidden width (0: h) */
+} colibri_moe_layer_params_t;
+
+/* Workspace of a step (the layers run one after another and share it):
+ * the largest colibri_moe_workspace_size_ex over the layers; 0 for an invalid
+ * shape, L or layer. */
+size_t colibri_moe_step_workspace_size(const colibri_moe_shape_t *s, int32_t L,
+                                       const colibri_moe_layer_params_t *layers);
+
+/* Runs the step on `stream`, eagerly (one layer after another, shared experts
+ * on the same stream).  1 <= L <= 4096; x 16-byte aligned; ws as for the
+ * layer.  T = 0 is a no-op. */
+int colibri_moe_step_forward(const colibri_moe_shape_t *s, int32_t L, const colibri_moe_layer_params_t *layers,
+                             int32_t residual, void *x, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Captures the same step into an executable HIP graph on the current device
+ * (T >= 1).  The graph holds x, ws and every weight pointer: they must stay
+ * valid, and launches of one graph must not overlap (they share x and ws).
+ * Creating a graph creates and destroys two streams and two events and
+ * launches nothing; the graph lives until colibri_moe_graph_destroy.  Each
+ * replay computes exactly what colibri_moe_step_forward computes (the same
+ * kernels in the same order on each branch). */
+typedef struct colibri_moe_graph colibri_moe_graph_t;
+int colibri_moe_graph_create(const colibri_moe_shape_t *s, int32_t L, const colibri_moe_layer_params_t *layers,
+                             int32_t residual, void *x, void *ws, size_t ws_bytes, colibri_moe_graph_t **graph);
+/* Replays the step on `stream` (same device as at creation). */
+int colibri_moe_graph_launch(colibri_moe_graph_t *graph, hipStream_t stream);
+/* Frees the graph (NULL: no-op).  No launch of it may still be pending. */
+int colibri_moe_graph_destroy(colibri_moe_graph_t *graph);
 
 /* ------------------------------------------------------------------ int8 expert weights
  * Expert weights stored as int8 codes with one fp32 scale per output column

@@ -28,7 +28,9 @@ EXPORTED = [
     "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
     "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
     "colibri_moe_workspace_size_ex", "colibri_moe_route_ex", "colibri_moe_combine_ex",
-    "colibri_moe_layer_forward_ex", "colibri_moe_status_string",
+    "colibri_moe_layer_forward_ex", "colibri_moe_step_workspace_size", "colibri_moe_step_forward",
+    "colibri_moe_graph_create", "colibri_moe_graph_launch", "colibri_moe_graph_destroy",
+    "colibri_moe_status_string",
 ]
 
 
@@ -57,6 +59,11 @@ class _ExpertsQ8(ctypes.Structure):
 class _Opts(ctypes.Structure):
     _fields_ = [("gate", ctypes.c_int), ("shared", ctypes.POINTER(_Experts)), ("shared_h", ctypes.c_int32),
                 ("residual", ctypes.c_void_p)]
+
+
+class _LayerParams(ctypes.Structure):
+    _fields_ = [("w_r", ctypes.c_void_p), ("b_r", ctypes.c_void_p), ("experts", _Experts), ("gate", ctypes.c_int),
+                ("shared", ctypes.POINTER(_Experts)), ("shared_h", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -116,10 +123,19 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_route_ex.argtypes = [SP, P, P, P, I, P, P, P, P]
     lib.colibri_moe_combine_ex.argtypes = [SP, P, P, P, P, P, P, P]
     lib.colibri_moe_layer_forward_ex.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), OP, P, P, P, P, P, Z, P]
+    LP = ctypes.POINTER(_LayerParams)
+    lib.colibri_moe_step_workspace_size.argtypes = [SP, i32, LP]
+    lib.colibri_moe_step_workspace_size.restype = Z
+    lib.colibri_moe_step_forward.argtypes = [SP, i32, LP, i32, P, P, Z, P]
+    lib.colibri_moe_graph_create.argtypes = [SP, i32, LP, i32, P, P, Z, ctypes.POINTER(P)]
+    lib.colibri_moe_graph_launch.argtypes = [P, P]
+    lib.colibri_moe_graph_destroy.argtypes = [P]
     for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up",
               "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
               "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
-              "colibri_moe_route_ex", "colibri_moe_combine_ex", "colibri_moe_layer_forward_ex"):
+              "colibri_moe_route_ex", "colibri_moe_combine_ex", "colibri_moe_layer_forward_ex",
+              "colibri_moe_step_forward", "colibri_moe_graph_create", "colibri_moe_graph_launch",
+              "colibri_moe_graph_destroy"):
         getattr(lib, f).restype = I
     lib.colibri_moe_status_string.argtypes = [I]
     lib.colibri_moe_status_string.restype = ctypes.c_char_p
@@ -264,6 +280,63 @@ def layer_forward_ex(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: int, 
                                                ctypes.byref(o), _ptr(out), _ptr(topk_idx), _ptr(topk_gate),
                                                _ptr(counts), _ptr(ws), ws_bytes, _stream(stream)),
            "colibri_moe_layer_forward_ex")
+
+
+# ------------------------------------------------------------------ multi-layer step, graph replay
+def _layer_params(layers):
+    """layers: list of dicts with w_r, w1, w2 (and b_r, w3, b1, b2, gate, shared,
+    shared_h).  Returns the ctypes array and the structs it points to."""
+    arr = (_LayerParams * len(layers))()
+    keep = []
+    for i, l in enumerate(layers):
+        sh = None
+        if l.get("shared") is not None:
+            d = l["shared"]
+            sh = _experts(d["w1"], d["w2"], d.get("w3"), d.get("b1"), d.get("b2"))
+            keep.append(sh)
+        arr[i] = _LayerParams(_ptr(l["w_r"]), _ptr(l.get("b_r")),
+                              _experts(l["w1"], l["w2"], l.get("w3"), l.get("b1"), l.get("b2")),
+                              _gate_code(l.get("gate", "pair")), ctypes.pointer(sh) if sh is not None else None,
+                              int(l.get("shared_h", 0)))
+    return arr, keep
+
+
+def step_workspace_size(shape: Shape, layers) -> int:
+    s = shape.c()
+    arr, keep = _layer_params(layers)
+    return int(load().colibri_moe_step_workspace_size(ctypes.byref(s), len(layers), arr))
+
+
+def step_forward(shape: Shape, layers, x, ws, ws_bytes: int, residual: bool = True, stream=None):
+    """x <- layer_l(x) (+ x) for every layer, in place on x."""
+    s = shape.c()
+    arr, keep = _layer_params(layers)
+    _check(load().colibri_moe_step_forward(ctypes.byref(s), len(layers), arr, int(bool(residual)), _ptr(x), _ptr(ws),
+                                           ws_bytes, _stream(stream)), "colibri_moe_step_forward")
+
+
+class Graph:
+    """A multi-layer step captured into a HIP graph (colibri_moe_graph_*).
+
+    The caller keeps x, ws and the weights alive while the graph exists."""
+
+    def __init__(self, shape: Shape, layers, x, ws, ws_bytes: int, residual: bool = True):
+        s = shape.c()
+        arr, keep = _layer_params(layers)
+        h = ctypes.c_void_p()
+        _check(load().colibri_moe_graph_create(ctypes.byref(s), len(layers), arr, int(bool(residual)), _ptr(x),
+                                               _ptr(ws), ws_bytes, ctypes.byref(h)), "colibri_moe_graph_create")
+        self._h = h
+
+    def launch(self, stream=None):
+        if self._h is None:
+            raise ValueError("graph is destroyed")
+        _check(load().colibri_moe_graph_launch(self._h, _stream(stream)), "colibri_moe_graph_launch")
+
+    def destroy(self):
+        if self._h is not None:
+            h, self._h = self._h, None
+            _check(load().colibri_moe_graph_destroy(h), "colibri_moe_graph_destroy")
 
 
 # ------------------------------------------------------------------ int8 expert weights

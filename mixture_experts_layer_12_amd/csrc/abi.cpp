@@ -1,6 +1,7 @@
 // C ABI of the MoE layer: host-side validation, workspace carving and the
 // launch sequence.  Every argument is checked before anything is launched;
-// nothing here allocates, frees or waits on the device.
+// nothing here allocates, frees or waits on the device, except that
+// colibri_moe_graph_create / _destroy make and free a HIP graph.
 //
 // Error convention follows the Colibri write-up [nxbn] http://m.nxbn.cn/news/48047
 // sections 3.3 and 5.1 (0 = success, negative codes for errors), failing
@@ -10,6 +11,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <new>
 
 #include "colibri_moe.h"
 #include "launchers.h"
@@ -103,12 +105,12 @@ int check_opts(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o) 
 }
 
 struct LayerWorkspace {
-    size_t idx, gate, counts, offsets, sorted, pos, y, sh_offsets, sh_y, ffn, total;
+    size_t idx, gate, counts, offsets, sorted, pos, y, sh_offsets, sh_y, sh_ffn, ffn, total;
 };
 
-// The plain layer's regions, then (with a shared expert) its offsets and
-// output rows; the FFN region last, sized for the larger of the routed and the
-// shared FFN (the shared expert runs first and is done with it).
+// The plain layer's regions, then (with a shared expert) its offsets, output
+// rows and FFN scratch of its own, so that it may run beside the routed FFN;
+// the routed FFN region last.
 LayerWorkspace layer_workspace(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o = nullptr) {
     LayerWorkspace L{};
     const size_t A = 2 * (size_t)s->T;
@@ -125,19 +127,26 @@ LayerWorkspace layer_workspace(const colibri_moe_shape_t *s, const colibri_moe_l
     L.sorted = take(A * 4);
     L.pos = take(A * 4);
     L.y = take(A * s->d * elem_size(s));
-    size_t ffn = ffn_workspace_bytes(*s);
     if (has_shared(o)) {
         const colibri_moe_shape_t sh = shared_shape(s, o);
         L.sh_offsets = take(2 * 4);
         L.sh_y = take(2 * (size_t)sh.T * s->d * elem_size(s));
-        ffn = std::max(ffn, ffn_workspace_bytes(sh));
+        L.sh_ffn = take(ffn_workspace_bytes(sh));
     }
-    L.ffn = take(ffn);
+    L.ffn = take(ffn_workspace_bytes(*s));
     L.total = off;
     return L;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? COLIBRI_OK : COLIBRI_ERR_HIP; }
+
+// A second stream for the shared expert: forked from the main stream before
+// routing (it reads only x), joined before the combine.  aux == nullptr: the
+// shared expert runs on the main stream.
+struct Branch {
+    hipStream_t aux = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
 
 // Steps 1-5 after the shape and expert checks.  ffn(sorted, offsets, y, ffn_ws,
 // reduce, &partials) runs both FFN layers; with Sd > 1 second-layer K splits
@@ -146,7 +155,7 @@ template <class Ffn>
 int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r, void *out,
                        int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
                        size_t ws_bytes, hipStream_t stream, const void *b2, int Sd, Ffn ffn,
-                       const colibri_moe_layer_opts_t *opts = nullptr) {
+                       const colibri_moe_layer_opts_t *opts = nullptr, const Branch &br = Branch{}) {
     if (!x || !w_r || !out) return COLIBRI_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(out, 16) || (b_r && !aligned(b_r, 4)) ||
         (topk_idx_out && !aligned(topk_idx_out, 4)) || (topk_gate_out && !aligned(topk_gate_out, 4)) ||
@@ -170,36 +179,106 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
     const void *residual = opts ? opts->residual : nullptr;
     void *sh_y = has_shared(opts) ? base + L.sh_y : nullptr;
 
-    hipError_t e;
-    if (route_dispatch_fusable(*s)) {
-        e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream, gate_mode);
-    } else {
-        e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream, gate_mode);
-        if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
-    }
-    if (e == hipSuccess && sh_y) {
-        // the shared expert over all T rows of x, before the routed FFN takes the FFN region
+    hipError_t e = hipSuccess;
+    const bool branch = sh_y && br.aux;
+    if (sh_y) {
+        // the shared expert over all T rows of x (a one-expert group, no gather)
+        hipStream_t ss = stream;
+        if (branch) {
+            e = hipEventRecord(br.fork, stream);
+            if (e == hipSuccess) e = hipStreamWaitEvent(br.aux, br.fork, 0);
+            ss = br.aux;
+        }
         const colibri_moe_shape_t sh = shared_shape(s, opts);
         int32_t *sh_off = reinterpret_cast<int32_t *>(base + L.sh_offsets);
-        e = launch_pair_offsets(sh_off, s->T, stream);
+        if (e == hipSuccess) e = launch_pair_offsets(sh_off, s->T, ss);
         if (e == hipSuccess)
-            e = launch_ffn_layers(sh, x, nullptr, sh_off, *opts->shared, sh_y, ffn_ws, true, stream, nullptr);
+            e = launch_ffn_layers(sh, x, nullptr, sh_off, *opts->shared, sh_y, base + L.sh_ffn, true, ss, nullptr);
+        if (e == hipSuccess && branch) e = hipEventRecord(br.join, ss);
+    }
+    if (e == hipSuccess) {
+        if (route_dispatch_fusable(*s)) {
+            e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream, gate_mode);
+        } else {
+            e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream, gate_mode);
+            if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
+        }
     }
     if (e != hipSuccess) return hip_status(e);
-    if (Sd > 1) {
-        const float *part = nullptr;
-        e = ffn(sorted, offsets, nullptr, ffn_ws, false, &part);
-        if (e == hipSuccess)
-            e = launch_combine_partials(*s, part, Sd, pos, idx, gate, s->act == COLIBRI_ACT_SWIGLU ? nullptr : b2,
-                                        out, stream, sh_y, residual);
-        return hip_status(e);
-    }
-    e = ffn(sorted, offsets, y, ffn_ws, true, nullptr);
-    if (e == hipSuccess) e = launch_combine(*s, y, pos, gate, out, stream, sh_y, residual);
+    const float *part = nullptr;
+    e = Sd > 1 ? ffn(sorted, offsets, nullptr, ffn_ws, false, &part) : ffn(sorted, offsets, y, ffn_ws, true, nullptr);
+    if (e == hipSuccess && branch) e = hipStreamWaitEvent(stream, br.join, 0);
+    if (e != hipSuccess) return hip_status(e);
+    if (Sd > 1)
+        e = launch_combine_partials(*s, part, Sd, pos, idx, gate, s->act == COLIBRI_ACT_SWIGLU ? nullptr : b2, out,
+                                    stream, sh_y, residual);
+    else
+        e = launch_combine(*s, y, pos, gate, out, stream, sh_y, residual);
     return hip_status(e);
 }
 
+constexpr int32_t kMaxLayers = 4096;
+
+colibri_moe_layer_opts_t step_opts(const colibri_moe_layer_params_t &p, const void *residual) {
+    colibri_moe_layer_opts_t o{};
+    o.gate = p.gate;
+    o.shared = p.shared;
+    o.shared_h = p.shared_h;
+    o.residual = residual;
+    return o;
+}
+
+int check_step(const colibri_moe_shape_t *s, int32_t L, const colibri_moe_layer_params_t *layers) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (L < 1 || L > kMaxLayers) return COLIBRI_ERR_UNSUPPORTED;
+    if (!layers) return COLIBRI_ERR_INVALID_ARG;
+    for (int32_t l = 0; l < L; ++l) {
+        const colibri_moe_layer_params_t &p = layers[l];
+        if (!p.w_r || !aligned(p.w_r, 16) || (p.b_r && !aligned(p.b_r, 4))) return COLIBRI_ERR_INVALID_ARG;
+        const colibri_moe_layer_opts_t o = step_opts(p, nullptr);
+        st = check_opts(s, &o);
+        if (st == COLIBRI_OK) st = check_experts(s, &p.experts);
+        if (st != COLIBRI_OK) return st;
+    }
+    return COLIBRI_OK;
+}
+
+size_t step_workspace(const colibri_moe_shape_t *s, int32_t L, const colibri_moe_layer_params_t *layers) {
+    size_t need = 0;
+    for (int32_t l = 0; l < L; ++l) {
+        const colibri_moe_layer_opts_t o = step_opts(layers[l], nullptr);
+        need = std::max(need, layer_workspace(s, &o).total);
+    }
+    return need;
+}
+
+// One layer of a step, in place on x.
+int step_layer(const colibri_moe_shape_t *s, const colibri_moe_layer_params_t &p, bool residual, void *x, void *ws,
+               size_t ws_bytes, hipStream_t stream, const Branch &br) {
+    const colibri_moe_layer_opts_t o = step_opts(p, residual ? x : nullptr);
+    return layer_forward_impl(
+        s, x, p.w_r, p.b_r, x, nullptr, nullptr, nullptr, ws, ws_bytes, stream, p.experts.b2, ffn_down_splits(*s),
+        [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce, const float **part) {
+            return launch_ffn_layers(*s, x, sorted, offsets, p.experts, y, ffn_ws, reduce, stream, part);
+        },
+        &o, br);
+}
+
+int check_step_buffers(const colibri_moe_shape_t *s, int32_t L, const colibri_moe_layer_params_t *layers, void *x,
+                       void *ws, size_t ws_bytes) {
+    if (!x || !aligned(x, 16)) return COLIBRI_ERR_INVALID_ARG;
+    if (ws_bytes < step_workspace(s, L, layers)) return COLIBRI_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    return COLIBRI_OK;
+}
+
 }  // namespace
+
+struct colibri_moe_graph {
+    hipGraphExec_t exec;
+    int device;
+};
 
 extern "C" {
 
@@ -417,6 +496,88 @@ int colibri_moe_layer_forward_ex(const colibri_moe_shape_t *s, const void *x, co
             return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream, part);
         },
         opts);
+}
+
+size_t colibri_moe_step_workspace_size(const colibri_moe_shape_t *s, int32_t L,
+                                       const colibri_moe_layer_params_t *layers) {
+    if (check_step(s, L, layers) != COLIBRI_OK || s->T == 0) return 0;
+    return step_workspace(s, L, layers);
+}
+
+int colibri_moe_step_forward(const colibri_moe_shape_t *s, int32_t L, const colibri_moe_layer_params_t *layers,
+                             int32_t residual, void *x, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_step(s, L, layers);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_step_buffers(s, L, layers, x, ws, ws_bytes);
+    for (int32_t l = 0; l < L && st == COLIBRI_OK; ++l)
+        st = step_layer(s, layers[l], residual != 0, x, ws, ws_bytes, stream, Branch{});
+    return st;
+}
+
+int colibri_moe_graph_create(const colibri_moe_shape_t *s, int32_t L, const colibri_moe_layer_params_t *layers,
+                             int32_t residual, void *x, void *ws, size_t ws_bytes, colibri_moe_graph_t **graph) {
+    if (!graph) return COLIBRI_ERR_INVALID_ARG;
+    *graph = nullptr;
+    int st = check_step(s, L, layers);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_ERR_UNSUPPORTED;
+    st = check_step_buffers(s, L, layers, x, ws, ws_bytes);
+    if (st != COLIBRI_OK) return st;
+
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return COLIBRI_ERR_HIP;
+    // a capture stream of our own (the caller's may be the null stream, which
+    // cannot be captured) and the shared experts' branch
+    hipStream_t cs = nullptr, aux = nullptr;
+    Branch br;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&aux, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&br.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&br.join, hipEventDisableTiming);
+    br.aux = aux;
+    hipGraph_t g = nullptr;
+    hipGraphExec_t exec = nullptr;
+    if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        for (int32_t l = 0; l < L && st == COLIBRI_OK; ++l)
+            st = step_layer(s, layers[l], residual != 0, x, ws, ws_bytes, cs, br);
+        const hipError_t ce = hipStreamEndCapture(cs, &g);  // always ends the capture
+        if (st == COLIBRI_OK && ce != hipSuccess) e = ce;
+        if (st == COLIBRI_OK && e == hipSuccess) e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    }
+    if (g) (void)hipGraphDestroy(g);
+    if (br.join) (void)hipEventDestroy(br.join);
+    if (br.fork) (void)hipEventDestroy(br.fork);
+    if (aux) (void)hipStreamDestroy(aux);
+    if (cs) (void)hipStreamDestroy(cs);
+    if (st == COLIBRI_OK && e != hipSuccess) st = COLIBRI_ERR_HIP;
+    if (st != COLIBRI_OK) {
+        if (exec) (void)hipGraphExecDestroy(exec);
+        return st;
+    }
+    colibri_moe_graph_t *gr = new (std::nothrow) colibri_moe_graph_t{exec, device};
+    if (!gr) {
+        (void)hipGraphExecDestroy(exec);
+        return COLIBRI_ERR_HIP;
+    }
+    *graph = gr;
+    return COLIBRI_OK;
+}
+
+int colibri_moe_graph_launch(colibri_moe_graph_t *graph, hipStream_t stream) {
+    if (!graph || !graph->exec) return COLIBRI_ERR_INVALID_ARG;
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) return COLIBRI_ERR_HIP;
+    if (device != graph->device) return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(hipGraphLaunch(graph->exec, stream));
+}
+
+int colibri_moe_graph_destroy(colibri_moe_graph_t *graph) {
+    if (!graph) return COLIBRI_OK;
+    const hipError_t e = graph->exec ? hipGraphExecDestroy(graph->exec) : hipSuccess;
+    delete graph;
+    return hip_status(e);
 }
 
 const char *colibri_moe_status_string(int status) {

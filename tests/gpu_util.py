@@ -90,6 +90,33 @@ def assert_close(a, b, dt, what):
         assert_bf16_close(a, b, what)
 
 
+def assert_layer_close(a, ref, dt, what, residual=None):
+    """Layer outputs with a shared expert, a residual or raw-logit gates.
+
+    fp32: the row rule.  bf16: |a - b| <= 1e-2 + 2e-2 M per element, where M is
+    the largest magnitude among b and the summands of the combine (g0 y0, g1 y1,
+    the shared row, the residual row).  Both sides store the expert rows in
+    bf16; where an fp32 sum lands on a rounding boundary the two round a row to
+    neighbouring values, and that one-ulp step is relative to the row, not to
+    the sum, which may cancel to far less.  With no addends and convex gates M
+    is at most the larger gated row."""
+    if dt == gen.F32:
+        assert_fp32_close(a, ref["out"], what)
+        return
+    a = np.asarray(a, np.float64)
+    b = np.asarray(ref["out"], np.float64)
+    g, y = ref["gate"], ref["y"]
+    M = np.maximum(np.abs(b), np.abs(g[:, :1] * y[:, 0]))
+    M = np.maximum(M, np.abs(g[:, 1:] * y[:, 1]))
+    if "y_shared" in ref:
+        M = np.maximum(M, np.abs(ref["y_shared"]))
+    if residual is not None:
+        M = np.maximum(M, np.abs(np.asarray(residual, np.float64)))
+    bad = np.abs(a - b) > 1e-2 + 2e-2 * M
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} elements outside |a-b| <= 1e-2 + 2e-2 M; "
+                           f"worst |a-b| = {np.abs(a - b).max():.3e}")
+
+
 # ------------------------------------------------------------------ near ties
 def near_tie_mask(lg: np.ndarray) -> np.ndarray:
     """Tokens whose 1st/2nd or 2nd/3rd logit margin (oracle fp64) is < NEAR_TIE."""

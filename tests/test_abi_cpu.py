@@ -305,3 +305,54 @@ def test_route_and_combine_ex_checks(lib):
     assert c(sh=fake(4) + 8) == moe.COLIBRI_ERR_INVALID_ARG
     assert c(res=fake(5) + 2) == moe.COLIBRI_ERR_INVALID_ARG
     assert c(y=None) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ multi-layer step, graph
+def params_c(n, **kw):
+    arr = (moe._LayerParams * n)()
+    for i in range(n):
+        base = dict(w_r=fake(40 + i), b_r=None, experts=moe._Experts(fake(50 + 3 * i), fake(51 + 3 * i),
+                                                                       fake(52 + 3 * i), None, None),
+                    gate=moe.GATE_PAIR, shared=None, shared_h=0)
+        base.update(kw)
+        arr[i] = moe._LayerParams(base["w_r"], base["b_r"], base["experts"], base["gate"], base["shared"],
+                                  base["shared_h"])
+    return arr
+
+
+def test_step_and_graph_checks(lib):
+    s = shape_c()
+    one = lib.colibri_moe_workspace_size(ctypes.byref(s))
+    assert lib.colibri_moe_step_workspace_size(ctypes.byref(s), 3, params_c(3)) == one
+    sh = moe._Experts(fake(7), fake(8), fake(9), None, None)
+    withsh = lib.colibri_moe_step_workspace_size(ctypes.byref(s), 2, params_c(2, shared=ctypes.pointer(sh)))
+    assert withsh > one
+    assert lib.colibri_moe_step_workspace_size(ctypes.byref(s), 0, params_c(1)) == 0
+    assert lib.colibri_moe_step_workspace_size(ctypes.byref(s), 4097, params_c(1)) == 0
+
+    def fwd(L=2, p=None, x=fake(1), ws_bytes=1 << 40, sh=s):
+        return lib.colibri_moe_step_forward(ctypes.byref(sh), L, p if p is not None else params_c(L), 1, x,
+                                            fake(20), ws_bytes, None)
+
+    assert fwd(L=0) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert fwd(x=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert fwd(x=fake(1) + 8) == moe.COLIBRI_ERR_INVALID_ARG
+    assert fwd(ws_bytes=one - 1) == moe.COLIBRI_ERR_WORKSPACE
+    assert fwd(p=params_c(2, w_r=None)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert fwd(p=params_c(2, gate=5)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert fwd(p=params_c(2, experts=moe._Experts(fake(4), None, fake(6), None, None))) == moe.COLIBRI_ERR_INVALID_ARG
+    assert fwd(p=params_c(2, shared=ctypes.pointer(sh), shared_h=100)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert fwd(sh=shape_c(T=0)) == 0  # T = 0: no-op
+    # graph creation validates the same way before any HIP call; T = 0 has no graph
+    h = ctypes.c_void_p(123)
+
+    def create(L=2, p=None, ws_bytes=1 << 40, sh=s, out=ctypes.byref(h)):
+        return lib.colibri_moe_graph_create(ctypes.byref(sh), L, p if p is not None else params_c(L), 1, fake(1),
+                                            fake(20), ws_bytes, out)
+
+    assert create(out=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert create(ws_bytes=one - 1) == moe.COLIBRI_ERR_WORKSPACE and h.value is None
+    assert create(p=params_c(2, gate=-2)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert create(sh=shape_c(T=0)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert lib.colibri_moe_graph_launch(None, None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert lib.colibri_moe_graph_destroy(None) == 0
