@@ -200,7 +200,7 @@ def main():
         evs[0].record(stream)
         moe.route(sh, x, w_r, b_r, idx, gate)
         evs[1].record(stream)
-        moe.dispatch(sh, idx, counts, offs, sa, ap_)
+        moe.dispatch(sh, idx, counts, offs, sa, ap_, ws=ws, ws_bytes=ws_bytes)
         evs[2].record(stream)
         moe.expert_ffn_up(sh, x, sa, offs, w["w1"], H, ws, ws_bytes, w3=w["w3"], b1=w["b1"])
         evs[3].record(stream)

@@ -116,7 +116,14 @@ int colibri_moe_route(const colibri_moe_shape_t *s, const void *x, const void *w
  *   assign_pos     [2T] int32 out: inverse permutation
  *   x, x_sorted    optional pair: when both are non-NULL, x_sorted[p] =
  *                  x[sorted_assign[p] / 2] ([T, d] -> [2T, d], dtype, 16-byte aligned)
- *   ws, ws_bytes   unused (may be NULL / 0) */
+ *   ws, ws_bytes   optional scratch (may be NULL / 0): with at least
+ *                  colibri_moe_dispatch_workspace_size(s) bytes, 256-byte aligned,
+ *                  large batches (2T >= 4096) spread the dispatch over the chip
+ *                  (count, scan and scatter kernels); the result is the same */
+/* Scratch that lets colibri_moe_dispatch use its multi-workgroup path (0 for
+ * batches that do not need it, and for an invalid shape). */
+size_t colibri_moe_dispatch_workspace_size(const colibri_moe_shape_t *s);
+
 int colibri_moe_dispatch(const colibri_moe_shape_t *s, const int32_t *topk_idx, int32_t *expert_counts,
                          int32_t *expert_offsets, int32_t *sorted_assign, int32_t *assign_pos,
                          const void *x, void *x_sorted, void *ws, size_t ws_bytes, hipStream_t stream);

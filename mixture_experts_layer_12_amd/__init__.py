@@ -24,8 +24,8 @@ GATE_PAIR, GATE_SOFTMAX, GATE_LINEAR = 0, 1, 2
 GATE_CODES = {"pair": GATE_PAIR, "softmax": GATE_SOFTMAX, "linear": GATE_LINEAR}
 
 EXPORTED = [
-    "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn",
-    "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
+    "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_dispatch_workspace_size",
+    "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
     "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
     "colibri_moe_workspace_size_ex", "colibri_moe_route_ex", "colibri_moe_combine_ex",
     "colibri_moe_layer_forward_ex", "colibri_moe_step_workspace_size", "colibri_moe_step_forward",
@@ -107,6 +107,8 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_workspace_size.argtypes = [SP]
     lib.colibri_moe_workspace_size.restype = Z
     lib.colibri_moe_route.argtypes = [SP, P, P, P, P, P, P, P]
+    lib.colibri_moe_dispatch_workspace_size.argtypes = [SP]
+    lib.colibri_moe_dispatch_workspace_size.restype = Z
     lib.colibri_moe_dispatch.argtypes = [SP, P, P, P, P, P, P, P, P, Z, P]
     lib.colibri_moe_expert_ffn.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, Z, P]
     lib.colibri_moe_expert_ffn_up.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, Z, P]
@@ -178,6 +180,11 @@ def _experts(w1, w2, w3=None, b1=None, b2=None) -> _Experts:
 def workspace_size(shape: Shape) -> int:
     s = shape.c()
     return int(load().colibri_moe_workspace_size(ctypes.byref(s)))
+
+
+def dispatch_workspace_size(shape: Shape) -> int:
+    s = shape.c()
+    return int(load().colibri_moe_dispatch_workspace_size(ctypes.byref(s)))
 
 
 def route(shape: Shape, x, w_r, b_r, topk_idx, topk_gate, logits=None, stream=None):

@@ -105,7 +105,7 @@ int check_opts(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o) 
 }
 
 struct LayerWorkspace {
-    size_t idx, gate, counts, offsets, sorted, pos, y, sh_offsets, sh_y, sh_ffn, ffn, total;
+    size_t idx, gate, counts, offsets, sorted, pos, disp, y, sh_offsets, sh_y, sh_ffn, ffn, total;
 };
 
 // The plain layer's regions, then (with a shared expert) its offsets, output
@@ -126,6 +126,7 @@ LayerWorkspace layer_workspace(const colibri_moe_shape_t *s, const colibri_moe_l
     L.offsets = take((size_t)(s->E + 1) * 4);
     L.sorted = take(A * 4);
     L.pos = take(A * 4);
+    L.disp = take(dispatch_scratch_bytes(*s));
     L.y = take(A * s->d * elem_size(s));
     if (has_shared(o)) {
         const colibri_moe_shape_t sh = shared_shape(s, o);
@@ -201,7 +202,9 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
             e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream, gate_mode);
         } else {
             e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream, gate_mode);
-            if (e == hipSuccess) e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream);
+            if (e == hipSuccess)
+                e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream,
+                                    dispatch_scratch_bytes(*s) ? base + L.disp : nullptr);
         }
     }
     if (e != hipSuccess) return hip_status(e);
@@ -299,11 +302,14 @@ int colibri_moe_route(const colibri_moe_shape_t *s, const void *x, const void *w
     return hip_status(launch_route(*s, x, w_r, b_r, topk_idx, topk_gate, logits, stream));
 }
 
+size_t colibri_moe_dispatch_workspace_size(const colibri_moe_shape_t *s) {
+    if (check_shape(s) != COLIBRI_OK || s->T == 0) return 0;
+    return dispatch_scratch_bytes(*s);
+}
+
 int colibri_moe_dispatch(const colibri_moe_shape_t *s, const int32_t *topk_idx, int32_t *expert_counts,
                          int32_t *expert_offsets, int32_t *sorted_assign, int32_t *assign_pos, const void *x,
                          void *x_sorted, void *ws, size_t ws_bytes, hipStream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
     int st = check_shape(s);
     if (st != COLIBRI_OK) return st;
     if (s->T == 0) return COLIBRI_OK;
@@ -314,7 +320,10 @@ int colibri_moe_dispatch(const colibri_moe_shape_t *s, const int32_t *topk_idx, 
         return COLIBRI_ERR_INVALID_ARG;
     if ((x == nullptr) != (x_sorted == nullptr)) return COLIBRI_ERR_INVALID_ARG;
     if (x && (!aligned(x, 16) || !aligned(x_sorted, 16))) return COLIBRI_ERR_INVALID_ARG;
-    hipError_t e = launch_dispatch(*s, topk_idx, expert_counts, expert_offsets, sorted_assign, assign_pos, stream);
+    const size_t dneed = dispatch_scratch_bytes(*s);
+    void *dws = (dneed && ws && ws_bytes >= dneed && aligned(ws, 256)) ? ws : nullptr;
+    hipError_t e =
+        launch_dispatch(*s, topk_idx, expert_counts, expert_offsets, sorted_assign, assign_pos, stream, dws);
     if (e == hipSuccess && x) e = launch_gather_rows(*s, x, sorted_assign, x_sorted, stream);
     return hip_status(e);
 }

@@ -25,8 +25,12 @@ hipError_t launch_route_dispatch(const colibri_moe_shape_t &s, const void *x, co
                                  int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st,
                                  int gate_mode = COLIBRI_GATE_PAIR);
 
+// scratch: dispatch_scratch_bytes(s) bytes (256-aligned) or nullptr; with it,
+// large batches run the multi-workgroup path (same result)
+size_t dispatch_scratch_bytes(const colibri_moe_shape_t &s);
 hipError_t launch_dispatch(const colibri_moe_shape_t &s, const int32_t *topk_idx, int32_t *counts,
-                           int32_t *offsets, int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st);
+                           int32_t *offsets, int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st,
+                           void *scratch = nullptr);
 
 hipError_t launch_gather_rows(const colibri_moe_shape_t &s, const void *x, const int32_t *sorted_assign,
                               void *x_sorted, hipStream_t st);

@@ -508,16 +508,20 @@ __global__ __launch_bounds__(kFusedWaves *kWave) void route_dispatch_mfma_kernel
 }
 
 // Waves per 16-token tile of the MFMA router: a power of two up to
-// mfma_maxw, each wave keeping at least 4 k-steps of 32 rows, G W <= 2048
-// waves in all; with at most kFusedGroups tiles also G W <= mfma_maxw (the
+// mfma_maxw, each wave keeping at least 4 k-steps of 32 rows, G W <=
+// kMfmaMaxWaves in all; with at most kFusedGroups tiles also G W <= mfma_maxw (the
 // fused kernel uses the same W, so both paths form every logit identically).
+#ifndef COLIBRI_MFMA_MAX_WAVES
+#define COLIBRI_MFMA_MAX_WAVES 8192
+#endif
+constexpr int kMfmaMaxWaves = COLIBRI_MFMA_MAX_WAVES;  // waves of one launch at most
 inline int mfma_waves(int T, int d, int EP) {
     const int G = ceil_div(T, 16);
     const int nks = d / 32;
     const int maxw = EP == 64 ? 8 : 16;
     int W = 1;
     const int fused = kFusedWaves < maxw ? kFusedWaves : maxw;  // the fused kernel's LDS holds maxw waves
-    while (W < maxw && nks >= 8 * W && G * W * 2 <= 2048 && (G > kFusedGroups || G * W * 2 <= fused))
+    while (W < maxw && nks >= 8 * W && G * W * 2 <= kMfmaMaxWaves && (G > kFusedGroups || G * W * 2 <= fused))
         W *= 2;
     return W;
 }

@@ -356,3 +356,16 @@ def test_step_and_graph_checks(lib):
     assert create(sh=shape_c(T=0)) == moe.COLIBRI_ERR_UNSUPPORTED
     assert lib.colibri_moe_graph_launch(None, None) == moe.COLIBRI_ERR_INVALID_ARG
     assert lib.colibri_moe_graph_destroy(None) == 0
+
+
+def test_dispatch_workspace_size(lib):
+    small = shape_c(T=2047)
+    large = shape_c(T=2048)
+    assert lib.colibri_moe_dispatch_workspace_size(ctypes.byref(small)) == 0
+    need = lib.colibri_moe_dispatch_workspace_size(ctypes.byref(large))
+    # two [2T / 64][E] int32 tables (chunk counts, chunk starts), 256-byte aligned
+    assert need == 2 * ((64 * 8 * 4 + 255) // 256 * 256)
+    assert lib.colibri_moe_dispatch_workspace_size(ctypes.byref(shape_c(T=2048, E=65))) == 0
+    # the layer's workspace holds it
+    assert lib.colibri_moe_workspace_size(ctypes.byref(large)) > lib.colibri_moe_workspace_size(
+        ctypes.byref(shape_c(T=2047))) + need

@@ -116,16 +116,23 @@ def test_route_bias_and_nan_ranking():
 
 
 # ------------------------------------------------------------------ dispatch
-def run_dispatch(idx: np.ndarray, E: int, x=None, dt=gen.BF16):
+def run_dispatch(idx: np.ndarray, E: int, x=None, dt=gen.BF16, multi=False):
+    """multi: hand the entry point scratch, so that large batches take the
+    multi-workgroup path (count, scan and scatter kernels)."""
     T = idx.shape[0]
     sh = moe.Shape(T, 64 if x is None else x.shape[1], 64, E, dt, moe.RELU)
+    ws, ws_bytes = None, 0
+    if multi:
+        ws_bytes = moe.dispatch_workspace_size(sh)
+        assert ws_bytes > 0 or 2 * T < 4096
+        ws = G.empty((max(ws_bytes, 256),), torch.uint8) if ws_bytes else None
     counts = G.empty((E,), torch.int32)
     offsets = G.empty((E + 1,), torch.int32)
     sa = G.empty((2 * T,), torch.int32)
     ap = G.empty((2 * T,), torch.int32)
     xd = G.dev(x) if x is not None else None
     xs = G.empty((2 * T, x.shape[1]), G.tdtype(dt)) if x is not None else None
-    moe.dispatch(sh, G.dev(idx.astype(np.int32)), counts, offsets, sa, ap, xd, xs)
+    moe.dispatch(sh, G.dev(idx.astype(np.int32)), counts, offsets, sa, ap, xd, xs, ws=ws, ws_bytes=ws_bytes)
     torch.cuda.synchronize()
     r = {"counts": counts.cpu().numpy(), "offsets": offsets.cpu().numpy(), "sorted_assign": sa.cpu().numpy(),
          "assign_pos": ap.cpu().numpy()}
@@ -144,26 +151,50 @@ DISPATCH_CASES = [(1, 8), (31, 4), (32, 4), (33, 4), (1000, 8), (4096, 8), (8192
                   (70001, 16)]
 
 
+@pytest.mark.parametrize("multi", [False, True], ids=["one-wg", "multi-wg"])
 @pytest.mark.parametrize("T,E", DISPATCH_CASES, ids=[f"T{t}-E{e}" for t, e in DISPATCH_CASES])
-def test_dispatch_bit_exact(T, E):
+def test_dispatch_bit_exact(T, E, multi):
     rng = np.random.default_rng(T + E)
     idx = _pairs(rng, T, E)
-    r = run_dispatch(idx, E)
+    r = run_dispatch(idx, E, multi=multi)
     ref = oracle.dispatch(idx, E)
     for k in ("counts", "offsets", "sorted_assign", "assign_pos"):
         assert np.array_equal(r[k], ref[k]), k
 
 
-def test_dispatch_degenerate_routings():
+@pytest.mark.parametrize("multi", [False, True], ids=["one-wg", "multi-wg"])
+def test_dispatch_degenerate_routings(multi):
     # every token to the same pair (other experts empty), and a Zipf-like skew
     for idx, E in ((np.tile([[6, 1]], (5000, 1)).astype(np.int32), 8),
                    (np.tile([[0, 63]], (129, 1)).astype(np.int32), 64),
+                   (np.tile([[0, 63]], (2049, 1)).astype(np.int32), 64),
                    (_pairs(np.random.default_rng(9), 20000, 16,
                            p=(np.arange(1, 17) ** -1.2) / (np.arange(1, 17) ** -1.2).sum()), 16)):
-        r = run_dispatch(idx, E)
+        r = run_dispatch(idx, E, multi=multi)
         ref = oracle.dispatch(idx, E)
         for k in ("counts", "offsets", "sorted_assign", "assign_pos"):
             assert np.array_equal(r[k], ref[k]), k
+
+
+def test_dispatch_multi_skips_out_of_range_indices():
+    """The multi-workgroup path with indices outside [0, E) scattered through a
+    large batch: the same counts, order and -1 markers as the one-workgroup path."""
+    rng = np.random.default_rng(12)
+    T, E = 3001, 8
+    idx = _pairs(rng, T, E)
+    flat = idx.reshape(-1)
+    bad = rng.choice(flat.size, 97, replace=False)
+    flat[bad] = rng.choice([-1, -7, E, E + 5], size=97)
+    one = run_dispatch(idx, E)
+    multi = run_dispatch(idx, E, multi=True)
+    for k in ("counts", "offsets", "sorted_assign", "assign_pos"):
+        assert np.array_equal(one[k], multi[k]), k
+    valid = (flat >= 0) & (flat < E)
+    assert multi["offsets"][-1] == valid.sum()
+    assert np.all(multi["assign_pos"][~valid] == -1)
+    assert np.all(multi["sorted_assign"][valid.sum():] == -1)
+    order = np.flatnonzero(valid)[np.argsort(flat[valid], kind="stable")]
+    assert np.array_equal(multi["sorted_assign"][:valid.sum()], order)
 
 
 def test_dispatch_row_gather():
