@@ -82,12 +82,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, 
 }
 
 // Same combine, but each expert row Y[p] is first formed from the second
-// layer's S split partial sums: Y[p] = bf16(sum_{s=0..S-1} part[s][p] + b2[e]),
-// the value the separate reduce would have stored.  The splits are added in
-// order s = 0, 1, ..., S-1 (the reduce uses the same order); their loads are
-// issued U at a time, both slots together, so a thread waits on memory
-// ceil(S / U) times rather than 2 S times.  VEC output columns per thread.
-template <int VEC, int U>
+// layer's S split partial sums: Y[p] = bf16(sum of part[s][p] + b2[e]), the
+// value the separate reduce would have stored.  The splits are added in the
+// reduce's order: 8 interleaved sums (sum j takes s = j, j + 8, ... in order),
+// then those 8 in order j = 0 .. 7 (for S <= 8 simply s = 0 .. S-1).  L = 1:
+// a thread forms both rows of its VEC output columns, loading U splits of each
+// at a time; L = 8: the 8 lanes of a group each form one interleaved sum and
+// lane 0 adds the 8 through shuffles and finishes the output (few outputs,
+// many splits: decode sizes).
+template <int VEC, int U, int L>
 __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__restrict__ part, int S,
                                                                const int32_t *__restrict__ pos,
                                                                const int32_t *__restrict__ idx,
@@ -97,11 +100,16 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                                                                const uint16_t *__restrict__ shared,
                                                                const uint16_t *__restrict__ residual) {
     typedef float fv __attribute__((ext_vector_type(VEC)));
+    static_assert(L == 1 || L == 8, "lanes per output");
+    static_assert(U % 8 == 0, "U keeps split s in interleaved sum s % 8");
+    constexpr int NJ = L == 1 ? 8 : 1;  // interleaved sums per thread
     const int vpr = d / VEC;
     const size_t total = (size_t)T * vpr;
     const int A = 2 * T;
     const size_t split_stride = (size_t)A * d;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int j0 = L == 1 ? 0 : (int)(threadIdx.x & (L - 1));  // this lane's interleaved sum
+    for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / L; i < total;
+         i += (size_t)gridDim.x * blockDim.x / L) {
         const int t = (int)(i / vpr);
         const int c = (int)(i % vpr) * VEC;
         int p[2], e[2];
@@ -112,35 +120,58 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
             e[sl] = idx[2 * t + sl];
             live[sl] = p[sl] >= 0 && p[sl] < A && e[sl] >= 0 && e[sl] < E;
         }
-        float y[2][VEC];
+        float y8[2][NJ][VEC];
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) y[sl][q] = 0.0f;
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) y8[sl][j][q] = 0.0f;
         // loads are unconditional (a dead slot reads row 0, then contributes
         // nothing), so no branch separates a load from its use
         auto load = [&](int sp, int sl) {
             const int row = live[sl] ? p[sl] : 0;
             return *reinterpret_cast<const fv *>(part + sp * split_stride + (size_t)row * d + c);
         };
-        // batches of U splits; a last, partial batch loads split S-1 in its unused
-        // slots and skips their additions, so the order of additions is unchanged
-        for (int sp = 0; sp < S; sp += U) {
+        // this lane's splits: s = j0 + L m; batches of U of them; a last, partial
+        // batch loads the lane's last split in its unused slots and skips their
+        // additions, so the order of additions is unchanged
+        const int nmine = S > j0 ? (S - j0 + L - 1) / L : 0;
+        for (int mb = 0; mb < nmine; mb += U) {
             fv a[2][U];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                for (int u = 0; u < U; ++u) a[sl][u] = load(min(sp + u, S - 1), sl);
+                for (int u = 0; u < U; ++u) a[sl][u] = load(j0 + L * min(mb + u, nmine - 1), sl);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (sp + u < S) {  // uniform; no break, so every index stays a constant
+                if (mb + u < nmine) {  // no break, so every index stays a constant
+                    const int j = L == 1 ? u % 8 : 0;  // L = 1: split mb + u, and mb is a multiple of 8
 #pragma unroll
                     for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                        for (int q = 0; q < VEC; ++q) y[sl][q] += a[sl][u][q];
+                        for (int q = 0; q < VEC; ++q) y8[sl][j][q] += a[sl][u][q];
                 }
             }
         }
+        // the 8 interleaved sums in order
+        float y[2][VEC];
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) {
+                float acc = 0.0f;
+                if constexpr (L == 1) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc += y8[sl][j][q];
+                } else {
+                    const int base = (int)(threadIdx.x & (kWave - 1)) & ~(L - 1);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc += __shfl(y8[sl][0][q], base + j);
+                }
+                y[sl][q] = acc;
+            }
+        if (j0 != 0) continue;
         float o[VEC];
 #pragma unroll
         for (int q = 0; q < VEC; ++q) o[q] = 0.0f;
@@ -194,10 +225,19 @@ hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *pa
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
                                    hipStream_t st, const void *shared, const void *residual) {
     const size_t total = (size_t)s.T * (s.d / 4);
-    const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
-    combine_partials_kernel<4, 16><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
-                                                          (const uint16_t *)b2, s.E, (uint16_t *)out, s.T, s.d,
-                                                          (const uint16_t *)shared, (const uint16_t *)residual);
+    if (S > 8 && total <= 65536) {  // few outputs and many splits: 8 lanes per output
+        const int blocks = (int)std::min<size_t>((total * 8 + 255) / 256, 8192);
+        combine_partials_kernel<4, 8, 8><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
+                                                                 (const uint16_t *)b2, s.E, (uint16_t *)out, s.T,
+                                                                 s.d, (const uint16_t *)shared,
+                                                                 (const uint16_t *)residual);
+    } else {
+        const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
+        combine_partials_kernel<4, 16, 1><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
+                                                                  (const uint16_t *)b2, s.E, (uint16_t *)out, s.T,
+                                                                  s.d, (const uint16_t *)shared,
+                                                                  (const uint16_t *)residual);
+    }
     return hipGetLastError();
 }
 

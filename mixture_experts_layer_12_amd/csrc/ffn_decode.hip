@@ -422,10 +422,21 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
         int e = 0;  // expert of this row: the last e with offsets[e] <= row
         for (int k = 1; k < E; ++k)
             if (offsets[k] <= row) e = k;
-        // splits added in order s = 0 .. S-1 (the combine uses the same order); their
-        // loads are issued U at a time so a thread waits on memory ceil(S / U) times
+        // First-layer splits are added in order s = 0 .. S-1 (the second layer's
+        // rebuild of H from them uses the same order).  Second-layer splits
+        // (bias only) go into 8 interleaved sums, sum j taking s = j, j + 8, ...
+        // in order, and the 8 sums are then added in order j = 0 .. 7: the order
+        // the combine uses, which spreads a row's splits over 8 lanes (for S <= 8
+        // it is the plain order).  Loads are issued U at a time so a thread waits
+        // on memory ceil(S / U) times.
         constexpr int U = 16;
-        float u[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        constexpr bool IL = (EPI == EPI_BIAS_ONLY);
+        constexpr int NJ = IL ? 8 : 1;
+        float u8[NJ][4], v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) u8[j][q] = 0.0f;
         const size_t split_stride = (size_t)A_total * NC;
         const float *src0 = part + (size_t)row * NC + col;
         // batches of U splits; a last, partial batch loads split S-1 in its unused
@@ -441,14 +452,20 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 #pragma unroll
             for (int k = 0; k < U; ++k) {
                 if (sp + k < S) {  // uniform; no break, so every index stays a constant
+                    const int kj = IL ? k % 8 : 0;  // U is a multiple of 8: sp + k = k (mod 8)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        u[q] += a[k][q];
+                        u8[kj][q] += a[k][q];
                         if (DUAL) v[q] += b[k][q];
                     }
                 }
             }
         }
+        float u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) u[q] = IL ? u[q] + u8[j][q] : u8[j][q];
         store_epilogue<EPI, 4>(C + (size_t)row * N + col, u, v, bias, e, N, col);
     }
 }
