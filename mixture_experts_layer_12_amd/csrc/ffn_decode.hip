@@ -514,7 +514,11 @@ DecodePlan decode_plan(const colibri_moe_shape_t &s, bool up, bool q8) {
 // The second layer rebuilds H from the first layer's split partials (instead
 // of a separate reduce launch) when the first layer is split, the staged H
 // slice fits in 64 KB of LDS, and the partial reads -- repeated once per column
-// group of the second layer -- stay within 5% of the second layer's weights.
+// group of the second layer -- stay within 5% of the second layer's weights,
+// or 25% with 16-row tiles (a handful of rows per expert: each workgroup then
+// stages a few KB, and the saved launch is worth more; measured on the
+// 15-expert layer at T = 1: 34.5 -> 32.4 us; at 32-row tiles the same rule
+// slowed the 8-expert layer at T = 64 from 94 to 110 us).
 bool decode_fuse_h(const colibri_moe_shape_t &s, bool q8) {
     if (!ffn_decode_eligible(s)) return false;
     const DecodePlan up = decode_plan(s, true, q8), down = decode_plan(s, false, q8);
@@ -524,7 +528,13 @@ bool decode_fuse_h(const colibri_moe_shape_t &s, bool q8) {
     if ((size_t)16 * down.MB * (klen_max * 2 + 16) > 64 * 1024) return false;
     const double reads = (double)((down.NCB + kDecWaves - 1) / kDecWaves) * up.part_bytes;
     const double down_weights = (double)down.slots * s.h * s.d * (q8 ? 1 : 2);
-    return reads <= 0.05 * down_weights;
+#ifndef COLIBRI_FUSE_H_READS
+#define COLIBRI_FUSE_H_READS 0.05
+#endif
+#ifndef COLIBRI_FUSE_H_READS_MB1
+#define COLIBRI_FUSE_H_READS_MB1 0.25
+#endif
+    return reads <= (down.MB == 1 ? COLIBRI_FUSE_H_READS_MB1 : COLIBRI_FUSE_H_READS) * down_weights;
 }
 
 size_t ffn_decode_scratch_bytes(const colibri_moe_shape_t &s) {
