@@ -232,9 +232,9 @@ int colibri_moe_layer_forward_ex(const colibri_moe_shape_t *s, const void *x, co
  * (the residual add is the fused one of [nxbn] section 2.1).  The pages keep
  * the launches of a step few and run routing and the GEMMs on two streams so
  * that they overlap ([zskr] section 5.3); here a step is captured once into a
- * HIP graph and replayed as one launch, and each layer's shared expert (which
- * reads only x) sits on a parallel branch of the graph beside routing and the
- * routed FFN. */
+ * HIP graph and replayed as one launch, and (T > 8) each layer's shared expert
+ * (which reads only x) sits on a parallel branch of the graph beside routing
+ * and the routed FFN. */
 typedef struct {
     const void *w_r;                     /* [d, E] dtype */
     const float *b_r;                    /* [E] fp32 or NULL */

@@ -182,6 +182,9 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
 
     hipError_t e = hipSuccess;
     const bool branch = sh_y && br.aux;
+    // a split second layer of the shared expert is left as partials for the
+    // combine, which forms the shared row from them as the reduce would
+    SharedPartials shp;
     if (sh_y) {
         // the shared expert over all T rows of x (a one-expert group, no gather)
         hipStream_t ss = stream;
@@ -193,8 +196,17 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
         const colibri_moe_shape_t sh = shared_shape(s, opts);
         int32_t *sh_off = reinterpret_cast<int32_t *>(base + L.sh_offsets);
         if (e == hipSuccess) e = launch_pair_offsets(sh_off, s->T, ss);
-        if (e == hipSuccess)
+        const int sh_S = ffn_down_splits(sh);
+        if (e == hipSuccess && sh_S > 1) {
+            shp.S = sh_S;
+            shp.stride = 2 * (size_t)sh.T * sh.d;
+            shp.b2 = sh.act == COLIBRI_ACT_SWIGLU ? nullptr : static_cast<const uint16_t *>(opts->shared->b2);
+            e = launch_ffn_layers(sh, x, nullptr, sh_off, *opts->shared, nullptr, base + L.sh_ffn, false, ss,
+                                  &shp.part);
+            sh_y = nullptr;
+        } else if (e == hipSuccess) {
             e = launch_ffn_layers(sh, x, nullptr, sh_off, *opts->shared, sh_y, base + L.sh_ffn, true, ss, nullptr);
+        }
         if (e == hipSuccess && branch) e = hipEventRecord(br.join, ss);
     }
     if (e == hipSuccess) {
@@ -214,9 +226,9 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
     if (e != hipSuccess) return hip_status(e);
     if (Sd > 1)
         e = launch_combine_partials(*s, part, Sd, pos, idx, gate, s->act == COLIBRI_ACT_SWIGLU ? nullptr : b2, out,
-                                    stream, sh_y, residual);
+                                    stream, sh_y, residual, shp);
     else
-        e = launch_combine(*s, y, pos, gate, out, stream, sh_y, residual);
+        e = launch_combine(*s, y, pos, gate, out, stream, sh_y, residual, shp);
     return hip_status(e);
 }
 
@@ -547,10 +559,15 @@ int colibri_moe_graph_create(const colibri_moe_shape_t *s, int32_t L, const coli
     br.aux = aux;
     hipGraph_t g = nullptr;
     hipGraphExec_t exec = nullptr;
+    // A few tokens (T <= 8): both the shared and the routed FFN split K until
+    // each alone fills the chip, and side by side they only contend (measured
+    // on the 15 + 1 shared layer at T = 1: 458 us for 8 layers with the branch,
+    // 432 without); from there on the branch pays (T = 64: 977 against 1180).
+    const Branch use = s->T > 8 ? br : Branch{};
     if (e == hipSuccess) e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
         for (int32_t l = 0; l < L && st == COLIBRI_OK; ++l)
-            st = step_layer(s, layers[l], residual != 0, x, ws, ws_bytes, cs, br);
+            st = step_layer(s, layers[l], residual != 0, x, ws, ws_bytes, cs, use);
         const hipError_t ce = hipStreamEndCapture(cs, &g);  // always ends the capture
         if (st == COLIBRI_OK && ce != hipSuccess) e = ce;
         if (st == COLIBRI_OK && e == hipSuccess) e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);

@@ -43,11 +43,51 @@ __device__ __forceinline__ void add_addends(float (&o)[VEC], const TE *__restric
     }
 }
 
+// The shared expert's row t, columns c .. c + VEC - 1, from its second layer's
+// S split partials (part[s][t][...], rows `stride` floats apart per split),
+// formed as the reduce forms it (8 interleaved sums in order, + b2, rounded to
+// bf16), then added to o.
+template <int VEC>
+__device__ __forceinline__ void add_shared_partials(float (&o)[VEC], const SharedPartials &sp, size_t at, int c) {
+    constexpr int U = 8;
+    float y8[8][VEC];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) y8[j][q] = 0.0f;
+    for (int s0 = 0; s0 < sp.S; s0 += U) {
+        float a[U][VEC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float *src = sp.part + (size_t)min(s0 + u, sp.S - 1) * sp.stride + at;
+#pragma unroll
+            for (int q4 = 0; q4 < VEC; q4 += 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(src + q4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a[u][q4 + r] = v[r];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s0 + u < sp.S)  // s0 is a multiple of 8: split s0 + u goes to sum u
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) y8[u][q] += a[u][q];
+    }
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += y8[j][q];
+        const float yb = acc + (sp.b2 ? bf16_to_f32(sp.b2[c + q]) : 0.0f);
+        o[q] += bf16_to_f32((uint16_t)f32_to_bf16_bits(yb));
+    }
+}
+
 template <typename TE>
 __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, const int32_t *__restrict__ pos,
                                                       const float *__restrict__ gate, TE *__restrict__ out, int T,
                                                       int d, const TE *__restrict__ shared,
-                                                      const TE *__restrict__ residual) {
+                                                      const TE *__restrict__ residual, SharedPartials sp) {
     constexpr int VEC = 16 / sizeof(TE);
     const int vpr = d / VEC;  // vectors per row
     const size_t total = (size_t)T * vpr;
@@ -69,7 +109,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, 
         float o[VEC];
 #pragma unroll
         for (int q = 0; q < VEC; ++q) o[q] = fmaf(g1, y1[q], g0 * y0[q]);
-        add_addends<TE, VEC>(o, shared, residual, (size_t)t * d + c);
+        if (sp.part) add_shared_partials<VEC>(o, sp, (size_t)t * d + c, c);  // bf16 layers only
+        add_addends<TE, VEC>(o, sp.part ? nullptr : shared, residual, (size_t)t * d + c);
         if constexpr (sizeof(TE) == 4) {
             *reinterpret_cast<f32x4 *>(out + (size_t)t * d + c) = f32x4{o[0], o[1], o[2], o[3]};
         } else {
@@ -98,7 +139,8 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                                                                const uint16_t *__restrict__ b2, int E,
                                                                uint16_t *__restrict__ out, int T, int d,
                                                                const uint16_t *__restrict__ shared,
-                                                               const uint16_t *__restrict__ residual) {
+                                                               const uint16_t *__restrict__ residual,
+                                                               SharedPartials sp) {
     typedef float fv __attribute__((ext_vector_type(VEC)));
     static_assert(L == 1 || L == 8, "lanes per output");
     static_assert(U % 8 == 0, "U keeps split s in interleaved sum s % 8");
@@ -171,6 +213,38 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                 }
                 y[sl][q] = acc;
             }
+        // the shared expert's row from its own split partials (L = 8: this lane's
+        // interleaved sum, added over the 8 lanes in order by lane 0)
+        float ysh[VEC];
+        if constexpr (L == 8) {
+            if (sp.part) {
+                float a8[VEC];
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) a8[q] = 0.0f;
+                const int nsh = sp.S > j0 ? (sp.S - j0 + L - 1) / L : 0;
+                for (int mb = 0; mb < nsh; mb += U) {
+                    fv a[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        a[u] = *reinterpret_cast<const fv *>(sp.part + (size_t)(j0 + L * min(mb + u, nsh - 1)) * sp.stride +
+                                                             (size_t)t * d + c);
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (mb + u < nsh)
+#pragma unroll
+                            for (int q = 0; q < VEC; ++q) a8[q] += a[u][q];
+                }
+                const int base = (int)(threadIdx.x & (kWave - 1)) & ~(L - 1);
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc += __shfl(a8[q], base + j);
+                    const float yb = acc + (sp.b2 ? bf16_to_f32(sp.b2[c + q]) : 0.0f);
+                    ysh[q] = bf16_to_f32((uint16_t)f32_to_bf16_bits(yb));
+                }
+            }
+        }
         if (j0 != 0) continue;
         float o[VEC];
 #pragma unroll
@@ -186,11 +260,19 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                 o[q] = sl == 0 ? g * yr : fmaf(g, yr, o[q]);
             }
         }
+        if (sp.part) {
+            if constexpr (L == 8) {
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) o[q] += ysh[q];
+            } else {
+                add_shared_partials<VEC>(o, sp, (size_t)t * d + c, c);
+            }
+        }
         if (shared || residual) {
             const size_t at = (size_t)t * d + c;
 #pragma unroll
             for (int q = 0; q < VEC; ++q) {
-                if (shared) o[q] += bf16_to_f32(shared[at + q]);
+                if (shared && !sp.part) o[q] += bf16_to_f32(shared[at + q]);
                 if (residual) o[q] += bf16_to_f32(residual[at + q]);
             }
         }
@@ -207,36 +289,37 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
 
 hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, const int32_t *assign_pos,
                           const float *topk_gate, void *out, hipStream_t st, const void *shared,
-                          const void *residual) {
+                          const void *residual, SharedPartials sp) {
     const int vec = s.dtype == COLIBRI_F32 ? 4 : 8;
     const size_t total = (size_t)s.T * (s.d / vec);
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
     if (s.dtype == COLIBRI_F32)
         combine_kernel<float><<<blocks, 256, 0, st>>>((const float *)y_sorted, assign_pos, topk_gate, (float *)out,
-                                                      s.T, s.d, (const float *)shared, (const float *)residual);
+                                                      s.T, s.d, (const float *)shared, (const float *)residual,
+                                                      SharedPartials{});  // fp32 layers have no split partials
     else
         combine_kernel<uint16_t><<<blocks, 256, 0, st>>>((const uint16_t *)y_sorted, assign_pos, topk_gate,
                                                          (uint16_t *)out, s.T, s.d, (const uint16_t *)shared,
-                                                         (const uint16_t *)residual);
+                                                         (const uint16_t *)residual, sp);
     return hipGetLastError();
 }
 
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
-                                   hipStream_t st, const void *shared, const void *residual) {
+                                   hipStream_t st, const void *shared, const void *residual, SharedPartials sp) {
     const size_t total = (size_t)s.T * (s.d / 4);
     if (S > 8 && total <= 65536) {  // few outputs and many splits: 8 lanes per output
         const int blocks = (int)std::min<size_t>((total * 8 + 255) / 256, 8192);
         combine_partials_kernel<4, 8, 8><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
                                                                  (const uint16_t *)b2, s.E, (uint16_t *)out, s.T,
                                                                  s.d, (const uint16_t *)shared,
-                                                                 (const uint16_t *)residual);
+                                                                 (const uint16_t *)residual, sp);
     } else {
         const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
         combine_partials_kernel<4, 16, 1><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
                                                                   (const uint16_t *)b2, s.E, (uint16_t *)out, s.T,
                                                                   s.d, (const uint16_t *)shared,
-                                                                  (const uint16_t *)residual);
+                                                                  (const uint16_t *)residual, sp);
     }
     return hipGetLastError();
 }

@@ -90,10 +90,22 @@ hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const
 // the scratch then holds the first layer's partials, then (256-aligned) the second's.
 bool decode_fuse_h(const colibri_moe_shape_t &s, bool q8 = false);
 // combine straight from the second layer's S split partials (adds them, b2, rounds Y, then gates)
-// shared, residual: optional [T, d] dtype addends (as in launch_combine)
+// A shared expert's second layer left as S split partials [S][rows][d] fp32
+// (row t = token t, `stride` = rows * d floats per split) with its bias b2 [d]
+// (bf16) or nullptr: the combine forms the shared row from them as the reduce
+// would.  part == nullptr: none.
+struct SharedPartials {
+    const float *part = nullptr;
+    int S = 0;
+    size_t stride = 0;
+    const uint16_t *b2 = nullptr;
+};
+// shared, residual: optional [T, d] dtype addends (as in launch_combine); sp:
+// the shared row from partials instead of `shared`
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
-                                   hipStream_t st, const void *shared = nullptr, const void *residual = nullptr);
+                                   hipStream_t st, const void *shared = nullptr, const void *residual = nullptr,
+                                   SharedPartials sp = SharedPartials{});
 // bf16 grouped MFMA GEMMs for T > 64 (ffn_gemm.hip).  A layer whose K is split
 // (gemm_splits > 1) writes fp32 partials [S][2T][cols] to scratch and then
 // reduces them (the second layer only when `reduce`; otherwise
@@ -140,7 +152,7 @@ hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, c
 // shared, residual: optional [T, d] dtype rows added after the gated pair
 hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, const int32_t *assign_pos,
                           const float *topk_gate, void *out, hipStream_t st, const void *shared = nullptr,
-                          const void *residual = nullptr);
+                          const void *residual = nullptr, SharedPartials sp = SharedPartials{});
 // offsets[0] = 0, offsets[1] = n (a one-expert group of n rows) by a kernel,
 // so the step can sit in a captured graph
 hipError_t launch_pair_offsets(int32_t *offsets, int n, hipStream_t st);
