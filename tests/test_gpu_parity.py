@@ -551,3 +551,48 @@ def test_layer_shape_edges(E, d, h, act, dt):
         near = G.near_tie_mask(lg)
         assert not np.any(np.any(gi != oracle.top2(lg), axis=1) & ~near)
         G.assert_close(G.host(out), ref["out"], dt, f"E={E} d={d} h={h} T={T}")
+
+
+ROUTER_SHAPES = [(24, 64, 1), (24, 320, 17), (40, 320, 33), (63, 192, 200), (48, 2048, 16), (9, 4096, 31),
+                 (2, 128, 40), (64, 128, 5)]
+
+
+@pytest.mark.parametrize("E,d,T", ROUTER_SHAPES, ids=[f"E{e}-d{d}-T{t}" for e, d, t in ROUTER_SHAPES])
+def test_router_odd_shapes_and_fused_path(E, d, T):
+    """The bf16 router at expert counts that leave part of a 16-expert column
+    tile empty, k-step counts that do not fill the waves evenly, and token
+    counts around the 16-token tiles; up to 32 tokens the layer routes with
+    the fused route + dispatch kernel, which must choose exactly what the route
+    entry point chooses."""
+    rng = np.random.default_rng(E * 1000 + d + T)
+    x = gen.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    w_r = gen.f32_to_bf16_bits((rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32))
+    b_r = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    sh = moe.Shape(T, d, 64, E, gen.BF16, moe.RELU)
+    idx = G.empty((T, 2), torch.int32)
+    gate = G.empty((T, 2), torch.float32)
+    lg = G.empty((T, E), torch.float32)
+    xd, wd, bd = G.dev(x), G.dev(w_r), G.dev(b_r)
+    moe.route(sh, xd, wd, bd, idx, gate, lg)
+    torch.cuda.synchronize()
+    idx_h, gate_h, lg_h = idx.cpu().numpy(), gate.cpu().numpy(), lg.cpu().numpy()
+    lg_ref = oracle.logits(x, w_r, b_r)
+    G.assert_fp32_close(lg_h, lg_ref, "logits")
+    assert np.array_equal(oracle.top2(lg_h.astype(np.float64)), idx_h)
+    near = G.near_tie_mask(lg_ref)
+    assert not np.any(np.any(idx_h != oracle.top2(lg_ref), axis=1) & ~near)
+    G.assert_fp32_close(gate_h, oracle.gates(lg_ref, idx_h), "gates")
+    # the whole layer (fused routing at T <= 32) picks the same experts and gates
+    w1 = G.dev(gen.f32_to_bf16_bits((rng.standard_normal((E, d, 64)) / np.sqrt(d)).astype(np.float32)))
+    w2 = G.dev(gen.f32_to_bf16_bits((rng.standard_normal((E, 64, d)) / 8).astype(np.float32)))
+    ws_bytes = moe.workspace_size(sh)
+    ws = G.empty((ws_bytes,), torch.uint8)
+    out = G.empty((T, d), torch.bfloat16)
+    idx2 = G.empty((T, 2), torch.int32)
+    gate2 = G.empty((T, 2), torch.float32)
+    counts = G.empty((E,), torch.int32)
+    moe.layer_forward(sh, xd, wd, bd, w1, w2, out, ws, ws_bytes, topk_idx=idx2, topk_gate=gate2, counts=counts)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), idx_h)
+    assert np.array_equal(gate2.cpu().numpy(), gate_h)
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(idx_h.reshape(-1), minlength=E))
