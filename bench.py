@@ -366,7 +366,7 @@ def main():
         log(f"cpu oracle: {cpu}")
 
     rec = {
-        "metric": "MoE-layer tokens/s (prefill) + us/step (decode); % of MFMA / HBM peak",
+        "metric": "MoE-layer tokens/s (prefill) + \u00b5s/step (decode); % of MFMA / HBM peak",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == gen.BF16 else "f32", "data": "synthetic (seeded Philox normals)",
