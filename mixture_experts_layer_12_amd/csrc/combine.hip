@@ -304,11 +304,14 @@ hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, co
     return hipGetLastError();
 }
 
+#ifndef COLIBRI_COMBINE_LANES_MIN_S
+#define COLIBRI_COMBINE_LANES_MIN_S 9
+#endif
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
                                    hipStream_t st, const void *shared, const void *residual, SharedPartials sp) {
     const size_t total = (size_t)s.T * (s.d / 4);
-    if (S > 8 && total <= 65536) {  // few outputs and many splits: 8 lanes per output
+    if (S >= COLIBRI_COMBINE_LANES_MIN_S && total <= 65536) {  // few outputs, several splits: 8 lanes per output
         const int blocks = (int)std::min<size_t>((total * 8 + 255) / 256, 8192);
         combine_partials_kernel<4, 8, 8><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
                                                                  (const uint16_t *)b2, s.E, (uint16_t *)out, s.T,
