@@ -16,9 +16,8 @@ hipError_t launch_route(const colibri_moe_shape_t &s, const void *x, const void 
                         int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t st,
                         int gate_mode = COLIBRI_GATE_PAIR);
 
-// route + dispatch in one launch for small batches (E <= 8, at most 2 token
-// groups of 64 / E rounded up to a power of two tokens); the results equal
-// launch_route followed by launch_dispatch bit for bit
+// route + dispatch in one launch for small batches (T <= 32; fp32 with E <= 2:
+// T <= 64); the results equal launch_route followed by launch_dispatch bit for bit
 bool route_dispatch_fusable(const colibri_moe_shape_t &s);
 hipError_t launch_route_dispatch(const colibri_moe_shape_t &s, const void *x, const void *w_r, const float *b_r,
                                  int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
@@ -89,7 +88,6 @@ hipError_t launch_decode_down(const colibri_moe_shape_t &s, const void *H, const
 // Decode sizes whose second layer rebuilds H from the first layer's partials;
 // the scratch then holds the first layer's partials, then (256-aligned) the second's.
 bool decode_fuse_h(const colibri_moe_shape_t &s, bool q8 = false);
-// combine straight from the second layer's S split partials (adds them, b2, rounds Y, then gates)
 // A shared expert's second layer left as S split partials [S][rows][d] fp32
 // (row t = token t, `stride` = rows * d floats per split) with its bias b2 [d]
 // (bf16) or nullptr: the combine forms the shared row from them as the reduce
@@ -100,8 +98,9 @@ struct SharedPartials {
     size_t stride = 0;
     const uint16_t *b2 = nullptr;
 };
-// shared, residual: optional [T, d] dtype addends (as in launch_combine); sp:
-// the shared row from partials instead of `shared`
+// combine straight from the second layer's S split partials (adds them, b2,
+// rounds Y, then gates).  shared, residual: optional [T, d] dtype addends (as
+// in launch_combine); sp: the shared row from partials instead of `shared`
 hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *part, int S, const int32_t *assign_pos,
                                    const int32_t *topk_idx, const float *topk_gate, const void *b2, void *out,
                                    hipStream_t st, const void *shared = nullptr, const void *residual = nullptr,

@@ -508,9 +508,10 @@ __global__ __launch_bounds__(kFusedWaves *kWave) void route_dispatch_mfma_kernel
 }
 
 // Waves per 16-token tile of the MFMA router: a power of two up to
-// mfma_maxw, each wave keeping at least 4 k-steps of 32 rows, G W <=
-// kMfmaMaxWaves in all; with at most kFusedGroups tiles also G W <= mfma_maxw (the
-// fused kernel uses the same W, so both paths form every logit identically).
+// mfma_maxw<EP>, each wave keeping at least 4 k-steps of 32 rows, G W <=
+// kMfmaMaxWaves in all; with at most kFusedGroups tiles also G W <= the fused
+// kernel's wave slots, min(kFusedWaves, mfma_maxw<EP>) (it uses the same W, so
+// both paths form every logit identically).
 #ifndef COLIBRI_MFMA_MAX_WAVES
 #define COLIBRI_MFMA_MAX_WAVES 8192
 #endif
@@ -518,9 +519,9 @@ constexpr int kMfmaMaxWaves = COLIBRI_MFMA_MAX_WAVES;  // waves of one launch at
 inline int mfma_waves(int T, int d, int EP) {
     const int G = ceil_div(T, 16);
     const int nks = d / 32;
-    const int maxw = EP == 64 ? 8 : 16;
+    const int maxw = EP == 64 ? mfma_maxw<64>() : mfma_maxw<32>();
     int W = 1;
-    const int fused = kFusedWaves < maxw ? kFusedWaves : maxw;  // the fused kernel's LDS holds maxw waves
+    const int fused = kFusedWaves < maxw ? kFusedWaves : maxw;
     while (W < maxw && nks >= 8 * W && G * W * 2 <= kMfmaMaxWaves && (G > kFusedGroups || G * W * 2 <= fused))
         W *= 2;
     return W;
