@@ -66,9 +66,12 @@ def load_library(path: Optional[str] = None):
     lib.oracle_round.argtypes = [_P, _P, z, i]
     lib.oracle_quantize_q8.argtypes = [_P, i, i, i, i, _P, _P]
     lib.oracle_ffn_rows_q8.argtypes = [i, i, i, i, i, _P, i, _P, _P] + [_P] * 8 + [_P]
+    lib.oracle_quantize_q4.argtypes = [_P, i, i, i, i, _P, _P, _P]
+    lib.oracle_ffn_rows_q4.argtypes = [i, i, i, i, i, _P, i, _P, _P] + [_P] * 11 + [_P]
     for f in ("oracle_set_threads", "oracle_logits", "oracle_top2", "oracle_gates", "oracle_dispatch",
               "oracle_ffn_rows", "oracle_combine", "oracle_layer", "oracle_round", "oracle_quantize_q8",
-              "oracle_ffn_rows_q8", "oracle_gates_mode", "oracle_combine_ex"):
+              "oracle_ffn_rows_q8", "oracle_gates_mode", "oracle_combine_ex", "oracle_quantize_q4",
+              "oracle_ffn_rows_q4"):
         getattr(lib, f).restype = None
     if path is None:
         _lib = lib
@@ -290,6 +293,66 @@ def layer_tokens_q8(x, w_r, q1, s1, q2, s2, act: str, tokens, b_r=None, q3=None,
     rt = np.repeat(np.arange(n, dtype=np.int32), 2)
     y = ffn_rows_q8(xs, rt, idx.reshape(-1), q1, s1, q2, s2, act, q3=q3, s3=s3, b1=b1, b2=b2, mirror=mirror,
                     lib=lib)
+    out = combine(y, np.arange(2 * n, dtype=np.int32), g, _dt(xs), lib=lib)
+    return {"logits": lg, "idx": idx, "gate": g, "y": y.reshape(n, 2, -1), "out": out}
+
+
+# ------------------------------------------------------------------ 4-bit expert weights
+Q4_GROUP = 128
+
+
+def quantize_q4(w, lib=None):
+    """4-bit codes [E, K, N] (uint8, 0..15), fp32 scales and uint8 zero points
+    [E, K/128, N] of w [E, K, N] (float32 or bf16 bits); W = s * (q - z)."""
+    lib = lib or load_library()
+    w = _c(w)
+    E, K, N = w.shape
+    if K % Q4_GROUP:
+        raise ValueError("K must be a multiple of 128")
+    q = np.empty((E, K, N), np.uint8)
+    s = np.empty((E, K // Q4_GROUP, N), np.float32)
+    z = np.empty((E, K // Q4_GROUP, N), np.uint8)
+    lib.oracle_quantize_q4(_ptr(w), _dt(w), E, K, N, _ptr(q), _ptr(s), _ptr(z))
+    return q, s, z
+
+
+def ffn_rows_q4(x, rows_token, rows_expert, w1q, w2q, act: str, w3q=None, b1=None, b2=None, mirror=True,
+                lib=None) -> np.ndarray:
+    """ffn_rows with 4-bit weights; each w*q is a (codes, scales, zeros) triple
+    as quantize_q4 returns it."""
+    lib = lib or load_library()
+    x, b1, b2 = _c(x), _c(b1), _c(b2)
+    dt = _dt(x)
+    for a in (b1, b2):
+        if a is not None and _dt(a) != dt:
+            raise TypeError("x and the biases share one dtype")
+    if act == "swiglu" and w3q is None:
+        raise ValueError("swiglu needs w3q")
+    f = lambda t: (None, None, None) if t is None else (_c(t[0], np.uint8), _c(t[1], np.float32), _c(t[2], np.uint8))
+    (q1, s1, z1), (q2, s2, z2), (q3, s3, z3) = f(w1q), f(w2q), f(w3q)
+    E, d, h = q1.shape
+    rt = _c(rows_token, np.int32)
+    re = _c(rows_expert, np.int32)
+    n = rt.shape[0]
+    y = np.empty((n, d), np.float64)
+    lib.oracle_ffn_rows_q4(d, h, dt, ACT[act], int(bool(mirror)), _ptr(x), n, _ptr(rt), _ptr(re), _ptr(q1),
+                           _ptr(s1), _ptr(z1), _ptr(q3), _ptr(s3), _ptr(z3), _ptr(q2), _ptr(s2), _ptr(z2),
+                           _ptr(b1), _ptr(b2), _ptr(y))
+    return y
+
+
+def layer_tokens_q4(x, w_r, w1q, w2q, act: str, tokens, b_r=None, w3q=None, b1=None, b2=None, mirror=True,
+                    idx_override=None, lib=None) -> Dict[str, np.ndarray]:
+    """layer_tokens with 4-bit expert weights."""
+    lib = lib or load_library()
+    tokens = np.asarray(tokens, np.int64)
+    xs = _c(np.asarray(x)[tokens])
+    lg = logits(xs, w_r, b_r, lib=lib)
+    idx = top2(lg, lib=lib) if idx_override is None else _c(idx_override, np.int32)
+    g = gates(lg, idx, lib=lib)
+    n = len(tokens)
+    rt = np.repeat(np.arange(n, dtype=np.int32), 2)
+    y = ffn_rows_q4(xs, rt, idx.reshape(-1), w1q, w2q, act, w3q=w3q, b1=b1, b2=b2, mirror=mirror, lib=lib)
     out = combine(y, np.arange(2 * n, dtype=np.int32), g, _dt(xs), lib=lib)
     return {"logits": lg, "idx": idx, "gate": g, "y": y.reshape(n, 2, -1), "out": out}
 

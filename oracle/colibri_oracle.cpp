@@ -30,7 +30,11 @@
 //    keeps the two softmax probabilities as they are; LINEAR_SCORE ([zskr]
 //    section 2.3) weights the outputs by the raw logits;
 //  * a shared expert ([rkmt] section 5.2) sees every token and adds its
-//    output with weight one; a residual row ([nxbn] section 2.1) is added last.
+//    output with weight one; a residual row ([nxbn] section 2.1) is added last;
+//  * 4-bit weights ([rkmt] section 4.2, AWQ with zero point, group 128): the
+//    groups run along the input channels, and the codes come from AWQ's
+//    closing min-max rounding (its activation-aware scale search needs
+//    calibration data and is not part of the stored format).
 //
 // Parity is pinned by the CPU tests (brute-force top-2, exhaustive tie
 // patterns, the page's printed gate pairs, a hand-worked dispatch, library
@@ -410,6 +414,96 @@ void oracle_ffn_rows_q8(int d, int h, int dt, int act, int mirror, const void *x
             const size_t whd = (size_t)e * h * d;
             output_row(h, d, act, mirror, dt, e, H,
                        [&](int j, int c) { return (double)s2[(size_t)e * d + c] * (double)q2[whd + (size_t)j * d + c]; },
+                       b2, y, y_out + (size_t)r * d);
+        }
+    }
+}
+
+// ---- 4-bit expert weights ([rkmt] section 4.2: 4-bit AWQ weights with a zero
+// point and a quantization group of 128).  A group is 128 consecutive input
+// channels k of one output column n of one expert; it has one fp32 scale and
+// one integer zero point.  AWQ's search for activation-aware scales needs
+// calibration activations; what is defined here is the storage format and the
+// min-max rounding that search ends with, in fp32, ties to even:
+//   mx, mn = the group's largest and smallest weight
+//   s = max(mx - mn, 1e-5) / 15
+//   z = -rint(mn / s) clamped to [0, 15]
+//   q = rint(w / s) + z clamped to [0, 15]
+// and the weight a code stands for is W = s * (q - z).
+constexpr int kQ4Group = 128;
+
+// q [E][K][N] codes (one per byte), scale and zero [E][K/128][N]; K % 128 == 0.
+void oracle_quantize_q4(const void *w, int dt, int E, int K, int N, uint8_t *q, float *scale, uint8_t *zero) {
+    const int G = K / kQ4Group;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long eg = 0; eg < (long)E * G; ++eg) {
+        const int e = (int)(eg / G), g = (int)(eg % G);
+        const size_t base = (size_t)e * K * N + (size_t)g * kQ4Group * N;  // row k0 = 128 g of expert e
+        const size_t sz = ((size_t)e * G + g) * N;
+        std::vector<float> mx(N), mn(N), sc(N), zf(N);
+        for (int n = 0; n < N; ++n) mx[n] = mn[n] = (float)load(w, dt, base + n);
+        for (int k = 1; k < kQ4Group; ++k)
+            for (int n = 0; n < N; ++n) {
+                const float v = (float)load(w, dt, base + (size_t)k * N + n);
+                if (v > mx[n]) mx[n] = v;
+                if (v < mn[n]) mn[n] = v;
+            }
+        for (int n = 0; n < N; ++n) {
+            const float range = mx[n] - mn[n];
+            sc[n] = (range > 1e-5f ? range : 1e-5f) / 15.0f;
+            float z = -std::nearbyint(mn[n] / sc[n]);  // default mode: ties to even
+            if (z < 0.0f) z = 0.0f;
+            if (z > 15.0f) z = 15.0f;
+            zf[n] = z;
+            scale[sz + n] = sc[n];
+            zero[sz + n] = (uint8_t)z;
+        }
+        for (int k = 0; k < kQ4Group; ++k)
+            for (int n = 0; n < N; ++n) {
+                const size_t i = base + (size_t)k * N + n;
+                float r = std::nearbyint((float)load(w, dt, i) / sc[n]) + zf[n];
+                if (r < 0.0f) r = 0.0f;
+                if (r > 15.0f) r = 15.0f;
+                q[i] = (uint8_t)r;
+            }
+    }
+}
+
+// Step 5 with 4-bit expert weights: the two-layer FFN on the dequantized
+// weights W[k][n] = s[k / 128][n] * (q[k][n] - z[k / 128][n]), each formed
+// exactly in double.  q1, q3 [E][d][h] with s1, z1, s3, z3 [E][d/128][h];
+// q2 [E][h][d] with s2, z2 [E][h/128][d].
+void oracle_ffn_rows_q4(int d, int h, int dt, int act, int mirror, const void *x, int nrows,
+                        const int32_t *row_token, const int32_t *row_expert, const uint8_t *q1, const float *s1,
+                        const uint8_t *z1, const uint8_t *q3, const float *s3, const uint8_t *z3, const uint8_t *q2,
+                        const float *s2, const uint8_t *z2, const void *b1, const void *b2, double *y_out) {
+    const int G1 = d / kQ4Group, G2 = h / kQ4Group;
+#pragma omp parallel
+    {
+        std::vector<double> xr(d), u(h), v(h), H(h), y(d);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; ++r) {
+            const int t = row_token[r], e = row_expert[r];
+            const size_t wdh = (size_t)e * d * h;
+            for (int k = 0; k < d; ++k) xr[k] = load(x, dt, (size_t)t * d + k);
+            std::fill(u.begin(), u.end(), 0.0);
+            std::fill(v.begin(), v.end(), 0.0);
+            for (int k = 0; k < d; ++k) {
+                const double xk = xr[k];
+                const size_t gz = ((size_t)e * G1 + k / kQ4Group) * h;
+                for (int j = 0; j < h; ++j)
+                    u[j] += xk * ((double)s1[gz + j] * ((double)q1[wdh + (size_t)k * h + j] - (double)z1[gz + j]));
+                if (act == ACT_SWIGLU)
+                    for (int j = 0; j < h; ++j)
+                        v[j] += xk * ((double)s3[gz + j] * ((double)q3[wdh + (size_t)k * h + j] - (double)z3[gz + j]));
+            }
+            hidden_row(h, act, mirror, dt, e, u, v, b1, H);
+            const size_t whd = (size_t)e * h * d;
+            output_row(h, d, act, mirror, dt, e, H,
+                       [&](int j, int c) {
+                           const size_t gz = ((size_t)e * G2 + j / kQ4Group) * d + c;
+                           return (double)s2[gz] * ((double)q2[whd + (size_t)j * d + c] - (double)z2[gz]);
+                       },
                        b2, y, y_out + (size_t)r * d);
         }
     }

@@ -475,6 +475,91 @@ def pin_q8_ffn_library(lib):
             np.testing.assert_allclose(y[r], ref, rtol=1e-11, atol=1e-13)
 
 
+# ----------------------------------------------------------------- 4-bit expert weights
+def pin_q4_quantize_hand_example(lib):
+    kv = _read_kv(os.path.join(GOLDEN, "q4_quantize_hand_example.txt"))
+    cols = []
+    for c in range(4):
+        col = np.full(128, kv[f"col{c}_rest"][0], np.float32)
+        col[:8] = kv[f"col{c}_head"]
+        cols.append(col)
+    w = np.stack(cols, axis=1)[None]  # [1, 128, 4]
+    for dt_w in (w, gen.f32_to_bf16_bits(w)):  # the values are bf16-exact too
+        q, sc, z = oracle.quantize_q4(dt_w, lib=lib)
+        for c in range(4):
+            want = [int(v) for v in kv[f"col{c}_q"]] + [int(kv[f"col{c}_qrest"][0])] * 120
+            assert q[0, :, c].tolist() == want, (c, q[0, :8, c])
+            assert sc[0, 0, c] == np.float32(kv[f"col{c}_s"][0]), (c, sc[0, 0, c])
+            assert z[0, 0, c] == int(kv[f"col{c}_z"][0]), (c, z[0, 0, c])
+
+
+def pin_q4_quantize_bounds(lib):
+    """Random groups: codes and zero points in [0, 15]; a code that was not
+    clamped stands for a weight within s/2 of w, and the group's smallest
+    weight gets code 0 whenever its zero point was not clamped; codes are
+    monotone in w inside a group; a group is 128 consecutive k of one column
+    (changing one weight moves only that group's scale)."""
+    rng = np.random.default_rng(31)
+    E, K, N = 2, 384, 24
+    w = (rng.standard_normal((E, K, N)) * rng.uniform(0.01, 3.0, (E, 1, N))).astype(np.float32)
+    w[0, 128:256, 3] += 5.0  # an all-positive group: its zero point clamps to 0
+    q, sc, z = oracle.quantize_q4(w, lib=lib)
+    assert q.min() >= 0 and q.max() <= 15 and z.min() >= 0 and z.max() <= 15
+    s_full = np.repeat(sc, 128, axis=1).astype(np.float64)
+    z_full = np.repeat(z, 128, axis=1).astype(np.float64)
+    deq = s_full * (q.astype(np.float64) - z_full)
+    raw = np.rint((w / np.repeat(sc, 128, axis=1)).astype(np.float32)).astype(np.float64) + z_full
+    unclamped = (raw >= 0) & (raw <= 15)
+    assert unclamped.mean() > 0.95
+    err = np.abs(deq - w.astype(np.float64))
+    assert np.all(err[unclamped] <= s_full[unclamped] * (0.5 + 1e-5)), err[unclamped].max()
+    g = w.reshape(E, K // 128, 128, N)
+    gq = q.reshape(E, K // 128, 128, N)
+    zmn = -np.rint((g.min(axis=2) / sc).astype(np.float32))
+    for e in range(E):
+        for gi in range(K // 128):
+            for n in range(N):
+                col, cq = g[e, gi, :, n], gq[e, gi, :, n]
+                o = np.argsort(col, kind="stable")
+                assert np.all(np.diff(cq[o].astype(int)) >= 0), (e, gi, n)
+                if 0 <= zmn[e, gi, n] <= 15:
+                    assert cq[o[0]] == 0, (e, gi, n)
+    assert z[0, 1, 3] == 0
+    w2 = w.copy()
+    w2[1, 200, 7] = 40.0
+    _, sc2, _ = oracle.quantize_q4(w2, lib=lib)
+    changed = np.argwhere(sc2 != sc)
+    assert changed.tolist() == [[1, 1, 7]], changed
+
+
+def pin_q4_ffn_library(lib):
+    """Random codes, scales and zero points against numpy matmuls on
+    s * (q - z) (fp64), groups of 128 along the input channels."""
+    rng = np.random.default_rng(32)
+    d, h, E = 256, 384, 2
+    x = _rand_f32(rng, (3, d))
+    for act in ("relu", "gelu", "swiglu"):
+        def mk(K, N):
+            return (rng.integers(0, 16, (E, K, N)).astype(np.uint8),
+                    (rng.uniform(0.5, 2.0, (E, K // 128, N)) / 15 / np.sqrt(K)).astype(np.float32),
+                    rng.integers(0, 16, (E, K // 128, N)).astype(np.uint8))
+        w1q, w3q, w2q = mk(d, h), mk(d, h), mk(h, d)
+        b1 = _rand_f32(rng, (E, h), 0.1) if act != "swiglu" else None
+        b2 = _rand_f32(rng, (E, d), 0.1) if act != "swiglu" else None
+        sw = act == "swiglu"
+        rows_t = np.array([0, 1, 2, 1], np.int32)
+        rows_e = np.array([1, 0, 1, 1], np.int32)
+        y = oracle.ffn_rows_q4(x, rows_t, rows_e, w1q, w2q, act, w3q=w3q if sw else None, b1=b1, b2=b2,
+                               mirror=False, lib=lib)
+        deq = lambda t, e: (np.repeat(t[1][e], 128, axis=0).astype(np.float64) *
+                            (t[0][e].astype(np.float64) - np.repeat(t[2][e], 128, axis=0).astype(np.float64)))
+        for r, (t, e) in enumerate(zip(rows_t, rows_e)):
+            ref = _np_ffn(x[t].astype(np.float64), deq(w1q, e), None if b1 is None else b1[e].astype(np.float64),
+                          deq(w2q, e), None if b2 is None else b2[e].astype(np.float64), act,
+                          deq(w3q, e) if sw else None)
+            np.testing.assert_allclose(y[r], ref, rtol=1e-11, atol=1e-13)
+
+
 # ----------------------------------------------------------------- gating variants, shared expert, residual
 def pin_gate_modes_hand_example(lib):
     kv = _read_kv(os.path.join(GOLDEN, "gate_modes_hand_example.txt"))

@@ -47,6 +47,17 @@ MUTANTS = {
                                  "sc[n - n0] = amax[n - n0] / 127.0f;"),
     "q8_scale_over_128": ("sc[n - n0] = amax[n - n0] > 0.0f ? amax[n - n0] / 127.0f : 1.0f;",
                           "sc[n - n0] = amax[n - n0] > 0.0f ? amax[n - n0] / 128.0f : 1.0f;"),
+    "q4_zero_sign_flipped": ("float z = -std::nearbyint(mn[n] / sc[n]);", "float z = std::nearbyint(mn[n] / sc[n]);"),
+    "q4_ties_away_from_zero": ("float r = std::nearbyint((float)load(w, dt, i) / sc[n]) + zf[n];",
+                               "float r = std::round((float)load(w, dt, i) / sc[n]) + zf[n];"),
+    "q4_scale_over_16": ("sc[n] = (range > 1e-5f ? range : 1e-5f) / 15.0f;",
+                         "sc[n] = (range > 1e-5f ? range : 1e-5f) / 16.0f;"),
+    "q4_zero_point_dropped": ("((double)q1[wdh + (size_t)k * h + j] - (double)z1[gz + j])",
+                              "(double)q1[wdh + (size_t)k * h + j]"),
+    "q4_w3_takes_w1_zero": ("((double)q3[wdh + (size_t)k * h + j] - (double)z3[gz + j])",
+                            "((double)q3[wdh + (size_t)k * h + j] - (double)z1[gz + j])"),
+    "q4_second_layer_unscaled": ("return (double)s2[gz] * ((double)q2[whd + (size_t)j * d + c] - (double)z2[gz]);",
+                                 "return ((double)q2[whd + (size_t)j * d + c] - (double)z2[gz]);"),
     "softmax_gates_renormalised": ("gate[2 * t] = std::exp(l[idx[2 * t]] - m) / z;",
                                    "gate[2 * t] = std::exp(l[idx[2 * t]] - m) / (std::exp(l[idx[2 * t]] - m) + "
                                    "std::exp(l[idx[2 * t + 1]] - m));"),
