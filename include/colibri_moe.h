@@ -312,6 +312,55 @@ int colibri_moe_layer_forward_q8(const colibri_moe_shape_t *s, const void *x, co
                                  float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* ------------------------------------------------------------------ 4-bit expert weights
+ * Expert weights stored as 4-bit codes with a zero point, in groups of 128
+ * input channels ([rkmt] section 4.2: 4-bit AWQ weights, quantization group
+ * 128, zero point; a quarter of the bf16 weight bytes plus the group scales):
+ *   W[e][k][n] = s[e][k/128][n] * (q[e][k][n] - z[e][k/128][n]),  q, z in [0, 15].
+ *   q1 [E][d/8][h], q3 [E][d/8][h] (SwiGLU only, else NULL), q2 [E][h/8][d]
+ *       uint32 words, 16-byte aligned; word (e, j, n) packs the codes of
+ *       k = 8j .. 8j+7 of column n, the code of k = 8j + i in bits 4i .. 4i+3
+ *   s1, s3 [E][d/128][h], s2 [E][h/128][d]   fp32 group scales, 16-byte aligned
+ *   z1, z3 [E][d/128][h], z2 [E][h/128][d]   uint8 zero points, 8-byte aligned
+ *   b1 [E][h], b2 [E][d]   as in colibri_moe_experts_t (NULL = zero; NULL for SwiGLU)
+ * The layer computes what it computes with the dequantized weights in full
+ * precision: each group's sum is formed from the codes and scaled once.
+ * These entry points stream weights at decode sizes: they take bf16 layers
+ * with T <= 64 and d, h multiples of 128, and return COLIBRI_ERR_UNSUPPORTED
+ * for other shapes. */
+typedef struct {
+    const uint32_t *q1, *q3, *q2;
+    const float *s1, *s3, *s2;
+    const uint8_t *z1, *z3, *z2;
+    const void *b1, *b2;
+} colibri_moe_experts_q4_t;
+
+/* 4-bit quantization of one weight tensor (producing q1, q3 or q2 with its
+ * scales and zero points), AWQ's min-max rounding with zero point.  For every
+ * expert e, group g (k = 128 g .. 128 g + 127) and column n, in fp32:
+ *   mx, mn = the largest and smallest w[e][k][n] of the group,
+ *   s = max(mx - mn, 1e-5) / 15,   z = -rint(mn / s) clamped to [0, 15],
+ *   q[e][k][n] = rint(w[e][k][n] / s) + z clamped to [0, 15]
+ * (rint: nearest, ties to even).  AWQ's activation-aware choice of scales
+ * needs calibration activations and is not done here.
+ *   w [E][K][N] dtype, 16-byte aligned;  q [E][K/8][N] uint32 out (packed as
+ *   above, 16-byte aligned);  s [E][K/128][N] fp32 out;  z [E][K/128][N] uint8 out.
+ * E, N >= 1; K >= 128 a multiple of 128; N a multiple of 4. */
+int colibri_moe_quantize_q4(const void *w, colibri_dtype_t dtype, int32_t E, int32_t K, int32_t N, uint32_t *q,
+                            float *s, uint8_t *z, hipStream_t stream);
+
+/* Step 4 with 4-bit expert weights; arguments as for colibri_moe_expert_ffn.
+ * ws must hold colibri_moe_workspace_size(s) bytes, 256-byte aligned. */
+int colibri_moe_expert_ffn_q4(const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                              const int32_t *expert_offsets, const colibri_moe_experts_q4_t *w, void *y_sorted,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps 1-5 with 4-bit expert weights; arguments as for colibri_moe_layer_forward. */
+int colibri_moe_layer_forward_q4(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                                 const colibri_moe_experts_q4_t *w, void *out, int32_t *topk_idx_out,
+                                 float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *colibri_moe_status_string(int status);
 

@@ -27,6 +27,7 @@ EXPORTED = [
     "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_dispatch_workspace_size",
     "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
     "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
+    "colibri_moe_quantize_q4", "colibri_moe_expert_ffn_q4", "colibri_moe_layer_forward_q4",
     "colibri_moe_workspace_size_ex", "colibri_moe_route_ex", "colibri_moe_combine_ex",
     "colibri_moe_layer_forward_ex", "colibri_moe_step_workspace_size", "colibri_moe_step_forward",
     "colibri_moe_graph_create", "colibri_moe_graph_launch", "colibri_moe_graph_destroy",
@@ -54,6 +55,10 @@ class _ExpertsQ8(ctypes.Structure):
     _fields_ = [("q1", ctypes.c_void_p), ("q3", ctypes.c_void_p), ("q2", ctypes.c_void_p),
                 ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
                 ("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
+
+
+class _ExpertsQ4(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q1", "q3", "q2", "s1", "s3", "s2", "z1", "z3", "z2", "b1", "b2")]
 
 
 class _Opts(ctypes.Structure):
@@ -119,6 +124,9 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_quantize_q8.argtypes = [P, I, i32, i32, i32, P, P, P]
     lib.colibri_moe_expert_ffn_q8.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ8), P, P, Z, P]
     lib.colibri_moe_layer_forward_q8.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ8), P, P, P, P, P, Z, P]
+    lib.colibri_moe_quantize_q4.argtypes = [P, I, i32, i32, i32, P, P, P, P]
+    lib.colibri_moe_expert_ffn_q4.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ4), P, P, Z, P]
+    lib.colibri_moe_layer_forward_q4.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ4), P, P, P, P, P, Z, P]
     OP = ctypes.POINTER(_Opts)
     lib.colibri_moe_workspace_size_ex.argtypes = [SP, OP]
     lib.colibri_moe_workspace_size_ex.restype = Z
@@ -135,6 +143,7 @@ def load(build_if_missing: bool = False):
     for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up",
               "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
               "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
+              "colibri_moe_quantize_q4", "colibri_moe_expert_ffn_q4", "colibri_moe_layer_forward_q4",
               "colibri_moe_route_ex", "colibri_moe_combine_ex", "colibri_moe_layer_forward_ex",
               "colibri_moe_step_forward", "colibri_moe_graph_create", "colibri_moe_graph_launch",
               "colibri_moe_graph_destroy"):
@@ -373,6 +382,40 @@ def layer_forward_q8(shape: Shape, x, w_r, b_r, q1, s1, q2, s2, out, ws, ws_byte
     _check(load().colibri_moe_layer_forward_q8(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
                                                _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
                                                ws_bytes, _stream(stream)), "colibri_moe_layer_forward_q8")
+
+
+# ------------------------------------------------------------------ 4-bit expert weights
+def _experts_q4(w1q, w2q, w3q=None, b1=None, b2=None) -> _ExpertsQ4:
+    t = lambda w: (None, None, None) if w is None else w
+    (q1, s1, z1), (q2, s2, z2), (q3, s3, z3) = t(w1q), t(w2q), t(w3q)
+    return _ExpertsQ4(_ptr(q1), _ptr(q3), _ptr(q2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(z1), _ptr(z3), _ptr(z2),
+                      _ptr(b1), _ptr(b2))
+
+
+def quantize_q4(w, dtype: int, E: int, K: int, N: int, q, scale, zero, stream=None):
+    """4-bit codes q [E, K/8, N] (uint32 words of 8 codes), fp32 scales and uint8
+    zero points [E, K/128, N] of w [E, K, N]."""
+    _check(load().colibri_moe_quantize_q4(_ptr(w), int(dtype), int(E), int(K), int(N), _ptr(q), _ptr(scale),
+                                          _ptr(zero), _stream(stream)), "colibri_moe_quantize_q4")
+
+
+def expert_ffn_q4(shape: Shape, x_rows, sorted_assign, offsets, w1q, w2q, y_sorted, ws, ws_bytes: int, w3q=None,
+                  b1=None, b2=None, stream=None):
+    """w1q, w2q, w3q: (codes, scales, zero points) device triples."""
+    s = shape.c()
+    e = _experts_q4(w1q, w2q, w3q, b1, b2)
+    _check(load().colibri_moe_expert_ffn_q4(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
+                                            ctypes.byref(e), _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
+           "colibri_moe_expert_ffn_q4")
+
+
+def layer_forward_q4(shape: Shape, x, w_r, b_r, w1q, w2q, out, ws, ws_bytes: int, w3q=None, b1=None, b2=None,
+                     topk_idx=None, topk_gate=None, counts=None, stream=None):
+    s = shape.c()
+    e = _experts_q4(w1q, w2q, w3q, b1, b2)
+    _check(load().colibri_moe_layer_forward_q4(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
+                                               _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
+                                               ws_bytes, _stream(stream)), "colibri_moe_layer_forward_q4")
 
 
 class MoELayer:

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcolibri_moe.so")
 
 SOURCES = ["abi.cpp", "route.hip", "dispatch.hip", "ffn.hip", "ffn_gemm.hip", "ffn_decode.hip", "combine.hip",
-           "quantize.hip"]
+           "quantize.hip", "ffn_decode_q4.hip"]
 ARCH = os.environ.get("COLIBRI_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

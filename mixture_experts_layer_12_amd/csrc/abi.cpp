@@ -77,6 +77,25 @@ int check_experts_q8(const colibri_moe_shape_t *s, const colibri_moe_experts_q8_
     return COLIBRI_OK;
 }
 
+// 4-bit expert weights: decode-size bf16 layers with d, h multiples of 128;
+// codes, scales and zero points present for the layers the call reads.
+int check_experts_q4(const colibri_moe_shape_t *s, const colibri_moe_experts_q4_t *w) {
+    if (!w) return COLIBRI_ERR_INVALID_ARG;
+    if (!ffn_q4_eligible(*s)) return COLIBRI_ERR_UNSUPPORTED;
+    auto ok = [](const uint32_t *q, const float *sc, const uint8_t *z) {
+        return q && sc && z && aligned(q, 16) && aligned(sc, 16) && aligned(z, 8);
+    };
+    if (!ok(w->q1, w->s1, w->z1) || !ok(w->q2, w->s2, w->z2)) return COLIBRI_ERR_INVALID_ARG;
+    if (s->act == COLIBRI_ACT_SWIGLU) {
+        if (!ok(w->q3, w->s3, w->z3)) return COLIBRI_ERR_INVALID_ARG;
+        if (w->b1 || w->b2) return COLIBRI_ERR_UNSUPPORTED;
+    } else {
+        if (w->q3 || w->s3 || w->z3) return COLIBRI_ERR_UNSUPPORTED;
+        if ((w->b1 && !aligned(w->b1, 2)) || (w->b2 && !aligned(w->b2, 2))) return COLIBRI_ERR_INVALID_ARG;
+    }
+    return COLIBRI_OK;
+}
+
 // The shared expert runs as a one-expert group over the T token rows of x:
 // shape {ceil(T / 2), d, shared_h, E = 1} (the FFN kernels work on 2T rows
 // of a shape; its one expert gets rows [0, T), so x is read in place and its
@@ -465,6 +484,54 @@ int colibri_moe_quantize_q8(const void *w, colibri_dtype_t dtype, int32_t E, int
     if ((int64_t)E * K * N > ((int64_t)1 << 40)) return COLIBRI_ERR_UNSUPPORTED;
     if (!aligned(w, 16) || !aligned(q, 4) || !aligned(scale, 4)) return COLIBRI_ERR_INVALID_ARG;
     return hip_status(launch_quantize_q8(w, dtype, E, K, N, q, scale, stream));
+}
+
+int colibri_moe_quantize_q4(const void *w, colibri_dtype_t dtype, int32_t E, int32_t K, int32_t N, uint32_t *q,
+                            float *scale, uint8_t *zero, hipStream_t stream) {
+    if (!w || !q || !scale || !zero) return COLIBRI_ERR_INVALID_ARG;
+    if (dtype != COLIBRI_F32 && dtype != COLIBRI_BF16) return COLIBRI_ERR_UNSUPPORTED;
+    if (E < 1 || K < 128 || K % 128 || N < 1 || N % 4) return COLIBRI_ERR_UNSUPPORTED;
+    if ((int64_t)E * K * N > ((int64_t)1 << 40)) return COLIBRI_ERR_UNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 16) || !aligned(zero, 4))
+        return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(launch_quantize_q4(w, dtype, E, K, N, q, scale, zero, stream));
+}
+
+int colibri_moe_layer_forward_q4(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                                 const colibri_moe_experts_q4_t *w, void *out, int32_t *topk_idx_out,
+                                 float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts_q4(s, w);
+    if (st != COLIBRI_OK) return st;
+    return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes,
+                              stream, w->b2, ffn_down_splits_q4(*s),
+                              [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
+                                  const float **part) {
+                                  return launch_ffn_layers_q4(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
+                                                              part);
+                              });
+}
+
+int colibri_moe_expert_ffn_q4(const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                              const int32_t *expert_offsets, const colibri_moe_experts_q4_t *w, void *y_sorted,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts_q4(s, w);
+    if (st != COLIBRI_OK) return st;
+    if (!x_rows || !expert_offsets || !y_sorted) return COLIBRI_ERR_INVALID_ARG;
+    if (!aligned(x_rows, 16) || !aligned(y_sorted, 16) || !aligned(expert_offsets, 4) ||
+        (sorted_assign && !aligned(sorted_assign, 4)))
+        return COLIBRI_ERR_INVALID_ARG;
+    const size_t need = ffn_workspace_bytes(*s);
+    if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    return hip_status(
+        launch_ffn_layers_q4(*s, x_rows, sorted_assign, expert_offsets, *w, y_sorted, ws, true, stream, nullptr));
 }
 
 size_t colibri_moe_workspace_size_ex(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *opts) {

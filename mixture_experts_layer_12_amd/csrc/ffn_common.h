@@ -46,4 +46,29 @@ __device__ __forceinline__ void store_epilogue(uint16_t *dst, const float (&u)[C
     }
 }
 
+// i-th set bit of a 64-bit mask (wave-uniform loop)
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int i) {
+    for (int q = 0; q < i; ++q) m &= m - 1;
+    return __ffsll((unsigned long long)m) - 1;
+}
+
+// Live expert `slot` (experts with rows, in index order): e, first row, row count.
+// Returns false when fewer experts are live.  Whole-wave call.
+__device__ __forceinline__ bool live_expert(const int32_t *__restrict__ offsets, int E, int A_total, int slot,
+                                            int &e, int &r0, int &count) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int lo_l = 0, cnt_l = 0;
+    if (lane < E) {
+        lo_l = min(max(offsets[lane], 0), A_total);
+        const int hi = min(max(offsets[lane + 1], lo_l), A_total);
+        cnt_l = hi - lo_l;
+    }
+    const uint64_t live = __ballot(cnt_l > 0);
+    if (__popcll(live) <= slot) return false;
+    e = nth_set_bit(live, slot);
+    r0 = __shfl(lo_l, e);
+    count = __shfl(cnt_l, e);
+    return true;
+}
+
 }  // namespace colibri

@@ -50,12 +50,6 @@ namespace {
 
 constexpr int kDecWaves = 4;  // waves (adjacent column blocks) per workgroup
 
-// i-th set bit of a 64-bit mask (wave-uniform loop)
-__device__ __forceinline__ int nth_set_bit(uint64_t m, int i) {
-    for (int q = 0; q < i; ++q) m &= m - 1;
-    return __ffsll((unsigned long long)m) - 1;
-}
-
 // The 8 x 8 bf16 block in rows r[0..7] (r[i] = columns c..c+7 of k-row i)
 // becomes eight B fragments: frag[j] = (k-rows 0..7 of column c + j).
 __device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], bf16x8 (&frag)[8]) {
@@ -106,25 +100,6 @@ __device__ __forceinline__ void transpose8x16_q8(const u32x4 (&r)[8], bf16x8 (&f
                                          q8_f32_bits(r[2 * p][j >> 2], j & 3), 0x07060302u);
         frag[jj] = __builtin_bit_cast(bf16x8, o);
     }
-}
-
-// Live expert `slot` (experts with rows, in index order): e, first row, row count.
-// Returns false when fewer experts are live.  Whole-wave call.
-__device__ __forceinline__ bool live_expert(const int32_t *__restrict__ offsets, int E, int A_total, int slot,
-                                            int &e, int &r0, int &count) {
-    const int lane = threadIdx.x & (kWave - 1);
-    int lo_l = 0, cnt_l = 0;
-    if (lane < E) {
-        lo_l = min(max(offsets[lane], 0), A_total);
-        const int hi = min(max(offsets[lane + 1], lo_l), A_total);
-        cnt_l = hi - lo_l;
-    }
-    const uint64_t live = __ballot(cnt_l > 0);
-    if (__popcll(live) <= slot) return false;
-    e = nth_set_bit(live, slot);
-    r0 = __shfl(lo_l, e);
-    count = __shfl(cnt_l, e);
-    return true;
 }
 
 // HEPI >= 0: second layer whose A rows (H) are rebuilt by the workgroup from
@@ -543,7 +518,7 @@ size_t ffn_decode_scratch_bytes(const colibri_moe_shape_t &s) {
         const size_t up = decode_plan(s, true, q8).part_bytes, down = decode_plan(s, false, q8).part_bytes;
         need = std::max(need, decode_fuse_h(s, q8) ? align256(up) + down : std::max(up, down));
     }
-    return need;
+    return std::max(need, ffn_decode_q4_scratch_bytes(s));  // 4-bit weights
 }
 
 namespace {

@@ -1,0 +1,364 @@
+// Weight-streaming expert FFN for decode-sized batches with 4-bit expert
+// weights (zero point, groups of 128 input channels).
+//
+// Colibri write-ups: [rkmt] http://news.rkmt.cn/news/2271114 section 4.2
+// (4-bit AWQ expert weights, quantization group 128, zero point: the weight
+// bytes a decode step streams drop to a quarter); [zskr]
+// http://www.zskr.cn/news/2272131 section 2.2 (top-2 activates 2 of the
+// experts: only their weights need to move).
+//
+//   W[e][k][n] = s[e][k/128][n] * (q[e][k][n] - z[e][k/128][n]),  q, z in [0, 15]
+//
+// Layout: word (e, j, n) of q [E][K/8][N] packs the codes of k = 8j .. 8j+7 of
+// column n (the code of k = 8j + i in bits 4i .. 4i+3), so one word is the
+// eight k a lane feeds to one column of v_mfma_f32_16x16x32_bf16, and a lane's
+// eight columns of a k-step are 32 contiguous bytes.
+//
+// Design (as the bf16 weight-streaming kernel, with the weights 4x smaller):
+//   * a wave owns (live expert, 128 columns -- SwiGLU: 64 of W1 and 64 of W3 --,
+//     K split); 4 waves of a workgroup take adjacent column blocks;
+//   * a code becomes an exact bf16 operand with no conversion: the bit
+//     pattern 0x4300 | q is the bf16 value 128 + q (bf16 has 7 fraction bits,
+//     so 128 .. 143 are exact), built for two k at once with one byte permute
+//     and one OR.  The MFMAs accumulate x * (128 + q) over a group, and one
+//     more MFMA per k-step against a B operand of ones accumulates the rows'
+//     sums of x over the group, so that at the end of every group
+//       total += s * (acc - (128 + z) * rowsum_x)
+//     is the group's exact contribution (up to fp32 rounding);
+//   * several k-steps of codes are in flight per wave (each k-step is 2 KB
+//     per wave); the group scales and zero points (40 bytes per lane and
+//     group) are read at each group's start and used at its end;
+//   * K splits run along whole groups; split partials (fp32) are added by
+//     the split reduce or, for the second layer inside the layer call, by the
+//     combine.
+#include "device_common.h"
+#include "ffn_common.h"
+#include "launchers.h"
+
+namespace colibri {
+namespace {
+
+constexpr int kQ4Waves = 4;   // waves (adjacent column blocks) per workgroup
+constexpr int kQ4Group = 128; // k per scale / zero point
+
+// The eight words of a lane's eight columns (w[j / 4][j % 4] = column j, k 0..7)
+// -> eight B fragments holding 128 + q.  Byte p of a word holds the codes of
+// k = 2p (low nibble) and 2p + 1 (high nibble); fragment dword p = k 2p, 2p + 1.
+__device__ __forceinline__ void unpack_q4(const u32x4 (&w)[2], bf16x8 (&frag)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t x = w[j >> 2][j & 3];
+        const uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
+        u32x4 o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)  // bytes: lo.p, 0, hi.p, 0  (selector 12 gives a zero byte)
+            o[p] = __builtin_amdgcn_perm(hi, lo, 0x0c000c00u | ((4u + p) << 16) | (uint32_t)p) | 0x43004300u;
+        frag[j] = __builtin_bit_cast(bf16x8, o);
+    }
+}
+
+template <int MB, int NST, int EPI, bool GATHER>
+__global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
+    const int32_t *__restrict__ offsets, int E, const uint32_t *__restrict__ Q0, const uint32_t *__restrict__ Q1,
+    const float *__restrict__ S0, const float *__restrict__ S1, const uint8_t *__restrict__ Z0,
+    const uint8_t *__restrict__ Z1, const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N,
+    int NCB, int S, float *__restrict__ part) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int WCOLS = DUAL ? 64 : 128;  // output columns per wave (per matrix)
+    constexpr int ROWS = MB * 16;
+    static_assert(NST % 4 == 0, "stages cover whole groups");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ncbg = (NCB + kQ4Waves - 1) / kQ4Waves;
+    const int cbg = blockIdx.x % ncbg;
+    const int rest = blockIdx.x / ncbg;
+    const int split = rest % S;
+    const int slot = rest / S;
+    const int cb = cbg * kQ4Waves + (int)(threadIdx.x / kWave);
+    if (cb >= NCB) return;
+
+    const int A_total = 2 * T;
+    int e, r0, count;
+    if (!live_expert(offsets, E, A_total, slot, e, r0, count)) return;
+
+    const int c = lane & 15;  // column group: columns ccol .. ccol + 7
+    const int g = lane >> 4;  // k group: k 8g .. 8g+7 of a 32-deep step
+    const bool third = DUAL && c >= 8;  // SwiGLU: lanes 8..15 hold W3's columns
+    const uint32_t *Qm = third ? Q1 : Q0;
+    const float *Sm = third ? S1 : S0;
+    const uint8_t *Zm = third ? Z1 : Z0;
+    const int ccol = cb * WCOLS + 8 * (DUAL ? (c & 7) : c);
+    const bool col_ok = ccol < N;
+    const int col = col_ok ? ccol : 0;  // padding lanes read column block 0 (never stored)
+    const int G = K / kQ4Group;
+    // word (k-step st, k group g) of this lane's columns: row 4 st + g of [K/8][N]
+    const uint32_t *q_base = Qm + (size_t)e * (K / 8) * N + (size_t)g * N + col;
+    const float *s_base = Sm + (size_t)e * G * N + col;
+    const uint8_t *z_base = Zm + (size_t)e * G * N + col;
+
+    // whole groups per split: k-steps [4 g_begin, 4 g_end)
+    const int g_begin = (int)((long)G * split / S), g_end = (int)((long)G * (split + 1) / S);
+    const int s_begin = 4 * g_begin, s_end = 4 * g_end;
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 x 8
+
+    for (int rc = 0; rc < count; rc += ROWS) {
+        const int rows = min(ROWS, count - rc);
+        // A rows of this lane: row (lane % 16) of each 16-row subtile; rows past
+        // the segment read row r0 instead (never stored)
+        const uint16_t *a_src[MB];
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi) {
+            const int r = mi * 16 + c;
+            const int p = r0 + rc + (r < rows ? r : 0);
+            long src = p;
+            if (GATHER) {
+                const int a = sorted_assign[p];
+                src = (a >= 0 && (a >> 1) < T) ? (a >> 1) : 0;
+            }
+            a_src[mi] = A + (size_t)src * K + 8 * g;
+        }
+
+        f32x4 acc[MB][8], rsum[MB], tot[MB][8];
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi) {
+            rsum[mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[mi][j] = tot[mi][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+
+        struct Stage {
+            u32x4 b[2];
+            u32x4 a[MB];
+        };
+        auto load_stage = [&](Stage &sg, int step) {
+            const uint32_t *p = q_base + (size_t)step * 4 * N;
+            sg.b[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+            sg.b[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 4));
+#pragma unroll
+            for (int mi = 0; mi < MB; ++mi) sg.a[mi] = *reinterpret_cast<const u32x4 *>(a_src[mi] + step * 32);
+        };
+        auto mma = [&](const Stage &sg) {
+            bf16x8 bfrag[8];
+            unpack_q4(sg.b, bfrag);
+#pragma unroll
+            for (int mi = 0; mi < MB; ++mi) {
+                const bf16x8 afrag = __builtin_bit_cast(bf16x8, sg.a[mi]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[mi][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[j], acc[mi][j], 0, 0, 0);
+                rsum[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, __builtin_bit_cast(bf16x8, ones), rsum[mi],
+                                                                  0, 0, 0);
+            }
+        };
+        // group grp: its scales and zero points (read at the group's start) fold
+        // the group's sums into the totals
+        f32x4 gs[2];
+        u32x2 gz;
+        auto load_group = [&](int grp) {
+            const float *sp = s_base + (size_t)grp * N;
+            gs[0] = *reinterpret_cast<const f32x4 *>(sp);
+            gs[1] = *reinterpret_cast<const f32x4 *>(sp + 4);
+            gz = *reinterpret_cast<const u32x2 *>(z_base + (size_t)grp * N);
+        };
+        auto finish_group = [&]() {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float sj = gs[j >> 2][j & 3];
+                const float zj = 128.0f + (float)((gz[j >> 2] >> (8 * (j & 3))) & 0xffu);
+#pragma unroll
+                for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        tot[mi][j][r] = fmaf(sj, fmaf(-zj, rsum[mi][r], acc[mi][j][r]), tot[mi][j][r]);
+                        acc[mi][j][r] = 0.0f;
+                    }
+            }
+#pragma unroll
+            for (int mi = 0; mi < MB; ++mi) rsum[mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        };
+
+        // NST stages (a multiple of 4: stage i holds step st + i, and a group
+        // starts at every stage i % 4 == 0).  The steady-state loop issues every
+        // prefetch unconditionally.
+        Stage sg[NST];
+#pragma unroll
+        for (int i = 0; i < NST; ++i)
+            if (s_begin + i < s_end) load_stage(sg[i], s_begin + i);
+        int st = s_begin;
+        for (; st + 2 * NST <= s_end; st += NST) {
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                if (i % 4 == 0) load_group((st + i) / 4);
+                mma(sg[i]);
+                load_stage(sg[i], st + NST + i);
+                if (i % 4 == 3) finish_group();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // fewer than 2 NST steps left: the stages hold st .. st + NST - 1 (those below s_end)
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            if (st + i < s_end) {
+                if (i % 4 == 0) load_group((st + i) / 4);
+                mma(sg[i]);
+                if (st + NST + i < s_end) load_stage(sg[i], st + NST + i);
+                if (i % 4 == 3) finish_group();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            if (st + NST + i < s_end) {
+                if (i % 4 == 0) load_group((st + NST + i) / 4);
+                mma(sg[i]);
+                if (i % 4 == 3) finish_group();
+            }
+        }
+
+        // accumulator register r of column j, subtile mi: row mi*16 + 4g + r,
+        // column ccol + j (SwiGLU: lanes c >= 8 hold the W3 product)
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = mi * 16 + 4 * g + r;
+                float u[8], v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    u[j] = tot[mi][j][r];
+                    v[j] = DUAL ? __shfl_xor(u[j], 8) : 0.0f;
+                }
+                if (row >= rows || !col_ok) continue;
+                if (S == 1) {
+                    if (DUAL && c >= 8) continue;
+                    store_epilogue8<EPI>(C + (size_t)(r0 + rc + row) * N + ccol, u, v, bias, e, N, ccol);
+                } else {
+                    // partial sums of this split: [split][row][NC], W3 products at column N + n
+                    const int NC = DUAL ? 2 * N : N;
+                    const int pcol = third ? N + ccol : ccol;
+                    float *dst = part + ((size_t)split * A_total + (r0 + rc + row)) * NC + pcol;
+                    *reinterpret_cast<f32x4 *>(dst) = f32x4{u[0], u[1], u[2], u[3]};
+                    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{u[4], u[5], u[6], u[7]};
+                }
+            }
+    }
+}
+
+struct Q4Plan {
+    int NCB, slots, S, MB;
+    size_t part_bytes;
+};
+
+// Column blocks, live-expert slots, row tile and K split of one layer.  S
+// minimises an estimate of the layer's time, as for the bf16 kernel: 256
+// workgroups make a round; a wave streams one k-step (2 KB of codes) per
+// ~0.45 us plus ~3 k-steps of start-up and epilogue; the stream cannot beat
+// ~6 TB/s; S > 1 adds the partials' write and read and a reduce launch.
+Q4Plan q4_plan(const colibri_moe_shape_t &s, bool up) {
+    Q4Plan p;
+    const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
+    const int K = up ? s.d : s.h;
+    const int N = up ? s.h : s.d;
+    p.MB = (2 * s.T <= 8 * s.E) ? 1 : 2;
+    p.NCB = (N + (dual ? 64 : 128) - 1) / (dual ? 64 : 128);
+    p.slots = std::min(s.E, 2 * s.T);
+    const int G = K / kQ4Group;
+    const long wg_per_split = (long)p.slots * ((p.NCB + kQ4Waves - 1) / kQ4Waves);
+    const double cols = (double)N * (dual ? 2 : 1);
+    const double weight_bytes = (double)p.slots * K * cols * 0.5;
+#ifndef COLIBRI_Q4_STEP_US
+#define COLIBRI_Q4_STEP_US 0.45
+#endif
+    const double step_us = COLIBRI_Q4_STEP_US;
+    p.S = 1;
+    double best = 1e300;
+    for (int S = 1; S <= G; ++S) {
+        const double rounds = (double)((wg_per_split * S + 255) / 256);
+        const double steps = 4.0 * ((G + S - 1) / S);
+        double us = std::max(rounds * (steps + 3.0) * step_us, weight_bytes / 6.0e6);
+        if (S > 1) us += 4.0 + 2.0 * S * (2.0 * s.T) * cols * 4 / 5.0e6;
+        if (us < best * 0.97) best = us, p.S = S;
+    }
+    p.part_bytes = p.S > 1 ? align256((size_t)p.S * 2 * s.T * (dual ? 2 : 1) * N * 4) : 0;
+    return p;
+}
+
+template <int EPI>
+hipError_t launch_q4_t(const colibri_moe_shape_t &s, const Q4Plan &p, bool gather, const void *Am, const int32_t *sa,
+                       const int32_t *offsets, const uint32_t *Q0, const uint32_t *Q1, const float *S0,
+                       const float *S1, const uint8_t *Z0, const uint8_t *Z1, const void *bias, void *C, int K, int N,
+                       void *scratch, hipStream_t st) {
+    float *part = static_cast<float *>(scratch);
+    const int blocks = p.slots * p.S * ((p.NCB + kQ4Waves - 1) / kQ4Waves);
+#define COLIBRI_Q4_LAUNCH(MBV, NSTV, G)                                                                              \
+    ffn_decode_q4_kernel<MBV, NSTV, EPI, G><<<blocks, kQ4Waves * kWave, 0, st>>>(                                    \
+        (const uint16_t *)Am, sa, s.T, offsets, s.E, Q0, Q1, S0, S1, Z0, Z1, (const uint16_t *)bias, (uint16_t *)C, K, \
+        N, p.NCB, p.S, part)
+    if (p.MB == 1) {
+        if (gather) COLIBRI_Q4_LAUNCH(1, 8, true);
+        else COLIBRI_Q4_LAUNCH(1, 8, false);
+    } else {
+        if (gather) COLIBRI_Q4_LAUNCH(2, 4, true);
+        else COLIBRI_Q4_LAUNCH(2, 4, false);
+    }
+#undef COLIBRI_Q4_LAUNCH
+    return hipGetLastError();
+}
+
+// bias-only view of the 4-bit weights for the split reduce
+colibri_moe_experts_t bias_view(const colibri_moe_experts_q4_t &w) {
+    colibri_moe_experts_t b{};
+    b.b1 = w.b1;
+    b.b2 = w.b2;
+    return b;
+}
+
+}  // namespace
+
+bool ffn_q4_eligible(const colibri_moe_shape_t &s) {
+    return ffn_decode_eligible(s) && s.d % kQ4Group == 0 && s.h % kQ4Group == 0;
+}
+
+size_t ffn_decode_q4_scratch_bytes(const colibri_moe_shape_t &s) {
+    if (!ffn_q4_eligible(s)) return 0;
+    return std::max(q4_plan(s, true).part_bytes, q4_plan(s, false).part_bytes);
+}
+
+int ffn_down_splits_q4(const colibri_moe_shape_t &s) { return q4_plan(s, false).S; }
+
+hipError_t launch_ffn_layers_q4(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                                const int32_t *offsets, const colibri_moe_experts_q4_t &w, void *y_sorted, void *ws,
+                                bool reduce, hipStream_t st, const float **down_partials) {
+    if (!ffn_q4_eligible(s)) return hipErrorInvalidValue;  // the callers check the shape first
+    char *H = static_cast<char *>(ws);
+    char *scratch = H + align256((size_t)2 * s.T * s.h * 2);
+    const bool gather = sorted_assign != nullptr;
+    const Q4Plan up = q4_plan(s, true), down = q4_plan(s, false);
+    hipError_t e;
+    switch (s.act) {
+        case COLIBRI_ACT_RELU:
+            e = launch_q4_t<EPI_ACT_RELU>(s, up, gather, x_rows, sorted_assign, offsets, w.q1, nullptr, w.s1, nullptr,
+                                          w.z1, nullptr, w.b1, H, s.d, s.h, scratch, st);
+            break;
+        case COLIBRI_ACT_GELU:
+            e = launch_q4_t<EPI_ACT_GELU>(s, up, gather, x_rows, sorted_assign, offsets, w.q1, nullptr, w.s1, nullptr,
+                                          w.z1, nullptr, w.b1, H, s.d, s.h, scratch, st);
+            break;
+        default:
+            e = launch_q4_t<EPI_SWIGLU>(s, up, gather, x_rows, sorted_assign, offsets, w.q1, w.q3, w.s1, w.s3, w.z1,
+                                        w.z3, nullptr, H, s.d, s.h, scratch, st);
+    }
+    const colibri_moe_experts_t bv = bias_view(w);
+    if (e == hipSuccess && up.S > 1)
+        e = launch_split_reduce(s, true, up.S, offsets, bv, H, reinterpret_cast<const float *>(scratch), st);
+    if (e != hipSuccess) return e;
+    const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
+    e = launch_q4_t<EPI_BIAS_ONLY>(s, down, false, H, nullptr, offsets, w.q2, nullptr, w.s2, nullptr, w.z2, nullptr,
+                                   b2, y_sorted, s.h, s.d, scratch, st);
+    if (down_partials) *down_partials = reinterpret_cast<const float *>(scratch);
+    if (e == hipSuccess && down.S > 1 && reduce)
+        e = launch_split_reduce(s, false, down.S, offsets, bv, y_sorted, reinterpret_cast<const float *>(scratch),
+                                st);
+    return e;
+}
+
+}  // namespace colibri

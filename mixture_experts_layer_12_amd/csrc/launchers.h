@@ -143,6 +143,16 @@ hipError_t launch_ffn_layers_q8(const colibri_moe_shape_t &s, const void *x_rows
 // Per-column int8 quantization of a weight tensor [E][K][N] (colibri_moe_quantize_q8).
 hipError_t launch_quantize_q8(const void *w, colibri_dtype_t dtype, int E, int K, int N, int8_t *q, float *scale,
                               hipStream_t st);
+// 4-bit expert weights (ffn_decode_q4.hip): decode sizes with d, h multiples of 128.
+bool ffn_q4_eligible(const colibri_moe_shape_t &s);
+size_t ffn_decode_q4_scratch_bytes(const colibri_moe_shape_t &s);
+int ffn_down_splits_q4(const colibri_moe_shape_t &s);
+hipError_t launch_ffn_layers_q4(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
+                                const int32_t *offsets, const colibri_moe_experts_q4_t &w, void *y_sorted, void *ws,
+                                bool reduce, hipStream_t st, const float **down_partials);
+// 4-bit codes with zero points in groups of 128 k (colibri_moe_quantize_q4).
+hipError_t launch_quantize_q4(const void *w, colibri_dtype_t dtype, int E, int K, int N, uint32_t *q, float *scale,
+                              uint8_t *zero, hipStream_t st);
 // H then Y (launch_ffn_layers with the second layer reduced).
 hipError_t launch_expert_ffn(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,

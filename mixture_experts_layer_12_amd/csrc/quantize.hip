@@ -13,6 +13,16 @@
 // the 4 maxima, a second writes the codes as one 32-bit store per k-row.
 // Neighbouring threads own neighbouring columns, so every k-row is read and
 // written in contiguous runs.
+//
+// 4-bit codes with a zero point ([rkmt] http://news.rkmt.cn/news/2271114
+// section 4.2: AWQ 4-bit weights, quantization group 128, zero point): a group
+// is 128 consecutive k of one column n; in fp32, with the group's largest and
+// smallest weight mx, mn:
+//   s = max(mx - mn, 1e-5) / 15,  z = -rint(mn / s) clamped to [0, 15],
+//   q = rint(w / s) + z clamped to [0, 15]   (rint: ties to even).
+// One thread owns 4 adjacent columns of one group: a first pass finds the
+// extremes, a second writes the codes packed 8 k to a 32-bit word (the code of
+// k = 8j + i in bits 4i .. 4i+3 of word j), one 16-byte store per 8 k-rows.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -67,6 +77,53 @@ __global__ __launch_bounds__(256) void quantize_q8_kernel(const TI *__restrict__
     }
 }
 
+template <typename TI>
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const TI *__restrict__ w, int E, int K, int N,
+                                                          uint32_t *__restrict__ q, float *__restrict__ scale,
+                                                          uint8_t *__restrict__ zero) {
+    constexpr int GK = 128;  // k per group
+    const int NG = N / 4, G = K / GK;
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long)E * G * NG) return;
+    const int e = (int)(i / ((long)G * NG)), g = (int)((i / NG) % G), n = (int)(i % NG) * 4;
+    const TI *src = w + (size_t)e * K * N + (size_t)g * GK * N + n;
+    float mx[4], mn[4];
+    load4<TI>(src, mx);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mn[j] = mx[j];
+    for (int k = 1; k < GK; ++k) {
+        float v[4];
+        load4<TI>(src + (size_t)k * N, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], v[j]), mn[j] = fminf(mn[j], v[j]);
+    }
+    float s[4], z[4];
+    uint32_t zw = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        s[j] = fmaxf(mx[j] - mn[j], 1e-5f) / 15.0f;
+        z[j] = fminf(fmaxf(-rintf(mn[j] / s[j]), 0.0f), 15.0f);
+        zw |= (uint32_t)z[j] << (8 * j);
+    }
+    const size_t gi = ((size_t)e * G + g) * N + n;
+    *reinterpret_cast<f32x4 *>(scale + gi) = f32x4{s[0], s[1], s[2], s[3]};
+    *reinterpret_cast<uint32_t *>(zero + gi) = zw;
+    for (int kb = 0; kb < GK / 8; ++kb) {
+        u32x4 words = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float v[4];
+            load4<TI>(src + (size_t)(8 * kb + t) * N, v);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float r = fminf(fmaxf(rintf(v[j] / s[j]) + z[j], 0.0f), 15.0f);
+                words[j] |= (uint32_t)r << (4 * t);
+            }
+        }
+        *reinterpret_cast<u32x4 *>(q + ((size_t)e * (K / 8) + (size_t)g * (GK / 8) + kb) * N + n) = words;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_q8(const void *w, colibri_dtype_t dtype, int E, int K, int N, int8_t *q, float *scale,
@@ -77,6 +134,18 @@ hipError_t launch_quantize_q8(const void *w, colibri_dtype_t dtype, int E, int K
         quantize_q8_kernel<float><<<blocks, 256, 0, st>>>(static_cast<const float *>(w), E, K, N, q, scale);
     else
         quantize_q8_kernel<uint16_t><<<blocks, 256, 0, st>>>(static_cast<const uint16_t *>(w), E, K, N, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_q4(const void *w, colibri_dtype_t dtype, int E, int K, int N, uint32_t *q, float *scale,
+                              uint8_t *zero, hipStream_t st) {
+    const long threads = (long)E * (K / 128) * (N / 4);
+    const int blocks = (int)((threads + 255) / 256);
+    if (dtype == COLIBRI_F32)
+        quantize_q4_kernel<float><<<blocks, 256, 0, st>>>(static_cast<const float *>(w), E, K, N, q, scale, zero);
+    else
+        quantize_q4_kernel<uint16_t><<<blocks, 256, 0, st>>>(static_cast<const uint16_t *>(w), E, K, N, q, scale,
+                                                             zero);
     return hipGetLastError();
 }
 

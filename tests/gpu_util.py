@@ -29,6 +29,8 @@ def dev(a: Optional[np.ndarray]):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return t.from_numpy(a.view(np.int16)).cuda().view(t.bfloat16)
+    if a.dtype == np.uint32:  # packed 4-bit codes: carried as int32
+        return t.from_numpy(a.view(np.int32)).cuda()
     return t.from_numpy(a).cuda()
 
 
@@ -186,6 +188,44 @@ def _device_experts_q8(wkey: str):
     return {k: dev(v) for k, v in _host_experts_q8(wkey).items()}
 
 
+def pack_q4(codes: np.ndarray) -> np.ndarray:
+    """Codes [E, K, N] (0..15) -> the library's words [E, K/8, N]: the code of
+    k = 8j + i in bits 4i .. 4i+3 of word j."""
+    E, K, N = codes.shape
+    c = codes.reshape(E, K // 8, 8, N).astype(np.uint32)
+    return np.bitwise_or.reduce(c << (4 * np.arange(8, dtype=np.uint32))[None, None, :, None], axis=2)
+
+
+def unpack_q4(words: np.ndarray) -> np.ndarray:
+    E, KB, N = words.shape
+    w = words.astype(np.uint32)[:, :, None, :] >> (4 * np.arange(8, dtype=np.uint32))[None, None, :, None]
+    return (w & 0xF).astype(np.uint8).reshape(E, KB * 8, N)
+
+
+@functools.lru_cache(maxsize=1)
+def _host_experts_q4(wkey: str):
+    """4-bit codes (unpacked and packed), scales and zero points of the seeded
+    weights, from the oracle's quantizer."""
+    w = _host_experts(wkey)
+    out = {"b1": w["b1"], "b2": w["b2"]}
+    for name, t in (("w1", "1"), ("w3", "3"), ("w2", "2")):
+        if w[name] is None:
+            out["w" + t + "q"] = None
+        else:
+            q, sc, z = oracle.quantize_q4(w[name])
+            out["w" + t + "q"] = (q, sc, z)
+    return out
+
+
+@functools.lru_cache(maxsize=1)
+def _device_experts_q4(wkey: str):
+    h = _host_experts_q4(wkey)
+    out = {"b1": dev(h["b1"]), "b2": dev(h["b2"])}
+    for k in ("w1q", "w3q", "w2q"):
+        out[k] = None if h[k] is None else (dev(pack_q4(h[k][0])), dev(h[k][1]), dev(h[k][2]))
+    return out
+
+
 class Layer:
     """Seeded inputs of one config at T tokens; expert weights load on first use."""
 
@@ -236,6 +276,23 @@ class Layer:
                                       b_r=w["b_r"], q3=w["q3"], s3=w["s3"], b1=w["b1"], b2=w["b2"], mirror=True,
                                       idx_override=idx_override)
 
+
+    @property
+    def hq4(self) -> Dict:
+        w = dict(_host_experts_q4(weight_key(self.key)))
+        w.update(host_router(self.key))
+        return w
+
+    @property
+    def dq4(self) -> Dict:
+        w = dict(_device_experts_q4(weight_key(self.key)))
+        w.update(device_router(self.key))
+        return w
+
+    def oracle_tokens_q4(self, tokens, idx_override=None):
+        w = self.hq4
+        return oracle.layer_tokens_q4(self.x, w["w_r"], w["w1q"], w["w2q"], self.cfg.act, tokens, b_r=w["b_r"],
+                                      w3q=w["w3q"], b1=w["b1"], b2=w["b2"], mirror=True, idx_override=idx_override)
 
     # ---- gating variants, shared expert, residual
     @property

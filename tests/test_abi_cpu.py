@@ -234,6 +234,72 @@ def test_quantize_checks(lib):
     assert call(sc=fake(2) + 1) == moe.COLIBRI_ERR_INVALID_ARG
 
 
+# ------------------------------------------------------------------ 4-bit expert weights
+def q4_experts(**kw):
+    names = ("q1", "q3", "q2", "s1", "s3", "s2", "z1", "z3", "z2", "b1", "b2")
+    base = {n: fake(10 + i) for i, n in enumerate(names[:9])}
+    base.update(b1=None, b2=None)
+    base.update(kw)
+    return moe._ExpertsQ4(*(base[n] for n in names))
+
+
+def ffn_q4_call(lib, s, e, ws_bytes=1 << 40, ws=fake(9), y=fake(8)):
+    return lib.colibri_moe_expert_ffn_q4(ctypes.byref(s), fake(0), fake(1), fake(2), ctypes.byref(e), y, ws,
+                                         ws_bytes, None)
+
+
+def test_q4_ffn_checks(lib):
+    s = shape_c()
+    assert s.d % 128 == 0 and s.h % 128 == 0
+    e = q4_experts()
+    # decode sizes only: bf16, T <= 64, d and h multiples of the 128-channel group
+    assert ffn_q4_call(lib, shape_c(T=65), e) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert ffn_q4_call(lib, shape_c(dtype=moe.F32), e) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert ffn_q4_call(lib, shape_c(d=s.d + 64), e) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert ffn_q4_call(lib, shape_c(h=s.h + 64), e) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert ffn_q4_call(lib, s, e, ws_bytes=1024) == moe.COLIBRI_ERR_WORKSPACE
+    # codes, scales and zero points of both layers are required; SwiGLU needs the third and takes no biases
+    for k in ("q1", "q2", "s1", "s2", "z1", "z2", "q3", "s3", "z3"):
+        assert ffn_q4_call(lib, s, q4_experts(**{k: None})) == moe.COLIBRI_ERR_INVALID_ARG, k
+    assert ffn_q4_call(lib, s, q4_experts(b2=fake(20))) == moe.COLIBRI_ERR_UNSUPPORTED
+    sr = shape_c(act=moe.GELU)
+    assert ffn_q4_call(lib, sr, q4_experts(z3=None, s3=None)) == moe.COLIBRI_ERR_UNSUPPORTED
+    # alignment: codes and scales 16 bytes, zero points 8
+    assert ffn_q4_call(lib, s, q4_experts(q2=fake(12) + 8)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert ffn_q4_call(lib, s, q4_experts(s1=fake(13) + 4)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert ffn_q4_call(lib, s, q4_experts(z2=fake(18) + 4)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert lib.colibri_moe_expert_ffn_q4(ctypes.byref(shape_c(T=0)), None, None, None, None, None, None, 0,
+                                         None) == 0
+
+
+def test_q4_layer_checks(lib):
+    s = shape_c()
+    need = lib.colibri_moe_workspace_size(ctypes.byref(s))
+
+    def call(sh=s, e=q4_experts(), ws_bytes=need, x=fake(0)):
+        return lib.colibri_moe_layer_forward_q4(ctypes.byref(sh), x, fake(1), None, ctypes.byref(e), fake(3), None,
+                                                None, None, fake(20), ws_bytes, None)
+
+    assert call(ws_bytes=need - 1) == moe.COLIBRI_ERR_WORKSPACE
+    assert call(x=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(sh=shape_c(T=100)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert call(e=q4_experts(z1=None)) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+def test_quantize_q4_checks(lib):
+    def call(w=fake(0), dtype=moe.BF16, E=2, K=256, N=128, q=fake(1), sc=fake(2), z=fake(3)):
+        return lib.colibri_moe_quantize_q4(w, dtype, E, K, N, q, sc, z, None)
+
+    for k in ("w", "q", "sc", "z"):
+        assert call(**{k: None}) == moe.COLIBRI_ERR_INVALID_ARG, k
+    assert call(K=192) == moe.COLIBRI_ERR_UNSUPPORTED  # whole groups of 128
+    assert call(K=0) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert call(N=130) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert call(dtype=5) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert call(q=fake(1) + 8) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(sc=fake(2) + 4) == moe.COLIBRI_ERR_INVALID_ARG
+
+
 # ------------------------------------------------------------------ gating variants, shared expert, residual
 def opts_c(gate=moe.GATE_PAIR, shared=None, shared_h=0, residual=None):
     return moe._Opts(gate, ctypes.pointer(shared) if shared is not None else None, shared_h, residual)
