@@ -15,9 +15,10 @@ region (decode steps are also reported host-inclusive, back to back).
 
 Prints one JSON line: whole-layer tokens/s, the roofline fraction of the
 dominant kernel, every kernel's time and fraction, decode microseconds per
-step at T=1 and T=64 with bf16 expert weights and with per-column int8
-expert weights (colibri_moe_layer_forward_q8, quantized on the GPU by the
-library's own quantizer), and the fp64 CPU oracle timed on the host cores.
+step at T=1 and T=64 with bf16 expert weights, with per-column int8 expert
+weights (colibri_moe_layer_forward_q8) and with 4-bit group-128 weights
+(colibri_moe_layer_forward_q4), both quantized on the GPU by the library's
+own quantizers, and the fp64 CPU oracle timed on the host cores.
 """
 from __future__ import annotations
 
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--rotate-gb", type=float, default=2.0, help="total bytes of rotated weight copies")
     ap.add_argument("--decode-T", default="1,64", help="decode batch sizes also timed (comma list, '' = none)")
     ap.add_argument("--decode-iters", type=int, default=200)
-    ap.add_argument("--no-q8", action="store_true", help="skip the int8-weight decode lines")
+    ap.add_argument("--no-q8", action="store_true", help="skip the int8- and 4-bit-weight decode lines")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the shared-expert / softmax-gating / residual layer lines")
     ap.add_argument("--step-layers", type=int, default=8,
@@ -330,6 +331,46 @@ def main():
             log(f"decode int8 weights T={tok}: {decode_q8[f'T={tok}']}")
         del qcopies, q0
 
+    # 4-bit expert weights (zero point, groups of 128 input channels), decode
+    # sizes only: quantized on the GPU by the library's own quantizer, rotated
+    # like the bf16 weights
+    decode_q4 = {}
+    if q8_ts and cfg.dtype == gen.BF16 and not args.no_q8 and cfg.d % 128 == 0 and cfg.h % 128 == 0:
+        q0 = {"b1": dw0["b1"], "b2": dw0["b2"]}
+        for name in ("w1", "w3", "w2"):
+            wt = dw0[name]
+            if wt is None:
+                q0[name + "q"] = None
+                continue
+            E_, K_, N_ = wt.shape
+            t = (torch.empty((E_, K_ // 8, N_), dtype=torch.int32, device=dev),
+                 torch.empty((E_, K_ // 128, N_), dtype=torch.float32, device=dev),
+                 torch.empty((E_, K_ // 128, N_), dtype=torch.uint8, device=dev))
+            moe.quantize_q4(wt, gen.BF16, E_, K_, N_, *t)
+            q0[name + "q"] = t
+        torch.cuda.synchronize()
+        nb = lambda v: 0 if v is None else (sum(a[0].numel() * a.element_size() for a in v) if isinstance(v, tuple)
+                                            else v[0].numel() * v.element_size())
+        up_q4_e = nb(q0["w1q"]) + nb(q0["w3q"]) + nb(q0["b1"])
+        down_q4_e = nb(q0["w2q"]) + nb(q0["b2"])
+        tb = lambda v: 0 if v is None else (sum(a.numel() * a.element_size() for a in v) if isinstance(v, tuple)
+                                            else v.numel() * v.element_size())
+        q4_layer_bytes = sum(tb(v) for v in q0.values())
+        R4 = max(1, math.ceil(args.rotate_gb * 1e9 / q4_layer_bytes))
+        cl = lambda v: None if v is None else (tuple(a.clone() for a in v) if isinstance(v, tuple) else v.clone())
+        q4copies = [q0] + [{k: cl(v) for k, v in q0.items()} for _ in range(R4 - 1)]
+        log(f"4-bit weights: {R4} copies x {q4_layer_bytes / 1e6:.1f} MB")
+
+        def step_q4(i, xx=x, s=sh, o=out):
+            w = q4copies[i % R4]
+            moe.layer_forward_q4(s, xx, w_r, b_r, w["w1q"], w["w2q"], o, ws, ws_bytes, w3q=w["w3q"], b1=w["b1"],
+                                 b2=w["b2"], counts=counts)
+
+        for tok in q8_ts:
+            decode_q4[f"T={tok}"] = decode_record(tok, *time_decode(step_q4, tok), up_q4_e, down_q4_e)
+            log(f"decode 4-bit weights T={tok}: {decode_q4[f'T={tok}']}")
+        del q4copies, q0
+
     # ---------------------------------------------------------------- layer variants
     # 15 routed + 1 shared expert, softmax over all experts (unnormalised pair),
     # residual added in the combine; beside it the same routed layer without the
@@ -374,6 +415,7 @@ def main():
                    "T": T, "E": cfg.E, "d": cfg.d, "h": cfg.h, "act": cfg.act, "weight_copies": R,
                    "experts_hit": hit},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "decode": decode, "decode_int8_weights": decode_q8,
+        "decode_int4_weights": decode_q4,
         "variants": variants, "multi_layer_step": steps,
         "timing": "GPU time (HIP events, queue pre-filled by a spin kernel)" if can_sleep else "GPU time (HIP events)",
     }

@@ -319,9 +319,10 @@ int colibri_moe_layer_forward_q8(const colibri_moe_shape_t *s, const void *x, co
  *   W[e][k][n] = s[e][k/128][n] * (q[e][k][n] - z[e][k/128][n]),  q, z in [0, 15].
  *   q1 [E][d/8][h], q3 [E][d/8][h] (SwiGLU only, else NULL), q2 [E][h/8][d]
  *       uint32 words, 16-byte aligned; word (e, j, n) packs the codes of
- *       k = 8j .. 8j+7 of column n, the code of k = 8j + i in bits 4i .. 4i+3
+ *       k = 8j .. 8j+7 of column n: the code of k = 8j + 2m in bits 4m .. 4m+3
+ *       and of k = 8j + 2m + 1 in bits 16 + 4m .. 16 + 4m + 3 (m = 0..3)
  *   s1, s3 [E][d/128][h], s2 [E][h/128][d]   fp32 group scales, 16-byte aligned
- *   z1, z3 [E][d/128][h], z2 [E][h/128][d]   uint8 zero points, 8-byte aligned
+ *   z1, z3 [E][d/128][h], z2 [E][h/128][d]   uint8 zero points, 4-byte aligned
  *   b1 [E][h], b2 [E][d]   as in colibri_moe_experts_t (NULL = zero; NULL for SwiGLU)
  * The layer computes what it computes with the dequantized weights in full
  * precision: each group's sum is formed from the codes and scaled once.
@@ -344,7 +345,8 @@ typedef struct {
  * (rint: nearest, ties to even).  AWQ's activation-aware choice of scales
  * needs calibration activations and is not done here.
  *   w [E][K][N] dtype, 16-byte aligned;  q [E][K/8][N] uint32 out (packed as
- *   above, 16-byte aligned);  s [E][K/128][N] fp32 out;  z [E][K/128][N] uint8 out.
+ *   above, 16-byte aligned);  s [E][K/128][N] fp32 out, 16-byte aligned;
+ *   z [E][K/128][N] uint8 out, 4-byte aligned.
  * E, N >= 1; K >= 128 a multiple of 128; N a multiple of 4. */
 int colibri_moe_quantize_q4(const void *w, colibri_dtype_t dtype, int32_t E, int32_t K, int32_t N, uint32_t *q,
                             float *s, uint8_t *z, hipStream_t stream);

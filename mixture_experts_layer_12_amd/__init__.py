@@ -393,7 +393,8 @@ def _experts_q4(w1q, w2q, w3q=None, b1=None, b2=None) -> _ExpertsQ4:
 
 
 def quantize_q4(w, dtype: int, E: int, K: int, N: int, q, scale, zero, stream=None):
-    """4-bit codes q [E, K/8, N] (uint32 words of 8 codes), fp32 scales and uint8
+    """4-bit codes q [E, K/8, N] (uint32 words of 8 codes: k = 8j + 2m in bits
+    4m..4m+3, k = 8j + 2m + 1 in bits 16+4m..16+4m+3), fp32 scales and uint8
     zero points [E, K/128, N] of w [E, K, N]."""
     _check(load().colibri_moe_quantize_q4(_ptr(w), int(dtype), int(E), int(K), int(N), _ptr(q), _ptr(scale),
                                           _ptr(zero), _stream(stream)), "colibri_moe_quantize_q4")

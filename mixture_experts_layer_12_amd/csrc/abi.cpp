@@ -83,7 +83,7 @@ int check_experts_q4(const colibri_moe_shape_t *s, const colibri_moe_experts_q4_
     if (!w) return COLIBRI_ERR_INVALID_ARG;
     if (!ffn_q4_eligible(*s)) return COLIBRI_ERR_UNSUPPORTED;
     auto ok = [](const uint32_t *q, const float *sc, const uint8_t *z) {
-        return q && sc && z && aligned(q, 16) && aligned(sc, 16) && aligned(z, 8);
+        return q && sc && z && aligned(q, 16) && aligned(sc, 16) && aligned(z, 4);
     };
     if (!ok(w->q1, w->s1, w->z1) || !ok(w->q2, w->s2, w->z2)) return COLIBRI_ERR_INVALID_ARG;
     if (s->act == COLIBRI_ACT_SWIGLU) {

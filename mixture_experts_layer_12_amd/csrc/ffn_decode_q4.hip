@@ -10,24 +10,27 @@
 //   W[e][k][n] = s[e][k/128][n] * (q[e][k][n] - z[e][k/128][n]),  q, z in [0, 15]
 //
 // Layout: word (e, j, n) of q [E][K/8][N] packs the codes of k = 8j .. 8j+7 of
-// column n (the code of k = 8j + i in bits 4i .. 4i+3), so one word is the
-// eight k a lane feeds to one column of v_mfma_f32_16x16x32_bf16, and a lane's
-// eight columns of a k-step are 32 contiguous bytes.
+// column n, the code of k = 8j + 2m in bits 4m .. 4m+3 and of k = 8j + 2m + 1
+// in bits 16 + 4m .. 16 + 4m + 3 (m = 0..3).  One word is the eight k a lane
+// feeds to one column of v_mfma_f32_16x16x32_bf16, a lane's four columns of a
+// k-step are one 16-byte load, and k-pair m of the word is the halfword pair
+// (word >> 4m) & 0x000f000f.
 //
 // Design (as the bf16 weight-streaming kernel, with the weights 4x smaller):
-//   * a wave owns (live expert, 128 columns -- SwiGLU: 64 of W1 and 64 of W3 --,
-//     K split); 4 waves of a workgroup take adjacent column blocks;
+//   * a wave owns (live expert, 64 columns -- SwiGLU: 32 of W1 and 32 of W3 --,
+//     K split); 4 waves of a workgroup take adjacent column blocks; few
+//     registers per wave, so several workgroups share a CU;
 //   * a code becomes an exact bf16 operand with no conversion: the bit
 //     pattern 0x4300 | q is the bf16 value 128 + q (bf16 has 7 fraction bits,
-//     so 128 .. 143 are exact), built for two k at once with one byte permute
-//     and one OR.  The MFMAs accumulate x * (128 + q) over a group, and one
+//     so 128 .. 143 are exact), built for two k at once with one shift and one
+//     AND-OR.  The MFMAs accumulate x * (128 + q) over a group, and one
 //     more MFMA per k-step against a B operand of ones accumulates the rows'
 //     sums of x over the group, so that at the end of every group
 //       total += s * (acc - (128 + z) * rowsum_x)
 //     is the group's exact contribution (up to fp32 rounding);
-//   * several k-steps of codes are in flight per wave (each k-step is 2 KB
-//     per wave); the group scales and zero points (40 bytes per lane and
-//     group) are read at each group's start and used at its end;
+//   * four k-steps of codes are in flight per wave (each k-step is 1 KB per
+//     wave); the group scales and zero points (20 bytes per lane and group)
+//     are read at each group's start and used at its end;
 //   * K splits run along whole groups; split partials (fp32) are added by
 //     the split reduce or, for the second layer inside the layer call, by the
 //     combine.
@@ -41,18 +44,15 @@ namespace {
 constexpr int kQ4Waves = 4;   // waves (adjacent column blocks) per workgroup
 constexpr int kQ4Group = 128; // k per scale / zero point
 
-// The eight words of a lane's eight columns (w[j / 4][j % 4] = column j, k 0..7)
-// -> eight B fragments holding 128 + q.  Byte p of a word holds the codes of
-// k = 2p (low nibble) and 2p + 1 (high nibble); fragment dword p = k 2p, 2p + 1.
-__device__ __forceinline__ void unpack_q4(const u32x4 (&w)[2], bf16x8 (&frag)[8]) {
+// The four words of a lane's four columns (w[j] = column j, k 0..7) -> four B
+// fragments holding 128 + q: fragment dword m (k 2m, 2m + 1) is the halfword
+// pair (w[j] >> 4m) & 0x000f000f over the pattern of 128.0 in both halves.
+__device__ __forceinline__ void unpack_q4(const u32x4 &w, bf16x8 (&frag)[4]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t x = w[j >> 2][j & 3];
-        const uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
+    for (int j = 0; j < 4; ++j) {
         u32x4 o;
 #pragma unroll
-        for (int p = 0; p < 4; ++p)  // bytes: lo.p, 0, hi.p, 0  (selector 12 gives a zero byte)
-            o[p] = __builtin_amdgcn_perm(hi, lo, 0x0c000c00u | ((4u + p) << 16) | (uint32_t)p) | 0x43004300u;
+        for (int m = 0; m < 4; ++m) o[m] = ((w[j] >> (4 * m)) & 0x000f000fu) | 0x43004300u;
         frag[j] = __builtin_bit_cast(bf16x8, o);
     }
 }
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
     const uint8_t *__restrict__ Z1, const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N,
     int NCB, int S, float *__restrict__ part) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    constexpr int WCOLS = DUAL ? 64 : 128;  // output columns per wave (per matrix)
+    constexpr int WCOLS = DUAL ? 32 : 64;  // output columns per wave (per matrix)
     constexpr int ROWS = MB * 16;
     static_assert(NST % 4 == 0, "stages cover whole groups");
     const int lane = threadIdx.x & (kWave - 1);
@@ -81,13 +81,13 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
     int e, r0, count;
     if (!live_expert(offsets, E, A_total, slot, e, r0, count)) return;
 
-    const int c = lane & 15;  // column group: columns ccol .. ccol + 7
+    const int c = lane & 15;  // column group: columns ccol .. ccol + 3
     const int g = lane >> 4;  // k group: k 8g .. 8g+7 of a 32-deep step
     const bool third = DUAL && c >= 8;  // SwiGLU: lanes 8..15 hold W3's columns
     const uint32_t *Qm = third ? Q1 : Q0;
     const float *Sm = third ? S1 : S0;
     const uint8_t *Zm = third ? Z1 : Z0;
-    const int ccol = cb * WCOLS + 8 * (DUAL ? (c & 7) : c);
+    const int ccol = cb * WCOLS + 4 * (DUAL ? (c & 7) : c);
     const bool col_ok = ccol < N;
     const int col = col_ok ? ccol : 0;  // padding lanes read column block 0 (never stored)
     const int G = K / kQ4Group;
@@ -118,33 +118,31 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
             a_src[mi] = A + (size_t)src * K + 8 * g;
         }
 
-        f32x4 acc[MB][8], rsum[MB], tot[MB][8];
+        f32x4 acc[MB][4], rsum[MB], tot[MB][4];
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi) {
             rsum[mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[mi][j] = tot[mi][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int j = 0; j < 4; ++j) acc[mi][j] = tot[mi][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
 
         struct Stage {
-            u32x4 b[2];
+            u32x4 b;
             u32x4 a[MB];
         };
         auto load_stage = [&](Stage &sg, int step) {
-            const uint32_t *p = q_base + (size_t)step * 4 * N;
-            sg.b[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-            sg.b[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 4));
+            sg.b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(q_base + (size_t)step * 4 * N));
 #pragma unroll
             for (int mi = 0; mi < MB; ++mi) sg.a[mi] = *reinterpret_cast<const u32x4 *>(a_src[mi] + step * 32);
         };
         auto mma = [&](const Stage &sg) {
-            bf16x8 bfrag[8];
+            bf16x8 bfrag[4];
             unpack_q4(sg.b, bfrag);
 #pragma unroll
             for (int mi = 0; mi < MB; ++mi) {
                 const bf16x8 afrag = __builtin_bit_cast(bf16x8, sg.a[mi]);
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < 4; ++j)
                     acc[mi][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[j], acc[mi][j], 0, 0, 0);
                 rsum[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, __builtin_bit_cast(bf16x8, ones), rsum[mi],
                                                                   0, 0, 0);
@@ -152,19 +150,17 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
         };
         // group grp: its scales and zero points (read at the group's start) fold
         // the group's sums into the totals
-        f32x4 gs[2];
-        u32x2 gz;
+        f32x4 gs;
+        uint32_t gz;
         auto load_group = [&](int grp) {
-            const float *sp = s_base + (size_t)grp * N;
-            gs[0] = *reinterpret_cast<const f32x4 *>(sp);
-            gs[1] = *reinterpret_cast<const f32x4 *>(sp + 4);
-            gz = *reinterpret_cast<const u32x2 *>(z_base + (size_t)grp * N);
+            gs = *reinterpret_cast<const f32x4 *>(s_base + (size_t)grp * N);
+            gz = *reinterpret_cast<const uint32_t *>(z_base + (size_t)grp * N);
         };
         auto finish_group = [&]() {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float sj = gs[j >> 2][j & 3];
-                const float zj = 128.0f + (float)((gz[j >> 2] >> (8 * (j & 3))) & 0xffu);
+            for (int j = 0; j < 4; ++j) {
+                const float sj = gs[j];
+                const float zj = 128.0f + (float)((gz >> (8 * j)) & 0xffu);
 #pragma unroll
                 for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
@@ -221,23 +217,22 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = mi * 16 + 4 * g + r;
-                float u[8], v[8];
+                float u[4], v[4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < 4; ++j) {
                     u[j] = tot[mi][j][r];
                     v[j] = DUAL ? __shfl_xor(u[j], 8) : 0.0f;
                 }
                 if (row >= rows || !col_ok) continue;
                 if (S == 1) {
                     if (DUAL && c >= 8) continue;
-                    store_epilogue8<EPI>(C + (size_t)(r0 + rc + row) * N + ccol, u, v, bias, e, N, ccol);
+                    store_epilogue<EPI, 4>(C + (size_t)(r0 + rc + row) * N + ccol, u, v, bias, e, N, ccol);
                 } else {
                     // partial sums of this split: [split][row][NC], W3 products at column N + n
                     const int NC = DUAL ? 2 * N : N;
                     const int pcol = third ? N + ccol : ccol;
                     float *dst = part + ((size_t)split * A_total + (r0 + rc + row)) * NC + pcol;
                     *reinterpret_cast<f32x4 *>(dst) = f32x4{u[0], u[1], u[2], u[3]};
-                    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{u[4], u[5], u[6], u[7]};
                 }
             }
     }
@@ -249,9 +244,10 @@ struct Q4Plan {
 };
 
 // Column blocks, live-expert slots, row tile and K split of one layer.  S
-// minimises an estimate of the layer's time, as for the bf16 kernel: 256
-// workgroups make a round; a wave streams one k-step (2 KB of codes) per
-// ~0.45 us plus ~3 k-steps of start-up and epilogue; the stream cannot beat
+// minimises an estimate of the layer's time, as for the bf16 kernel: a round
+// is 256 CUs times the workgroups one CU holds (3 with 16-row tiles, 2 with
+// 32: the kernel's register budget); a wave streams one k-step (1 KB of codes)
+// per ~0.5 us plus ~3 k-steps of start-up and epilogue; the stream cannot beat
 // ~6 TB/s; S > 1 adds the partials' write and read and a reduce launch.
 Q4Plan q4_plan(const colibri_moe_shape_t &s, bool up) {
     Q4Plan p;
@@ -259,20 +255,21 @@ Q4Plan q4_plan(const colibri_moe_shape_t &s, bool up) {
     const int K = up ? s.d : s.h;
     const int N = up ? s.h : s.d;
     p.MB = (2 * s.T <= 8 * s.E) ? 1 : 2;
-    p.NCB = (N + (dual ? 64 : 128) - 1) / (dual ? 64 : 128);
+    p.NCB = (N + (dual ? 32 : 64) - 1) / (dual ? 32 : 64);
     p.slots = std::min(s.E, 2 * s.T);
     const int G = K / kQ4Group;
     const long wg_per_split = (long)p.slots * ((p.NCB + kQ4Waves - 1) / kQ4Waves);
     const double cols = (double)N * (dual ? 2 : 1);
     const double weight_bytes = (double)p.slots * K * cols * 0.5;
 #ifndef COLIBRI_Q4_STEP_US
-#define COLIBRI_Q4_STEP_US 0.45
+#define COLIBRI_Q4_STEP_US 0.5
 #endif
     const double step_us = COLIBRI_Q4_STEP_US;
     p.S = 1;
     double best = 1e300;
     for (int S = 1; S <= G; ++S) {
-        const double rounds = (double)((wg_per_split * S + 255) / 256);
+        const long per_round = 256L * (p.MB == 1 ? 3 : 2);
+        const double rounds = (double)((wg_per_split * S + per_round - 1) / per_round);
         const double steps = 4.0 * ((G + S - 1) / S);
         double us = std::max(rounds * (steps + 3.0) * step_us, weight_bytes / 6.0e6);
         if (S > 1) us += 4.0 + 2.0 * S * (2.0 * s.T) * cols * 4 / 5.0e6;
@@ -294,8 +291,8 @@ hipError_t launch_q4_t(const colibri_moe_shape_t &s, const Q4Plan &p, bool gathe
         (const uint16_t *)Am, sa, s.T, offsets, s.E, Q0, Q1, S0, S1, Z0, Z1, (const uint16_t *)bias, (uint16_t *)C, K, \
         N, p.NCB, p.S, part)
     if (p.MB == 1) {
-        if (gather) COLIBRI_Q4_LAUNCH(1, 8, true);
-        else COLIBRI_Q4_LAUNCH(1, 8, false);
+        if (gather) COLIBRI_Q4_LAUNCH(1, 4, true);
+        else COLIBRI_Q4_LAUNCH(1, 4, false);
     } else {
         if (gather) COLIBRI_Q4_LAUNCH(2, 4, true);
         else COLIBRI_Q4_LAUNCH(2, 4, false);

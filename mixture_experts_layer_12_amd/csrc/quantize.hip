@@ -21,8 +21,9 @@
 //   s = max(mx - mn, 1e-5) / 15,  z = -rint(mn / s) clamped to [0, 15],
 //   q = rint(w / s) + z clamped to [0, 15]   (rint: ties to even).
 // One thread owns 4 adjacent columns of one group: a first pass finds the
-// extremes, a second writes the codes packed 8 k to a 32-bit word (the code of
-// k = 8j + i in bits 4i .. 4i+3 of word j), one 16-byte store per 8 k-rows.
+// extremes, a second writes the codes packed 8 k to a 32-bit word (word j: the
+// code of k = 8j + 2m in bits 4m .. 4m+3, of k = 8j + 2m + 1 in bits 16 + 4m ..
+// 16 + 4m + 3), one 16-byte store per 8 k-rows.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const TI *__restrict__
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float r = fminf(fmaxf(rintf(v[j] / s[j]) + z[j], 0.0f), 15.0f);
-                words[j] |= (uint32_t)r << (4 * t);
+                words[j] |= (uint32_t)r << (4 * (t >> 1) + 16 * (t & 1));
             }
         }
         *reinterpret_cast<u32x4 *>(q + ((size_t)e * (K / 8) + (size_t)g * (GK / 8) + kb) * N + n) = words;

@@ -188,17 +188,20 @@ def _device_experts_q8(wkey: str):
     return {k: dev(v) for k, v in _host_experts_q8(wkey).items()}
 
 
+# bit offset of the code of k = 8j + i inside word j: 4m for k = 8j + 2m, 16 + 4m for k = 8j + 2m + 1
+Q4_SHIFT = np.array([4 * (i // 2) + 16 * (i % 2) for i in range(8)], np.uint32)
+
+
 def pack_q4(codes: np.ndarray) -> np.ndarray:
-    """Codes [E, K, N] (0..15) -> the library's words [E, K/8, N]: the code of
-    k = 8j + i in bits 4i .. 4i+3 of word j."""
+    """Codes [E, K, N] (0..15) -> the library's words [E, K/8, N]."""
     E, K, N = codes.shape
     c = codes.reshape(E, K // 8, 8, N).astype(np.uint32)
-    return np.bitwise_or.reduce(c << (4 * np.arange(8, dtype=np.uint32))[None, None, :, None], axis=2)
+    return np.bitwise_or.reduce(c << Q4_SHIFT[None, None, :, None], axis=2)
 
 
 def unpack_q4(words: np.ndarray) -> np.ndarray:
     E, KB, N = words.shape
-    w = words.astype(np.uint32)[:, :, None, :] >> (4 * np.arange(8, dtype=np.uint32))[None, None, :, None]
+    w = words.astype(np.uint32)[:, :, None, :] >> Q4_SHIFT[None, None, :, None]
     return (w & 0xF).astype(np.uint8).reshape(E, KB * 8, N)
 
 

@@ -264,10 +264,10 @@ def test_q4_ffn_checks(lib):
     assert ffn_q4_call(lib, s, q4_experts(b2=fake(20))) == moe.COLIBRI_ERR_UNSUPPORTED
     sr = shape_c(act=moe.GELU)
     assert ffn_q4_call(lib, sr, q4_experts(z3=None, s3=None)) == moe.COLIBRI_ERR_UNSUPPORTED
-    # alignment: codes and scales 16 bytes, zero points 8
+    # alignment: codes and scales 16 bytes, zero points 4
     assert ffn_q4_call(lib, s, q4_experts(q2=fake(12) + 8)) == moe.COLIBRI_ERR_INVALID_ARG
     assert ffn_q4_call(lib, s, q4_experts(s1=fake(13) + 4)) == moe.COLIBRI_ERR_INVALID_ARG
-    assert ffn_q4_call(lib, s, q4_experts(z2=fake(18) + 4)) == moe.COLIBRI_ERR_INVALID_ARG
+    assert ffn_q4_call(lib, s, q4_experts(z2=fake(18) + 2)) == moe.COLIBRI_ERR_INVALID_ARG
     assert lib.colibri_moe_expert_ffn_q4(ctypes.byref(shape_c(T=0)), None, None, None, None, None, None, 0,
                                          None) == 0
 
