@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                                                                SharedPartials sp) {
     typedef float fv __attribute__((ext_vector_type(VEC)));
     static_assert(L == 1 || L == 8, "lanes per output");
-    static_assert(U % 8 == 0, "U keeps split s in interleaved sum s % 8");
+    static_assert(U % 8 == 0 || (L == 1 && U < 8), "a batch keeps split s in interleaved sum s % 8 (U < 8: S <= U)");
     constexpr int NJ = L == 1 ? 8 : 1;  // interleaved sums per thread
     const int vpr = d / VEC;
     const size_t total = (size_t)T * vpr;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (mb + u < nmine) {  // no break, so every index stays a constant
-                    const int j = L == 1 ? u % 8 : 0;  // L = 1: split mb + u, and mb is a multiple of 8
+                    const int j = L == 1 ? u % 8 : 0;  // L = 1: split mb + u; mb % 8 == 0 (U < 8: mb = 0)
 #pragma unroll
                     for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
@@ -318,11 +318,19 @@ hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *pa
                                                                  s.d, (const uint16_t *)shared,
                                                                  (const uint16_t *)residual, sp);
     } else {
+        // one thread per output vector; batches no larger than S, so a thread
+        // loads only the splits it adds
         const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
-        combine_partials_kernel<4, 16, 1><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
-                                                                  (const uint16_t *)b2, s.E, (uint16_t *)out, s.T,
-                                                                  s.d, (const uint16_t *)shared,
-                                                                  (const uint16_t *)residual, sp);
+#define COLIBRI_COMBINE_PARTIALS(UV)                                                                           \
+    combine_partials_kernel<4, UV, 1><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,        \
+                                                              (const uint16_t *)b2, s.E, (uint16_t *)out, s.T, \
+                                                              s.d, (const uint16_t *)shared,                   \
+                                                              (const uint16_t *)residual, sp)
+        if (S <= 2) COLIBRI_COMBINE_PARTIALS(2);
+        else if (S <= 4) COLIBRI_COMBINE_PARTIALS(4);
+        else if (S <= 8) COLIBRI_COMBINE_PARTIALS(8);
+        else COLIBRI_COMBINE_PARTIALS(16);
+#undef COLIBRI_COMBINE_PARTIALS
     }
     return hipGetLastError();
 }

@@ -378,8 +378,9 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
 
 // Adds the S split partials of every row in order 0..S-1 and applies the
 // epilogue: H (first layer) or Y (second layer) in bf16.  One thread per 4
-// output columns.
-template <int EPI>
+// output columns.  U: splits loaded per batch (a multiple of 8, or S <= U < 8:
+// one batch).
+template <int EPI, int U>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ part, int S, int T,
                                                            const int32_t *__restrict__ offsets, int E,
                                                            const uint16_t *__restrict__ bias,
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
         // the combine uses, which spreads a row's splits over 8 lanes (for S <= 8
         // it is the plain order).  Loads are issued U at a time so a thread waits
         // on memory ceil(S / U) times.
-        constexpr int U = 16;
+        static_assert(U % 8 == 0 || U < 8, "a batch keeps split s in interleaved sum s % 8");
         constexpr bool IL = (EPI == EPI_BIAS_ONLY);
         constexpr int NJ = IL ? 8 : 1;
         float u8[NJ][4], v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 #pragma unroll
             for (int k = 0; k < U; ++k) {
                 if (sp + k < S) {  // uniform; no break, so every index stays a constant
-                    const int kj = IL ? k % 8 : 0;  // U is a multiple of 8: sp + k = k (mod 8)
+                    const int kj = IL ? k % 8 : 0;  // sp + k = k (mod 8): U % 8 == 0, or sp = 0
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         u8[kj][q] += a[k][q];
@@ -557,8 +558,15 @@ hipError_t launch_reduce_t(const colibri_moe_shape_t &s, int S, const int32_t *o
                            int N, const void *scratch, hipStream_t st) {
     const size_t total = (size_t)2 * s.T * (N / 4);
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
-    split_reduce_kernel<EPI><<<blocks, 256, 0, st>>>((const float *)scratch, S, s.T, offsets, s.E,
-                                                     (const uint16_t *)bias, (uint16_t *)C, N);
+    // batches no larger than S: a thread loads only the splits it adds
+#define COLIBRI_REDUCE_LAUNCH(UV)                                                                             \
+    split_reduce_kernel<EPI, UV><<<blocks, 256, 0, st>>>((const float *)scratch, S, s.T, offsets, s.E,        \
+                                                         (const uint16_t *)bias, (uint16_t *)C, N)
+    if (S <= 2) COLIBRI_REDUCE_LAUNCH(2);
+    else if (S <= 4) COLIBRI_REDUCE_LAUNCH(4);
+    else if (S <= 8) COLIBRI_REDUCE_LAUNCH(8);
+    else COLIBRI_REDUCE_LAUNCH(16);
+#undef COLIBRI_REDUCE_LAUNCH
     return hipGetLastError();
 }
 
