@@ -143,7 +143,9 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                                                                SharedPartials sp) {
     typedef float fv __attribute__((ext_vector_type(VEC)));
     static_assert(L == 1 || L == 8, "lanes per output");
-    static_assert(U % 8 == 0 || (L == 1 && U < 8), "a batch keeps split s in interleaved sum s % 8 (U < 8: S <= U)");
+    // L = 1: a batch of U splits keeps split s in interleaved sum s % 8 when U is a
+    // multiple of 8, or when one batch holds them all (the host keeps S <= U < 8)
+    static_assert(L == 8 || U % 8 == 0 || U < 8, "batch size");
     constexpr int NJ = L == 1 ? 8 : 1;  // interleaved sums per thread
     const int vpr = d / VEC;
     const size_t total = (size_t)T * vpr;
@@ -312,11 +314,18 @@ hipError_t launch_combine_partials(const colibri_moe_shape_t &s, const float *pa
                                    hipStream_t st, const void *shared, const void *residual, SharedPartials sp) {
     const size_t total = (size_t)s.T * (s.d / 4);
     if (S >= COLIBRI_COMBINE_LANES_MIN_S && total <= 65536) {  // few outputs, several splits: 8 lanes per output
+        // a lane adds ceil(S / 8) splits, loaded in batches no larger than that
         const int blocks = (int)std::min<size_t>((total * 8 + 255) / 256, 8192);
-        combine_partials_kernel<4, 8, 8><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,
-                                                                 (const uint16_t *)b2, s.E, (uint16_t *)out, s.T,
-                                                                 s.d, (const uint16_t *)shared,
-                                                                 (const uint16_t *)residual, sp);
+        const int per_lane = (S + 7) / 8;
+#define COLIBRI_COMBINE_LANES(UV)                                                                              \
+    combine_partials_kernel<4, UV, 8><<<blocks, 256, 0, st>>>(part, S, assign_pos, topk_idx, topk_gate,        \
+                                                              (const uint16_t *)b2, s.E, (uint16_t *)out, s.T, \
+                                                              s.d, (const uint16_t *)shared,                   \
+                                                              (const uint16_t *)residual, sp)
+        if (per_lane <= 2) COLIBRI_COMBINE_LANES(2);
+        else if (per_lane <= 4) COLIBRI_COMBINE_LANES(4);
+        else COLIBRI_COMBINE_LANES(8);
+#undef COLIBRI_COMBINE_LANES
     } else {
         // one thread per output vector; batches no larger than S, so a thread
         // loads only the splits it adds

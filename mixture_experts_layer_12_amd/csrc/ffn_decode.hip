@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kDecWaves *kWave) void ffn_decode_kernel(
         const int rows = min(ROWS, count - rc);
         if constexpr (HFROMP) {
             constexpr bool HDUAL = (HEPI == EPI_SWIGLU);
-            constexpr int U = 16;
+            constexpr int U = 8;  // splits loaded per batch (the first layer's S is mostly <= 8)
             const int NCU = HDUAL ? 2 * K : K;  // columns of a first-layer partial row
             const size_t split_stride = (size_t)A_total * NCU;
             __syncthreads();  // the previous chunk's H reads are done
