@@ -28,9 +28,14 @@
 //     sums of x over the group, so that at the end of every group
 //       total += s * (acc - (128 + z) * rowsum_x)
 //     is the group's exact contribution (up to fp32 rounding);
-//   * four k-steps of codes are in flight per wave (each k-step is 1 KB per
-//     wave); the group scales and zero points (20 bytes per lane and group)
-//     are read at each group's start and used at its end;
+//   * the rows (A operand) of a group -- 128 k of every row of the tile -- are
+//     loaded once per workgroup, a share per thread, and staged in LDS (two
+//     buffers, one barrier per group), where the four waves read their
+//     fragments: a wave's global loads are its codes only;
+//   * the codes of the next group's four k-steps are in flight during a group
+//     (each k-step is 1 KB per wave); the group scales and zero points (20
+//     bytes per lane and group) are read at each group's start and used at
+//     its end;
 //   * K splits run along whole groups; split partials (fp32) are added by
 //     the split reduce or, for the second layer inside the layer call, by the
 //     combine.
@@ -57,7 +62,7 @@ __device__ __forceinline__ void unpack_q4(const u32x4 &w, bf16x8 (&frag)[4]) {
     }
 }
 
-template <int MB, int NST, int EPI, bool GATHER>
+template <int MB, int EPI, bool GATHER>
 __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
     const int32_t *__restrict__ offsets, int E, const uint32_t *__restrict__ Q0, const uint32_t *__restrict__ Q1,
@@ -67,7 +72,10 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr int WCOLS = DUAL ? 32 : 64;  // output columns per wave (per matrix)
     constexpr int ROWS = MB * 16;
-    static_assert(NST % 4 == 0, "stages cover whole groups");
+    // the rows of one group staged in LDS, row pitch 136 bf16 (272 bytes: the
+    // 16 rows one fragment read touches start in distinct banks); two buffers
+    constexpr int APITCH = kQ4Group + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t arows[2][ROWS * APITCH];
     const int lane = threadIdx.x & (kWave - 1);
     const int ncbg = (NCB + kQ4Waves - 1) / kQ4Waves;
     const int cbg = blockIdx.x % ncbg;
@@ -75,11 +83,11 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
     const int split = rest % S;
     const int slot = rest / S;
     const int cb = cbg * kQ4Waves + (int)(threadIdx.x / kWave);
-    if (cb >= NCB) return;
+    const bool active = cb < NCB;  // waves past the last column block only help stage the rows
 
     const int A_total = 2 * T;
     int e, r0, count;
-    if (!live_expert(offsets, E, A_total, slot, e, r0, count)) return;
+    if (!live_expert(offsets, E, A_total, slot, e, r0, count)) return;  // the same for every wave
 
     const int c = lane & 15;  // column group: columns ccol .. ccol + 3
     const int g = lane >> 4;  // k group: k 8g .. 8g+7 of a 32-deep step
@@ -96,27 +104,36 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
     const float *s_base = Sm + (size_t)e * G * N + col;
     const uint8_t *z_base = Zm + (size_t)e * G * N + col;
 
-    // whole groups per split: k-steps [4 g_begin, 4 g_end)
+    // whole groups per split: groups [g_begin, g_end), k-steps 4 g_begin ..
     const int g_begin = (int)((long)G * split / S), g_end = (int)((long)G * (split + 1) / S);
-    const int s_begin = 4 * g_begin, s_end = 4 * g_end;
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 x 8
+    // this thread's share of a staged group: 16-byte chunk q of rows ar0 + 16 m
+    const int aq = threadIdx.x & 15, ar0 = (threadIdx.x >> 4) & 15;
 
     for (int rc = 0; rc < count; rc += ROWS) {
         const int rows = min(ROWS, count - rc);
-        // A rows of this lane: row (lane % 16) of each 16-row subtile; rows past
-        // the segment read row r0 instead (never stored)
-        const uint16_t *a_src[MB];
+        const uint16_t *asrc[MB];  // rows past the segment read row r0 instead (never stored)
 #pragma unroll
-        for (int mi = 0; mi < MB; ++mi) {
-            const int r = mi * 16 + c;
+        for (int m = 0; m < MB; ++m) {
+            const int r = ar0 + 16 * m;
             const int p = r0 + rc + (r < rows ? r : 0);
             long src = p;
             if (GATHER) {
                 const int a = sorted_assign[p];
                 src = (a >= 0 && (a >> 1) < T) ? (a >> 1) : 0;
             }
-            a_src[mi] = A + (size_t)src * K + 8 * g;
+            asrc[m] = A + (size_t)src * K + 8 * aq;
         }
+        u32x4 ra[MB];
+        auto load_rows = [&](int grp) {
+#pragma unroll
+            for (int m = 0; m < MB; ++m) ra[m] = *reinterpret_cast<const u32x4 *>(asrc[m] + (size_t)grp * kQ4Group);
+        };
+        auto store_rows = [&](int buf) {
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+                *reinterpret_cast<u32x4 *>(&arows[buf][(ar0 + 16 * m) * APITCH + 8 * aq]) = ra[m];
+        };
 
         f32x4 acc[MB][4], rsum[MB], tot[MB][4];
 #pragma unroll
@@ -125,22 +142,18 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[mi][j] = tot[mi][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
-
-        struct Stage {
-            u32x4 b;
-            u32x4 a[MB];
+        u32x4 wb[4];  // the codes of the group's four k-steps
+        auto load_codes = [&](int kk, int step) {
+            wb[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(q_base + (size_t)step * 4 * N));
         };
-        auto load_stage = [&](Stage &sg, int step) {
-            sg.b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(q_base + (size_t)step * 4 * N));
-#pragma unroll
-            for (int mi = 0; mi < MB; ++mi) sg.a[mi] = *reinterpret_cast<const u32x4 *>(a_src[mi] + step * 32);
-        };
-        auto mma = [&](const Stage &sg) {
+        // k-step kk of the group in buffer buf: rows mi*16 + c, k 32 kk + 8g .. + 7
+        auto mma = [&](int kk, int buf) {
             bf16x8 bfrag[4];
-            unpack_q4(sg.b, bfrag);
+            unpack_q4(wb[kk], bfrag);
 #pragma unroll
             for (int mi = 0; mi < MB; ++mi) {
-                const bf16x8 afrag = __builtin_bit_cast(bf16x8, sg.a[mi]);
+                const bf16x8 afrag = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(&arows[buf][(mi * 16 + c) * APITCH + 32 * kk + 8 * g]));
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[mi][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[j], acc[mi][j], 0, 0, 0);
@@ -148,8 +161,7 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
                                                                   0, 0, 0);
             }
         };
-        // group grp: its scales and zero points (read at the group's start) fold
-        // the group's sums into the totals
+        // the group's scales and zero points (read at its start) fold its sums into the totals
         f32x4 gs;
         uint32_t gz;
         auto load_group = [&](int grp) {
@@ -173,42 +185,41 @@ __global__ __launch_bounds__(kQ4Waves *kWave) void ffn_decode_q4_kernel(
             for (int mi = 0; mi < MB; ++mi) rsum[mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         };
 
-        // NST stages (a multiple of 4: stage i holds step st + i, and a group
-        // starts at every stage i % 4 == 0).  The steady-state loop issues every
-        // prefetch unconditionally.
-        Stage sg[NST];
+        // group g_begin + j sits in buffer j % 2; the rows of the next group are
+        // loaded during a group and stored at its end, behind one barrier; the
+        // codes of the next group's four k-steps are in flight during a group
+        __syncthreads();  // the previous row chunk's reads are done
+        load_rows(g_begin);
+        store_rows(0);
+        __syncthreads();
+        if (g_begin + 1 < g_end) load_rows(g_begin + 1);
+        if (active)
 #pragma unroll
-        for (int i = 0; i < NST; ++i)
-            if (s_begin + i < s_end) load_stage(sg[i], s_begin + i);
-        int st = s_begin;
-        for (; st + 2 * NST <= s_end; st += NST) {
+            for (int kk = 0; kk < 4; ++kk) load_codes(kk, 4 * g_begin + kk);
+        int grp = g_begin;
+        for (; grp + 1 < g_end; ++grp) {
+            const int buf = (grp - g_begin) & 1;
+            if (active) {
+                load_group(grp);
 #pragma unroll
-            for (int i = 0; i < NST; ++i) {
-                if (i % 4 == 0) load_group((st + i) / 4);
-                mma(sg[i]);
-                load_stage(sg[i], st + NST + i);
-                if (i % 4 == 3) finish_group();
-                __builtin_amdgcn_sched_barrier(0);
+                for (int kk = 0; kk < 4; ++kk) {
+                    mma(kk, buf);
+                    load_codes(kk, 4 * (grp + 1) + kk);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                finish_group();
             }
+            store_rows(buf ^ 1);  // its last reads were before the previous barrier
+            __syncthreads();
+            load_rows(min(grp + 2, g_end - 1));
         }
-        // fewer than 2 NST steps left: the stages hold st .. st + NST - 1 (those below s_end)
+        if (active) {  // the last group
+            load_group(grp);
 #pragma unroll
-        for (int i = 0; i < NST; ++i) {
-            if (st + i < s_end) {
-                if (i % 4 == 0) load_group((st + i) / 4);
-                mma(sg[i]);
-                if (st + NST + i < s_end) load_stage(sg[i], st + NST + i);
-                if (i % 4 == 3) finish_group();
-            }
+            for (int kk = 0; kk < 4; ++kk) mma(kk, (grp - g_begin) & 1);
+            finish_group();
         }
-#pragma unroll
-        for (int i = 0; i < NST; ++i) {
-            if (st + NST + i < s_end) {
-                if (i % 4 == 0) load_group((st + NST + i) / 4);
-                mma(sg[i]);
-                if (i % 4 == 3) finish_group();
-            }
-        }
+        if (!active) continue;
 
         // accumulator register r of column j, subtile mi: row mi*16 + 4g + r,
         // column ccol + j (SwiGLU: lanes c >= 8 hold the W3 product)
@@ -245,7 +256,7 @@ struct Q4Plan {
 
 // Column blocks, live-expert slots, row tile and K split of one layer.  S
 // minimises an estimate of the layer's time, as for the bf16 kernel: a round
-// is 256 CUs times the workgroups one CU holds (3 with 16-row tiles, 2 with
+// is 256 CUs times the workgroups one CU holds (4 with 16-row tiles, 2 with
 // 32: the kernel's register budget); a wave streams one k-step (1 KB of codes)
 // per ~0.5 us plus ~3 k-steps of start-up and epilogue; the stream cannot beat
 // ~6 TB/s; S > 1 adds the partials' write and read and a reduce launch.
@@ -268,7 +279,7 @@ Q4Plan q4_plan(const colibri_moe_shape_t &s, bool up) {
     p.S = 1;
     double best = 1e300;
     for (int S = 1; S <= G; ++S) {
-        const long per_round = 256L * (p.MB == 1 ? 3 : 2);
+        const long per_round = 256L * (p.MB == 1 ? 4 : 2);
         const double rounds = (double)((wg_per_split * S + per_round - 1) / per_round);
         const double steps = 4.0 * ((G + S - 1) / S);
         double us = std::max(rounds * (steps + 3.0) * step_us, weight_bytes / 6.0e6);
@@ -286,16 +297,16 @@ hipError_t launch_q4_t(const colibri_moe_shape_t &s, const Q4Plan &p, bool gathe
                        void *scratch, hipStream_t st) {
     float *part = static_cast<float *>(scratch);
     const int blocks = p.slots * p.S * ((p.NCB + kQ4Waves - 1) / kQ4Waves);
-#define COLIBRI_Q4_LAUNCH(MBV, NSTV, G)                                                                              \
-    ffn_decode_q4_kernel<MBV, NSTV, EPI, G><<<blocks, kQ4Waves * kWave, 0, st>>>(                                    \
+#define COLIBRI_Q4_LAUNCH(MBV, G)                                                                                    \
+    ffn_decode_q4_kernel<MBV, EPI, G><<<blocks, kQ4Waves * kWave, 0, st>>>(                                          \
         (const uint16_t *)Am, sa, s.T, offsets, s.E, Q0, Q1, S0, S1, Z0, Z1, (const uint16_t *)bias, (uint16_t *)C, K, \
         N, p.NCB, p.S, part)
     if (p.MB == 1) {
-        if (gather) COLIBRI_Q4_LAUNCH(1, 4, true);
-        else COLIBRI_Q4_LAUNCH(1, 4, false);
+        if (gather) COLIBRI_Q4_LAUNCH(1, true);
+        else COLIBRI_Q4_LAUNCH(1, false);
     } else {
-        if (gather) COLIBRI_Q4_LAUNCH(2, 4, true);
-        else COLIBRI_Q4_LAUNCH(2, 4, false);
+        if (gather) COLIBRI_Q4_LAUNCH(2, true);
+        else COLIBRI_Q4_LAUNCH(2, false);
     }
 #undef COLIBRI_Q4_LAUNCH
     return hipGetLastError();
