@@ -198,3 +198,26 @@ def test_q4_rejects_unsupported_shapes():
         with pytest.raises(moe.ColibriError) as ei:
             moe.expert_ffn_q4(sh, 1 << 20, 1 << 20, 1 << 20, fake, fake, 1 << 20, 1 << 20, 1 << 40)
         assert ei.value.status == moe.COLIBRI_ERR_UNSUPPORTED
+
+
+# seeded random decode shapes: expert counts 2..16, d and h multiples of the
+# 128-channel group, every activation, ragged and skewed batches
+def _random_q4_cases(n=12, seed=45):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append((int(rng.choice([1, 2, 3, 5, 8, 13, 21, 33, 48, 64])), int(rng.integers(2, 17)),
+                    128 * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 12)),
+                    str(rng.choice(["relu", "gelu", "swiglu"])), bool(rng.integers(0, 2))))
+    return out
+
+
+RANDOM_Q4 = _random_q4_cases()
+
+
+@pytest.mark.parametrize("T,E,d,h,act,two", RANDOM_Q4,
+                         ids=[f"T{c[0]}-E{c[1]}-d{c[2]}-h{c[3]}-{c[4]}" + ("-two" if c[5] else "") for c in RANDOM_Q4])
+def test_ffn_q4_random_shapes(T, E, d, h, act, two):
+    x, qw, idx = small_q4_case(act, T, E, d, h, seed=T * 31 + E * 7 + d + h, two_experts=two)
+    y, y_ref = run_ffn_q4(x, qw, idx, act, E, gather=True)
+    G.assert_bf16_close(y, y_ref, f"q4 ffn random T={T} E={E} d={d} h={h} {act}")
