@@ -46,8 +46,10 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kCusPerXcd = 32;  // a scheduling group fits the CUs of one XCD
 
+constexpr int kCus = kXcds * kCusPerXcd;
+
 struct Tile {
-    int e, row0, rows, n0, split;
+    int e, row0, rows, n0, split, S;  // S: K splits of this tile
 };
 
 // Row tiles of expert e: count_e rows are cut into ceil(count_e / BMB) row
@@ -62,43 +64,55 @@ __device__ __forceinline__ int row_tiles(int rows, int BMB, int BM) {
     return mt;
 }
 
-// Block b -> (expert, row range, first column, K split); column tiles: NT,
-// K splits: S.  Whole-wave call; every lane gets the same answer.  Returns
-// false for surplus blocks (the grid is sized for the worst case).
-template <int BMB, int BM, int BN>
-__device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets, int E, int A, int NT, int S, int b,
-                                            Tile &t) {
+// Row tiles of every expert (lane e holds expert e's) and their prefix sums.
+// Whole-wave call; every lane gets the same total.
+struct TileTable {
+    int lo, hi, mt, rt, tiles, incl, total;
+};
+template <int BMB, int BM>
+__device__ __forceinline__ TileTable tile_table(const int32_t *__restrict__ offsets, int E, int A, int NT) {
     const int lane = threadIdx.x & (kWave - 1);
-    int lo = 0, hi = 0;
+    TileTable tt;
+    tt.lo = 0, tt.hi = 0;
     if (lane < E) {
-        lo = min(max(offsets[lane], 0), A);
-        hi = min(max(offsets[lane + 1], lo), A);
+        tt.lo = min(max(offsets[lane], 0), A);
+        tt.hi = min(max(offsets[lane + 1], tt.lo), A);
     }
-    const int mt = row_tiles(hi - lo, BMB, BM);           // row tiles of expert `lane`
-    const int rt = mt > 0 ? (hi - lo + mt - 1) / mt : 0;  // rows per row tile (<= BM)
-    const int tiles = mt * NT;
-    int incl = tiles;
+    tt.mt = row_tiles(tt.hi - tt.lo, BMB, BM);                      // row tiles of expert `lane`
+    tt.rt = tt.mt > 0 ? (tt.hi - tt.lo + tt.mt - 1) / tt.mt : 0;  // rows per row tile (<= BM)
+    tt.tiles = tt.mt * NT;
+    tt.incl = tt.tiles;
 #pragma unroll
     for (int s = 1; s < kWave; s <<= 1) {
-        const int o = __shfl_up(incl, s);
-        if (lane >= s) incl += o;
+        const int o = __shfl_up(tt.incl, s);
+        if (lane >= s) tt.incl += o;
     }
-    const int total = __shfl(incl, kWave - 1);
-    if (b >= total * S) return false;
-    // keep consecutive logical indices on one XCD: block b runs on XCD b % 8;
-    // the index is split-major, so one XCD works on one K range of neighbouring tiles
-    const int xcd = b % kXcds, i = b / kXcds;
-    const int q = total * S / kXcds, r = total * S % kXcds;
-    const int LS = xcd * q + min(xcd, r) + i;
-    t.split = LS / total;
-    const int L = LS - t.split * total;
-    const int excl = incl - tiles;
-    const uint64_t m = __ballot(lane < E && L >= excl && L < incl);
+    tt.total = __shfl(tt.incl, kWave - 1);
+    return tt;
+}
+
+// Tiles that run with the whole K range: all of them, or -- with a tail
+// split, when the tiles fill some rounds of one workgroup per CU plus a last
+// round of at most half the CUs -- the full rounds, and the last round's
+// tiles run as two K halves (twice as many half-length workgroups, so the
+// last round takes about half as long).
+__device__ __forceinline__ int whole_tiles(int total, int S, bool tail_split) {
+    if (!tail_split || S != 1 || total <= kCus) return total;
+    const int tail = total % kCus;
+    return (tail > 0 && 2 * tail <= kCus) ? total - tail : total;
+}
+
+// Logical tile L -> expert, row range and first column.  Inside an expert,
+// column tiles go in groups of gn, each with all mte row tiles, gn * mte <= one
+// XCD's CUs so that a group's tiles are resident together.
+template <int BN>
+__device__ __forceinline__ void tile_at(const TileTable &tt, int E, int NT, int L, Tile &t) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int excl = tt.incl - tt.tiles;
+    const uint64_t m = __ballot(lane < E && L >= excl && L < tt.incl);
     const int e = __ffsll((unsigned long long)m) - 1;
-    const int mte = __shfl(mt, e);
+    const int mte = __shfl(tt.mt, e);
     const int local = L - __shfl(excl, e);
-    // inside the expert: groups of gn column tiles, each with all mte row tiles,
-    // gn * mte <= one XCD's CUs so that a group's tiles are resident together
     const int gn = max(1, kCusPerXcd / mte);
     const int ng = local / (mte * gn);
     const int gs = min(gn, NT - ng * gn);
@@ -106,10 +120,34 @@ __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets,
     const int mi = rr / gs;
     const int ni = ng * gn + rr % gs;
     t.e = e;
-    const int rte = __shfl(rt, e);
-    t.row0 = __shfl(lo, e) + mi * rte;
-    t.rows = min(rte, __shfl(hi, e) - t.row0);
+    const int rte = __shfl(tt.rt, e);
+    t.row0 = __shfl(tt.lo, e) + mi * rte;
+    t.rows = min(rte, __shfl(tt.hi, e) - t.row0);
     t.n0 = ni * BN;
+}
+
+// Block b -> (expert, row range, first column, K split); column tiles: NT,
+// K splits: S (or a tail split, see whole_tiles).  Whole-wave call; every lane
+// gets the same answer.  Returns false for surplus blocks (the grid is sized
+// for the worst case).
+template <int BMB, int BM, int BN>
+__device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets, int E, int A, int NT, int S,
+                                            bool tail_split, int b, Tile &t) {
+    const TileTable tt = tile_table<BMB, BM>(offsets, E, A, NT);
+    const int total = tt.total;
+    const int F = whole_tiles(total, S, tail_split);
+    if (b >= (S > 1 ? total * S : F + 2 * (total - F))) return false;
+    // logical tiles [base, base + cnt), SS splits each; blocks bb = 0 .. cnt * SS - 1
+    int base = 0, cnt = S == 1 ? F : total, SS = S, bb = b;
+    if (S == 1 && b >= F) base = F, cnt = total - F, SS = 2, bb = b - F;  // F is a multiple of 8
+    // keep consecutive logical indices on one XCD: block b runs on XCD b % 8;
+    // the index is split-major, so one XCD works on one K range of neighbouring tiles
+    const int xcd = bb % kXcds, i = bb / kXcds;
+    const int q = cnt * SS / kXcds, r = cnt * SS % kXcds;
+    const int LS = xcd * q + min(xcd, r) + i;
+    t.split = LS / cnt;
+    t.S = SS;
+    tile_at<BN>(tt, E, NT, base + LS - t.split * cnt, t);
     return true;
 }
 
@@ -198,7 +236,7 @@ template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, 
 __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
-    const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NT, int S,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NT, int S, int tail_split,
     float *__restrict__ part) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr int NB = DUAL ? 2 : 1;             // weight matrices per tile
@@ -233,12 +271,14 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     const int wm = w / WN, wn = w % WN;
 
     Tile tl;
-    if (!locate_tile<BMB, BM, BNC>(offsets, E, 2 * T, NT, S, blockIdx.x, tl)) return;  // uniform per block
+    if (!locate_tile<BMB, BM, BNC>(offsets, E, 2 * T, NT, S, tail_split != 0, blockIdx.x, tl))
+        return;  // uniform per block
     const int e = __builtin_amdgcn_readfirstlane(tl.e);
     const int row0 = __builtin_amdgcn_readfirstlane(tl.row0);
     const int rows = __builtin_amdgcn_readfirstlane(tl.rows);
     const int n0 = __builtin_amdgcn_readfirstlane(tl.n0);
     const int split = __builtin_amdgcn_readfirstlane(tl.split);
+    const int SK = __builtin_amdgcn_readfirstlane(tl.S);  // K splits of this tile
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_byte *)lds;
 
     // ---- copy sources.  Rows past the expert's segment read its first row and
@@ -387,8 +427,8 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     constexpr int KS = BK / 16;
     constexpr int DPW = A_PW + B_PW;
     // this block's K range: k-tiles [kt0, kt0 + KT) of the K / BK
-    const int kt0 = split * (K / BK) / S;
-    const int KT = (split + 1) * (K / BK) / S - kt0;
+    const int kt0 = split * (K / BK) / SK;
+    const int KT = (split + 1) * (K / BK) / SK - kt0;
     auto ktile = [&](int t) { return kt0 + (t < KT ? t : KT - 1); };
     auto main_loop = [&](auto lv) {
         Frags f[2];
@@ -463,7 +503,7 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
             loader_loop();
             wait_vmcnt<0>();
             __syncthreads();
-            if (S == 1) __syncthreads();
+            if (SK == 1) __syncthreads();
             return;
         }
         if (live_sm == SM) main_loop_spec(std::integral_constant<int, SM>{});
@@ -480,7 +520,7 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     // ---- K split: the fp32 partial sums go to part[split][row][col] (SwiGLU: the
     // W3 products at col + N); a later kernel adds the splits and applies the epilogue
     // 32x32 accumulator layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4, column l%32
-    if (S > 1) {
+    if (SK > 1) {
         constexpr int NC = DUAL ? 2 : 1;
         float *pb = part + ((size_t)split * 2 * T + row0) * (size_t)(NC * N);
 #pragma unroll
@@ -538,6 +578,52 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     }
 }
 
+// Tail split, second half: the tiles of the last round were run as two K
+// halves into part[0..1][row][col] (SwiGLU: W3 products at col + N); the halves
+// are added in order (0 + half 0 + half 1, as the split reduce does), the
+// epilogue applied and the bf16 tile stored.  Block b: tail tile b / RB, tile
+// rows [(b % RB) RPB, +RPB); one thread per 4 columns of one row.
+template <int BMB, int BM, int BNC>
+struct TailReduceGrid {
+    static constexpr int Q = BNC / 4;                  // 4-column groups per tile row
+    static constexpr int RPB = 256 / Q;                // tile rows per block
+    static constexpr int RB = (BM + RPB - 1) / RPB;    // blocks per tile
+    static constexpr int blocks = (kCus / 2) * RB;     // at most kCus / 2 tail tiles
+};
+template <int BMB, int BM, int BNC, int EPI>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float *__restrict__ part, int T,
+                                                          const int32_t *__restrict__ offsets, int E, int NT,
+                                                          const uint16_t *__restrict__ bias, uint16_t *__restrict__ C,
+                                                          int N) {
+    using G = TailReduceGrid<BMB, BM, BNC>;
+    static_assert(256 % G::Q == 0, "whole rows per block");
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    const int NC = DUAL ? 2 * N : N;
+    const int tile = blockIdx.x / G::RB, rb = blockIdx.x % G::RB;
+    const TileTable tt = tile_table<BMB, BM>(offsets, E, 2 * T, NT);
+    const int F = whole_tiles(tt.total, 1, true);
+    if (tile >= tt.total - F) return;  // uniform per block
+    Tile tl;
+    tile_at<BNC>(tt, E, NT, F + tile, tl);
+    const int rl = rb * G::RPB + (int)threadIdx.x / G::Q, n = tl.n0 + ((int)threadIdx.x % G::Q) * 4;
+    if (rl >= tl.rows || n >= N) return;
+    const size_t half = (size_t)2 * T * NC;
+    const float *src = part + (size_t)(tl.row0 + rl) * NC + n;
+    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(src), a1 = *reinterpret_cast<const f32x4 *>(src + half);
+    f32x4 b0 = {0.0f, 0.0f, 0.0f, 0.0f}, b1 = b0;
+    if (DUAL) {
+        b0 = *reinterpret_cast<const f32x4 *>(src + N);
+        b1 = *reinterpret_cast<const f32x4 *>(src + half + N);
+    }
+    float u[4], v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        u[c] = (0.0f + a0[c]) + a1[c];
+        v[c] = (0.0f + b0[c]) + b1[c];
+    }
+    store_epilogue<EPI, 4>(C + (size_t)(tl.row0 + rl) * N + n, u, v, bias, tl.e, N, n);
+}
+
 // Tile shapes, BK = 64, one workgroup per CU:
 //   big: row tiles of 256 rows (up to 320 when a small tail is spread over
 //        them) x 256 weight columns (SwiGLU: 128 outputs of both W1 and W3);
@@ -560,7 +646,7 @@ GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up) {
     const long A = 2L * s.T;
     const long KT = K / kBK;
     const int BMB = mid ? 128 : 256;
-    GemmPlan best{mid, BMB, 0, 1};
+    GemmPlan best{mid, BMB, 0, 1, false};
     double best_cost = 1e300;
     // Expected row tiles: one per expert while experts hold at most a tile's
     // rows, else one per base tile height.  Estimated time: (rounds of 256
@@ -570,7 +656,11 @@ GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up) {
     // for a big tile), plus, when K is split, the fp32 partials written and
     // read once (~5 TB/s) and a ~4 us reduce launch.  Splits keep at least 4
     // k-tiles per block.  Ties keep the wider tile and the smaller S.
+#ifdef COLIBRI_GEMM_MID_WIDTHS
+    const int widths[2] = {COLIBRI_GEMM_MID_WIDTHS};
+#else
     const int widths[2] = {256, 128};
+#endif
     for (int wi = 0; wi < (mid ? 2 : 1); ++wi) {
         const long BNC = mid ? widths[wi] : (dual ? 128 : 256);
         const long NT = (N + BNC - 1) / BNC;
@@ -581,8 +671,22 @@ GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up) {
             const double part_bytes = (double)S * A * N * (dual ? 2 : 1) * 4;
             double us = (double)((tiles * S + 255) / 256) * ((double)KT / S + 2.0) * t_kt;
             if (S > 1) us += 2.0 * part_bytes / 5.0e6 + 4.0;
-            if (us < best_cost - 1e-9) best_cost = us, best = {mid, BMB, (int)BNC, (int)S};
+            if (us < best_cost - 1e-9) best_cost = us, best = {mid, BMB, (int)BNC, (int)S, false};
         }
+    }
+    // First layer, no K split: when the expected tiles fill whole rounds of one
+    // workgroup per CU plus a last round of at most half the CUs, that round's
+    // tiles run as two K halves (the kernel decides from the actual tile count;
+    // the halves' sums go through the partials and a small reduce).
+#ifdef COLIBRI_GEMM_NO_TAIL
+    if (false) {
+#else
+    if (up && best.S == 1) {
+#endif
+        const long NT = (N + best.BNC - 1) / best.BNC;
+        const long tiles = std::max<long>(std::min<long>(s.E, A), (A + BMB - 1) / BMB) * NT;
+        const long tail = tiles % 256;
+        best.tail = KT >= 8 && tiles > 256 && tail > 0 && 2 * tail <= 256;  // halves of >= 4 k-tiles
     }
     return best;
 }
@@ -592,22 +696,29 @@ namespace {
 template <int BMB, int BM, int BN, int WPE, int BLD, int BST, int EPI>
 hipError_t launch_shape(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
                         const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
-                        int S, float *part, hipStream_t st) {
+                        int S, bool tail, float *part, hipStream_t st) {
     constexpr int BNC = EPI == EPI_SWIGLU ? BN / 2 : BN;
     const int A = 2 * s.T;
     const int NT = (N + BNC - 1) / BNC;
     const int mtiles = (A + BMB - 1) / BMB + std::min(s.E, A);  // bound on the row tiles of all experts
-    const dim3 grid(mtiles * NT * S);
+    const dim3 grid(mtiles * NT * (tail ? 2 : S));
     constexpr int threads = (2 * 4 + BLD) * kWave;
     if (gather)
         ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, true, WPE, BLD, BST><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
-            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, part);
+            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, tail ? 1 : 0, part);
     else
         ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, false, WPE, BLD, BST><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
-            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, part);
-    return hipGetLastError();
+            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, tail ? 1 : 0, part);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && tail) {
+        constexpr int blocks = TailReduceGrid<BMB, BM, BNC>::blocks;
+        tail_reduce_kernel<BMB, BM, BNC, EPI><<<blocks, 256, 0, st>>>(part, s.T, offsets, s.E, NT,
+                                                                      (const uint16_t *)bias, (uint16_t *)C, N);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 template <int EPI>
@@ -617,12 +728,13 @@ hipError_t launch_gemm(const GemmPlan &p, bool gather, const colibri_moe_shape_t
     if constexpr (EPI != EPI_SWIGLU) {
         if (p.mid && p.BNC == 256)
             return launch_shape<128, 192, 256, 2, 2, 3, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S,
-                                                             part, st);
+                                                             p.tail, part, st);
         if (p.mid)
             return launch_shape<128, 192, 128, 2, 2, 6, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S,
-                                                             part, st);
+                                                             p.tail, part, st);
     }
-    return launch_shape<256, 320, 256, 2, 0, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S, part, st);
+    return launch_shape<256, 320, 256, 2, 0, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S, p.tail,
+                                                     part, st);
 }
 
 }  // namespace
@@ -633,7 +745,9 @@ int gemm_splits(const colibri_moe_shape_t &s, bool up) {
 }
 
 size_t gemm_scratch_bytes(const colibri_moe_shape_t &s, bool up) {
-    const int S = gemm_splits(s, up);
+    if (s.dtype != COLIBRI_BF16 || s.T <= 0) return 0;
+    const GemmPlan p = gemm_plan(s, up);
+    const int S = p.tail ? 2 : p.S;
     if (S <= 1) return 0;
     const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
     return align256((size_t)S * 2 * s.T * (size_t)(up ? s.h : s.d) * (dual ? 2 : 1) * 4);

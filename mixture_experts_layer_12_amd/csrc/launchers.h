@@ -114,6 +114,7 @@ struct GemmPlan {
     int BMB;   // base row-tile height
     int BNC;   // output columns per tile
     int S;     // K splits
+    bool tail; // first layer, S == 1: the last, partial round of tiles runs as two K halves
 };
 GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up);
 int gemm_splits(const colibri_moe_shape_t &s, bool up);

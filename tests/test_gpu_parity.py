@@ -272,6 +272,26 @@ def test_ffn_ragged_columns_and_presorted_rows(dt):
         G.assert_close(y, y_ref, dt, f"y_sorted gather={gather}")
 
 
+# first layers whose tiles fill a round of one workgroup per CU plus a last
+# round of at most half the CUs (17 or 33 column tiles per expert): that round's
+# tiles run as two K halves and a small kernel adds the halves; "skew" routes
+# every token to experts 0 and 1, so the kernel finds too few tiles to split
+TAIL_CASES = [(80, 16, 512, 2176, "swiglu", None), (100, 8, 512, 8448, "gelu", None),
+              (400, 16, 512, 2176, "swiglu", "skew")]
+
+
+@pytest.mark.parametrize("T,E,d,h,act,mode", TAIL_CASES,
+                         ids=[f"T{c[0]}-E{c[1]}-d{c[2]}-h{c[3]}-{c[4]}" + (f"-{c[5]}" if c[5] else "")
+                              for c in TAIL_CASES])
+def test_ffn_tail_split(T, E, d, h, act, mode):
+    w, idx = small_ffn_case(act, gen.BF16, T=T, E=E, d=d, h=h, seed=T + E)
+    if mode == "skew":
+        idx[:, 0], idx[:, 1] = 0, 1
+    for gather in (True, False):
+        y, y_ref = run_ffn(w, idx, act, gen.BF16, E=E, gather=gather)
+        G.assert_bf16_close(y, y_ref, f"tail split T={T} gather={gather}")
+
+
 DECODE_CASES = [(1, 8, 256, 384, "swiglu"), (1, 2, 128, 320, "gelu"), (5, 8, 192, 256, "relu"),
                 (16, 4, 256, 320, "swiglu"), (33, 8, 128, 192, "gelu"), (64, 8, 256, 256, "swiglu"),
                 (64, 64, 64, 128, "relu"), (2, 16, 1024, 512, "swiglu")]
