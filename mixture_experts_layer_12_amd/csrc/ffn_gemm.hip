@@ -656,11 +656,7 @@ GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up) {
     // for a big tile), plus, when K is split, the fp32 partials written and
     // read once (~5 TB/s) and a ~4 us reduce launch.  Splits keep at least 4
     // k-tiles per block.  Ties keep the wider tile and the smaller S.
-#ifdef COLIBRI_GEMM_MID_WIDTHS
-    const int widths[2] = {COLIBRI_GEMM_MID_WIDTHS};
-#else
     const int widths[2] = {256, 128};
-#endif
     for (int wi = 0; wi < (mid ? 2 : 1); ++wi) {
         const long BNC = mid ? widths[wi] : (dual ? 128 : 256);
         const long NT = (N + BNC - 1) / BNC;
@@ -678,11 +674,7 @@ GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up) {
     // workgroup per CU plus a last round of at most half the CUs, that round's
     // tiles run as two K halves (the kernel decides from the actual tile count;
     // the halves' sums go through the partials and a small reduce).
-#ifdef COLIBRI_GEMM_NO_TAIL
-    if (false) {
-#else
     if (up && best.S == 1) {
-#endif
         const long NT = (N + best.BNC - 1) / best.BNC;
         const long tiles = std::max<long>(std::min<long>(s.E, A), (A + BMB - 1) / BMB) * NT;
         const long tail = tiles % 256;
