@@ -292,6 +292,29 @@ def test_ffn_tail_split(T, E, d, h, act, mode):
         G.assert_bf16_close(y, y_ref, f"tail split T={T} gather={gather}")
 
 
+def test_ffn_tail_split_full_size():
+    """8-expert SwiGLU layer at T = 512 (d = 2048, h = 5632): 352 first-layer tiles, of which the 96
+    of the last round run as K halves; a seeded sample of rows of every expert against the oracle."""
+    T, E, d, h, act = 512, 8, 2048, 5632, "swiglu"
+    w, idx = small_ffn_case(act, gen.BF16, T=T, E=E, d=d, h=h, seed=11)
+    ref = oracle.dispatch(idx, E)
+    sh = moe.Shape(T, d, h, E, gen.BF16, moe.ACT_CODES[act])
+    ws_bytes = moe.workspace_size(sh)
+    ws = G.empty((ws_bytes,), torch.uint8)
+    y = G.empty((2 * T, d), G.tdtype(gen.BF16))
+    moe.expert_ffn(sh, G.dev(w["x"]), G.dev(ref["sorted_assign"]), G.dev(ref["offsets"]), G.dev(w["w1"]),
+                   G.dev(w["w2"]), y, ws, ws_bytes, w3=G.dev(w["w3"]))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    off = ref["offsets"]
+    pos = np.unique(np.concatenate([[off[e], off[e + 1] - 1] for e in range(E) if off[e + 1] > off[e]] +
+                                   [rng.choice(2 * T, size=32, replace=False)]))
+    rows_t = ref["sorted_assign"][pos] // 2
+    rows_e = idx.reshape(-1)[ref["sorted_assign"][pos]]
+    y_ref = oracle.ffn_rows(w["x"], rows_t, rows_e, w["w1"], w["w2"], act, w3=w["w3"], mirror=True)
+    G.assert_bf16_close(G.host(y)[pos], y_ref, "tail split, full size")
+
+
 DECODE_CASES = [(1, 8, 256, 384, "swiglu"), (1, 2, 128, 320, "gelu"), (5, 8, 192, 256, "relu"),
                 (16, 4, 256, 320, "swiglu"), (33, 8, 128, 192, "gelu"), (64, 8, 256, 256, "swiglu"),
                 (64, 64, 64, 128, "relu"), (2, 16, 1024, 512, "swiglu")]
