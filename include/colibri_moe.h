@@ -171,6 +171,32 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
                               float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* ------------------------------------------------------------------ allocation-free layer
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): colibri_moe_layer_forward with its workspace taken from a
+ * device array inside the library instead of from the caller.
+ *   - The array holds COLIBRI_MOE_NOALLOC_SCRATCH_BYTES (32 MiB); every GPU
+ *     the library runs on holds its own copy until the process ends.  Shapes
+ *     whose colibri_moe_workspace_size exceeds it are rejected with
+ *     COLIBRI_ERR_WORKSPACE before anything is launched (every decode batch of
+ *     the 8-expert and Mixtral-shaped layers fits, and the 8-expert layer up
+ *     to T = 512; the prefill batches do not).
+ *   - The call allocates and frees nothing; its first call on a device looks
+ *     up that device's copy of the array (hipGetSymbolAddress) and caches it.
+ *   - Every call on one GPU uses that GPU's one array, and the array keeps
+ *     whatever the last call left in it (nothing in it needs to start at
+ *     zero): calls that overlap on one GPU -- on different streams, or from
+ *     different threads without ordering -- race and give wrong results.
+ *     Order them on one stream, or use colibri_moe_layer_forward with
+ *     separate workspaces.
+ * Arguments, results and every other status as for colibri_moe_layer_forward
+ * (with the same inputs it returns bit-identical outputs). */
+#define COLIBRI_MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int colibri_moe_layer_forward_noalloc(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                                      const colibri_moe_experts_t *w, void *out, int32_t *topk_idx_out,
+                                      float *topk_gate_out, int32_t *expert_counts_out, hipStream_t stream);
+
 /* ------------------------------------------------------------------ layer variants
  * Gating of the chosen pair (the selection itself always ranks the logits
  * under (logit descending, index ascending)):

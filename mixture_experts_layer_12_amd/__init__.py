@@ -26,6 +26,7 @@ GATE_CODES = {"pair": GATE_PAIR, "softmax": GATE_SOFTMAX, "linear": GATE_LINEAR}
 EXPORTED = [
     "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_dispatch_workspace_size",
     "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
+    "colibri_moe_layer_forward_noalloc",
     "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
     "colibri_moe_quantize_q4", "colibri_moe_expert_ffn_q4", "colibri_moe_layer_forward_q4",
     "colibri_moe_workspace_size_ex", "colibri_moe_route_ex", "colibri_moe_combine_ex",
@@ -120,6 +121,7 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_expert_ffn_down.argtypes = [SP, P, P, ctypes.POINTER(_Experts), P, P, Z, P]
     lib.colibri_moe_combine.argtypes = [SP, P, P, P, P, P]
     lib.colibri_moe_layer_forward.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, P, P, P, Z, P]
+    lib.colibri_moe_layer_forward_noalloc.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, P, P, P]
     i32 = ctypes.c_int32
     lib.colibri_moe_quantize_q8.argtypes = [P, I, i32, i32, i32, P, P, P]
     lib.colibri_moe_expert_ffn_q8.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ8), P, P, Z, P]
@@ -142,7 +144,7 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_graph_destroy.argtypes = [P]
     for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up",
               "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
-              "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
+              "colibri_moe_layer_forward_noalloc", "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
               "colibri_moe_quantize_q4", "colibri_moe_expert_ffn_q4", "colibri_moe_layer_forward_q4",
               "colibri_moe_route_ex", "colibri_moe_combine_ex", "colibri_moe_layer_forward_ex",
               "colibri_moe_step_forward", "colibri_moe_graph_create", "colibri_moe_graph_launch",
@@ -249,6 +251,20 @@ def layer_forward(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: int, w3=
     _check(load().colibri_moe_layer_forward(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
                                             _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
                                             ws_bytes, _stream(stream)), "colibri_moe_layer_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # COLIBRI_MOE_NOALLOC_SCRATCH_BYTES
+
+
+def layer_forward_noalloc(shape: Shape, x, w_r, b_r, w1, w2, out, w3=None, b1=None, b2=None, topk_idx=None,
+                          topk_gate=None, counts=None, stream=None):
+    """colibri_moe_layer_forward on the library's own device scratch array (no
+    workspace argument, nothing allocated).  Calls that overlap on one GPU race."""
+    s = shape.c()
+    e = _experts(w1, w2, w3, b1, b2)
+    _check(load().colibri_moe_layer_forward_noalloc(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
+                                                    _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts),
+                                                    _stream(stream)), "colibri_moe_layer_forward_noalloc")
 
 
 # ------------------------------------------------------------------ gating variants, shared expert, residual

@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <new>
 
 #include "colibri_moe.h"
@@ -171,16 +172,24 @@ struct Branch {
 // Steps 1-5 after the shape and expert checks.  ffn(sorted, offsets, y, ffn_ws,
 // reduce, &partials) runs both FFN layers; with Sd > 1 second-layer K splits
 // the combine adds the splits' partials (with b2) instead of a separate reduce.
-template <class Ffn>
-int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r, void *out,
-                       int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
-                       size_t ws_bytes, hipStream_t stream, const void *b2, int Sd, Ffn ffn,
-                       const colibri_moe_layer_opts_t *opts = nullptr, const Branch &br = Branch{}) {
+// The layer's own tensor arguments (not the experts, not the workspace).
+int check_layer_io(const void *x, const void *w_r, const float *b_r, const void *out, const int32_t *topk_idx_out,
+                   const float *topk_gate_out, const int32_t *expert_counts_out) {
     if (!x || !w_r || !out) return COLIBRI_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(out, 16) || (b_r && !aligned(b_r, 4)) ||
         (topk_idx_out && !aligned(topk_idx_out, 4)) || (topk_gate_out && !aligned(topk_gate_out, 4)) ||
         (expert_counts_out && !aligned(expert_counts_out, 4)))
         return COLIBRI_ERR_INVALID_ARG;
+    return COLIBRI_OK;
+}
+
+template <class Ffn>
+int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r, void *out,
+                       int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
+                       size_t ws_bytes, hipStream_t stream, const void *b2, int Sd, Ffn ffn,
+                       const colibri_moe_layer_opts_t *opts = nullptr, const Branch &br = Branch{}) {
+    const int io = check_layer_io(x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out);
+    if (io != COLIBRI_OK) return io;
     const LayerWorkspace L = layer_workspace(s, opts);
     if (ws_bytes < L.total) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
@@ -304,6 +313,34 @@ int check_step_buffers(const colibri_moe_shape_t *s, int32_t L, const colibri_mo
     if (!x || !aligned(x, 16)) return COLIBRI_ERR_INVALID_ARG;
     if (ws_bytes < step_workspace(s, L, layers)) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    return COLIBRI_OK;
+}
+
+// ------------------------------------------------------------------ allocation-free layer
+// Workspace of colibri_moe_layer_forward_noalloc: a file-scope device array,
+// one copy on every GPU the library runs on, kept until the process ends.  In
+// host code `scratch` only names the symbol; its device address on the
+// current GPU comes from hipGetSymbolAddress, looked up once per device and
+// cached below, and only that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[COLIBRI_MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch`.
+int noalloc_scratch(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return COLIBRI_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return COLIBRI_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr || !aligned(p, 256)) return COLIBRI_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
     return COLIBRI_OK;
 }
 
@@ -432,6 +469,30 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
     if (st != COLIBRI_OK) return st;
     return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes,
                               stream, w->b2, ffn_down_splits(*s),
+                              [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
+                                  const float **part) {
+                                  return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
+                                                           part);
+                              });
+}
+
+int colibri_moe_layer_forward_noalloc(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
+                                      const colibri_moe_experts_t *w, void *out, int32_t *topk_idx_out,
+                                      float *topk_gate_out, int32_t *expert_counts_out, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_OK;
+    st = check_experts(s, w);
+    if (st != COLIBRI_OK) return st;
+    st = check_layer_io(x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out);
+    if (st != COLIBRI_OK) return st;
+    if (layer_workspace(s).total > (size_t)COLIBRI_MOE_NOALLOC_SCRATCH_BYTES) return COLIBRI_ERR_WORKSPACE;
+    void *ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st != COLIBRI_OK) return st;
+    // the same launch sequence as colibri_moe_layer_forward, on the device array
+    return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws,
+                              (size_t)COLIBRI_MOE_NOALLOC_SCRATCH_BYTES, stream, w->b2, ffn_down_splits(*s),
                               [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
                                   const float **part) {
                                   return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,

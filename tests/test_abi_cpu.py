@@ -435,3 +435,22 @@ def test_dispatch_workspace_size(lib):
     # the layer's workspace holds it
     assert lib.colibri_moe_workspace_size(ctypes.byref(large)) > lib.colibri_moe_workspace_size(
         ctypes.byref(shape_c(T=2047))) + need
+
+
+def test_layer_noalloc_checks(lib):
+    """The allocation-free layer validates on the host like the layer, and
+    refuses a batch whose workspace exceeds its device array before it touches
+    the GPU (no call here reaches the array's lookup)."""
+    e = moe._Experts(fake(10), fake(11), fake(12), None, None)
+    call = lambda s, x=fake(0), w_r=fake(1), out=fake(2): lib.colibri_moe_layer_forward_noalloc(
+        ctypes.byref(s), x, w_r, None, ctypes.byref(e), out, None, None, None, None)
+    assert call(shape_c(T=0), x=None, w_r=None, out=None) == moe.COLIBRI_OK
+    assert call(shape_c(k=3)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert call(shape_c(), x=None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert call(shape_c(), out=fake(2) + 8) == moe.COLIBRI_ERR_INVALID_ARG
+    big = shape_c(T=4096, d=4096, h=14336, E=8)
+    assert lib.colibri_moe_workspace_size(ctypes.byref(big)) > moe.NOALLOC_SCRATCH_BYTES
+    assert call(big) == moe.COLIBRI_ERR_WORKSPACE
+    no_w3 = moe._Experts(fake(10), None, fake(12), None, None)
+    assert lib.colibri_moe_layer_forward_noalloc(ctypes.byref(shape_c()), fake(0), fake(1), None, ctypes.byref(no_w3),
+                                                 fake(2), None, None, None, None) == moe.COLIBRI_ERR_INVALID_ARG
