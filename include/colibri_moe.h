@@ -171,6 +171,23 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
                               float *topk_gate_out, int32_t *expert_counts_out, void *ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* Where colibri_moe_layer_forward (and _ex, _q8, _q4, whatever their
+ * options) leaves its routing and dispatch results inside the caller's
+ * workspace: byte offsets from the workspace start.  Once the call's work on
+ * its stream has completed, the workspace holds
+ *   expert_offsets [E + 1], sorted_assign [2T], assign_pos [2T]   int32 (always),
+ *   topk_idx [T, 2] int32, topk_gate [T, 2] fp32, expert_counts [E] int32
+ *       (each only when the call's own output pointer for it was NULL),
+ * with the meaning of colibri_moe_dispatch's outputs ([zskr] section 3.2:
+ * counts per expert, then offsets; 3.3: one contiguous row range per expert).
+ * The next call that uses the workspace overwrites them.  Returns
+ * COLIBRI_ERR_INVALID_ARG for a NULL layout, the shape's status otherwise
+ * (the offsets are those of colibri_moe_workspace_size's workspace; T >= 1). */
+typedef struct {
+    size_t topk_idx, topk_gate, expert_counts, expert_offsets, sorted_assign, assign_pos;
+} colibri_moe_workspace_layout_t;
+int colibri_moe_workspace_layout(const colibri_moe_shape_t *s, colibri_moe_workspace_layout_t *layout);
+
 /* ------------------------------------------------------------------ allocation-free layer
  * For callers that cannot allocate device memory or pass a workspace (code
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -26,7 +26,7 @@ GATE_CODES = {"pair": GATE_PAIR, "softmax": GATE_SOFTMAX, "linear": GATE_LINEAR}
 EXPORTED = [
     "colibri_moe_workspace_size", "colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_dispatch_workspace_size",
     "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up", "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
-    "colibri_moe_layer_forward_noalloc",
+    "colibri_moe_layer_forward_noalloc", "colibri_moe_workspace_layout",
     "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
     "colibri_moe_quantize_q4", "colibri_moe_expert_ffn_q4", "colibri_moe_layer_forward_q4",
     "colibri_moe_workspace_size_ex", "colibri_moe_route_ex", "colibri_moe_combine_ex",
@@ -60,6 +60,11 @@ class _ExpertsQ8(ctypes.Structure):
 
 class _ExpertsQ4(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("q1", "q3", "q2", "s1", "s3", "s2", "z1", "z3", "z2", "b1", "b2")]
+
+
+class _WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("topk_idx", "topk_gate", "expert_counts", "expert_offsets",
+                                                "sorted_assign", "assign_pos")]
 
 
 class _Opts(ctypes.Structure):
@@ -122,6 +127,7 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_combine.argtypes = [SP, P, P, P, P, P]
     lib.colibri_moe_layer_forward.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, P, P, P, Z, P]
     lib.colibri_moe_layer_forward_noalloc.argtypes = [SP, P, P, P, ctypes.POINTER(_Experts), P, P, P, P, P]
+    lib.colibri_moe_workspace_layout.argtypes = [SP, ctypes.POINTER(_WsLayout)]
     i32 = ctypes.c_int32
     lib.colibri_moe_quantize_q8.argtypes = [P, I, i32, i32, i32, P, P, P]
     lib.colibri_moe_expert_ffn_q8.argtypes = [SP, P, P, P, ctypes.POINTER(_ExpertsQ8), P, P, Z, P]
@@ -144,7 +150,8 @@ def load(build_if_missing: bool = False):
     lib.colibri_moe_graph_destroy.argtypes = [P]
     for f in ("colibri_moe_route", "colibri_moe_dispatch", "colibri_moe_expert_ffn", "colibri_moe_expert_ffn_up",
               "colibri_moe_expert_ffn_down", "colibri_moe_combine", "colibri_moe_layer_forward",
-              "colibri_moe_layer_forward_noalloc", "colibri_moe_quantize_q8", "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
+              "colibri_moe_layer_forward_noalloc", "colibri_moe_workspace_layout", "colibri_moe_quantize_q8",
+              "colibri_moe_expert_ffn_q8", "colibri_moe_layer_forward_q8",
               "colibri_moe_quantize_q4", "colibri_moe_expert_ffn_q4", "colibri_moe_layer_forward_q4",
               "colibri_moe_route_ex", "colibri_moe_combine_ex", "colibri_moe_layer_forward_ex",
               "colibri_moe_step_forward", "colibri_moe_graph_create", "colibri_moe_graph_launch",
@@ -161,13 +168,42 @@ def status_string(status: int) -> str:
 
 
 # ------------------------------------------------------------------ marshalling
-def _ptr(t) -> Optional[int]:
-    """Device pointer of a tensor (or None).  Accepts raw integers for tests."""
+def _ptr(t, nbytes: int = 0, es: int = 0, name: str = "tensor") -> Optional[int]:
+    """Device pointer of a tensor (or None), after checking that the tensor can
+    be what the call reads or writes there: contiguous, on a GPU, elements of
+    es bytes (0: any) and at least nbytes long.  A raw integer is passed as it
+    is (tests hand the library addresses directly)."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: a GPU tensor is needed, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (the library reads it densely, row-major)")
+    if es and t.element_size() != es:
+        raise TypeError(f"{name}: elements of {es} bytes expected, got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: holds {have} bytes, the call's shape needs {nbytes}")
     return t.data_ptr()
+
+
+def _ws(ws, ws_bytes: Optional[int]):
+    """Workspace pointer and byte count: by default the tensor's own size; a
+    count larger than the tensor is refused."""
+    if ws is None or isinstance(ws, int):
+        return ws, int(ws_bytes or 0)
+    have = ws.numel() * ws.element_size()
+    if ws_bytes is None:
+        ws_bytes = have
+    if ws_bytes > have:
+        raise ValueError(f"ws_bytes = {ws_bytes} exceeds the workspace tensor's {have} bytes")
+    return _ptr(ws, name="ws"), int(ws_bytes)
+
+
+def _es(shape) -> int:
+    return 4 if shape.dtype == F32 else 2
 
 
 def _stream(stream) -> Optional[int]:
@@ -184,8 +220,14 @@ def _check(status: int, where: str):
         raise ColibriError(status, where)
 
 
-def _experts(w1, w2, w3=None, b1=None, b2=None) -> _Experts:
-    return _Experts(_ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2))
+def _experts(w1, w2, w3=None, b1=None, b2=None, shape=None, h=None) -> _Experts:
+    """Expert weights [E][d][h] / [E][h][d] and biases; with a shape, each
+    tensor is checked against it (h: a hidden width other than the shape's)."""
+    if shape is None:
+        return _Experts(_ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2))
+    E, d, h, es = shape.E, shape.d, h or shape.h, _es(shape)
+    return _Experts(_ptr(w1, E * d * h * es, es, "w1"), _ptr(w3, E * d * h * es, es, "w3"),
+                    _ptr(w2, E * h * d * es, es, "w2"), _ptr(b1, E * h * es, es, "b1"), _ptr(b2, E * d * es, es, "b2"))
 
 
 def workspace_size(shape: Shape) -> int:
@@ -193,64 +235,115 @@ def workspace_size(shape: Shape) -> int:
     return int(load().colibri_moe_workspace_size(ctypes.byref(s)))
 
 
+def workspace_layout(shape: Shape) -> dict:
+    """Byte offsets of the routing and dispatch results a layer call leaves in
+    its workspace (colibri_moe_workspace_layout)."""
+    s = shape.c()
+    lay = _WsLayout()
+    _check(load().colibri_moe_workspace_layout(ctypes.byref(s), ctypes.byref(lay)), "colibri_moe_workspace_layout")
+    return {n: int(getattr(lay, n)) for n, _ in _WsLayout._fields_}
+
+
 def dispatch_workspace_size(shape: Shape) -> int:
     s = shape.c()
     return int(load().colibri_moe_dispatch_workspace_size(ctypes.byref(s)))
 
 
+def _router_args(shape: Shape, x, w_r, b_r):
+    es = _es(shape)
+    return (_ptr(x, shape.T * shape.d * es, es, "x"), _ptr(w_r, shape.d * shape.E * es, es, "w_r"),
+            _ptr(b_r, shape.E * 4, 4, "b_r"))
+
+
+def _routing_outs(shape: Shape, topk_idx, topk_gate, counts):
+    T = shape.T
+    return (_ptr(topk_idx, 2 * T * 4, 4, "topk_idx"), _ptr(topk_gate, 2 * T * 4, 4, "topk_gate"),
+            _ptr(counts, shape.E * 4, 4, "counts"))
+
+
 def route(shape: Shape, x, w_r, b_r, topk_idx, topk_gate, logits=None, stream=None):
     s = shape.c()
-    _check(load().colibri_moe_route(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(topk_idx),
-                                    _ptr(topk_gate), _ptr(logits), _stream(stream)), "colibri_moe_route")
+    idx, gate, _ = _routing_outs(shape, topk_idx, topk_gate, None)
+    _check(load().colibri_moe_route(ctypes.byref(s), *_router_args(shape, x, w_r, b_r), idx, gate,
+                                    _ptr(logits, shape.T * shape.E * 4, 4, "logits"), _stream(stream)),
+           "colibri_moe_route")
 
 
 def dispatch(shape: Shape, topk_idx, counts, offsets, sorted_assign, assign_pos, x=None, x_sorted=None,
-             ws=None, ws_bytes: int = 0, stream=None):
+             ws=None, ws_bytes: Optional[int] = None, stream=None):
     s = shape.c()
-    _check(load().colibri_moe_dispatch(ctypes.byref(s), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
-                                       _ptr(sorted_assign), _ptr(assign_pos), _ptr(x), _ptr(x_sorted), _ptr(ws),
-                                       ws_bytes, _stream(stream)), "colibri_moe_dispatch")
+    A, es = 2 * shape.T, _es(shape)
+    wsp, wsb = _ws(ws, ws_bytes)
+    _check(load().colibri_moe_dispatch(ctypes.byref(s), _ptr(topk_idx, A * 4, 4, "topk_idx"),
+                                       _ptr(counts, shape.E * 4, 4, "counts"),
+                                       _ptr(offsets, (shape.E + 1) * 4, 4, "offsets"),
+                                       _ptr(sorted_assign, A * 4, 4, "sorted_assign"),
+                                       _ptr(assign_pos, A * 4, 4, "assign_pos"),
+                                       _ptr(x, shape.T * shape.d * es, es, "x"),
+                                       _ptr(x_sorted, A * shape.d * es, es, "x_sorted"), wsp, wsb, _stream(stream)),
+           "colibri_moe_dispatch")
 
 
-def expert_ffn(shape: Shape, x_rows, sorted_assign, offsets, w1, w2, y_sorted, ws, ws_bytes: int, w3=None, b1=None,
-               b2=None, stream=None):
+def _rows_args(shape: Shape, x_rows, sorted_assign, offsets, K: int):
+    """A operand rows: X [T, K] read through sorted_assign, or sorted rows [2T, K]."""
+    A, es = 2 * shape.T, _es(shape)
+    return (_ptr(x_rows, (shape.T if sorted_assign is not None else A) * K * es, es, "x_rows"),
+            _ptr(sorted_assign, A * 4, 4, "sorted_assign"), _ptr(offsets, (shape.E + 1) * 4, 4, "offsets"))
+
+
+def expert_ffn(shape: Shape, x_rows, sorted_assign, offsets, w1, w2, y_sorted, ws, ws_bytes: Optional[int] = None,
+               w3=None, b1=None, b2=None, stream=None):
     s = shape.c()
-    e = _experts(w1, w2, w3, b1, b2)
-    _check(load().colibri_moe_expert_ffn(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
-                                         ctypes.byref(e), _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
-           "colibri_moe_expert_ffn")
+    e = _experts(w1, w2, w3, b1, b2, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_expert_ffn(ctypes.byref(s), *_rows_args(shape, x_rows, sorted_assign, offsets, shape.d),
+                                         ctypes.byref(e), _ptr(y_sorted, 2 * shape.T * shape.d * es, es, "y_sorted"),
+                                         *_ws(ws, ws_bytes), _stream(stream)), "colibri_moe_expert_ffn")
 
 
-def expert_ffn_up(shape: Shape, x_rows, sorted_assign, offsets, w1, h_rows, ws=None, ws_bytes: int = 0, w3=None,
-                  b1=None, stream=None):
+def expert_ffn_up(shape: Shape, x_rows, sorted_assign, offsets, w1, h_rows, ws=None, ws_bytes: Optional[int] = None,
+                  w3=None, b1=None, stream=None):
     s = shape.c()
-    e = _experts(w1, None, w3, b1, None)
-    _check(load().colibri_moe_expert_ffn_up(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
-                                            ctypes.byref(e), _ptr(h_rows), _ptr(ws), ws_bytes, _stream(stream)),
-           "colibri_moe_expert_ffn_up")
+    e = _experts(w1, None, w3, b1, None, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_expert_ffn_up(ctypes.byref(s), *_rows_args(shape, x_rows, sorted_assign, offsets,
+                                                                        shape.d), ctypes.byref(e),
+                                            _ptr(h_rows, 2 * shape.T * shape.h * es, es, "h_rows"),
+                                            *_ws(ws, ws_bytes), _stream(stream)), "colibri_moe_expert_ffn_up")
 
 
-def expert_ffn_down(shape: Shape, h_rows, offsets, w2, y_sorted, ws=None, ws_bytes: int = 0, b2=None, stream=None):
+def expert_ffn_down(shape: Shape, h_rows, offsets, w2, y_sorted, ws=None, ws_bytes: Optional[int] = None, b2=None,
+                    stream=None):
     s = shape.c()
-    e = _experts(None, w2, None, None, b2)
-    _check(load().colibri_moe_expert_ffn_down(ctypes.byref(s), _ptr(h_rows), _ptr(offsets), ctypes.byref(e),
-                                              _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
-           "colibri_moe_expert_ffn_down")
+    e = _experts(None, w2, None, None, b2, shape=shape)
+    es = _es(shape)
+    h, _, off = _rows_args(shape, h_rows, None, offsets, shape.h)
+    _check(load().colibri_moe_expert_ffn_down(ctypes.byref(s), h, off, ctypes.byref(e),
+                                              _ptr(y_sorted, 2 * shape.T * shape.d * es, es, "y_sorted"),
+                                              *_ws(ws, ws_bytes), _stream(stream)), "colibri_moe_expert_ffn_down")
+
+
+def _combine_args(shape: Shape, y_sorted, assign_pos, topk_gate, out):
+    A, es = 2 * shape.T, _es(shape)
+    return (_ptr(y_sorted, A * shape.d * es, es, "y_sorted"), _ptr(assign_pos, A * 4, 4, "assign_pos"),
+            _ptr(topk_gate, A * 4, 4, "topk_gate"), _ptr(out, shape.T * shape.d * es, es, "out"))
 
 
 def combine(shape: Shape, y_sorted, assign_pos, topk_gate, out, stream=None):
     s = shape.c()
-    _check(load().colibri_moe_combine(ctypes.byref(s), _ptr(y_sorted), _ptr(assign_pos), _ptr(topk_gate),
-                                      _ptr(out), _stream(stream)), "colibri_moe_combine")
+    _check(load().colibri_moe_combine(ctypes.byref(s), *_combine_args(shape, y_sorted, assign_pos, topk_gate, out),
+                                      _stream(stream)), "colibri_moe_combine")
 
 
-def layer_forward(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: int, w3=None, b1=None, b2=None,
-                  topk_idx=None, topk_gate=None, counts=None, stream=None):
+def layer_forward(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: Optional[int] = None, w3=None, b1=None,
+                  b2=None, topk_idx=None, topk_gate=None, counts=None, stream=None):
     s = shape.c()
-    e = _experts(w1, w2, w3, b1, b2)
-    _check(load().colibri_moe_layer_forward(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
-                                            _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
-                                            ws_bytes, _stream(stream)), "colibri_moe_layer_forward")
+    e = _experts(w1, w2, w3, b1, b2, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_layer_forward(ctypes.byref(s), *_router_args(shape, x, w_r, b_r), ctypes.byref(e),
+                                            _ptr(out, shape.T * shape.d * es, es, "out"),
+                                            *_routing_outs(shape, topk_idx, topk_gate, counts), *_ws(ws, ws_bytes),
+                                            _stream(stream)), "colibri_moe_layer_forward")
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # COLIBRI_MOE_NOALLOC_SCRATCH_BYTES
@@ -261,9 +354,11 @@ def layer_forward_noalloc(shape: Shape, x, w_r, b_r, w1, w2, out, w3=None, b1=No
     """colibri_moe_layer_forward on the library's own device scratch array (no
     workspace argument, nothing allocated).  Calls that overlap on one GPU race."""
     s = shape.c()
-    e = _experts(w1, w2, w3, b1, b2)
-    _check(load().colibri_moe_layer_forward_noalloc(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
-                                                    _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts),
+    e = _experts(w1, w2, w3, b1, b2, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_layer_forward_noalloc(ctypes.byref(s), *_router_args(shape, x, w_r, b_r),
+                                                    ctypes.byref(e), _ptr(out, shape.T * shape.d * es, es, "out"),
+                                                    *_routing_outs(shape, topk_idx, topk_gate, counts),
                                                     _stream(stream)), "colibri_moe_layer_forward_noalloc")
 
 
@@ -272,13 +367,18 @@ def _gate_code(gate) -> int:
     return GATE_CODES[gate] if isinstance(gate, str) else int(gate)
 
 
-def _opts(gate="pair", shared=None, shared_h: int = 0, residual=None):
+def _opts(gate="pair", shared=None, shared_h: int = 0, residual=None, shape=None):
     """ctypes options and the experts struct it points to (keep both alive).
-    ``shared``: dict with the shared expert's w1, w2 (and w3, b1, b2)."""
+    ``shared``: dict with the shared expert's w1, w2 (and w3, b1, b2); with a
+    shape the tensors are checked against it (the shared expert is one expert
+    of hidden width shared_h, 0 = the shape's h)."""
     sh = None
+    one = None if shape is None else Shape(shape.T, shape.d, shape.h, 1, shape.dtype, shape.act)
     if shared is not None:
-        sh = _experts(shared["w1"], shared["w2"], shared.get("w3"), shared.get("b1"), shared.get("b2"))
-    o = _Opts(_gate_code(gate), ctypes.pointer(sh) if sh is not None else None, int(shared_h), _ptr(residual))
+        sh = _experts(shared["w1"], shared["w2"], shared.get("w3"), shared.get("b1"), shared.get("b2"), shape=one,
+                      h=int(shared_h) or None)
+    res = _ptr(residual) if shape is None else _ptr(residual, shape.T * shape.d * _es(shape), _es(shape), "residual")
+    o = _Opts(_gate_code(gate), ctypes.pointer(sh) if sh is not None else None, int(shared_h), res)
     return o, sh
 
 
@@ -290,46 +390,51 @@ def workspace_size_ex(shape: Shape, gate="pair", shared=None, shared_h: int = 0,
 
 def route_ex(shape: Shape, x, w_r, b_r, gate, topk_idx, topk_gate, logits=None, stream=None):
     s = shape.c()
-    _check(load().colibri_moe_route_ex(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), _gate_code(gate),
-                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(logits), _stream(stream)),
+    idx, g, _ = _routing_outs(shape, topk_idx, topk_gate, None)
+    _check(load().colibri_moe_route_ex(ctypes.byref(s), *_router_args(shape, x, w_r, b_r), _gate_code(gate), idx, g,
+                                       _ptr(logits, shape.T * shape.E * 4, 4, "logits"), _stream(stream)),
            "colibri_moe_route_ex")
 
 
 def combine_ex(shape: Shape, y_sorted, assign_pos, topk_gate, out, shared_y=None, residual=None, stream=None):
     s = shape.c()
-    _check(load().colibri_moe_combine_ex(ctypes.byref(s), _ptr(y_sorted), _ptr(assign_pos), _ptr(topk_gate),
-                                         _ptr(shared_y), _ptr(residual), _ptr(out), _stream(stream)),
+    y, ap, g, o = _combine_args(shape, y_sorted, assign_pos, topk_gate, out)
+    n, es = shape.T * shape.d * _es(shape), _es(shape)
+    _check(load().colibri_moe_combine_ex(ctypes.byref(s), y, ap, g, _ptr(shared_y, n, es, "shared_y"),
+                                         _ptr(residual, n, es, "residual"), o, _stream(stream)),
            "colibri_moe_combine_ex")
 
 
-def layer_forward_ex(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: int, w3=None, b1=None, b2=None,
-                     gate="pair", shared=None, shared_h: int = 0, residual=None, topk_idx=None, topk_gate=None,
-                     counts=None, stream=None):
+def layer_forward_ex(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: Optional[int] = None, w3=None, b1=None,
+                     b2=None, gate="pair", shared=None, shared_h: int = 0, residual=None, topk_idx=None,
+                     topk_gate=None, counts=None, stream=None):
     s = shape.c()
-    e = _experts(w1, w2, w3, b1, b2)
-    o, keep = _opts(gate, shared, shared_h, residual)
-    _check(load().colibri_moe_layer_forward_ex(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
-                                               ctypes.byref(o), _ptr(out), _ptr(topk_idx), _ptr(topk_gate),
-                                               _ptr(counts), _ptr(ws), ws_bytes, _stream(stream)),
-           "colibri_moe_layer_forward_ex")
+    e = _experts(w1, w2, w3, b1, b2, shape=shape)
+    o, keep = _opts(gate, shared, shared_h, residual, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_layer_forward_ex(ctypes.byref(s), *_router_args(shape, x, w_r, b_r), ctypes.byref(e),
+                                               ctypes.byref(o), _ptr(out, shape.T * shape.d * es, es, "out"),
+                                               *_routing_outs(shape, topk_idx, topk_gate, counts), *_ws(ws, ws_bytes),
+                                               _stream(stream)), "colibri_moe_layer_forward_ex")
 
 
 # ------------------------------------------------------------------ multi-layer step, graph replay
-def _layer_params(layers):
+def _layer_params(layers, shape=None):
     """layers: list of dicts with w_r, w1, w2 (and b_r, w3, b1, b2, gate, shared,
-    shared_h).  Returns the ctypes array and the structs it points to."""
+    shared_h).  Returns the ctypes array and the structs it points to; with a
+    shape every tensor is checked against it."""
     arr = (_LayerParams * len(layers))()
     keep = []
     for i, l in enumerate(layers):
-        sh = None
-        if l.get("shared") is not None:
-            d = l["shared"]
-            sh = _experts(d["w1"], d["w2"], d.get("w3"), d.get("b1"), d.get("b2"))
+        o, sh = _opts(l.get("gate", "pair"), l.get("shared"), int(l.get("shared_h", 0)), None, shape=shape)
+        if sh is not None:
             keep.append(sh)
-        arr[i] = _LayerParams(_ptr(l["w_r"]), _ptr(l.get("b_r")),
-                              _experts(l["w1"], l["w2"], l.get("w3"), l.get("b1"), l.get("b2")),
-                              _gate_code(l.get("gate", "pair")), ctypes.pointer(sh) if sh is not None else None,
-                              int(l.get("shared_h", 0)))
+        if shape is None:
+            w_r, b_r = _ptr(l["w_r"]), _ptr(l.get("b_r"))
+        else:
+            _, w_r, b_r = _router_args(shape.with_T(0), None, l["w_r"], l.get("b_r"))
+        arr[i] = _LayerParams(w_r, b_r, _experts(l["w1"], l["w2"], l.get("w3"), l.get("b1"), l.get("b2"), shape=shape),
+                              o.gate, o.shared, o.shared_h)
     return arr, keep
 
 
@@ -339,12 +444,14 @@ def step_workspace_size(shape: Shape, layers) -> int:
     return int(load().colibri_moe_step_workspace_size(ctypes.byref(s), len(layers), arr))
 
 
-def step_forward(shape: Shape, layers, x, ws, ws_bytes: int, residual: bool = True, stream=None):
+def step_forward(shape: Shape, layers, x, ws, ws_bytes: Optional[int] = None, residual: bool = True, stream=None):
     """x <- layer_l(x) (+ x) for every layer, in place on x."""
     s = shape.c()
-    arr, keep = _layer_params(layers)
-    _check(load().colibri_moe_step_forward(ctypes.byref(s), len(layers), arr, int(bool(residual)), _ptr(x), _ptr(ws),
-                                           ws_bytes, _stream(stream)), "colibri_moe_step_forward")
+    arr, keep = _layer_params(layers, shape)
+    es = _es(shape)
+    _check(load().colibri_moe_step_forward(ctypes.byref(s), len(layers), arr, int(bool(residual)),
+                                           _ptr(x, shape.T * shape.d * es, es, "x"), *_ws(ws, ws_bytes),
+                                           _stream(stream)), "colibri_moe_step_forward")
 
 
 class Graph:
@@ -352,12 +459,14 @@ class Graph:
 
     The caller keeps x, ws and the weights alive while the graph exists."""
 
-    def __init__(self, shape: Shape, layers, x, ws, ws_bytes: int, residual: bool = True):
+    def __init__(self, shape: Shape, layers, x, ws, ws_bytes: Optional[int] = None, residual: bool = True):
         s = shape.c()
-        arr, keep = _layer_params(layers)
+        arr, keep = _layer_params(layers, shape)
         h = ctypes.c_void_p()
-        _check(load().colibri_moe_graph_create(ctypes.byref(s), len(layers), arr, int(bool(residual)), _ptr(x),
-                                               _ptr(ws), ws_bytes, ctypes.byref(h)), "colibri_moe_graph_create")
+        es = _es(shape)
+        _check(load().colibri_moe_graph_create(ctypes.byref(s), len(layers), arr, int(bool(residual)),
+                                               _ptr(x, shape.T * shape.d * es, es, "x"), *_ws(ws, ws_bytes),
+                                               ctypes.byref(h)), "colibri_moe_graph_create")
         self._h = h
 
     def launch(self, stream=None):
@@ -372,67 +481,91 @@ class Graph:
 
 
 # ------------------------------------------------------------------ int8 expert weights
-def _experts_q8(q1, s1, q2, s2, q3=None, s3=None, b1=None, b2=None) -> _ExpertsQ8:
-    return _ExpertsQ8(_ptr(q1), _ptr(q3), _ptr(q2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(b1), _ptr(b2))
+def _experts_q8(q1, s1, q2, s2, q3=None, s3=None, b1=None, b2=None, shape=None) -> _ExpertsQ8:
+    if shape is None:
+        return _ExpertsQ8(_ptr(q1), _ptr(q3), _ptr(q2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(b1), _ptr(b2))
+    E, d, h, es = shape.E, shape.d, shape.h, _es(shape)
+    return _ExpertsQ8(_ptr(q1, E * d * h, 1, "q1"), _ptr(q3, E * d * h, 1, "q3"), _ptr(q2, E * h * d, 1, "q2"),
+                      _ptr(s1, E * h * 4, 4, "s1"), _ptr(s3, E * h * 4, 4, "s3"), _ptr(s2, E * d * 4, 4, "s2"),
+                      _ptr(b1, E * h * es, es, "b1"), _ptr(b2, E * d * es, es, "b2"))
 
 
 def quantize_q8(w, dtype: int, E: int, K: int, N: int, q, scale, stream=None):
     """Per-column int8 codes q [E, K, N] and fp32 scales [E, N] of w [E, K, N]."""
-    _check(load().colibri_moe_quantize_q8(_ptr(w), int(dtype), int(E), int(K), int(N), _ptr(q), _ptr(scale),
-                                          _stream(stream)), "colibri_moe_quantize_q8")
+    n, es = E * K * N, 4 if dtype == F32 else 2
+    _check(load().colibri_moe_quantize_q8(_ptr(w, n * es, es, "w"), int(dtype), int(E), int(K), int(N),
+                                          _ptr(q, n, 1, "q"), _ptr(scale, E * N * 4, 4, "scale"), _stream(stream)),
+           "colibri_moe_quantize_q8")
 
 
-def expert_ffn_q8(shape: Shape, x_rows, sorted_assign, offsets, q1, s1, q2, s2, y_sorted, ws, ws_bytes: int,
-                  q3=None, s3=None, b1=None, b2=None, stream=None):
+def expert_ffn_q8(shape: Shape, x_rows, sorted_assign, offsets, q1, s1, q2, s2, y_sorted, ws,
+                  ws_bytes: Optional[int] = None, q3=None, s3=None, b1=None, b2=None, stream=None):
     s = shape.c()
-    e = _experts_q8(q1, s1, q2, s2, q3, s3, b1, b2)
-    _check(load().colibri_moe_expert_ffn_q8(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
-                                            ctypes.byref(e), _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
-           "colibri_moe_expert_ffn_q8")
+    e = _experts_q8(q1, s1, q2, s2, q3, s3, b1, b2, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_expert_ffn_q8(ctypes.byref(s), *_rows_args(shape, x_rows, sorted_assign, offsets,
+                                                                        shape.d), ctypes.byref(e),
+                                            _ptr(y_sorted, 2 * shape.T * shape.d * es, es, "y_sorted"),
+                                            *_ws(ws, ws_bytes), _stream(stream)), "colibri_moe_expert_ffn_q8")
 
 
-def layer_forward_q8(shape: Shape, x, w_r, b_r, q1, s1, q2, s2, out, ws, ws_bytes: int, q3=None, s3=None, b1=None,
-                     b2=None, topk_idx=None, topk_gate=None, counts=None, stream=None):
+def layer_forward_q8(shape: Shape, x, w_r, b_r, q1, s1, q2, s2, out, ws, ws_bytes: Optional[int] = None, q3=None,
+                     s3=None, b1=None, b2=None, topk_idx=None, topk_gate=None, counts=None, stream=None):
     s = shape.c()
-    e = _experts_q8(q1, s1, q2, s2, q3, s3, b1, b2)
-    _check(load().colibri_moe_layer_forward_q8(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
-                                               _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
-                                               ws_bytes, _stream(stream)), "colibri_moe_layer_forward_q8")
+    e = _experts_q8(q1, s1, q2, s2, q3, s3, b1, b2, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_layer_forward_q8(ctypes.byref(s), *_router_args(shape, x, w_r, b_r), ctypes.byref(e),
+                                               _ptr(out, shape.T * shape.d * es, es, "out"),
+                                               *_routing_outs(shape, topk_idx, topk_gate, counts), *_ws(ws, ws_bytes),
+                                               _stream(stream)), "colibri_moe_layer_forward_q8")
 
 
 # ------------------------------------------------------------------ 4-bit expert weights
-def _experts_q4(w1q, w2q, w3q=None, b1=None, b2=None) -> _ExpertsQ4:
+def _experts_q4(w1q, w2q, w3q=None, b1=None, b2=None, shape=None) -> _ExpertsQ4:
     t = lambda w: (None, None, None) if w is None else w
     (q1, s1, z1), (q2, s2, z2), (q3, s3, z3) = t(w1q), t(w2q), t(w3q)
-    return _ExpertsQ4(_ptr(q1), _ptr(q3), _ptr(q2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(z1), _ptr(z3), _ptr(z2),
-                      _ptr(b1), _ptr(b2))
+    if shape is None:
+        return _ExpertsQ4(_ptr(q1), _ptr(q3), _ptr(q2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(z1), _ptr(z3), _ptr(z2),
+                          _ptr(b1), _ptr(b2))
+    E, d, h, es = shape.E, shape.d, shape.h, _es(shape)
+    up, dn = E * d * h, E * h * d  # weights per layer
+    return _ExpertsQ4(_ptr(q1, up // 2, 4, "q1"), _ptr(q3, up // 2, 4, "q3"), _ptr(q2, dn // 2, 4, "q2"),
+                      _ptr(s1, up // 128 * 4, 4, "s1"), _ptr(s3, up // 128 * 4, 4, "s3"), _ptr(s2, dn // 128 * 4, 4, "s2"),
+                      _ptr(z1, up // 128, 1, "z1"), _ptr(z3, up // 128, 1, "z3"), _ptr(z2, dn // 128, 1, "z2"),
+                      _ptr(b1, E * h * es, es, "b1"), _ptr(b2, E * d * es, es, "b2"))
 
 
 def quantize_q4(w, dtype: int, E: int, K: int, N: int, q, scale, zero, stream=None):
     """4-bit codes q [E, K/8, N] (uint32 words of 8 codes: k = 8j + 2m in bits
     4m..4m+3, k = 8j + 2m + 1 in bits 16+4m..16+4m+3), fp32 scales and uint8
     zero points [E, K/128, N] of w [E, K, N]."""
-    _check(load().colibri_moe_quantize_q4(_ptr(w), int(dtype), int(E), int(K), int(N), _ptr(q), _ptr(scale),
-                                          _ptr(zero), _stream(stream)), "colibri_moe_quantize_q4")
+    n, es = E * K * N, 4 if dtype == F32 else 2
+    _check(load().colibri_moe_quantize_q4(_ptr(w, n * es, es, "w"), int(dtype), int(E), int(K), int(N),
+                                          _ptr(q, n // 2, 4, "q"), _ptr(scale, n // 128 * 4, 4, "scale"),
+                                          _ptr(zero, n // 128, 1, "zero"), _stream(stream)), "colibri_moe_quantize_q4")
 
 
-def expert_ffn_q4(shape: Shape, x_rows, sorted_assign, offsets, w1q, w2q, y_sorted, ws, ws_bytes: int, w3q=None,
-                  b1=None, b2=None, stream=None):
+def expert_ffn_q4(shape: Shape, x_rows, sorted_assign, offsets, w1q, w2q, y_sorted, ws,
+                  ws_bytes: Optional[int] = None, w3q=None, b1=None, b2=None, stream=None):
     """w1q, w2q, w3q: (codes, scales, zero points) device triples."""
     s = shape.c()
-    e = _experts_q4(w1q, w2q, w3q, b1, b2)
-    _check(load().colibri_moe_expert_ffn_q4(ctypes.byref(s), _ptr(x_rows), _ptr(sorted_assign), _ptr(offsets),
-                                            ctypes.byref(e), _ptr(y_sorted), _ptr(ws), ws_bytes, _stream(stream)),
-           "colibri_moe_expert_ffn_q4")
+    e = _experts_q4(w1q, w2q, w3q, b1, b2, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_expert_ffn_q4(ctypes.byref(s), *_rows_args(shape, x_rows, sorted_assign, offsets,
+                                                                        shape.d), ctypes.byref(e),
+                                            _ptr(y_sorted, 2 * shape.T * shape.d * es, es, "y_sorted"),
+                                            *_ws(ws, ws_bytes), _stream(stream)), "colibri_moe_expert_ffn_q4")
 
 
-def layer_forward_q4(shape: Shape, x, w_r, b_r, w1q, w2q, out, ws, ws_bytes: int, w3q=None, b1=None, b2=None,
-                     topk_idx=None, topk_gate=None, counts=None, stream=None):
+def layer_forward_q4(shape: Shape, x, w_r, b_r, w1q, w2q, out, ws, ws_bytes: Optional[int] = None, w3q=None,
+                     b1=None, b2=None, topk_idx=None, topk_gate=None, counts=None, stream=None):
     s = shape.c()
-    e = _experts_q4(w1q, w2q, w3q, b1, b2)
-    _check(load().colibri_moe_layer_forward_q4(ctypes.byref(s), _ptr(x), _ptr(w_r), _ptr(b_r), ctypes.byref(e),
-                                               _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(ws),
-                                               ws_bytes, _stream(stream)), "colibri_moe_layer_forward_q4")
+    e = _experts_q4(w1q, w2q, w3q, b1, b2, shape=shape)
+    es = _es(shape)
+    _check(load().colibri_moe_layer_forward_q4(ctypes.byref(s), *_router_args(shape, x, w_r, b_r), ctypes.byref(e),
+                                               _ptr(out, shape.T * shape.d * es, es, "out"),
+                                               *_routing_outs(shape, topk_idx, topk_gate, counts), *_ws(ws, ws_bytes),
+                                               _stream(stream)), "colibri_moe_layer_forward_q4")
 
 
 class MoELayer:

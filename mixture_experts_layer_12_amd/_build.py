@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcolibri_moe.so")
 
-SOURCES = ["abi.cpp", "route.hip", "dispatch.hip", "ffn.hip", "ffn_gemm.hip", "ffn_decode.hip", "combine.hip",
+SOURCES = ["abi.cpp", "validate.cpp", "route.hip", "dispatch.hip", "ffn.hip", "ffn_gemm.hip", "ffn_decode.hip", "combine.hip",
            "quantize.hip", "ffn_decode_q4.hip"]
 ARCH = os.environ.get("COLIBRI_OFFLOAD_ARCH", "gfx950")
 

@@ -16,6 +16,7 @@
 
 #include "colibri_moe.h"
 #include "launchers.h"
+#include "validate.h"
 
 using namespace colibri;
 
@@ -161,6 +162,69 @@ LayerWorkspace layer_workspace(const colibri_moe_shape_t *s, const colibri_moe_l
 
 int hip_status(hipError_t e) { return e == hipSuccess ? COLIBRI_OK : COLIBRI_ERR_HIP; }
 
+// ------------------------------------------------------------------ COLIBRI_MOE_VALIDATE=1
+// The argument groups the entry points share; each adds its checks to v.
+void v_router(Validator &v, const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r) {
+    v.finite(x, (size_t)s->T * s->d, s->dtype).finite(w_r, (size_t)s->d * s->E, s->dtype);
+    v.finite(b_r, (size_t)s->E, COLIBRI_F32);
+}
+
+void v_experts(Validator &v, const colibri_moe_shape_t *s, const colibri_moe_experts_t *w, bool up = true,
+               bool down = true) {
+    const size_t E = s->E, d = s->d, h = s->h;
+    if (up) v.finite(w->w1, E * d * h, s->dtype).finite(w->w3, E * d * h, s->dtype).finite(w->b1, E * h, s->dtype);
+    if (down) v.finite(w->w2, E * h * d, s->dtype).finite(w->b2, E * d, s->dtype);
+}
+
+void v_experts_q8(Validator &v, const colibri_moe_shape_t *s, const colibri_moe_experts_q8_t *w) {
+    const size_t E = s->E, d = s->d, h = s->h;
+    v.range(w->q1, E * d * h).range(w->q3, E * d * h).range(w->q2, E * h * d);
+    v.finite(w->s1, E * h, COLIBRI_F32).finite(w->s3, E * h, COLIBRI_F32).finite(w->s2, E * d, COLIBRI_F32);
+    v.finite(w->b1, E * h, s->dtype).finite(w->b2, E * d, s->dtype);
+}
+
+void v_experts_q4(Validator &v, const colibri_moe_shape_t *s, const colibri_moe_experts_q4_t *w) {
+    const size_t E = s->E, d = s->d, h = s->h;
+    v.range(w->q1, E * d / 8 * h * 4).range(w->q3, E * d / 8 * h * 4).range(w->q2, E * h / 8 * d * 4);
+    v.finite(w->s1, E * d / 128 * h, COLIBRI_F32).finite(w->s3, E * d / 128 * h, COLIBRI_F32);
+    v.finite(w->s2, E * h / 128 * d, COLIBRI_F32);
+    v.range(w->z1, E * d / 128 * h).range(w->z3, E * d / 128 * h).range(w->z2, E * h / 128 * d);
+    v.finite(w->b1, E * h, s->dtype).finite(w->b2, E * d, s->dtype);
+}
+
+// the layer's outputs and workspace
+void v_layer_out(Validator &v, const colibri_moe_shape_t *s, const void *out, const int32_t *idx, const float *gate,
+                 const int32_t *counts) {
+    const size_t T = s->T;
+    v.range(out, T * s->d * elem_size(s)).range(idx, 2 * T * 4).range(gate, 2 * T * 4).range(counts, s->E * 4);
+}
+
+// a stream under graph capture cannot be waited on; a captured step is
+// validated once, before its capture starts
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
+void v_opts(Validator &v, const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o) {
+    if (!o) return;
+    v.finite(o->residual, (size_t)s->T * s->d, s->dtype);
+    if (o->shared) {
+        const colibri_moe_shape_t sh = shared_shape(s, o);
+        v_experts(v, &sh, o->shared);
+    }
+}
+
+// the rows the FFN reads: X [T, d] through sorted_assign, or sorted rows [2T, d];
+// offsets [E + 1] and sorted_assign [2T] as dispatch writes them
+void v_ffn_rows(Validator &v, const colibri_moe_shape_t *s, const void *x_rows, const int32_t *sorted_assign,
+                const int32_t *offsets, int K) {
+    const size_t A = 2 * (size_t)s->T;
+    v.finite(x_rows, (sorted_assign ? (size_t)s->T : A) * K, s->dtype);
+    v.indices(sorted_assign, A, -1, (int32_t)A - 1).offsets(offsets, s->E + 1, (int32_t)A);
+}
+
+
 // A second stream for the shared expert: forked from the main stream before
 // routing (it reads only x), joined before the combine.  aux == nullptr: the
 // shared expert runs on the main stream.
@@ -183,16 +247,26 @@ int check_layer_io(const void *x, const void *w_r, const float *b_r, const void 
     return COLIBRI_OK;
 }
 
-template <class Ffn>
+// vexp(v) adds the checks of the weights (and of a caller workspace) under
+// COLIBRI_MOE_VALIDATE=1.
+template <class Ffn, class VExp>
 int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r, void *out,
                        int32_t *topk_idx_out, float *topk_gate_out, int32_t *expert_counts_out, void *ws,
-                       size_t ws_bytes, hipStream_t stream, const void *b2, int Sd, Ffn ffn,
+                       size_t ws_bytes, hipStream_t stream, const void *b2, int Sd, Ffn ffn, VExp vexp,
                        const colibri_moe_layer_opts_t *opts = nullptr, const Branch &br = Branch{}) {
     const int io = check_layer_io(x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out);
     if (io != COLIBRI_OK) return io;
     const LayerWorkspace L = layer_workspace(s, opts);
     if (ws_bytes < L.total) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled() && !capturing(stream)) {
+        Validator v(stream);
+        v_router(v, s, x, w_r, b_r);
+        v_layer_out(v, s, out, topk_idx_out, topk_gate_out, expert_counts_out);
+        v_opts(v, s, opts);
+        vexp(v);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
 
     char *base = static_cast<char *>(ws);
     int32_t *idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t *>(base + L.idx);
@@ -305,6 +379,10 @@ int step_layer(const colibri_moe_shape_t *s, const colibri_moe_layer_params_t &p
         [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce, const float **part) {
             return launch_ffn_layers(*s, x, sorted, offsets, p.experts, y, ffn_ws, reduce, stream, part);
         },
+        [&](Validator &v) {
+            v_experts(v, s, &p.experts);
+            v.range(ws, ws_bytes);
+        },
         &o, br);
 }
 
@@ -358,6 +436,17 @@ size_t colibri_moe_workspace_size(const colibri_moe_shape_t *s) {
     return layer_workspace(s).total;
 }
 
+int colibri_moe_workspace_layout(const colibri_moe_shape_t *s, colibri_moe_workspace_layout_t *layout) {
+    if (!layout) return COLIBRI_ERR_INVALID_ARG;
+    const int st = check_shape(s);
+    if (st != COLIBRI_OK) return st;
+    if (s->T == 0) return COLIBRI_ERR_INVALID_ARG;
+    // the routing and dispatch regions lead every layer workspace, whatever the options
+    const LayerWorkspace L = layer_workspace(s);
+    *layout = {L.idx, L.gate, L.counts, L.offsets, L.sorted, L.pos};
+    return COLIBRI_OK;
+}
+
 int colibri_moe_route(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
                       int32_t *topk_idx, float *topk_gate, float *logits, hipStream_t stream) {
     int st = check_shape(s);
@@ -367,6 +456,13 @@ int colibri_moe_route(const colibri_moe_shape_t *s, const void *x, const void *w
     if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(topk_idx, 4) || !aligned(topk_gate, 4) ||
         (b_r && !aligned(b_r, 4)) || (logits && !aligned(logits, 4)))
         return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        v_router(v, s, x, w_r, b_r);
+        v.range(topk_idx, 2 * (size_t)s->T * 4).range(topk_gate, 2 * (size_t)s->T * 4);
+        v.range(logits, (size_t)s->T * s->E * 4);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_route(*s, x, w_r, b_r, topk_idx, topk_gate, logits, stream));
 }
 
@@ -390,6 +486,15 @@ int colibri_moe_dispatch(const colibri_moe_shape_t *s, const int32_t *topk_idx, 
     if (x && (!aligned(x, 16) || !aligned(x_sorted, 16))) return COLIBRI_ERR_INVALID_ARG;
     const size_t dneed = dispatch_scratch_bytes(*s);
     void *dws = (dneed && ws && ws_bytes >= dneed && aligned(ws, 256)) ? ws : nullptr;
+    if (validate_enabled()) {
+        Validator v(stream);
+        const size_t A = 2 * (size_t)s->T;
+        v.indices(topk_idx, A, 0, s->E - 1);  // the input contract: every index in [0, E)
+        v.range(expert_counts, (size_t)s->E * 4).range(expert_offsets, (size_t)(s->E + 1) * 4);
+        v.range(sorted_assign, A * 4).range(assign_pos, A * 4).range(dws, dneed);
+        v.range(x, (size_t)s->T * s->d * elem_size(s)).range(x_sorted, A * s->d * elem_size(s));
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     hipError_t e =
         launch_dispatch(*s, topk_idx, expert_counts, expert_offsets, sorted_assign, assign_pos, stream, dws);
     if (e == hipSuccess && x) e = launch_gather_rows(*s, x, sorted_assign, x_sorted, stream);
@@ -411,6 +516,13 @@ int colibri_moe_expert_ffn(const colibri_moe_shape_t *s, const void *x_rows, con
     const size_t need = ffn_workspace_bytes(*s);
     if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        v_ffn_rows(v, s, x_rows, sorted_assign, expert_offsets, s->d);
+        v_experts(v, s, w);
+        v.range(y_sorted, 2 * (size_t)s->T * s->d * elem_size(s)).range(ws, ws_bytes);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_expert_ffn(*s, x_rows, sorted_assign, expert_offsets, *w, y_sorted, ws, stream));
 }
 
@@ -429,6 +541,13 @@ int colibri_moe_expert_ffn_up(const colibri_moe_shape_t *s, const void *x_rows, 
     const size_t need = ffn_up_scratch_bytes(*s);
     if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
     if (need && (!ws || !aligned(ws, 256))) return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        v_ffn_rows(v, s, x_rows, sorted_assign, expert_offsets, s->d);
+        v_experts(v, s, w, true, false);
+        v.range(h_rows, 2 * (size_t)s->T * s->h * elem_size(s)).range(need ? ws : nullptr, ws_bytes);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_ffn_up(*s, x_rows, sorted_assign, expert_offsets, *w, h_rows, ws, stream));
 }
 
@@ -445,6 +564,13 @@ int colibri_moe_expert_ffn_down(const colibri_moe_shape_t *s, const void *h_rows
     const size_t need = ffn_down_scratch_bytes(*s);
     if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
     if (need && (!ws || !aligned(ws, 256))) return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        v_ffn_rows(v, s, h_rows, nullptr, expert_offsets, s->h);
+        v_experts(v, s, w, false, true);
+        v.range(y_sorted, 2 * (size_t)s->T * s->d * elem_size(s)).range(need ? ws : nullptr, ws_bytes);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_ffn_down(*s, h_rows, expert_offsets, *w, y_sorted, ws, stream));
 }
 
@@ -456,6 +582,13 @@ int colibri_moe_combine(const colibri_moe_shape_t *s, const void *y_sorted, cons
     if (!y_sorted || !assign_pos || !topk_gate || !out) return COLIBRI_ERR_INVALID_ARG;
     if (!aligned(y_sorted, 16) || !aligned(out, 16) || !aligned(assign_pos, 4) || !aligned(topk_gate, 4))
         return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        const size_t A = 2 * (size_t)s->T;
+        v.finite(y_sorted, A * s->d, s->dtype).indices(assign_pos, A, -1, (int32_t)A - 1);
+        v.finite(topk_gate, A, COLIBRI_F32).range(out, (size_t)s->T * s->d * elem_size(s));
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_combine(*s, y_sorted, assign_pos, topk_gate, out, stream));
 }
 
@@ -473,6 +606,10 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
                                   const float **part) {
                                   return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
                                                            part);
+                              },
+                              [&](Validator &v) {
+                                  v_experts(v, s, w);
+                                  v.range(ws, ws_bytes);
                               });
 }
 
@@ -497,7 +634,8 @@ int colibri_moe_layer_forward_noalloc(const colibri_moe_shape_t *s, const void *
                                   const float **part) {
                                   return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
                                                            part);
-                              });
+                              },
+                              [&](Validator &v) { v_experts(v, s, w); });
 }
 
 int colibri_moe_layer_forward_q8(const colibri_moe_shape_t *s, const void *x, const void *w_r, const float *b_r,
@@ -515,6 +653,10 @@ int colibri_moe_layer_forward_q8(const colibri_moe_shape_t *s, const void *x, co
                                   const float **part) {
                                   return launch_ffn_layers_q8(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
                                                               part);
+                              },
+                              [&](Validator &v) {
+                                  v_experts_q8(v, s, w);
+                                  v.range(ws, ws_bytes);
                               });
 }
 
@@ -533,6 +675,13 @@ int colibri_moe_expert_ffn_q8(const colibri_moe_shape_t *s, const void *x_rows, 
     const size_t need = ffn_workspace_bytes(*s);
     if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        v_ffn_rows(v, s, x_rows, sorted_assign, expert_offsets, s->d);
+        v_experts_q8(v, s, w);
+        v.range(y_sorted, 2 * (size_t)s->T * s->d * elem_size(s)).range(ws, ws_bytes);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(
         launch_ffn_layers_q8(*s, x_rows, sorted_assign, expert_offsets, *w, y_sorted, ws, true, stream, nullptr));
 }
@@ -544,6 +693,12 @@ int colibri_moe_quantize_q8(const void *w, colibri_dtype_t dtype, int32_t E, int
     if (E < 1 || K < 1 || N < 1 || N % 4) return COLIBRI_ERR_UNSUPPORTED;
     if ((int64_t)E * K * N > ((int64_t)1 << 40)) return COLIBRI_ERR_UNSUPPORTED;
     if (!aligned(w, 16) || !aligned(q, 4) || !aligned(scale, 4)) return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        const size_t n = (size_t)E * K * N;
+        v.finite(w, n, dtype).range(q, n).range(scale, (size_t)E * N * 4);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_quantize_q8(w, dtype, E, K, N, q, scale, stream));
 }
 
@@ -555,6 +710,12 @@ int colibri_moe_quantize_q4(const void *w, colibri_dtype_t dtype, int32_t E, int
     if ((int64_t)E * K * N > ((int64_t)1 << 40)) return COLIBRI_ERR_UNSUPPORTED;
     if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 16) || !aligned(zero, 4))
         return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        const size_t n = (size_t)E * K * N;
+        v.finite(w, n, dtype).range(q, n / 2).range(scale, n / 128 * 4).range(zero, n / 128);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_quantize_q4(w, dtype, E, K, N, q, scale, zero, stream));
 }
 
@@ -573,6 +734,10 @@ int colibri_moe_layer_forward_q4(const colibri_moe_shape_t *s, const void *x, co
                                   const float **part) {
                                   return launch_ffn_layers_q4(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
                                                               part);
+                              },
+                              [&](Validator &v) {
+                                  v_experts_q4(v, s, w);
+                                  v.range(ws, ws_bytes);
                               });
 }
 
@@ -591,6 +756,13 @@ int colibri_moe_expert_ffn_q4(const colibri_moe_shape_t *s, const void *x_rows, 
     const size_t need = ffn_workspace_bytes(*s);
     if (ws_bytes < need) return COLIBRI_ERR_WORKSPACE;
     if (!ws || !aligned(ws, 256)) return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        v_ffn_rows(v, s, x_rows, sorted_assign, expert_offsets, s->d);
+        v_experts_q4(v, s, w);
+        v.range(y_sorted, 2 * (size_t)s->T * s->d * elem_size(s)).range(ws, ws_bytes);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(
         launch_ffn_layers_q4(*s, x_rows, sorted_assign, expert_offsets, *w, y_sorted, ws, true, stream, nullptr));
 }
@@ -611,6 +783,13 @@ int colibri_moe_route_ex(const colibri_moe_shape_t *s, const void *x, const void
     if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(topk_idx, 4) || !aligned(topk_gate, 4) ||
         (b_r && !aligned(b_r, 4)) || (logits && !aligned(logits, 4)))
         return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        v_router(v, s, x, w_r, b_r);
+        v.range(topk_idx, 2 * (size_t)s->T * 4).range(topk_gate, 2 * (size_t)s->T * 4);
+        v.range(logits, (size_t)s->T * s->E * 4);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_route(*s, x, w_r, b_r, topk_idx, topk_gate, logits, stream, gate));
 }
 
@@ -624,6 +803,14 @@ int colibri_moe_combine_ex(const colibri_moe_shape_t *s, const void *y_sorted, c
     if (!aligned(y_sorted, 16) || !aligned(out, 16) || !aligned(assign_pos, 4) || !aligned(topk_gate, 4) ||
         (shared_y && !aligned(shared_y, 16)) || (residual && !aligned(residual, 16)))
         return COLIBRI_ERR_INVALID_ARG;
+    if (validate_enabled()) {
+        Validator v(stream);
+        const size_t A = 2 * (size_t)s->T;
+        v.finite(y_sorted, A * s->d, s->dtype).indices(assign_pos, A, -1, (int32_t)A - 1);
+        v.finite(topk_gate, A, COLIBRI_F32).range(out, (size_t)s->T * s->d * elem_size(s));
+        v.finite(shared_y, (size_t)s->T * s->d, s->dtype).finite(residual, (size_t)s->T * s->d, s->dtype);
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
     return hip_status(launch_combine(*s, y_sorted, assign_pos, topk_gate, out, stream, shared_y, residual));
 }
 
@@ -643,6 +830,10 @@ int colibri_moe_layer_forward_ex(const colibri_moe_shape_t *s, const void *x, co
         ffn_down_splits(*s),
         [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce, const float **part) {
             return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream, part);
+        },
+        [&](Validator &v) {
+            v_experts(v, s, w);
+            v.range(ws, ws_bytes);
         },
         opts);
 }
@@ -673,6 +864,18 @@ int colibri_moe_graph_create(const colibri_moe_shape_t *s, int32_t L, const coli
     if (s->T == 0) return COLIBRI_ERR_UNSUPPORTED;
     st = check_step_buffers(s, L, layers, x, ws, ws_bytes);
     if (st != COLIBRI_OK) return st;
+    if (validate_enabled()) {  // once here: a stream under capture cannot be waited on
+        Validator v(nullptr);
+        v.finite(x, (size_t)s->T * s->d, s->dtype).range(ws, ws_bytes);
+        for (int32_t l = 0; l < L; ++l) {
+            const colibri_moe_layer_params_t &p = layers[l];
+            v.finite(p.w_r, (size_t)s->d * s->E, s->dtype).finite(p.b_r, (size_t)s->E, COLIBRI_F32);
+            v_experts(v, s, &p.experts);
+            const colibri_moe_layer_opts_t o = step_opts(p, nullptr);
+            v_opts(v, s, &o);
+        }
+        if (v.status() != COLIBRI_OK) return v.status();
+    }
 
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return COLIBRI_ERR_HIP;

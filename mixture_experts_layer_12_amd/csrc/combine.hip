@@ -25,10 +25,12 @@
 namespace colibri {
 namespace {
 
-// o[q] += shared[t][c + q], then residual[t][c + q] (each optional)
+// o[q] += shared[t][c + q], then residual[t][c + q] (each optional).  The
+// residual may be the output buffer itself (an in-place layer): each element is
+// read here, by the thread that stores it afterwards, so neither pointer is
+// declared restrict.
 template <typename TE, int VEC>
-__device__ __forceinline__ void add_addends(float (&o)[VEC], const TE *__restrict__ shared,
-                                            const TE *__restrict__ residual, size_t at) {
+__device__ __forceinline__ void add_addends(float (&o)[VEC], const TE *shared, const TE *residual, size_t at) {
     if (shared) {
         float v[VEC];
         Vec16<TE>::load(shared + at, v);
@@ -85,9 +87,8 @@ __device__ __forceinline__ void add_shared_partials(float (&o)[VEC], const Share
 
 template <typename TE>
 __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, const int32_t *__restrict__ pos,
-                                                      const float *__restrict__ gate, TE *__restrict__ out, int T,
-                                                      int d, const TE *__restrict__ shared,
-                                                      const TE *__restrict__ residual, SharedPartials sp) {
+                                                      const float *__restrict__ gate, TE *out, int T, int d,
+                                                      const TE *shared, const TE *residual, SharedPartials sp) {
     constexpr int VEC = 16 / sizeof(TE);
     const int vpr = d / VEC;  // vectors per row
     const size_t total = (size_t)T * vpr;
@@ -137,10 +138,8 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                                                                const int32_t *__restrict__ idx,
                                                                const float *__restrict__ gate,
                                                                const uint16_t *__restrict__ b2, int E,
-                                                               uint16_t *__restrict__ out, int T, int d,
-                                                               const uint16_t *__restrict__ shared,
-                                                               const uint16_t *__restrict__ residual,
-                                                               SharedPartials sp) {
+                                                               uint16_t *out, int T, int d, const uint16_t *shared,
+                                                               const uint16_t *residual, SharedPartials sp) {
     typedef float fv __attribute__((ext_vector_type(VEC)));
     static_assert(L == 1 || L == 8, "lanes per output");
     // L = 1: a batch of U splits keeps split s in interleaved sum s % 8 when U is a

@@ -53,15 +53,112 @@ def tdtype(dt: int):
 
 
 # ------------------------------------------------------------------ tolerances
+# fp32 values are judged element by element: |a - b| <= 1e-4 * S, where S is
+# the element's own last sum taken over absolute values -- for a dot product
+# sum_j |x_j w_j| + |bias| (a logit; an expert row's column, whose terms are
+# the stored hidden values times the second-layer weights) -- and, for a value
+# computed from such sums (a gate, a combined output), their S carried through
+# that last step.  Float accumulation error is a small multiple of
+# sqrt(n) * 2^-24 * S, and S does not vanish where a sum cancels to almost
+# nothing, so the rule holds every element to the error its arithmetic allows.
+
+
+def _f64(a):
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        a = gen.bf16_bits_to_f32(a)
+    return a.astype(np.float64)
+
+
+def logits_scale(x, w_r, b_r=None) -> np.ndarray:
+    """S[t, e] = |b_r[e]| + sum_j |x[t, j] w_r[j, e]|."""
+    S = np.abs(_f64(x)) @ np.abs(_f64(w_r))
+    if b_r is not None:
+        S = S + np.abs(_f64(b_r))[None, :]
+    return S
+
+
+def gates_scale(S_lg: np.ndarray, idx: np.ndarray, g: np.ndarray, lg: np.ndarray, mode: str = "pair") -> np.ndarray:
+    """Scale of each chosen gate, the logits' scale carried through the gate.
+    pair: g0 = sigma(l_i0 - l_i1), so |dg| <= g0 g1 (|dl_i0| + |dl_i1|);
+    softmax over all experts: dg_s = g_s (dl_s - sum_e p_e dl_e), so
+    |dg_s| <= g_s (|dl_s| + max_e |dl_e|).  Plus the scale of the gate's own
+    arithmetic: g0 + g1 = 1 for the pair (g1 is formed as 1 - g0, so its error
+    is that of g0, whatever its size), |g_s| for the softmax gates."""
+    rows = np.arange(idx.shape[0])
+    S0, S1 = S_lg[rows, idx[:, 0]], S_lg[rows, idx[:, 1]]
+    g = np.asarray(g, np.float64)
+    if mode == "pair":
+        return (g[:, 0] * g[:, 1] * (S0 + S1))[:, None] + 1.0
+    return g * (np.stack([S0, S1], 1) + S_lg.max(axis=1, keepdims=True)) + np.abs(g)
+
+
+def ffn_scale(x, rows_token, rows_expert, w1, w2, act: str, w3=None, b1=None, b2=None) -> np.ndarray:
+    """Scale of each expert row y[p] = b2 + H W2 (the second layer's sum):
+    |b2[c]| + sum_j |H_j W2[j, c]|, with H the row's hidden values (fp64)."""
+    x = _f64(x)
+    w1, w2, w3, b1, b2 = (_f64(a) for a in (w1, w2, w3, b1, b2))
+    rows_token = np.asarray(rows_token)
+    rows_expert = np.asarray(rows_expert)
+    S = np.zeros((len(rows_token), w2.shape[2]))
+    for e in np.unique(rows_expert):
+        sel = np.flatnonzero(rows_expert == e)
+        xe = x[rows_token[sel]]
+        u = xe @ w1[e]
+        if act == "swiglu":
+            H = u / (1.0 + np.exp(-u)) * (xe @ w3[e])
+        else:
+            if b1 is not None:
+                u = u + b1[e]
+            if act == "relu":
+                H = np.maximum(u, 0.0)
+            else:
+                from scipy.special import erf
+                H = 0.5 * u * (1.0 + erf(u / np.sqrt(2.0)))
+        S[sel] = np.abs(H) @ np.abs(w2[e]) + (np.abs(b2[e]) if b2 is not None else 0.0)
+    return S
+
+
+def combine_scale(g, y, S_y=None, S_g=None) -> np.ndarray:
+    """Scale of out[t] = g0 y0 + g1 y1: |g0 y0| + |g1 y1|, plus g_s S_y_s for the
+    rows' own error and S_g_s |y_s| for the gates' (when given).  g [T, 2],
+    y [T, 2, d]."""
+    g = np.asarray(g, np.float64)[:, :, None]
+    y = np.asarray(y, np.float64)
+    S = (np.abs(g * y)).sum(1)
+    if S_y is not None:
+        S = S + (np.abs(g) * S_y).sum(1)
+    if S_g is not None:
+        S = S + (np.asarray(S_g)[:, :, None] * np.abs(y)).sum(1)
+    return S
+
+
+def layer_scale(x, w_r, b_r, w1, w2, act, tokens, idx, ref, w3=None, b1=None, b2=None, gate="pair",
+                shared=None, residual=None) -> np.ndarray:
+    """Scale of the layer output of each token in `tokens` (routed to idx [n, 2];
+    ref: the oracle's layer_tokens result for them)."""
+    xs = np.asarray(x)[tokens]
+    S_lg = logits_scale(xs, w_r, b_r)
+    S_g = None if gate == "linear" else gates_scale(S_lg, idx, ref["gate"], ref["logits"], gate)
+    if gate == "linear":  # the gates are the logits themselves
+        rows = np.arange(len(tokens))
+        S_g = np.stack([S_lg[rows, idx[:, 0]], S_lg[rows, idx[:, 1]]], 1)
+    n = len(tokens)
+    S_y = ffn_scale(xs, np.repeat(np.arange(n), 2), idx.reshape(-1), w1, w2, act, w3=w3, b1=b1, b2=b2)
+    S = combine_scale(ref["gate"], ref["y"], S_y.reshape(n, 2, -1), S_g)
+    if shared is not None:
+        S = S + ffn_scale(xs, np.arange(n), np.zeros(n, np.int64), shared["w1"], shared["w2"], act,
+                          w3=shared.get("w3"), b1=shared.get("b1"), b2=shared.get("b2")) + np.abs(ref["y_shared"])
+    if residual is not None:
+        S = S + np.abs(_f64(np.asarray(residual)[tokens]))
+    return S
+
+
 def fp32_rel_err(a, b) -> float:
     """Largest per-row relative error: max over rows r of
-    max_c |a_rc - b_rc| / max_c |b_rc|  (a 1-D array is one row).
-
-    fp32 accumulation error scales with the magnitude of the summands, i.e.
-    with the row's scale, not with each element, so an elementwise ratio is
-    unbounded where a sum cancels to near zero; each output vector (a token's
-    logits, gates or hidden/output row) is therefore judged against its own
-    largest element."""
+    max_c |a_rc - b_rc| / max_c |b_rc|  (a 1-D array is one row)."""
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     if b.size == 0:
@@ -72,9 +169,23 @@ def fp32_rel_err(a, b) -> float:
     return float((np.abs(a2 - b2).max(axis=1) / scale).max())
 
 
-def assert_fp32_close(a, b, what, tol=1e-4):
-    err = fp32_rel_err(a, b)
-    assert err <= tol, f"{what}: max relative error {err:.3e} > {tol:.0e}"
+def assert_fp32_close(a, b, S, what, tol=1e-4):
+    """Both fp32 rules: every element within tol * S (its own scale, above),
+    and every row within tol of its largest |reference| (the row rule).  S is
+    larger than the row's largest element almost everywhere (a sum's absolute
+    terms add up to more than its result), so neither rule implies the other:
+    the first bounds each element by the error its own arithmetic allows, the
+    second keeps the bound from growing with S."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    S = np.broadcast_to(np.asarray(S, np.float64), b.shape)
+    err = np.abs(a - b)
+    bad = err > tol * S
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} elements outside |a-b| <= {tol:.0e} S; "
+                           f"worst |a-b|/S = {float((err / np.maximum(S, 1e-300)).max()):.3e}")
+    row = fp32_rel_err(a, b)
+    assert row <= tol, f"{what}: row relative error {row:.3e} > {tol:.0e}"
+    return float((err / np.maximum(S, 1e-300)).max()) if err.size else 0.0
 
 
 def assert_bf16_close(a, b, what, atol=1e-2, rtol=2e-2):
@@ -85,17 +196,19 @@ def assert_bf16_close(a, b, what, atol=1e-2, rtol=2e-2):
                            f"worst |a-b| = {np.abs(a - b).max():.3e}")
 
 
-def assert_close(a, b, dt, what):
+def assert_close(a, b, dt, what, scale=None):
+    """fp32: the per-element scale rule (scale required); bf16: the allclose rule."""
     if dt == gen.F32:
-        assert_fp32_close(a, b, what)
+        assert scale is not None, f"{what}: an fp32 comparison needs the elements' scale"
+        assert_fp32_close(a, b, scale, what)
     else:
         assert_bf16_close(a, b, what)
 
 
-def assert_layer_close(a, ref, dt, what, residual=None):
+def assert_layer_close(a, ref, dt, what, residual=None, scale=None):
     """Layer outputs with a shared expert, a residual or raw-logit gates.
 
-    fp32: the row rule.  bf16: |a - b| <= 1e-2 + 2e-2 M per element, where M is
+    fp32: the per-element scale rule (scale required).  bf16: |a - b| <= 1e-2 + 2e-2 M per element, where M is
     the largest magnitude among b and the summands of the combine (g0 y0, g1 y1,
     the shared row, the residual row).  Both sides store the expert rows in
     bf16; where an fp32 sum lands on a rounding boundary the two round a row to
@@ -103,7 +216,8 @@ def assert_layer_close(a, ref, dt, what, residual=None):
     the sum, which may cancel to far less.  With no addends and convex gates M
     is at most the larger gated row."""
     if dt == gen.F32:
-        assert_fp32_close(a, ref["out"], what)
+        assert scale is not None, f"{what}: an fp32 comparison needs the elements' scale"
+        assert_fp32_close(a, ref["out"], scale, what)
         return
     a = np.asarray(a, np.float64)
     b = np.asarray(ref["out"], np.float64)
@@ -120,12 +234,38 @@ def assert_layer_close(a, ref, dt, what, residual=None):
 
 
 # ------------------------------------------------------------------ near ties
-def near_tie_mask(lg: np.ndarray) -> np.ndarray:
-    """Tokens whose 1st/2nd or 2nd/3rd logit margin (oracle fp64) is < NEAR_TIE."""
+def _margins(lg: np.ndarray):
     s = -np.sort(-lg, axis=1)
     m12 = s[:, 0] - s[:, 1]
     m23 = s[:, 1] - s[:, 2] if lg.shape[1] > 2 else np.full(lg.shape[0], np.inf)
+    return m12, m23
+
+
+def near_tie_mask(lg: np.ndarray) -> np.ndarray:
+    """Tokens whose 1st/2nd or 2nd/3rd logit margin (oracle fp64) is < NEAR_TIE."""
+    m12, m23 = _margins(lg)
     return np.minimum(m12, m23) < NEAR_TIE
+
+
+def assert_selection(idx: np.ndarray, lg_ref: np.ndarray, tag: str = ""):
+    """The GPU's expert pair of every token against the oracle's top-2 of its
+    fp64 logits.  Exact, except where fp32 summation order may decide:
+      * 2nd/3rd margin < NEAR_TIE: the second expert may differ (exempt);
+      * only the 1st/2nd margin < NEAR_TIE: the same two experts must be
+        chosen, in either slot order.
+    Returns the mask of tokens whose indices differ from the oracle's and the
+    near-tie counts for the report."""
+    idx_ref = oracle.top2(lg_ref)
+    m12, m23 = _margins(lg_ref)
+    near23 = m23 < NEAR_TIE
+    near12 = (m12 < NEAR_TIE) & ~near23
+    diff = np.any(idx != idx_ref, axis=1)
+    same_pair = np.all(np.sort(idx, axis=1) == np.sort(idx_ref, axis=1), axis=1)
+    bad = diff & ~near23 & ~(near12 & same_pair)
+    assert not bad.any(), (f"{tag}: {int(bad.sum())} tokens routed differently outside the near-tie rule "
+                           f"(first at token {int(np.flatnonzero(bad)[0])})")
+    return diff, {"near_tie_tokens": int((near12 | near23).sum()), "near_tie_2nd_3rd": int(near23.sum()),
+                  "near_tie_1st_2nd_only": int(near12.sum()), "index_mismatches_on_near_ties": int(diff.sum())}
 
 
 def report(record: Dict):

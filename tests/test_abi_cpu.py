@@ -454,3 +454,36 @@ def test_layer_noalloc_checks(lib):
     no_w3 = moe._Experts(fake(10), None, fake(12), None, None)
     assert lib.colibri_moe_layer_forward_noalloc(ctypes.byref(shape_c()), fake(0), fake(1), None, ctypes.byref(no_w3),
                                                  fake(2), None, None, None, None) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+def test_validate_env_rejects_non_device_pointers(lib, monkeypatch):
+    """COLIBRI_MOE_VALIDATE=1: every tensor argument must lie inside a device
+    allocation; the fake addresses used above are not, so each entry point
+    returns INVALID_ARG on the host, before anything is launched."""
+    monkeypatch.setenv("COLIBRI_MOE_VALIDATE", "1")
+    s = shape_c()
+    assert route_call(lib, s) == moe.COLIBRI_ERR_INVALID_ARG
+    assert lib.colibri_moe_dispatch(ctypes.byref(s), fake(0), fake(1), fake(2), fake(3), fake(4), None, None, None,
+                                    0, None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert lib.colibri_moe_combine(ctypes.byref(s), fake(0), fake(1), fake(2), fake(3), None) == \
+        moe.COLIBRI_ERR_INVALID_ARG
+    e = moe._Experts(fake(10), fake(11), fake(12), None, None)
+    ws_bytes = lib.colibri_moe_workspace_size(ctypes.byref(s))
+    assert lib.colibri_moe_layer_forward(ctypes.byref(s), fake(0), fake(1), None, ctypes.byref(e), fake(2), None,
+                                         None, None, fake(20), ws_bytes, None) == moe.COLIBRI_ERR_INVALID_ARG
+    assert lib.colibri_moe_expert_ffn(ctypes.byref(s), fake(0), fake(1), fake(2), ctypes.byref(e), fake(3),
+                                      fake(20), ws_bytes, None) == moe.COLIBRI_ERR_INVALID_ARG
+    # the shape and pointer checks still come first
+    assert route_call(lib, shape_c(k=3)) == moe.COLIBRI_ERR_UNSUPPORTED
+    assert route_call(lib, s, x=None) == moe.COLIBRI_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors(lib):
+    """The binding hands the library device pointers only: a host tensor is refused before the call."""
+    torch = pytest.importorskip("torch")
+    s = moe.Shape(T=4, d=64, h=64, E=4, dtype=moe.BF16, act=moe.RELU)
+    host = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.route(s, host, fake(1), None, fake(2), fake(3))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.combine(s, fake(0), fake(1), fake(2), host)

@@ -46,20 +46,17 @@ def run_route(layer):
 def check_route(layer, idx, gate, lg_gpu, tag):
     w = G.host_router(layer.key)
     lg_ref = oracle.logits(layer.x, w["w_r"], w["b_r"])
-    G.assert_fp32_close(lg_gpu, lg_ref, f"{tag} logits")
+    S_lg = G.logits_scale(layer.x, w["w_r"], w["b_r"])
+    G.assert_fp32_close(lg_gpu, lg_ref, S_lg, f"{tag} logits")
     # the GPU's selection is exactly the oracle's top-2 of the GPU's own logits
     assert np.array_equal(oracle.top2(lg_gpu.astype(np.float64)), idx), f"{tag}: top-2 of own logits"
-    idx_ref = oracle.top2(lg_ref)
-    near = G.near_tie_mask(lg_ref)
-    diff = np.any(idx != idx_ref, axis=1)
-    assert not np.any(diff & ~near), f"{tag}: {int((diff & ~near).sum())} non-near-tie tokens routed differently"
+    diff, ties = G.assert_selection(idx, lg_ref, tag)
     # gates: fp32 rule against the oracle's gates for the GPU's chosen pair
     g_ref = oracle.gates(lg_ref, idx)
-    G.assert_fp32_close(gate, g_ref, f"{tag} gates")
+    G.assert_fp32_close(gate, g_ref, G.gates_scale(S_lg, idx, g_ref, lg_ref), f"{tag} gates")
     assert np.all(gate[:, 0] + gate[:, 1] == np.float32(1.0)), f"{tag}: gates must sum to exactly 1 in fp32"
     assert np.all(gate[:, 0] >= 0.5)
-    G.report({"check": "route", "case": tag, "tokens": int(layer.T), "near_tie_tokens": int(near.sum()),
-              "index_mismatches_on_near_ties": int(diff.sum())})
+    G.report({"check": "route", "case": tag, "tokens": int(layer.T), **ties})
 
 
 ROUTE_CASES = [("tiny", 32), ("e8", 1), ("e8", 64), ("e8", 512), ("mixtral_decode", 1), ("mixtral_decode", 4),
@@ -95,7 +92,8 @@ def test_route_expert_counts_and_ties(E, dt):
     assert np.array_equal(lg.astype(np.float64), lg_ref)           # integer sums are exact in fp32
     assert np.array_equal(idx, oracle.top2(lg_ref))                # ties resolved to the lower index
     assert tuple(idx[5]) == (0, 1) and gate[5].tolist() == [0.5, 0.5]
-    G.assert_fp32_close(gate, oracle.gates(lg_ref, idx), f"gates E={E}")
+    g_ref = oracle.gates(lg_ref, idx)
+    G.assert_fp32_close(gate, g_ref, G.gates_scale(G.logits_scale(x, w_r), idx, g_ref, lg_ref), f"gates E={E}")
 
 
 def test_route_bias_and_nan_ranking():
@@ -231,7 +229,9 @@ def small_ffn_case(act, dt, T=300, E=8, d=256, h=384, skew=None, seed=0):
     return w, idx
 
 
-def run_ffn(w, idx, act, dt, E, gather=True):
+def run_ffn(w, idx, act, dt, E, gather=True, scale_out=None):
+    """y_sorted from the GPU and the oracle; with a list for scale_out, the fp32
+    scale of every row is appended to it (None for bf16)."""
     T, d = w["x"].shape
     h = w["w1"].shape[2]
     ref = oracle.dispatch(idx, E)
@@ -250,6 +250,9 @@ def run_ffn(w, idx, act, dt, E, gather=True):
     rows_e = idx.reshape(-1)[ref["sorted_assign"]]
     y_ref = oracle.ffn_rows(w["x"], rows_t, rows_e, w["w1"], w["w2"], act, w3=w["w3"], b1=w["b1"], b2=w["b2"],
                             mirror=True)
+    if scale_out is not None:
+        scale_out.append(G.ffn_scale(w["x"], rows_t, rows_e, w["w1"], w["w2"], act, w3=w["w3"], b1=w["b1"],
+                                     b2=w["b2"]) if dt == gen.F32 else None)
     return G.host(y), y_ref
 
 
@@ -259,8 +262,9 @@ FFN_CASES = [(a, dt) for a in ("relu", "gelu", "swiglu") for dt in (gen.F32, gen
 @pytest.mark.parametrize("act,dt", FFN_CASES, ids=[f"{a}-{'f32' if d == 0 else 'bf16'}" for a, d in FFN_CASES])
 def test_ffn_parity_small(act, dt):
     w, idx = small_ffn_case(act, dt)
-    y, y_ref = run_ffn(w, idx, act, dt, E=8)
-    G.assert_close(y, y_ref, dt, f"y_sorted {act}")
+    sc = []
+    y, y_ref = run_ffn(w, idx, act, dt, E=8, scale_out=sc)
+    G.assert_close(y, y_ref, dt, f"y_sorted {act}", scale=sc[0])
 
 
 @pytest.mark.parametrize("dt", [gen.F32, gen.BF16])
@@ -268,8 +272,9 @@ def test_ffn_ragged_columns_and_presorted_rows(dt):
     # h = 320 and d = 192: column counts that are not multiples of 128
     w, idx = small_ffn_case("gelu", dt, T=173, E=5, d=192, h=320, seed=4)
     for gather in (True, False):
-        y, y_ref = run_ffn(w, idx, "gelu", dt, E=5, gather=gather)
-        G.assert_close(y, y_ref, dt, f"y_sorted gather={gather}")
+        sc = []
+        y, y_ref = run_ffn(w, idx, "gelu", dt, E=5, gather=gather, scale_out=sc)
+        G.assert_close(y, y_ref, dt, f"y_sorted gather={gather}", scale=sc[0])
 
 
 # first layers whose tiles fill a round of one workgroup per CU plus a last
@@ -335,7 +340,7 @@ def test_ffn_decode_expert_over_32_rows():
     idx[:, 0], idx[:, 1] = 0, 1
     y, y_ref = run_ffn(w, idx, "swiglu", gen.BF16, E=8)
     G.assert_bf16_close(y, y_ref, "decode chunked rows")
-    # repeated calls reuse the split-K counters: results must not change
+    # a repeated call on the same workspace (which holds the first call's partials) gives the same bits
     y2, _ = run_ffn(w, idx, "swiglu", gen.BF16, E=8)
     assert np.array_equal(y, y2)
 
@@ -460,11 +465,15 @@ def test_combine_parity(dt):
     torch.cuda.synchronize()
     y64 = yf.astype(np.float64) if dt == gen.F32 else gen.bf16_bits_to_f32(y).astype(np.float64)
     ref = oracle.combine(y64, ap, gate.astype(np.float64), dt)
-    G.assert_close(G.host(out), ref, dt, "combine")
+    G.assert_close(G.host(out), ref, dt, "combine",
+                   scale=G.combine_scale(gate, np.stack([y64[ap[0::2]], y64[ap[1::2]]], 1)))
 
 
 # ------------------------------------------------------------------ whole layer
 def run_layer(layer, stream=None):
+    """The layer through colibri_moe_layer_forward; besides its outputs, the
+    dispatch it computed internally (offsets and both permutations), read from
+    the workspace at the offsets colibri_moe_workspace_layout reports."""
     sh = layer.shape
     ws_bytes = moe.workspace_size(sh)
     ws = G.empty((ws_bytes,), torch.uint8)
@@ -476,39 +485,79 @@ def run_layer(layer, stream=None):
     moe.layer_forward(sh, G.dev(layer.x), dw["w_r"], dw["b_r"], dw["w1"], dw["w2"], out, ws, ws_bytes, w3=dw["w3"],
                       b1=dw["b1"], b2=dw["b2"], topk_idx=idx, topk_gate=gate, counts=counts, stream=stream)
     torch.cuda.synchronize()
-    return {"out": out, "idx": idx.cpu().numpy(), "gate": gate.cpu().numpy(), "counts": counts.cpu().numpy()}
+    lay = moe.workspace_layout(sh)
+    wsh = ws.cpu().numpy()
+    i32 = lambda off, n: wsh[off:off + 4 * n].view(np.int32).copy()
+    return {"out": out, "idx": idx.cpu().numpy(), "gate": gate.cpu().numpy(), "counts": counts.cpu().numpy(),
+            "offsets": i32(lay["expert_offsets"], sh.E + 1), "sorted_assign": i32(lay["sorted_assign"], 2 * sh.T),
+            "assign_pos": i32(lay["assign_pos"], 2 * sh.T)}
 
 
-LAYER_CASES = [("tiny", 32, None), ("e8", 1, None), ("e8", 64, None), ("e8", 512, 48), ("mixtral_decode", 1, None),
-               ("mixtral_decode", 4, None), ("mixtral_decode", 16, 6), ("mixtral_decode", 32, 6),
-               ("mixtral_prefill", 4096, 12), ("skew16", 8192, 48)]
+def tile_edge_rows(offsets: np.ndarray) -> np.ndarray:
+    """Expert-sorted rows at the edges of the grouped GEMM's tiles: the first
+    and last row of every row tile of every expert -- under both tilings the
+    GEMM uses (256-row tiles, up to 320 when a small tail is spread over them;
+    128-row tiles, up to 192), an expert of R rows being cut into equal tiles
+    -- and of every 32-row subtile inside each tile."""
+    rows = set()
+    for BMB, BM in ((256, 320), (128, 192)):
+        for e in range(len(offsets) - 1):
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            R = hi - lo
+            if R == 0:
+                continue
+            mt = -(-R // BMB)
+            tail = R % BMB
+            if mt > 1 and tail != 0 and tail <= BMB // 4 and R <= BM * (mt - 1):
+                mt -= 1
+            rt = -(-R // mt)
+            for t0 in range(lo, hi, rt):
+                t1 = min(t0 + rt, hi)
+                for s0 in range(t0, t1, 32):
+                    rows.update((s0, min(s0 + 31, t1 - 1)))
+                rows.add(t1 - 1)
+    return np.array(sorted(rows), np.int64)
 
 
-@pytest.mark.parametrize("key,T,sample", LAYER_CASES, ids=[f"{k}-T{t}" for k, t, _ in LAYER_CASES])
-def test_layer_parity(key, T, sample):
+# token selection: every token, or the tokens owning the rows at the GEMM's tile edges
+LAYER_CASES = [("tiny", 32, "all"), ("e8", 1, "all"), ("e8", 64, "all"), ("e8", 512, "all"),
+               ("mixtral_decode", 1, "all"), ("mixtral_decode", 4, "all"), ("mixtral_decode", 16, "all"),
+               ("mixtral_decode", 32, "all"), ("mixtral_prefill", 4096, "tiles"), ("skew16", 8192, "tiles")]
+
+
+@pytest.mark.parametrize("key,T,which", LAYER_CASES, ids=[f"{k}-T{t}" for k, t, _ in LAYER_CASES])
+def test_layer_parity(key, T, which):
     layer = G.seeded_layer(key, T)
+    print(f"layer parity {key} T={T}", flush=True)
     r = run_layer(layer)
     w = layer.hw
+    E = layer.cfg.E
     # routing over all tokens
     lg_ref = oracle.logits(layer.x, w["w_r"], w["b_r"])
-    idx_ref = oracle.top2(lg_ref)
-    near = G.near_tie_mask(lg_ref)
-    diff = np.any(r["idx"] != idx_ref, axis=1)
-    assert not np.any(diff & ~near), f"{int((diff & ~near).sum())} non-near-tie tokens routed differently"
-    assert np.array_equal(r["counts"], oracle.dispatch(r["idx"], layer.cfg.E)["counts"])
+    diff, ties = G.assert_selection(r["idx"], lg_ref, f"{key}/T={T}")
+    # the layer's own dispatch (the fused route + dispatch kernel up to 32 tokens) is
+    # exactly the oracle's dispatch of the indices it chose
+    d_ref = oracle.dispatch(r["idx"], E)
+    for k in ("counts", "offsets", "sorted_assign", "assign_pos"):
+        assert np.array_equal(r[k], d_ref[k]), f"{key}/T={T}: layer dispatch {k} differs from the oracle's"
     assert r["counts"].sum() == 2 * T
     assert np.all(r["gate"].sum(1) == np.float32(1.0))
     out = G.host(r["out"])
     assert np.all(np.isfinite(out))
-    # outputs: every token at small sizes, a seeded sample at large ones, plus every exempt token
-    rng = np.random.default_rng(T)
-    toks = np.arange(T) if sample is None else np.sort(rng.choice(T, size=sample, replace=False))
-    toks = np.union1d(toks, np.flatnonzero(diff))
+    if which == "all":
+        toks = np.arange(T)
+    else:
+        edge = tile_edge_rows(r["offsets"])
+        toks = np.unique(r["sorted_assign"][edge] >> 1)
+    toks = np.union1d(toks, np.flatnonzero(diff))  # every token whose indices differ
     ref = layer.oracle_tokens(toks, idx_override=r["idx"][toks])
     assert np.array_equal(ref["idx"], r["idx"][toks])
-    G.assert_close(out[toks], ref["out"], layer.cfg.dtype, f"{key}/T={T} out")
-    G.report({"check": "layer", "case": f"{key}/T={T}", "tokens_compared": int(len(toks)),
-              "near_tie_tokens": int(near.sum()), "index_mismatches_on_near_ties": int(diff.sum()),
+    scale = None
+    if layer.cfg.dtype == gen.F32:
+        scale = G.layer_scale(layer.x, w["w_r"], w["b_r"], w["w1"], w["w2"], layer.cfg.act, toks, r["idx"][toks],
+                              ref, w3=w["w3"], b1=w["b1"], b2=w["b2"])
+    G.assert_close(out[toks], ref["out"], layer.cfg.dtype, f"{key}/T={T} out", scale=scale)
+    G.report({"check": "layer", "case": f"{key}/T={T}", "tokens_compared": int(len(toks)), **ties,
               "counts": r["counts"].tolist()})
 
 
@@ -554,8 +603,11 @@ def test_ffn_up_down_compose(act, dt):
     moe.expert_ffn_down(sh, H, off, dw["w2"], y, ws, ws_bytes, b2=dw["b2"])
     torch.cuda.synchronize()
     assert torch.equal(y, y_full)
-    G.assert_close(G.host(y), oracle.ffn_rows(w["x"], ref["sorted_assign"] // 2, idx.reshape(-1)[ref["sorted_assign"]],
-                                              w["w1"], w["w2"], act, w3=w["w3"], b1=w["b1"], b2=w["b2"]), dt, "y")
+    rt, re = ref["sorted_assign"] // 2, idx.reshape(-1)[ref["sorted_assign"]]
+    scale = G.ffn_scale(w["x"], rt, re, w["w1"], w["w2"], act, w3=w["w3"], b1=w["b1"], b2=w["b2"]) \
+        if dt == gen.F32 else None
+    G.assert_close(G.host(y), oracle.ffn_rows(w["x"], rt, re, w["w1"], w["w2"], act, w3=w["w3"], b1=w["b1"],
+                                              b2=w["b2"]), dt, "y", scale=scale)
 
 
 def test_layer_deterministic_and_stream():
@@ -591,9 +643,10 @@ def test_layer_shape_edges(E, d, h, act, dt):
         ref = oracle.layer_tokens(x, w_r, w["w1"], w["w2"], act, np.arange(T), w3=w["w3"], b1=w["b1"], b2=w["b2"],
                                   idx_override=gi)
         lg = ref["logits"]
-        near = G.near_tie_mask(lg)
-        assert not np.any(np.any(gi != oracle.top2(lg), axis=1) & ~near)
-        G.assert_close(G.host(out), ref["out"], dt, f"E={E} d={d} h={h} T={T}")
+        G.assert_selection(gi, lg, f"E={E} d={d} h={h} T={T}")
+        scale = G.layer_scale(x, w_r, None, w["w1"], w["w2"], act, np.arange(T), gi, ref, w3=w["w3"], b1=w["b1"],
+                              b2=w["b2"]) if dt == gen.F32 else None
+        G.assert_close(G.host(out), ref["out"], dt, f"E={E} d={d} h={h} T={T}", scale=scale)
 
 
 ROUTER_SHAPES = [(24, 64, 1), (24, 320, 17), (40, 320, 33), (63, 192, 200), (48, 2048, 16), (9, 4096, 31),
@@ -620,11 +673,12 @@ def test_router_odd_shapes_and_fused_path(E, d, T):
     torch.cuda.synchronize()
     idx_h, gate_h, lg_h = idx.cpu().numpy(), gate.cpu().numpy(), lg.cpu().numpy()
     lg_ref = oracle.logits(x, w_r, b_r)
-    G.assert_fp32_close(lg_h, lg_ref, "logits")
+    S_lg = G.logits_scale(x, w_r, b_r)
+    G.assert_fp32_close(lg_h, lg_ref, S_lg, "logits")
     assert np.array_equal(oracle.top2(lg_h.astype(np.float64)), idx_h)
-    near = G.near_tie_mask(lg_ref)
-    assert not np.any(np.any(idx_h != oracle.top2(lg_ref), axis=1) & ~near)
-    G.assert_fp32_close(gate_h, oracle.gates(lg_ref, idx_h), "gates")
+    G.assert_selection(idx_h, lg_ref, "router odd shapes")
+    g_ref = oracle.gates(lg_ref, idx_h)
+    G.assert_fp32_close(gate_h, g_ref, G.gates_scale(S_lg, idx_h, g_ref, lg_ref), "gates")
     # the whole layer (fused routing at T <= 32) picks the same experts and gates
     w1 = G.dev(gen.f32_to_bf16_bits((rng.standard_normal((E, d, 64)) / np.sqrt(d)).astype(np.float32)))
     w2 = G.dev(gen.f32_to_bf16_bits((rng.standard_normal((E, 64, d)) / 8).astype(np.float32)))

@@ -148,9 +148,7 @@ def test_layer_q8_parity(key, T, sample):
     out, idx, gate = run_layer_q8(layer)
     w = layer.hq8
     lg_ref = oracle.logits(layer.x, w["w_r"], w["b_r"])
-    near = G.near_tie_mask(lg_ref)
-    diff = np.any(idx != oracle.top2(lg_ref), axis=1)
-    assert not np.any(diff & ~near)
+    diff, _ = G.assert_selection(idx, lg_ref, "q8")
     rng = np.random.default_rng(T + 7)
     toks = np.arange(T) if sample is None else np.sort(rng.choice(T, size=sample, replace=False))
     toks = np.union1d(toks, np.flatnonzero(diff))

@@ -103,11 +103,14 @@ def test_step_and_graph(key, T, L, gate, shared, residual):
                                   b1=h["b1"], b2=h["b2"], mirror=True, idx_override=idxs[l][toks], gate=gate,
                                   shared=h.get("shared"), residual=xin if residual else None)
         lg = oracle.logits(xin, h["w_r"], h["b_r"])
-        near = G.near_tie_mask(lg)
-        diff = np.any(idxs[l] != oracle.top2(lg), axis=1)
-        assert not np.any(diff & ~near), f"layer {l}: routed differently outside near ties"
+        G.assert_selection(idxs[l], lg, f"layer {l}")
+        scale = None
+        if cfg.dtype == gen.F32:
+            scale = G.layer_scale(xin, h["w_r"], h["b_r"], h["w1"], h["w2"], cfg.act, toks, idxs[l][toks], ref,
+                                  w3=h["w3"], b1=h["b1"], b2=h["b2"], gate=gate, shared=h.get("shared"),
+                                  residual=xin if residual else None)
         G.assert_layer_close(G.host(xs[l + 1])[toks], ref, cfg.dtype, f"{key} layer {l}",
-                             residual=G.host(xs[l])[toks] if residual else None)
+                             residual=G.host(xs[l])[toks] if residual else None, scale=scale)
 
     # the step entry point is the chain, bit for bit
     ws_bytes = moe.step_workspace_size(shape, devl)
