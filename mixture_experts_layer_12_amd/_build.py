@@ -1,7 +1,9 @@
 """Build the HIP library libcolibri_moe.so for gfx950, in-tree.
 
 Each source under csrc/ is compiled to an object with hipcc (in parallel), then
-the objects are linked into one shared library next to this file.
+the objects are linked into one shared library next to this file.  The two
+measurement kernels of csrc/ceilings.hip (used by the benchmark only) go into
+a library of their own, libcolibri_ceilings.so.
 """
 from __future__ import annotations
 
@@ -16,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcolibri_moe.so")
+CEIL_LIB = os.path.join(PKG, "libcolibri_ceilings.so")
+CEIL_SOURCES = ["ceilings.hip"]
 
 SOURCES = ["abi.cpp", "validate.cpp", "route.hip", "dispatch.hip", "ffn.hip", "ffn_gemm.hip", "ffn_decode.hip", "combine.hip",
            "quantize.hip", "ffn_decode_q4.hip"]
@@ -47,18 +51,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str):
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES) + len(CEIL_SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, SOURCES + CEIL_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CEIL_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEIL_LIB}")
     return LIB
 
 
