@@ -9,9 +9,10 @@ namespace colibri {
 // the matching W3 product v) at output column n of expert e.
 enum Epi { EPI_ACT_RELU = 0, EPI_ACT_GELU = 1, EPI_SWIGLU = 2, EPI_BIAS_ONLY = 3 };
 
+// (bf16 outputs only: the callers store the value rounded to bf16)
 template <int EPI>
 __device__ __forceinline__ float epi_value(float u, float v, const uint16_t *__restrict__ bias, int e, int N, int n) {
-    if (EPI == EPI_SWIGLU) return silu(u) * v;
+    if (EPI == EPI_SWIGLU) return silu_bf16out(u) * v;
     const float b = bias ? bf16_to_f32(bias[(size_t)e * N + n]) : 0.0f;
     if (EPI == EPI_ACT_RELU) return apply_act<ACT_RELU>(u + b);
     if (EPI == EPI_ACT_GELU) return apply_act<ACT_GELU>(u + b);

@@ -52,22 +52,44 @@ struct Tile {
     int e, row0, rows, n0, split, S;  // S: K splits of this tile
 };
 
-// Row tiles of expert e: count_e rows are cut into ceil(count_e / BMB) row
-// tiles, except that a tail of at most BMB / 4 rows is spread over the other
-// tiles when they stay within BM rows (an expert of 1030 rows runs as 4 tiles
-// of ~258 rows, not 4 full tiles plus a 6-row tile that would stream the whole
-// weight panel for 6 rows); the tiles of an expert are of (nearly) equal size.
-__device__ __forceinline__ int row_tiles(int rows, int BMB, int BM) {
-    int mt = (rows + BMB - 1) / BMB;
-    const int tail = rows % BMB;
-    if (mt > 1 && tail != 0 && tail <= BMB / 4 && rows <= BM * (mt - 1)) mt -= 1;
-    return mt;
-}
+// Row tiles of expert e.  Two rules, both giving every tile at most BM rows:
+//  * big tiles (BMB = 256, BM = 320; two wave rows of up to five 32-row
+//    subtiles): the expert's ceil(count_e / 64) row pairs -- one subtile for
+//    each wave row -- are dealt out as evenly as possible over
+//    ceil(count_e / BM) tiles, so that every tile's two wave rows carry the
+//    same number of subtiles (an expert of 1025 rows runs as 320 + 256 + 256 +
+//    193 rows: 5 + 4 + 4 + 4 subtile pairs, where equal tiles of 257 rows
+//    would split 9 subtiles 5 / 4 and run every tile at the pace of 5);
+//  * mid tiles: ceil(count_e / BMB) tiles of (nearly) equal size, except that
+//    a tail of at most BMB / 4 rows is spread over the other tiles when they
+//    stay within BM rows (a small tail tile would stream the whole weight
+//    panel for a few rows).
+// A tile m of expert e starts at lo + m * u + min(m, r) * g and holds up to
+// u + (m < r ? g : 0) rows (the expert's last tile: what is left).
+template <int BMB, int BM>
+struct RowSplit {
+    static constexpr bool kPairs = (BMB == 256);
+    int mt, u, r, g;
+    __device__ __forceinline__ RowSplit(int rows) {
+        if (rows <= 0) {
+            mt = u = r = g = 0;
+        } else if (kPairs) {
+            const int P = (rows + 63) / 64;  // subtile pairs
+            mt = (rows + BM - 1) / BM;
+            u = 64 * (P / mt), r = P % mt, g = 64;
+        } else {
+            mt = (rows + BMB - 1) / BMB;
+            const int tail = rows % BMB;
+            if (mt > 1 && tail != 0 && tail <= BMB / 4 && rows <= BM * (mt - 1)) mt -= 1;
+            u = (rows + mt - 1) / mt, r = 0, g = 0;
+        }
+    }
+};
 
 // Row tiles of every expert (lane e holds expert e's) and their prefix sums.
 // Whole-wave call; every lane gets the same total.
 struct TileTable {
-    int lo, hi, mt, rt, tiles, incl, total;
+    int lo, hi, mt, u, r, g, tiles, incl, total;
 };
 template <int BMB, int BM>
 __device__ __forceinline__ TileTable tile_table(const int32_t *__restrict__ offsets, int E, int A, int NT) {
@@ -78,8 +100,8 @@ __device__ __forceinline__ TileTable tile_table(const int32_t *__restrict__ offs
         tt.lo = min(max(offsets[lane], 0), A);
         tt.hi = min(max(offsets[lane + 1], tt.lo), A);
     }
-    tt.mt = row_tiles(tt.hi - tt.lo, BMB, BM);                      // row tiles of expert `lane`
-    tt.rt = tt.mt > 0 ? (tt.hi - tt.lo + tt.mt - 1) / tt.mt : 0;  // rows per row tile (<= BM)
+    const RowSplit<BMB, BM> rs(tt.hi - tt.lo);  // row tiles of expert `lane`
+    tt.mt = rs.mt, tt.u = rs.u, tt.r = rs.r, tt.g = rs.g;
     tt.tiles = tt.mt * NT;
     tt.incl = tt.tiles;
 #pragma unroll
@@ -120,9 +142,9 @@ __device__ __forceinline__ void tile_at(const TileTable &tt, int E, int NT, int 
     const int mi = rr / gs;
     const int ni = ng * gn + rr % gs;
     t.e = e;
-    const int rte = __shfl(tt.rt, e);
-    t.row0 = __shfl(tt.lo, e) + mi * rte;
-    t.rows = min(rte, __shfl(tt.hi, e) - t.row0);
+    const int u = __shfl(tt.u, e), r = __shfl(tt.r, e), g = __shfl(tt.g, e);
+    t.row0 = __shfl(tt.lo, e) + mi * u + min(mi, r) * g;
+    t.rows = min(u + (mi < r ? g : 0), __shfl(tt.hi, e) - t.row0);
     t.n0 = ni * BN;
 }
 
@@ -559,7 +581,7 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
             for (int r = 0; r < 16; ++r) {
                 const int rl = wrow + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 float v;
-                if (EPI == EPI_SWIGLU) v = silu(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
+                if (EPI == EPI_SWIGLU) v = silu_bf16out(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
                 else if (EPI == EPI_ACT_RELU) v = apply_act<ACT_RELU>(acc[0][i][j][r] + bv);
                 else if (EPI == EPI_ACT_GELU) v = apply_act<ACT_GELU>(acc[0][i][j][r] + bv);
                 else v = acc[0][i][j][r] + bv;

@@ -382,8 +382,9 @@ def test_ffn_decode_h_from_partials(T, E, d, h, act, skew):
 
 
 ROW_TILE_COUNTS = {
-    # large tiles (256 rows, up to 320): 641 -> 3 x 214, 321 -> 2 x 161, 650 -> 3 x 217, 320 -> 1 x 320,
-    # 1030 -> 4 x 258; subtiles split 4/3, 3/3, 5/5, 5/4 over the two wave rows, or leave one empty
+    # large tiles (up to 320 rows, 64-row pairs dealt out evenly): 641 -> 256 + 256 + 129,
+    # 321 -> 192 + 129, 320 -> 320, 650 -> 256 + 256 + 138, 1030 -> 320 + 256 + 256 + 198, 33 -> 33
+    # (subtiles 2 / 1 over the two wave rows), 1 and 10 -> one subtile, the other wave row empty
     "big": [641, 321, 320, 33, 1, 0, 650, 10, 1030],
     # mid-size tiles (128 rows, up to 192; no more than 160 rows per expert on average):
     # 129 -> 1 x 129, 160 -> 1 x 160, 192 -> 2 x 96, 193 -> 97 + 96, 255 -> 128 + 127
@@ -493,29 +494,37 @@ def run_layer(layer, stream=None):
             "assign_pos": i32(lay["assign_pos"], 2 * sh.T)}
 
 
+def row_tile_starts(R: int, big: bool):
+    """First rows (relative to the expert's first row) of the grouped GEMM's row
+    tiles of an expert of R rows.  Big tiles (up to 320 rows): the expert's
+    ceil(R / 64) 64-row pairs dealt out evenly over ceil(R / 320) tiles; mid
+    tiles (128 rows, up to 192): equal tiles, a tail of at most 32 rows spread
+    over the others."""
+    if big:
+        P, mt = -(-R // 64), -(-R // 320)
+        q, r = divmod(P, mt)
+        return [64 * (m * q + min(m, r)) for m in range(mt)]
+    mt = -(-R // 128)
+    if mt > 1 and R % 128 != 0 and R % 128 <= 32 and R <= 192 * (mt - 1):
+        mt -= 1
+    rt = -(-R // mt)
+    return list(range(0, R, rt))
+
+
 def tile_edge_rows(offsets: np.ndarray) -> np.ndarray:
     """Expert-sorted rows at the edges of the grouped GEMM's tiles: the first
-    and last row of every row tile of every expert -- under both tilings the
-    GEMM uses (256-row tiles, up to 320 when a small tail is spread over them;
-    128-row tiles, up to 192), an expert of R rows being cut into equal tiles
-    -- and of every 32-row subtile inside each tile."""
+    and last row of every row tile of every expert, under both tilings the
+    GEMM uses, and of every 32-row subtile inside each tile."""
     rows = set()
-    for BMB, BM in ((256, 320), (128, 192)):
+    for big in (True, False):
         for e in range(len(offsets) - 1):
             lo, hi = int(offsets[e]), int(offsets[e + 1])
-            R = hi - lo
-            if R == 0:
+            if hi == lo:
                 continue
-            mt = -(-R // BMB)
-            tail = R % BMB
-            if mt > 1 and tail != 0 and tail <= BMB // 4 and R <= BM * (mt - 1):
-                mt -= 1
-            rt = -(-R // mt)
-            for t0 in range(lo, hi, rt):
-                t1 = min(t0 + rt, hi)
+            starts = [lo + s for s in row_tile_starts(hi - lo, big)] + [hi]
+            for t0, t1 in zip(starts[:-1], starts[1:]):
                 for s0 in range(t0, t1, 32):
                     rows.update((s0, min(s0 + 31, t1 - 1)))
-                rows.add(t1 - 1)
     return np.array(sorted(rows), np.int64)
 
 
