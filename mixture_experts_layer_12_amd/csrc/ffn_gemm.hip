@@ -438,6 +438,21 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
                 for (int j = 0; j < SJ; ++j)
                     acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[b][j], acc[b][i][j], 0, 0, 0);
         }
+        // Schedule the k-step as one MFMA, then one LDS read (of the next k-step's
+        // operands, read before this step in the source), alternating for as long
+        // as both last: left to itself the compiler bunches the reads and the two
+        // waves of a SIMD then wait for LDS at the same time (measured on the
+        // Mixtral-shaped prefill: first layer 1747 -> 1696 us, second 904 -> 841).
+        if constexpr (LV > 0) {
+            constexpr int NM = LV * NB * SJ, NR = LV + 2 * NB * SJ;
+#pragma unroll
+            for (int q = 0; q < (NM < NR ? NM : NR); ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+            if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+            if constexpr (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+        }
     };
 
     // ---- main loop over a ring of STAGES LDS stages.  The operands of k-step ks+1 are
