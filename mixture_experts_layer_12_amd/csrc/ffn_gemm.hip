@@ -173,6 +173,18 @@ __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets,
     return true;
 }
 
+// f(integral_constant<int, n>) for the runtime n in [0, N] (larger n: N)
+template <int N, class F>
+__device__ __forceinline__ void with_live_count(int n, F &&f) {
+    if constexpr (N > 0) {
+        if (n < N) {
+            with_live_count<N - 1>(n, f);
+            return;
+        }
+    }
+    f(std::integral_constant<int, N>{});
+}
+
 // 16-byte chunk swizzle inside an A row of BK bf16 (BK/8 chunks): the 16 rows
 // that one ds_read_b128 phase touches land on 16 distinct 16-byte bank slots
 // of the 256-byte bank window.
@@ -534,7 +546,9 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
             if (kt + BST < KT) issue_b(kt % BST, kt0 + kt + BST);
         }
     };
-    // the common live counts get their own copy of the loop, free of per-subtile tests
+    // every live count 0 .. SM gets its own copy of the loop, free of per-subtile
+    // tests and with its MFMAs and LDS reads interleaved (a wave row of a tile
+    // whose subtile count is odd has one subtile fewer than the other)
     if constexpr (SPEC) {
         if (w >= NW) {  // loader wave: the main loop's barriers, the one below, the epilogue's
             loader_loop();
@@ -543,13 +557,9 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
             if (SK == 1) __syncthreads();
             return;
         }
-        if (live_sm == SM) main_loop_spec(std::integral_constant<int, SM>{});
-        else if (live_sm == SM - 1) main_loop_spec(std::integral_constant<int, SM - 1>{});
-        else main_loop_spec(std::integral_constant<int, -1>{});
+        with_live_count<SM>(live_sm, [&](auto lv) { main_loop_spec(lv); });
     } else {
-        if (live_sm == SM) main_loop(std::integral_constant<int, SM>{});
-        else if (live_sm == SM - 1) main_loop(std::integral_constant<int, SM - 1>{});
-        else main_loop(std::integral_constant<int, -1>{});
+        with_live_count<SM>(live_sm, [&](auto lv) { main_loop(lv); });
     }
     wait_vmcnt<0>();
     __syncthreads();
