@@ -358,16 +358,25 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     if (gcol >= N) gcol = 0;
     const uint32_t b_voff = (uint32_t)((((lane & 7) >> 1) * N + gcol) * 2);
     const uint16_t *b_base = (mat ? B1 : B0) + (size_t)e * K * N + (size_t)(cw / HPB) * 4 * N;
+    size_t b_row[B_PW];  // first weight row of B copy q, relative to the k-tile's first row, times N
+#pragma unroll
+    for (int q = 0; q < B_PW; ++q) b_row[q] = (size_t)4 * (NW / HPB) * q * N;
 
+    // copy m (m < A_PW: A copy m; else B copy m - A_PW) of k-tile kt into stage s
+    auto copy_one = [&](int m, int s, int k0, const uint16_t *bk) {
+        const uint32_t sa = lds0 + s * STAGE_BYTES;
+        if (m < A_PW) {
+            if ((a_live >> m) & 1) dma16(a_src[m] + k0, sa + (w + NW * m) * 1024);
+        } else {
+            const int q = m - A_PW;
+            dma16_s(b_voff, bk + b_row[q], sa + A_BYTES + (w + NW * q) * 1024);
+        }
+    };
     auto issue = [&](int s, int kt) {
         const int k0 = kt * BK;
-        const uint32_t sa = lds0 + s * STAGE_BYTES;
+        const uint16_t *bk = b_base + (size_t)k0 * N;
 #pragma unroll
-        for (int q = 0; q < A_PW; ++q)
-            if ((a_live >> q) & 1) dma16(a_src[q] + k0, sa + (w + NW * q) * 1024);
-#pragma unroll
-        for (int q = 0; q < B_PW; ++q)
-            dma16_s(b_voff, b_base + (size_t)(k0 + 4 * (NW / HPB) * q) * N, sa + A_BYTES + (w + NW * q) * 1024);
+        for (int m = 0; m < A_PW + B_PW; ++m) copy_one(m, s, k0, bk);
     };
     // SPEC copies: A of k-tile kt into A stage s (compute waves), B of k-tile kt into B stage t (loader waves)
     auto issue_a = [&](int s, int kt) {
@@ -467,6 +476,30 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
         }
     };
 
+    // The tile's last k-step with the copies of k-tile kt into stage s placed
+    // between its MFMAs (copy m after MFMA m): right after the barrier both waves
+    // of a SIMD issue their copies at the same time, and issued in one run they
+    // would leave the matrix unit idle meanwhile.
+    auto mma_issue = [&](const Frags &f, auto lv, int s, int kt) {
+        constexpr int LV = decltype(lv)::value;
+        static_assert(LV >= 0, "compile-time live count");
+        constexpr int DPW_ = A_PW + B_PW;
+        const int k0 = kt * BK;
+        const uint16_t *bk = b_base + (size_t)k0 * N;
+#pragma unroll
+        for (int i = 0; i < LV; ++i)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < SJ; ++j) {
+                    acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[b][j], acc[b][i][j], 0, 0, 0);
+                    const int m = (i * NB + b) * SJ + j;  // a constant once the loops are unrolled
+                    if (m < DPW_) copy_one(m, s, k0, bk);
+                }
+#pragma unroll
+        for (int m = LV * NB * SJ; m < DPW_; ++m) copy_one(m, s, k0, bk);
+    };
+
     // ---- main loop over a ring of STAGES LDS stages.  The operands of k-step ks+1 are
     // read while k-step ks is multiplied; the workgroup barrier sits before the last
     // k-step of a tile, so the next tile's first reads overlap that step's MFMAs.
@@ -501,10 +534,9 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
             }
             wait_vmcnt<(STAGES - 2) * DPW>();  // k-tile kt+1 has landed (this wave's copies)
             __syncthreads();                    // ... everyone's; and k-tile kt is fully read
-            issue(s, ktile(kt + STAGES));
             const int sn = ((kt + 1) % STAGES) * STAGE_BYTES;
             if (kt + 1 < KT) read_frags(sn, sn + A_BYTES, 0, f[0], lv);
-            mma(f[(KS - 1) & 1], lv);
+            mma_issue(f[(KS - 1) & 1], lv, s, ktile(kt + STAGES));  // refills stage s
         }
     };
     // ---- SPEC: compute waves.  A stage kt & 1, B stage kt % BST.  Barrier P publishes
