@@ -227,6 +227,24 @@ int colibri_moe_layer_forward_noalloc(const colibri_moe_shape_t *s, const void *
  *                         (LINEAR_SCORE, [zskr] section 2.3) */
 typedef enum { COLIBRI_GATE_PAIR = 0, COLIBRI_GATE_SOFTMAX = 1, COLIBRI_GATE_LINEAR = 2 } colibri_gate_t;
 
+/* Where the combine (step 5) runs in a layer call:
+ *   COLIBRI_COMBINE_AUTO      the library's choice for the shape (the faster of
+ *                             the two below as measured on MI355X)
+ *   COLIBRI_COMBINE_SEPARATE  a kernel of its own after the FFN
+ *   COLIBRI_COMBINE_FOLD      folded into the epilogue of the second FFN layer
+ *                             where that layer is a grouped GEMM (bf16, T > 64,
+ *                             no shared expert left as split partials): the
+ *                             tile that completes a token's two expert rows
+ *                             writes its output ([nxbn] section 2.1 fuses the
+ *                             stages after the matmul into its kernel); else
+ *                             as SEPARATE
+ * The output is the same bit for bit whichever runs. */
+typedef enum {
+    COLIBRI_COMBINE_AUTO = 0,
+    COLIBRI_COMBINE_SEPARATE = 1,
+    COLIBRI_COMBINE_FOLD = 2
+} colibri_combine_t;
+
 /* Options of colibri_moe_layer_forward_ex:
  *   gate      gating of the routed pair (above)
  *   shared    an always-on shared expert applied to every token with weight 1
@@ -236,6 +254,7 @@ typedef enum { COLIBRI_GATE_PAIR = 0, COLIBRI_GATE_SOFTMAX = 1, COLIBRI_GATE_LIN
  *   residual  [T, d] dtype, 16-byte aligned, added to the output ([nxbn]
  *             section 2.1: residual add fused with the expert computation); or
  *             NULL.  It may be the same buffer as out (an in-place update).
+ *   combine   where the combine runs (above; a zeroed struct gives AUTO)
  * out[t] = g0 y(t, slot 0) + g1 y(t, slot 1) + y_shared(t) + residual[t], summed
  * in fp32 and rounded once; y_shared is stored in dtype like the routed rows. */
 typedef struct {
@@ -243,6 +262,7 @@ typedef struct {
     const colibri_moe_experts_t *shared;
     int32_t shared_h; /* hidden width of the shared expert (0: h); a multiple of 64 */
     const void *residual;
+    int32_t combine; /* colibri_combine_t */
 } colibri_moe_layer_opts_t;
 
 /* Workspace of colibri_moe_layer_forward_ex for these options (NULL opts =

@@ -69,7 +69,10 @@ class _WsLayout(ctypes.Structure):
 
 class _Opts(ctypes.Structure):
     _fields_ = [("gate", ctypes.c_int), ("shared", ctypes.POINTER(_Experts)), ("shared_h", ctypes.c_int32),
-                ("residual", ctypes.c_void_p)]
+                ("residual", ctypes.c_void_p), ("combine", ctypes.c_int32)]
+
+
+COMBINE = {"auto": 0, "separate": 1, "fold": 2}
 
 
 class _LayerParams(ctypes.Structure):
@@ -367,18 +370,22 @@ def _gate_code(gate) -> int:
     return GATE_CODES[gate] if isinstance(gate, str) else int(gate)
 
 
-def _opts(gate="pair", shared=None, shared_h: int = 0, residual=None, shape=None):
+def _opts(gate="pair", shared=None, shared_h: int = 0, residual=None, shape=None, combine="auto"):
     """ctypes options and the experts struct it points to (keep both alive).
     ``shared``: dict with the shared expert's w1, w2 (and w3, b1, b2); with a
     shape the tensors are checked against it (the shared expert is one expert
-    of hidden width shared_h, 0 = the shape's h)."""
+    of hidden width shared_h, 0 = the shape's h).  ``combine``: "auto" (the
+    library's choice), "separate" (a kernel of its own) or "fold" (in the
+    second layer's epilogue where that layer is a grouped GEMM)."""
     sh = None
     one = None if shape is None else Shape(shape.T, shape.d, shape.h, 1, shape.dtype, shape.act)
     if shared is not None:
         sh = _experts(shared["w1"], shared["w2"], shared.get("w3"), shared.get("b1"), shared.get("b2"), shape=one,
                       h=int(shared_h) or None)
     res = _ptr(residual) if shape is None else _ptr(residual, shape.T * shape.d * _es(shape), _es(shape), "residual")
-    o = _Opts(_gate_code(gate), ctypes.pointer(sh) if sh is not None else None, int(shared_h), res)
+    if combine not in COMBINE:
+        raise ValueError(f"combine must be one of {sorted(COMBINE)}, not {combine!r}")
+    o = _Opts(_gate_code(gate), ctypes.pointer(sh) if sh is not None else None, int(shared_h), res, COMBINE[combine])
     return o, sh
 
 
@@ -407,10 +414,10 @@ def combine_ex(shape: Shape, y_sorted, assign_pos, topk_gate, out, shared_y=None
 
 def layer_forward_ex(shape: Shape, x, w_r, b_r, w1, w2, out, ws, ws_bytes: Optional[int] = None, w3=None, b1=None,
                      b2=None, gate="pair", shared=None, shared_h: int = 0, residual=None, topk_idx=None,
-                     topk_gate=None, counts=None, stream=None):
+                     topk_gate=None, counts=None, stream=None, combine="auto"):
     s = shape.c()
     e = _experts(w1, w2, w3, b1, b2, shape=shape)
-    o, keep = _opts(gate, shared, shared_h, residual, shape=shape)
+    o, keep = _opts(gate, shared, shared_h, residual, shape=shape, combine=combine)
     es = _es(shape)
     _check(load().colibri_moe_layer_forward_ex(ctypes.byref(s), *_router_args(shape, x, w_r, b_r), ctypes.byref(e),
                                                ctypes.byref(o), _ptr(out, shape.T * shape.d * es, es, "out"),

@@ -117,6 +117,9 @@ int check_opts(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o) 
     if (o->gate != COLIBRI_GATE_PAIR && o->gate != COLIBRI_GATE_SOFTMAX && o->gate != COLIBRI_GATE_LINEAR)
         return COLIBRI_ERR_UNSUPPORTED;
     if (o->residual && !aligned(o->residual, 16)) return COLIBRI_ERR_INVALID_ARG;
+    if (o->combine != COLIBRI_COMBINE_AUTO && o->combine != COLIBRI_COMBINE_SEPARATE &&
+        o->combine != COLIBRI_COMBINE_FOLD)
+        return COLIBRI_ERR_UNSUPPORTED;
     if (o->shared_h < 0 || o->shared_h % 64 || o->shared_h > (1 << 20)) return COLIBRI_ERR_UNSUPPORTED;
     if (o->shared) {
         const colibri_moe_shape_t sh = shared_shape(s, o);
@@ -126,7 +129,7 @@ int check_opts(const colibri_moe_shape_t *s, const colibri_moe_layer_opts_t *o) 
 }
 
 struct LayerWorkspace {
-    size_t idx, gate, counts, offsets, sorted, pos, disp, y, sh_offsets, sh_y, sh_ffn, ffn, total;
+    size_t idx, gate, counts, offsets, sorted, pos, disp, arrive, y, sh_offsets, sh_y, sh_ffn, ffn, total;
 };
 
 // The plain layer's regions, then (with a shared expert) its offsets, output
@@ -148,6 +151,7 @@ LayerWorkspace layer_workspace(const colibri_moe_shape_t *s, const colibri_moe_l
     L.sorted = take(A * 4);
     L.pos = take(A * 4);
     L.disp = take(dispatch_scratch_bytes(*s));
+    L.arrive = take(combine_fold_counts(*s) * 4);
     L.y = take(A * s->d * elem_size(s));
     if (has_shared(o)) {
         const colibri_moe_shape_t sh = shared_shape(s, o);
@@ -311,6 +315,16 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
         }
         if (e == hipSuccess && branch) e = hipEventRecord(br.join, ss);
     }
+    // the combine folded into the second layer's epilogue where that layer is a
+    // grouped GEMM and the caller (or, by default, the library) picks it; a
+    // shared expert on a parallel branch is joined before the second layer then
+    const size_t narrive = combine_fold_counts(*s);
+    // (its counts are zeroed by the dispatch kernels; a shared expert left as
+    // split partials goes to the separate combine)
+    const int mode = opts ? opts->combine : COLIBRI_COMBINE_AUTO;
+    const bool fold = narrive > 0 && !route_dispatch_fusable(*s) && shp.part == nullptr &&
+                      (mode == COLIBRI_COMBINE_FOLD || (mode == COLIBRI_COMBINE_AUTO && combine_fold_preferred(*s)));
+    int32_t *arrive = fold ? reinterpret_cast<int32_t *>(base + L.arrive) : nullptr;
     if (e == hipSuccess) {
         if (route_dispatch_fusable(*s)) {
             e = launch_route_dispatch(*s, x, w_r, b_r, idx, gate, counts, offsets, sorted, pos, stream, gate_mode);
@@ -318,12 +332,29 @@ int layer_forward_impl(const colibri_moe_shape_t *s, const void *x, const void *
             e = launch_route(*s, x, w_r, b_r, idx, gate, nullptr, stream, gate_mode);
             if (e == hipSuccess)
                 e = launch_dispatch(*s, idx, counts, offsets, sorted, pos, stream,
-                                    dispatch_scratch_bytes(*s) ? base + L.disp : nullptr);
+                                    dispatch_scratch_bytes(*s) ? base + L.disp : nullptr, arrive,
+                                    fold ? narrive : 0);
         }
     }
     if (e != hipSuccess) return hip_status(e);
     const float *part = nullptr;
-    e = Sd > 1 ? ffn(sorted, offsets, nullptr, ffn_ws, false, &part) : ffn(sorted, offsets, y, ffn_ws, true, nullptr);
+    if (fold) {
+        if (branch) e = hipStreamWaitEvent(stream, br.join, 0);
+        CombineFold cf;
+        cf.arrive = arrive;
+        cf.sorted = sorted;
+        cf.pos = pos;
+        cf.idx = idx;
+        cf.gate = gate;
+        cf.out = static_cast<uint16_t *>(out);
+        cf.shared = static_cast<const uint16_t *>(sh_y);
+        cf.residual = static_cast<const uint16_t *>(residual);
+        cf.b2 = s->act == COLIBRI_ACT_SWIGLU ? nullptr : static_cast<const uint16_t *>(b2);
+        if (e == hipSuccess) e = ffn(sorted, offsets, y, ffn_ws, false, &part, &cf);
+        return hip_status(e);
+    }
+    e = Sd > 1 ? ffn(sorted, offsets, nullptr, ffn_ws, false, &part, nullptr)
+               : ffn(sorted, offsets, y, ffn_ws, true, nullptr, nullptr);
     if (e == hipSuccess && branch) e = hipStreamWaitEvent(stream, br.join, 0);
     if (e != hipSuccess) return hip_status(e);
     if (Sd > 1)
@@ -376,8 +407,9 @@ int step_layer(const colibri_moe_shape_t *s, const colibri_moe_layer_params_t &p
     const colibri_moe_layer_opts_t o = step_opts(p, residual ? x : nullptr);
     return layer_forward_impl(
         s, x, p.w_r, p.b_r, x, nullptr, nullptr, nullptr, ws, ws_bytes, stream, p.experts.b2, ffn_down_splits(*s),
-        [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce, const float **part) {
-            return launch_ffn_layers(*s, x, sorted, offsets, p.experts, y, ffn_ws, reduce, stream, part);
+        [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce, const float **part,
+            const CombineFold *fold) {
+            return launch_ffn_layers(*s, x, sorted, offsets, p.experts, y, ffn_ws, reduce, stream, part, fold);
         },
         [&](Validator &v) {
             v_experts(v, s, &p.experts);
@@ -603,9 +635,9 @@ int colibri_moe_layer_forward(const colibri_moe_shape_t *s, const void *x, const
     return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes,
                               stream, w->b2, ffn_down_splits(*s),
                               [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
-                                  const float **part) {
+                                  const float **part, const CombineFold *fold) {
                                   return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
-                                                           part);
+                                                           part, fold);
                               },
                               [&](Validator &v) {
                                   v_experts(v, s, w);
@@ -631,9 +663,9 @@ int colibri_moe_layer_forward_noalloc(const colibri_moe_shape_t *s, const void *
     return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws,
                               (size_t)COLIBRI_MOE_NOALLOC_SCRATCH_BYTES, stream, w->b2, ffn_down_splits(*s),
                               [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
-                                  const float **part) {
+                                  const float **part, const CombineFold *fold) {
                                   return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
-                                                           part);
+                                                           part, fold);
                               },
                               [&](Validator &v) { v_experts(v, s, w); });
 }
@@ -650,7 +682,8 @@ int colibri_moe_layer_forward_q8(const colibri_moe_shape_t *s, const void *x, co
     return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes,
                               stream, w->b2, ffn_down_splits(*s, true),
                               [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
-                                  const float **part) {
+                                  const float **part, const CombineFold *fold) {
+                                  if (fold) return hipErrorInvalidValue;  // decode sizes only: never folded
                                   return launch_ffn_layers_q8(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
                                                               part);
                               },
@@ -731,7 +764,8 @@ int colibri_moe_layer_forward_q4(const colibri_moe_shape_t *s, const void *x, co
     return layer_forward_impl(s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes,
                               stream, w->b2, ffn_down_splits_q4(*s),
                               [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce,
-                                  const float **part) {
+                                  const float **part, const CombineFold *fold) {
+                                  if (fold) return hipErrorInvalidValue;  // decode sizes only: never folded
                                   return launch_ffn_layers_q4(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream,
                                                               part);
                               },
@@ -828,8 +862,9 @@ int colibri_moe_layer_forward_ex(const colibri_moe_shape_t *s, const void *x, co
     return layer_forward_impl(
         s, x, w_r, b_r, out, topk_idx_out, topk_gate_out, expert_counts_out, ws, ws_bytes, stream, w->b2,
         ffn_down_splits(*s),
-        [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce, const float **part) {
-            return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream, part);
+        [&](const int32_t *sorted, const int32_t *offsets, void *y, void *ffn_ws, bool reduce, const float **part,
+            const CombineFold *fold) {
+            return launch_ffn_layers(*s, x, sorted, offsets, *w, y, ffn_ws, reduce, stream, part, fold);
         },
         [&](Validator &v) {
             v_experts(v, s, w);

@@ -18,72 +18,10 @@
 // 16-byte loads and the sum is formed in fp32, then rounded once to the
 // storage type.  A slot whose assign_pos is negative (an out-of-range expert
 // index upstream) contributes nothing.
-#include "device_common.h"
-#include "ffn_common.h"
-#include "launchers.h"
+#include "combine_common.h"
 
 namespace colibri {
 namespace {
-
-// o[q] += shared[t][c + q], then residual[t][c + q] (each optional).  The
-// residual may be the output buffer itself (an in-place layer): each element is
-// read here, by the thread that stores it afterwards, so neither pointer is
-// declared restrict.
-template <typename TE, int VEC>
-__device__ __forceinline__ void add_addends(float (&o)[VEC], const TE *shared, const TE *residual, size_t at) {
-    if (shared) {
-        float v[VEC];
-        Vec16<TE>::load(shared + at, v);
-#pragma unroll
-        for (int q = 0; q < VEC; ++q) o[q] += v[q];
-    }
-    if (residual) {
-        float v[VEC];
-        Vec16<TE>::load(residual + at, v);
-#pragma unroll
-        for (int q = 0; q < VEC; ++q) o[q] += v[q];
-    }
-}
-
-// The shared expert's row t, columns c .. c + VEC - 1, from its second layer's
-// S split partials (part[s][t][...], rows `stride` floats apart per split),
-// formed as the reduce forms it (8 interleaved sums in order, + b2, rounded to
-// bf16), then added to o.
-template <int VEC>
-__device__ __forceinline__ void add_shared_partials(float (&o)[VEC], const SharedPartials &sp, size_t at, int c) {
-    constexpr int U = 8;
-    float y8[8][VEC];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int q = 0; q < VEC; ++q) y8[j][q] = 0.0f;
-    for (int s0 = 0; s0 < sp.S; s0 += U) {
-        float a[U][VEC];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float *src = sp.part + (size_t)min(s0 + u, sp.S - 1) * sp.stride + at;
-#pragma unroll
-            for (int q4 = 0; q4 < VEC; q4 += 4) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(src + q4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) a[u][q4 + r] = v[r];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (s0 + u < sp.S)  // s0 is a multiple of 8: split s0 + u goes to sum u
-#pragma unroll
-                for (int q = 0; q < VEC; ++q) y8[u][q] += a[u][q];
-    }
-#pragma unroll
-    for (int q = 0; q < VEC; ++q) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc += y8[j][q];
-        const float yb = acc + (sp.b2 ? bf16_to_f32(sp.b2[c + q]) : 0.0f);
-        o[q] += bf16_to_f32((uint16_t)f32_to_bf16_bits(yb));
-    }
-}
 
 template <typename TE>
 __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, const int32_t *__restrict__ pos,
@@ -92,46 +30,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, 
     constexpr int VEC = 16 / sizeof(TE);
     const int vpr = d / VEC;  // vectors per row
     const size_t total = (size_t)T * vpr;
-    const int A = 2 * T;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-        const int t = (int)(i / vpr);
-        const int c = (int)(i % vpr) * VEC;
-        const int p0 = pos[2 * t], p1 = pos[2 * t + 1];
-        const float g0 = gate[2 * t], g1 = gate[2 * t + 1];
-        float y0[VEC], y1[VEC];
-        if (p0 >= 0 && p0 < A) Vec16<TE>::load(y + (size_t)p0 * d + c, y0);
-        else
-#pragma unroll
-            for (int q = 0; q < VEC; ++q) y0[q] = 0.0f;
-        if (p1 >= 0 && p1 < A) Vec16<TE>::load(y + (size_t)p1 * d + c, y1);
-        else
-#pragma unroll
-            for (int q = 0; q < VEC; ++q) y1[q] = 0.0f;
-        float o[VEC];
-#pragma unroll
-        for (int q = 0; q < VEC; ++q) o[q] = fmaf(g1, y1[q], g0 * y0[q]);
-        if (sp.part) add_shared_partials<VEC>(o, sp, (size_t)t * d + c, c);  // bf16 layers only
-        add_addends<TE, VEC>(o, sp.part ? nullptr : shared, residual, (size_t)t * d + c);
-        if constexpr (sizeof(TE) == 4) {
-            *reinterpret_cast<f32x4 *>(out + (size_t)t * d + c) = f32x4{o[0], o[1], o[2], o[3]};
-        } else {
-            u32x4 ov;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ov[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
-            *reinterpret_cast<u32x4 *>(out + (size_t)t * d + c) = ov;
-        }
-    }
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x)
+        combine_rows_vec<TE>(y, pos, gate, out, T, d, shared, residual, sp, (int)(i / vpr), (int)(i % vpr) * VEC);
 }
 
 // Same combine, but each expert row Y[p] is first formed from the second
 // layer's S split partial sums: Y[p] = bf16(sum of part[s][p] + b2[e]), the
-// value the separate reduce would have stored.  The splits are added in the
-// reduce's order: 8 interleaved sums (sum j takes s = j, j + 8, ... in order),
-// then those 8 in order j = 0 .. 7 (for S <= 8 simply s = 0 .. S-1).  L = 1:
-// a thread forms both rows of its VEC output columns, loading U splits of each
-// at a time; L = 8: the 8 lanes of a group each form one interleaved sum and
-// lane 0 adds the 8 through shuffles and finishes the output (few outputs,
-// many splits: decode sizes).
+// value the separate reduce would have stored, in the reduce's order (see
+// combine_partials_vec).  L = 1: a thread forms both rows of its VEC output
+// columns, loading U splits of each at a time; L = 8: the 8 lanes of a group
+// each form one interleaved sum and lane 0 adds the 8 through shuffles and
+// finishes the output (few outputs, many splits: decode sizes).
 template <int VEC, int U, int L>
 __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__restrict__ part, int S,
                                                                const int32_t *__restrict__ pos,
@@ -142,15 +51,19 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                                                                const uint16_t *residual, SharedPartials sp) {
     typedef float fv __attribute__((ext_vector_type(VEC)));
     static_assert(L == 1 || L == 8, "lanes per output");
-    // L = 1: a batch of U splits keeps split s in interleaved sum s % 8 when U is a
-    // multiple of 8, or when one batch holds them all (the host keeps S <= U < 8)
-    static_assert(L == 8 || U % 8 == 0 || U < 8, "batch size");
-    constexpr int NJ = L == 1 ? 8 : 1;  // interleaved sums per thread
     const int vpr = d / VEC;
     const size_t total = (size_t)T * vpr;
+    if constexpr (L == 1) {
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+             i += (size_t)gridDim.x * blockDim.x)
+            combine_partials_vec<VEC, U>(part, S, pos, idx, gate, b2, E, out, T, d, shared, residual, sp,
+                                         (int)(i / vpr), (int)(i % vpr) * VEC);
+        return;
+    }
     const int A = 2 * T;
     const size_t split_stride = (size_t)A * d;
-    const int j0 = L == 1 ? 0 : (int)(threadIdx.x & (L - 1));  // this lane's interleaved sum
+    const int j0 = (int)(threadIdx.x & (L - 1));  // this lane's interleaved sum
+    const int base = (int)(threadIdx.x & (kWave - 1)) & ~(L - 1);
     for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / L; i < total;
          i += (size_t)gridDim.x * blockDim.x / L) {
         const int t = (int)(i / vpr);
@@ -163,18 +76,16 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
             e[sl] = idx[2 * t + sl];
             live[sl] = p[sl] >= 0 && p[sl] < A && e[sl] >= 0 && e[sl] < E;
         }
-        float y8[2][NJ][VEC];
+        float y8[2][VEC];
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int q = 0; q < VEC; ++q) y8[sl][j][q] = 0.0f;
+            for (int q = 0; q < VEC; ++q) y8[sl][q] = 0.0f;
         // loads are unconditional (a dead slot reads row 0, then contributes
         // nothing), so no branch separates a load from its use
-        auto load = [&](int sp, int sl) {
+        auto load = [&](int s, int sl) {
             const int row = live[sl] ? p[sl] : 0;
-            return *reinterpret_cast<const fv *>(part + sp * split_stride + (size_t)row * d + c);
+            return *reinterpret_cast<const fv *>(part + s * split_stride + (size_t)row * d + c);
         };
         // this lane's splits: s = j0 + L m; batches of U of them; a last, partial
         // batch loads the lane's last split in its unused slots and skips their
@@ -189,11 +100,10 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (mb + u < nmine) {  // no break, so every index stays a constant
-                    const int j = L == 1 ? u % 8 : 0;  // L = 1: split mb + u; mb % 8 == 0 (U < 8: mb = 0)
 #pragma unroll
                     for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                        for (int q = 0; q < VEC; ++q) y8[sl][j][q] += a[sl][u][q];
+                        for (int q = 0; q < VEC; ++q) y8[sl][q] += a[sl][u][q];
                 }
             }
         }
@@ -204,71 +114,45 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
 #pragma unroll
             for (int q = 0; q < VEC; ++q) {
                 float acc = 0.0f;
-                if constexpr (L == 1) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc += y8[sl][j][q];
-                } else {
-                    const int base = (int)(threadIdx.x & (kWave - 1)) & ~(L - 1);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) acc += __shfl(y8[sl][0][q], base + j);
-                }
+                for (int j = 0; j < 8; ++j) acc += __shfl(y8[sl][q], base + j);
                 y[sl][q] = acc;
             }
-        // the shared expert's row from its own split partials (L = 8: this lane's
-        // interleaved sum, added over the 8 lanes in order by lane 0)
+        // the shared expert's row from its own split partials: this lane's
+        // interleaved sum, added over the 8 lanes in order by lane 0
         float ysh[VEC];
-        if constexpr (L == 8) {
-            if (sp.part) {
-                float a8[VEC];
+        if (sp.part) {
+            float a8[VEC];
 #pragma unroll
-                for (int q = 0; q < VEC; ++q) a8[q] = 0.0f;
-                const int nsh = sp.S > j0 ? (sp.S - j0 + L - 1) / L : 0;
-                for (int mb = 0; mb < nsh; mb += U) {
-                    fv a[U];
+            for (int q = 0; q < VEC; ++q) a8[q] = 0.0f;
+            const int nsh = sp.S > j0 ? (sp.S - j0 + L - 1) / L : 0;
+            for (int mb = 0; mb < nsh; mb += U) {
+                fv a[U];
 #pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        a[u] = *reinterpret_cast<const fv *>(sp.part + (size_t)(j0 + L * min(mb + u, nsh - 1)) * sp.stride +
-                                                             (size_t)t * d + c);
+                for (int u = 0; u < U; ++u)
+                    a[u] = *reinterpret_cast<const fv *>(sp.part + (size_t)(j0 + L * min(mb + u, nsh - 1)) * sp.stride +
+                                                         (size_t)t * d + c);
 #pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        if (mb + u < nsh)
+                for (int u = 0; u < U; ++u)
+                    if (mb + u < nsh)
 #pragma unroll
-                            for (int q = 0; q < VEC; ++q) a8[q] += a[u][q];
-                }
-                const int base = (int)(threadIdx.x & (kWave - 1)) & ~(L - 1);
+                        for (int q = 0; q < VEC; ++q) a8[q] += a[u][q];
+            }
 #pragma unroll
-                for (int q = 0; q < VEC; ++q) {
-                    float acc = 0.0f;
+            for (int q = 0; q < VEC; ++q) {
+                float acc = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc += __shfl(a8[q], base + j);
-                    const float yb = acc + (sp.b2 ? bf16_to_f32(sp.b2[c + q]) : 0.0f);
-                    ysh[q] = bf16_to_f32((uint16_t)f32_to_bf16_bits(yb));
-                }
+                for (int j = 0; j < 8; ++j) acc += __shfl(a8[q], base + j);
+                const float yb = acc + (sp.b2 ? bf16_to_f32(sp.b2[c + q]) : 0.0f);
+                ysh[q] = bf16_to_f32((uint16_t)f32_to_bf16_bits(yb));
             }
         }
         if (j0 != 0) continue;
         float o[VEC];
+        gate_partial_sums<VEC>(o, y, live, e, gate, b2, d, t, c);
+        if (sp.part)
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) o[q] = 0.0f;
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-            if (!live[sl]) continue;
-            const float g = gate[2 * t + sl];
-#pragma unroll
-            for (int q = 0; q < VEC; ++q) {
-                const float yb = y[sl][q] + (b2 ? bf16_to_f32(b2[(size_t)e[sl] * d + c + q]) : 0.0f);
-                const float yr = bf16_to_f32((uint16_t)f32_to_bf16_bits(yb));  // Y is a bf16 value
-                o[q] = sl == 0 ? g * yr : fmaf(g, yr, o[q]);
-            }
-        }
-        if (sp.part) {
-            if constexpr (L == 8) {
-#pragma unroll
-                for (int q = 0; q < VEC; ++q) o[q] += ysh[q];
-            } else {
-                add_shared_partials<VEC>(o, sp, (size_t)t * d + c, c);
-            }
-        }
+            for (int q = 0; q < VEC; ++q) o[q] += ysh[q];
         if (shared || residual) {
             const size_t at = (size_t)t * d + c;
 #pragma unroll
@@ -277,12 +161,8 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(const float *__re
                 if (residual) o[q] += bf16_to_f32(residual[at + q]);
             }
         }
-        uint16_t *dst = out + (size_t)t * d + c;
-        if constexpr (VEC == 4) {
-            *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        } else {
-            dst[0] = (uint16_t)f32_to_bf16_bits(o[0]);
-        }
+        static_assert(VEC == 4, "4 columns per output");
+        *reinterpret_cast<u32x2 *>(out + (size_t)t * d + c) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
 }
 

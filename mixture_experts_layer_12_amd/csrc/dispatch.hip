@@ -25,11 +25,24 @@ namespace {
 constexpr int kDispatchWaves = 16;
 constexpr int kDispatchThreads = kDispatchWaves * kWave;
 
+// zero[0 .. n) = 0 by the whole grid (zero: 16-byte aligned or nullptr), with
+// 16-byte vector stores.
+__device__ __forceinline__ void zero_words(int32_t *zero, size_t n) {
+    if (zero == nullptr) return;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    u32x4 *z4 = reinterpret_cast<u32x4 *>(zero);
+    for (size_t i = i0; i < n / 4; i += stride) z4[i] = u32x4{0u, 0u, 0u, 0u};
+    for (size_t i = n / 4 * 4 + i0; i < n; i += stride) zero[i] = 0;
+}
+
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(const int32_t *__restrict__ idx, int A, int E,
                                                                     int32_t *__restrict__ counts,
                                                                     int32_t *__restrict__ offsets,
                                                                     int32_t *__restrict__ sorted_assign,
-                                                                    int32_t *__restrict__ assign_pos) {
+                                                                    int32_t *__restrict__ assign_pos,
+                                                                    int32_t *__restrict__ zero, size_t nzero) {
+    zero_words(zero, nzero);
     __shared__ DispatchShared<kDispatchWaves> sh;
     dispatch_block<kDispatchWaves>([&](int a) { return idx[a]; }, A, E, counts, offsets, sorted_assign, assign_pos,
                                    sh);
@@ -58,7 +71,10 @@ constexpr int kChunkWaves = 4;  // chunks (waves) per workgroup of the count and
 
 __global__ __launch_bounds__(kChunkWaves *kWave) void dispatch_count_kernel(const int32_t *__restrict__ idx, int A,
                                                                             int E, int nchunks,
-                                                                            int32_t *__restrict__ hist) {
+                                                                            int32_t *__restrict__ hist,
+                                                                            int32_t *__restrict__ zero,
+                                                                            size_t nzero) {
+    zero_words(zero, nzero);
     const int c = (int)blockIdx.x * kChunkWaves + (int)(threadIdx.x / kWave);
     if (c >= nchunks) return;  // uniform per wave
     const int lane = threadIdx.x & (kWave - 1);
@@ -179,19 +195,19 @@ size_t dispatch_scratch_bytes(const colibri_moe_shape_t &s) {
 
 hipError_t launch_dispatch(const colibri_moe_shape_t &s, const int32_t *topk_idx, int32_t *counts,
                            int32_t *offsets, int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st,
-                           void *scratch) {
+                           void *scratch, int32_t *zero, size_t nzero) {
     const int A = 2 * s.T;
     const size_t need = dispatch_scratch_bytes(s);
     if (need == 0 || scratch == nullptr) {
         dispatch_kernel<<<1, kDispatchThreads, 0, st>>>(topk_idx, A, s.E, counts, offsets, sorted_assign,
-                                                        assign_pos);
+                                                        assign_pos, zero, nzero);
         return hipGetLastError();
     }
     const int nchunks = ceil_div(A, kWave);
     int32_t *hist = static_cast<int32_t *>(scratch);
     int32_t *base = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) + need / 2);
     const int blocks = ceil_div(nchunks, kChunkWaves);
-    dispatch_count_kernel<<<blocks, kChunkWaves * kWave, 0, st>>>(topk_idx, A, s.E, nchunks, hist);
+    dispatch_count_kernel<<<blocks, kChunkWaves * kWave, 0, st>>>(topk_idx, A, s.E, nchunks, hist, zero, nzero);
     dispatch_scan_kernel<<<1, kScanParts * kWave, 0, st>>>(hist, nchunks, s.E, base, counts, offsets);
     dispatch_scatter_kernel<<<blocks, kChunkWaves * kWave, 0, st>>>(topk_idx, A, s.E, nchunks, base, offsets,
                                                                     sorted_assign, assign_pos);

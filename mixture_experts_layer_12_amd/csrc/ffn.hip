@@ -211,16 +211,32 @@ hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const
     return launch_gemm_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
 }
 
+size_t combine_fold_counts(const colibri_moe_shape_t &s) {
+    if (s.dtype != COLIBRI_BF16 || s.T <= 0 || ffn_decode_eligible(s) || !gemm_fold_ok(s)) return 0;
+    const GemmPlan p = gemm_plan(s, false);
+    return (size_t)s.T * (size_t)ceil_div(s.d, p.BNC);
+}
+
+// The fold pays one L2 write-back and one L2 invalidation per tile of the
+// second layer (cross-XCD visibility of the rows it reads), atomics and its
+// tail work; measured on MI355X it does not beat the separate combine at the
+// benchmarked shapes, so the default keeps the kernel.
+bool combine_fold_preferred(const colibri_moe_shape_t &s) {
+    (void)s;
+    return false;
+}
+
 hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
                            const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st,
-                           bool reduce) {
+                           bool reduce, const CombineFold *fold) {
+    if (fold && combine_fold_counts(s) == 0) return hipErrorInvalidValue;  // no fold at this shape
     if (ffn_decode_eligible(s)) return launch_decode_down(s, H, offsets, decode_weights(w), y_sorted, scratch, reduce, st);
     const int A = 2 * s.T;
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
     if (s.dtype == COLIBRI_F32)
         return launch_gemm_f32<EPI_BIAS_ONLY>(false, H, nullptr, s.T, offsets, s.E, w.w2, nullptr, b2, y_sorted, s.h,
                                               s.d, A, st);
-    return launch_gemm_down(s, H, offsets, w, y_sorted, scratch, reduce, st);
+    return launch_gemm_down(s, H, offsets, w, y_sorted, scratch, reduce, st, fold);
 }
 
 namespace {
@@ -248,7 +264,8 @@ hipError_t decode_layers(const colibri_moe_shape_t &s, const void *x_rows, const
 
 hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
-                             bool reduce, hipStream_t st, const float **down_partials) {
+                             bool reduce, hipStream_t st, const float **down_partials, const CombineFold *fold) {
+    if (fold && combine_fold_counts(s) == 0) return hipErrorInvalidValue;  // no fold at this shape
     if (ffn_decode_eligible(s))
         return decode_layers(s, x_rows, sorted_assign, offsets, decode_weights(w), y_sorted, ws, reduce, st,
                              down_partials);
@@ -258,7 +275,7 @@ hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, c
     if (down_partials) *down_partials = reinterpret_cast<const float *>(scratch);
     hipError_t e = launch_ffn_up(s, x_rows, sorted_assign, offsets, w, H, scratch, st);
     if (e != hipSuccess) return e;
-    return launch_ffn_down(s, H, offsets, w, y_sorted, scratch, st, reduce);
+    return launch_ffn_down(s, H, offsets, w, y_sorted, scratch, st, reduce, fold);
 }
 
 hipError_t launch_ffn_layers_q8(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,

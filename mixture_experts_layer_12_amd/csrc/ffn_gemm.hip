@@ -33,7 +33,13 @@
 //     barrier per k-tile sits before the tile's last k-step;
 //   * epilogue: bias + ReLU/GELU, silu(u)*v (the W1 and W3 tiles of a column
 //     block live in the same wave and lane), or bias only; the bf16 tile is
-//     staged through LDS and written back with 16-byte row stores.
+//     staged through LDS and written back with 16-byte row stores;
+//   * combine folded into GEMM2 ([nxbn] section 2.1 fuses the stages that
+//     follow the matmul into its kernel; section 3.3 defines the gated sum):
+//     after storing its rows, a tile counts itself in per (token, column
+//     tile), and the tile that completes a token's two slots writes that
+//     token's output columns (see CombineFold).
+#include "combine_common.h"
 #include "device_common.h"
 #include "ffn_common.h"
 #include "launchers.h"
@@ -265,14 +271,130 @@ __device__ __forceinline__ void wait_live_stage(int n_a) {
 // A ring.  Split over waves, the weights run BST - 1 tiles ahead while A
 // (rows already in L2) runs one tile ahead.  All waves meet at the same
 // barriers; the loader waves leave after the last one.
+// ---- the combine folded into GEMM2's epilogue (CombineFold).  Called by every
+// wave of the workgroup (NWT waves) once the tile's Y rows (SK == 1) or split
+// partials (SK > 1) are stored.  Lane l of wave w counts in tile row w + NWT l;
+// a lane whose count completes its token's 2 SK arrivals marks it, and the
+// wave then forms the marked tokens' output columns n0 .. n0 + BNC - 1, RPP
+// tokens at a time, with the combine kernels' own per-vector code.
+template <int RPP, int LPR, class F>
+__device__ __forceinline__ void fold_marked(uint64_t m, int t, F &&fn) {
+    static_assert(RPP * LPR == kWave, "lane groups");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = lane / LPR, cv = lane % LPR;
+    while (m) {  // m is the same in every lane
+        int src = -1;
+#pragma unroll
+        for (int r = 0; r < RPP; ++r) {
+            const int b = m ? __builtin_ctzll(m) : -1;
+            if (r == q) src = b;
+            if (m) m &= m - 1;
+        }
+        const int tt = __shfl(t, src < 0 ? 0 : src);
+        if (src >= 0) fn(tt, cv);
+    }
+}
+
+// 4 columns per lane, LPR lanes per token
+template <int U, int LPR>
+__device__ __forceinline__ void fold_partials(uint64_t m, int t, const CombineFold &f, const float *part, int S, int E,
+                                              int T, int N, int n0) {
+    fold_marked<kWave / LPR, LPR>(m, t, [&](int tt, int cv) {
+        const int c = n0 + 4 * cv;
+        if (c < N)
+            combine_partials_vec<4, U>(part, S, f.pos, f.idx, f.gate, f.b2, E, f.out, T, N, f.shared, f.residual,
+                                       SharedPartials{}, tt, c);
+    });
+}
+
+constexpr int kFoldMaxSplits = 4;  // more splits: the separate combine (registers)
+
+template <int NWT, int BNC>
+__device__ __forceinline__ void fold_combine(const CombineFold &f, const uint16_t *Y, const float *part, int T, int E,
+                                             int N, int NT, int n0, int row0, int rows, int SK, uint8_t *lds) {
+    static_assert(BNC == 256 || BNC == 128, "column tile");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = (int)(threadIdx.x / kWave);
+    volatile int *any = reinterpret_cast<volatile int *>(lds);  // the LDS tile is free from here on
+    // Release: every wave's stores have reached the L2 (vmcnt counts stores
+    // on this chip) before the barrier; then one agent-scope release fence, a
+    // write-back of the XCD's L2, covers the whole tile.  Fences here cost an
+    // L2 scan each, so the tile issues one per direction, not one per wave.
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (w == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) *any = 0;
+    }
+    __syncthreads();
+    const int rl = w + NWT * lane;  // rows <= NWT * 64
+    int t = 0;
+    bool fin = false;
+    if (rl < rows) {
+        t = f.sorted[row0 + rl] >> 1;
+        fin = atomicAdd(f.arrive + (size_t)t * NT + n0 / BNC, 1) == 2 * SK - 1;
+    }
+    const uint64_t m = __ballot(fin);
+    if (m != 0 && lane == 0) *any = 1;
+    __syncthreads();
+    if (*any == 0) return;  // the same in every wave
+    // Acquire: one agent-scope acquire fence (invalidates this CU's L1 and the
+    // XCD's L2) orders every wave's reads below after the counts it observed.
+    if (w == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+    if (m == 0) return;
+    if (SK == 1) {
+        // one 16-byte vector (8 bf16 columns) per lane, RPP tokens per pass,
+        // the loads of UNR passes in flight together
+        constexpr int LPR = BNC / 8, RPP = kWave / LPR, UNR = 2;
+        const int q = lane / LPR;
+        const int c = n0 + 8 * (lane % LPR);
+        uint64_t mm = m;
+        while (mm) {  // the same in every lane
+            int tt[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                int src = -1;
+#pragma unroll
+                for (int r = 0; r < RPP; ++r) {
+                    const int b = mm ? __builtin_ctzll(mm) : -1;
+                    if (r == q) src = b;
+                    if (mm) mm &= mm - 1;
+                }
+                const int v = __shfl(t, src < 0 ? 0 : src);
+                tt[u] = (src >= 0 && c < N) ? v : -1;
+            }
+            RowsVec rv[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+                if (tt[u] >= 0) rows_vec_load<uint16_t>(rv[u], Y, f.pos, f.gate, T, N, f.shared, f.residual, tt[u], c);
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+                if (tt[u] >= 0)
+                    rows_vec_finish<uint16_t>(rv[u], f.shared != nullptr, f.residual != nullptr, f.out,
+                                              SharedPartials{}, N, tt[u], c);
+        }
+        return;
+    }
+    // 4 columns per lane
+    constexpr int LPR = BNC / 4 < kWave ? BNC / 4 : kWave;
+#pragma unroll
+    for (int h = 0; h < BNC; h += 4 * LPR) {
+        if (SK <= 2) fold_partials<2, LPR>(m, t, f, part, SK, E, T, N, n0 + h);
+        else fold_partials<4, LPR>(m, t, f, part, SK, E, T, N, n0 + h);  // SK <= kFoldMaxSplits
+    }
+}
+
 template <int BMB, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, bool GATHER, int WPE, int BLD = 0,
           int BST = 2>
 __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ sorted_assign, int T,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int K, int N, int NT, int S, int tail_split,
-    float *__restrict__ part) {
+    float *__restrict__ part, CombineFold fold) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    // the combine folds into GEMM2 only (bias-only epilogue); fold.arrive is the same in every thread
+    const bool folded = EPI == EPI_BIAS_ONLY && fold.arrive != nullptr;
     constexpr int NB = DUAL ? 2 : 1;             // weight matrices per tile
     constexpr int NW = WM * WN;
     constexpr int BNC = DUAL ? BN / 2 : BN;      // output columns per tile
@@ -587,6 +709,7 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
             wait_vmcnt<0>();
             __syncthreads();
             if (SK == 1) __syncthreads();
+            if (folded) fold_combine<NW + BLD, BNC>(fold, C, part, T, E, N, NT, n0, row0, rows, SK, lds);
             return;
         }
         with_live_count<SM>(live_sm, [&](auto lv) { main_loop_spec(lv); });
@@ -619,6 +742,7 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
                 }
             }
         }
+        if (folded) fold_combine<NW + BLD, BNC>(fold, C, part, T, E, N, NT, n0, row0, rows, SK, lds);
         return;
     }
 
@@ -655,6 +779,7 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
             *reinterpret_cast<u32x4 *>(C + (size_t)(row0 + rl) * N + n) =
                 *reinterpret_cast<const u32x4 *>(Cs + rl * BNC + cv * 8);
     }
+    if (folded) fold_combine<NW + BLD, BNC>(fold, C, part, T, E, N, NT, n0, row0, rows, SK, lds);
 }
 
 // Tail split, second half: the tiles of the last round were run as two K
@@ -767,21 +892,22 @@ namespace {
 template <int BMB, int BM, int BN, int WPE, int BLD, int BST, int EPI>
 hipError_t launch_shape(bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
                         const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
-                        int S, bool tail, float *part, hipStream_t st) {
+                        int S, bool tail, float *part, const CombineFold *fold, hipStream_t st) {
     constexpr int BNC = EPI == EPI_SWIGLU ? BN / 2 : BN;
     const int A = 2 * s.T;
     const int NT = (N + BNC - 1) / BNC;
     const int mtiles = (A + BMB - 1) / BMB + std::min(s.E, A);  // bound on the row tiles of all experts
     const dim3 grid(mtiles * NT * (tail ? 2 : S));
     constexpr int threads = (2 * 4 + BLD) * kWave;
+    const CombineFold cf = fold ? *fold : CombineFold{};
     if (gather)
         ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, true, WPE, BLD, BST><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
-            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, tail ? 1 : 0, part);
+            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, tail ? 1 : 0, part, cf);
     else
         ffn_gemm_kernel<BMB, BM, BN, kBK, 2, 4, 2, EPI, false, WPE, BLD, BST><<<grid, threads, 0, st>>>(
             (const uint16_t *)Am, sa, s.T, offsets, s.E, (const uint16_t *)B0, (const uint16_t *)B1,
-            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, tail ? 1 : 0, part);
+            (const uint16_t *)bias, (uint16_t *)C, K, N, NT, S, tail ? 1 : 0, part, cf);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && tail) {
         constexpr int blocks = TailReduceGrid<BMB, BM, BNC>::blocks;
@@ -795,20 +921,26 @@ hipError_t launch_shape(bool gather, const colibri_moe_shape_t &s, const void *A
 template <int EPI>
 hipError_t launch_gemm(const GemmPlan &p, bool gather, const colibri_moe_shape_t &s, const void *Am, const int32_t *sa,
                        const int32_t *offsets, const void *B0, const void *B1, const void *bias, void *C, int K, int N,
-                       float *part, hipStream_t st) {
+                       float *part, hipStream_t st, const CombineFold *fold = nullptr) {
     if constexpr (EPI != EPI_SWIGLU) {
         if (p.mid && p.BNC == 256)
             return launch_shape<128, 192, 256, 2, 2, 3, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S,
-                                                             p.tail, part, st);
+                                                             p.tail, part, fold, st);
         if (p.mid)
             return launch_shape<128, 192, 128, 2, 2, 6, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S,
-                                                             p.tail, part, st);
+                                                             p.tail, part, fold, st);
     }
     return launch_shape<256, 320, 256, 2, 0, 2, EPI>(gather, s, Am, sa, offsets, B0, B1, bias, C, K, N, p.S, p.tail,
-                                                     part, st);
+                                                     part, fold, st);
 }
 
 }  // namespace
+
+bool gemm_fold_ok(const colibri_moe_shape_t &s) {
+    if (s.dtype != COLIBRI_BF16 || s.T <= 0) return false;
+    const GemmPlan p = gemm_plan(s, false);
+    return !p.tail && p.S <= kFoldMaxSplits;
+}
 
 int gemm_splits(const colibri_moe_shape_t &s, bool up) {
     if (s.dtype != COLIBRI_BF16 || s.T <= 0) return 1;
@@ -849,13 +981,15 @@ hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, cons
 }
 
 hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                            const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st) {
+                            const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st,
+                            const CombineFold *fold) {
     const void *b2 = s.act == COLIBRI_ACT_SWIGLU ? nullptr : w.b2;
     const GemmPlan p = gemm_plan(s, false);
+    if (fold && p.tail) return hipErrorInvalidValue;  // the second layer never runs a tail split
     float *part = static_cast<float *>(scratch);
     hipError_t e = launch_gemm<EPI_BIAS_ONLY>(p, false, s, H, nullptr, offsets, w.w2, nullptr, b2, y, s.h, s.d, part,
-                                              st);
-    if (e == hipSuccess && p.S > 1 && reduce) e = launch_split_reduce(s, false, p.S, offsets, w, y, part, st);
+                                              st, fold);
+    if (e == hipSuccess && p.S > 1 && reduce && !fold) e = launch_split_reduce(s, false, p.S, offsets, w, y, part, st);
     return e;
 }
 

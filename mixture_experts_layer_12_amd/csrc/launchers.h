@@ -27,9 +27,11 @@ hipError_t launch_route_dispatch(const colibri_moe_shape_t &s, const void *x, co
 // scratch: dispatch_scratch_bytes(s) bytes (256-aligned) or nullptr; with it,
 // large batches run the multi-workgroup path (same result)
 size_t dispatch_scratch_bytes(const colibri_moe_shape_t &s);
+// zero [nzero] (or nullptr): int32 words the dispatch kernels set to 0 on the
+// way (the arrival counts of a folded combine, see CombineFold)
 hipError_t launch_dispatch(const colibri_moe_shape_t &s, const int32_t *topk_idx, int32_t *counts,
                            int32_t *offsets, int32_t *sorted_assign, int32_t *assign_pos, hipStream_t st,
-                           void *scratch = nullptr);
+                           void *scratch = nullptr, int32_t *zero = nullptr, size_t nzero = 0);
 
 hipError_t launch_gather_rows(const colibri_moe_shape_t &s, const void *x, const int32_t *sorted_assign,
                               void *x_sorted, hipStream_t st);
@@ -43,10 +45,12 @@ size_t ffn_workspace_bytes(const colibri_moe_shape_t &s);
 hipError_t launch_ffn_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                          const int32_t *offsets, const colibri_moe_experts_t &w, void *h_rows, void *scratch,
                          hipStream_t st);
-// reduce = false (when ffn_down_splits(s) > 1) leaves the split partials in scratch
+// reduce = false (when ffn_down_splits(s) > 1) leaves the split partials in
+// scratch; fold: the combine folded into the second layer (see CombineFold)
+struct CombineFold;
 hipError_t launch_ffn_down(const colibri_moe_shape_t &s, const void *h_rows, const int32_t *offsets,
                            const colibri_moe_experts_t &w, void *y_sorted, void *scratch, hipStream_t st,
-                           bool reduce = true);
+                           bool reduce = true, const CombineFold *fold = nullptr);
 // Decode-sized batches (bf16, T <= 64) use the weight-streaming kernel.
 struct DecodePlan {
     int NCB;            // column blocks per expert
@@ -98,6 +102,33 @@ struct SharedPartials {
     size_t stride = 0;
     const uint16_t *b2 = nullptr;
 };
+// The combine folded into the epilogue of the second layer's grouped GEMM
+// (bf16, T > 64).  Every tile stores its Y rows (or its split partials) as
+// usual, then counts itself in at arrive[t * NT + column tile] for each token t
+// of its rows (NT = the layer's column tiles); the tile whose count completes
+// token t's 2 S arrivals (two slots, S K splits each) forms out[t] over its
+// columns with the combine's own arithmetic (combine_common.h), so the output
+// does not depend on which tile finishes last and equals the separate
+// combine's bit for bit.  arrive must be zero on entry (the layer's dispatch
+// zeroes it).  Both slots of every token must hold a valid expert, which the
+// layer's routing guarantees.  A shared expert enters as finished rows only
+// (its split partials go to the separate combine, which has the registers).
+struct CombineFold {
+    int32_t *arrive = nullptr;        // [T][NT] counts
+    const int32_t *sorted = nullptr;  // sorted row -> assignment 2 t + slot
+    const int32_t *pos = nullptr;     // assignment -> sorted row
+    const int32_t *idx = nullptr;     // expert of each assignment (split partials)
+    const float *gate = nullptr;
+    uint16_t *out = nullptr;
+    const uint16_t *shared = nullptr;    // [T, d] or nullptr
+    const uint16_t *residual = nullptr;  // [T, d] or nullptr
+    const uint16_t *b2 = nullptr;  // second-layer bias [E][d] or nullptr (split partials)
+};
+// Arrival counts a folded combine needs for shape s (0: the combine cannot be
+// folded at this shape).
+size_t combine_fold_counts(const colibri_moe_shape_t &s);
+// COLIBRI_COMBINE_AUTO: fold at this shape (measured faster than the kernel).
+bool combine_fold_preferred(const colibri_moe_shape_t &s);
 // combine straight from the second layer's S split partials (adds them, b2,
 // rounds Y, then gates).  shared, residual: optional [T, d] dtype addends (as
 // in launch_combine); sp: the shared row from partials instead of `shared`
@@ -118,12 +149,15 @@ struct GemmPlan {
 };
 GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up);
 int gemm_splits(const colibri_moe_shape_t &s, bool up);
+// The second layer's plan admits the folded combine (no tail split, few K splits).
+bool gemm_fold_ok(const colibri_moe_shape_t &s);
 size_t gemm_scratch_bytes(const colibri_moe_shape_t &s, bool up);
 hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                           const int32_t *offsets, const colibri_moe_experts_t &w, void *H, void *scratch,
                           hipStream_t st);
 hipError_t launch_gemm_down(const colibri_moe_shape_t &s, const void *H, const int32_t *offsets,
-                            const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st);
+                            const colibri_moe_experts_t &w, void *y, void *scratch, bool reduce, hipStream_t st,
+                            const CombineFold *fold = nullptr);
 // Adds the S split partials of one layer and applies that layer's epilogue
 // (bias + activation, SwiGLU, or bias only), storing the dtype result.
 hipError_t launch_split_reduce(const colibri_moe_shape_t &s, bool up, int S, const int32_t *offsets,
@@ -134,9 +168,12 @@ int ffn_down_splits(const colibri_moe_shape_t &s, bool q8 = false);
 // Both layers with H and the scratch carved from ws (H first, then the scratch).
 // reduce = false (when ffn_down_splits(s) > 1) leaves the second layer's split
 // partials in the scratch, at *down_partials.
+// fold (combine_fold_counts(s) > 0 only): the combine folded into the second
+// layer, which then writes out instead of leaving Y or partials to a combine.
 hipError_t launch_ffn_layers(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                              const int32_t *offsets, const colibri_moe_experts_t &w, void *y_sorted, void *ws,
-                             bool reduce, hipStream_t st, const float **down_partials);
+                             bool reduce, hipStream_t st, const float **down_partials,
+                             const CombineFold *fold = nullptr);
 // launch_ffn_layers with int8 expert weights: decode sizes only (bf16, T <= 64).
 hipError_t launch_ffn_layers_q8(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,
                                 const int32_t *offsets, const colibri_moe_experts_q8_t &w, void *y_sorted, void *ws,

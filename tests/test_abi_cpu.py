@@ -338,6 +338,15 @@ def test_layer_ex_checks(lib):
     assert layer_ex_call(lib, s, opts_c(residual=fake(30) + 8)) == moe.COLIBRI_ERR_INVALID_ARG
     assert layer_ex_call(lib, s, opts_c(shared=sh, shared_h=-64)) == moe.COLIBRI_ERR_UNSUPPORTED
     assert layer_ex_call(lib, s, opts_c(shared=sh, shared_h=100)) == moe.COLIBRI_ERR_UNSUPPORTED
+    for bad in (-1, 3):  # colibri_combine_t
+        o = opts_c()
+        o.combine = bad
+        assert layer_ex_call(lib, s, o) == moe.COLIBRI_ERR_UNSUPPORTED
+        assert lib.colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(o)) == 0
+    o = opts_c()
+    o.combine = moe.COMBINE["separate"]
+    assert lib.colibri_moe_workspace_size_ex(ctypes.byref(s), ctypes.byref(o)) == \
+        lib.colibri_moe_workspace_size(ctypes.byref(s))
     # the shared expert is checked like the routed ones (SwiGLU: W1, W3, W2 and no biases)
     for bad, code in ((moe._Experts(None, fake(8), fake(9), None, None), moe.COLIBRI_ERR_INVALID_ARG),
                       (moe._Experts(fake(7), None, fake(9), None, None), moe.COLIBRI_ERR_INVALID_ARG),
