@@ -56,6 +56,7 @@ constexpr int kCus = kXcds * kCusPerXcd;
 
 struct Tile {
     int e, row0, rows, n0, split, S;  // S: K splits of this tile
+    int tpos, ntail;                  // tail split: this tile's place among the ntail tail tiles, else -1
 };
 
 // Row tiles of expert e.  Two rules, both giving every tile at most BM rows:
@@ -119,15 +120,28 @@ __device__ __forceinline__ TileTable tile_table(const int32_t *__restrict__ offs
     return tt;
 }
 
-// Tiles that run with the whole K range: all of them, or -- with a tail
-// split, when the tiles fill some rounds of one workgroup per CU plus a last
-// round of at most half the CUs -- the full rounds, and the last round's
-// tiles run as two K halves (twice as many half-length workgroups, so the
-// last round takes about half as long).
-__device__ __forceinline__ int whole_tiles(int total, int S, bool tail_split) {
-    if (!tail_split || S != 1 || total <= kCus) return total;
+// Tail split: tiles fill some rounds of one workgroup per CU and a last,
+// partial round.  The full rounds run whole; the last round's tail tiles run
+// as f K parts each (f * tail <= kCus, so the parts take one round of about
+// 1/f the length), f = the largest of 2 .. kTailMax that fits and leaves each
+// part at least 4 k-tiles; a tail of more than half the CUs runs whole.  The
+// parts write fp32 partials [part][tail tile][tile row][tile column] and
+// tail_reduce_kernel adds them.  Both kernels derive the plan from the actual
+// tile count.
+constexpr int kTailMax = 4;
+struct TailPlan {
+    int F, f;  // tiles that run whole; K parts of each tail tile (1: none)
+};
+__host__ __device__ __forceinline__ TailPlan tail_plan(int total, int kts, bool tail_split) {
+    TailPlan p{total, 1};
+    if (!tail_split || total <= kCus) return p;
     const int tail = total % kCus;
-    return (tail > 0 && 2 * tail <= kCus) ? total - tail : total;
+    if (tail == 0) return p;
+    int f = kCus / tail;
+    f = f < kTailMax ? f : kTailMax;
+    while (f > 1 && kts / f < 4) --f;
+    if (f > 1) p = {total - tail, f};
+    return p;
 }
 
 // Logical tile L -> expert, row range and first column.  Inside an expert,
@@ -160,14 +174,15 @@ __device__ __forceinline__ void tile_at(const TileTable &tt, int E, int NT, int 
 // for the worst case).
 template <int BMB, int BM, int BN>
 __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets, int E, int A, int NT, int S,
-                                            bool tail_split, int b, Tile &t) {
+                                            bool tail_split, int kts, int b, Tile &t) {
     const TileTable tt = tile_table<BMB, BM>(offsets, E, A, NT);
     const int total = tt.total;
-    const int F = whole_tiles(total, S, tail_split);
-    if (b >= (S > 1 ? total * S : F + 2 * (total - F))) return false;
+    const TailPlan tp = tail_plan(total, kts, tail_split && S == 1);
+    if (b >= (S > 1 ? total * S : tp.F + tp.f * (total - tp.F))) return false;
     // logical tiles [base, base + cnt), SS splits each; blocks bb = 0 .. cnt * SS - 1
-    int base = 0, cnt = S == 1 ? F : total, SS = S, bb = b;
-    if (S == 1 && b >= F) base = F, cnt = total - F, SS = 2, bb = b - F;  // F is a multiple of 8
+    int base = 0, cnt = S == 1 ? tp.F : total, SS = S, bb = b;
+    const bool tail = S == 1 && b >= tp.F;
+    if (tail) base = tp.F, cnt = total - tp.F, SS = tp.f, bb = b - tp.F;  // F is a multiple of 8
     // keep consecutive logical indices on one XCD: block b runs on XCD b % 8;
     // the index is split-major, so one XCD works on one K range of neighbouring tiles
     const int xcd = bb % kXcds, i = bb / kXcds;
@@ -175,11 +190,12 @@ __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets,
     const int LS = xcd * q + min(xcd, r) + i;
     t.split = LS / cnt;
     t.S = SS;
+    t.tpos = tail ? LS - t.split * cnt : -1;
+    t.ntail = tail ? cnt : 0;
     tile_at<BN>(tt, E, NT, base + LS - t.split * cnt, t);
     return true;
 }
 
-// f(integral_constant<int, n>) for the runtime n in [0, N] (larger n: N)
 template <int N, class F>
 __device__ __forceinline__ void with_live_count(int n, F &&f) {
     if constexpr (N > 0) {
@@ -427,7 +443,7 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     const int wm = w / WN, wn = w % WN;
 
     Tile tl;
-    if (!locate_tile<BMB, BM, BNC>(offsets, E, 2 * T, NT, S, tail_split != 0, blockIdx.x, tl))
+    if (!locate_tile<BMB, BM, BNC>(offsets, E, 2 * T, NT, S, tail_split != 0, K / BK, blockIdx.x, tl))
         return;  // uniform per block
     const int e = __builtin_amdgcn_readfirstlane(tl.e);
     const int row0 = __builtin_amdgcn_readfirstlane(tl.row0);
@@ -720,11 +736,17 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     __syncthreads();
 
     // ---- K split: the fp32 partial sums go to part[split][row][col] (SwiGLU: the
-    // W3 products at col + N); a later kernel adds the splits and applies the epilogue
+    // W3 products at col + N), a tail tile's to part[part][tail tile][tile row][tile
+    // column] (SwiGLU: W3 at + BNC); a later kernel adds them and applies the epilogue
     // 32x32 accumulator layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4, column l%32
     if (SK > 1) {
         constexpr int NC = DUAL ? 2 : 1;
-        float *pb = part + ((size_t)split * 2 * T + row0) * (size_t)(NC * N);
+        const int tpos = __builtin_amdgcn_readfirstlane(tl.tpos);
+        const int RW = tpos >= 0 ? NC * BNC : NC * N;  // floats per partial row
+        const int WO = tpos >= 0 ? BNC : N;            // SwiGLU: offset of the W3 products
+        const int c0 = tpos >= 0 ? n0 : 0;             // first column of a partial row
+        float *pb = tpos >= 0 ? part + ((size_t)split * tl.ntail + tpos) * BM * (size_t)RW
+                              : part + ((size_t)split * 2 * T + row0) * (size_t)RW;
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
             if (i >= live_sm) break;
@@ -736,9 +758,9 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
                 for (int r = 0; r < 16; ++r) {
                     const int rl = wrow + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                     if (rl >= rows) continue;
-                    float *dst = pb + (size_t)rl * (NC * N) + n;
+                    float *dst = pb + (size_t)rl * RW + (n - c0);
                     dst[0] = acc[0][i][j][r];
-                    if (DUAL) dst[N] = acc[NB - 1][i][j][r];
+                    if (DUAL) dst[WO] = acc[NB - 1][i][j][r];
                 }
             }
         }
@@ -782,48 +804,50 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
     if (folded) fold_combine<NW + BLD, BNC>(fold, C, part, T, E, N, NT, n0, row0, rows, SK, lds);
 }
 
-// Tail split, second half: the tiles of the last round were run as two K
-// halves into part[0..1][row][col] (SwiGLU: W3 products at col + N); the halves
-// are added in order (0 + half 0 + half 1, as the split reduce does), the
-// epilogue applied and the bf16 tile stored.  Block b: tail tile b / RB, tile
-// rows [(b % RB) RPB, +RPB); one thread per 4 columns of one row.
+// Tail split, second half: the tail tiles (see tail_plan) ran as f K parts
+// into part[part][tail tile][tile row][tile column] (SwiGLU: W3 products at
+// + BNC); the parts are added in order (0 + part 0 + part 1 + ..., as the
+// split reduce does), the epilogue applied and the bf16 tile stored.  Block
+// b: tail tile b / RB, tile rows [(b % RB) RPB, +RPB); one thread per 4
+// columns of one row.
 template <int BMB, int BM, int BNC>
 struct TailReduceGrid {
     static constexpr int Q = BNC / 4;                  // 4-column groups per tile row
     static constexpr int RPB = 256 / Q;                // tile rows per block
     static constexpr int RB = (BM + RPB - 1) / RPB;    // blocks per tile
-    static constexpr int blocks = (kCus / 2) * RB;     // at most kCus / 2 tail tiles
+    static constexpr int blocks = kCus * RB;           // fewer than kCus tail tiles
 };
 template <int BMB, int BM, int BNC, int EPI>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(const float *__restrict__ part, int T,
-                                                          const int32_t *__restrict__ offsets, int E, int NT,
+                                                          const int32_t *__restrict__ offsets, int E, int NT, int kts,
                                                           const uint16_t *__restrict__ bias, uint16_t *__restrict__ C,
                                                           int N) {
     using G = TailReduceGrid<BMB, BM, BNC>;
     static_assert(256 % G::Q == 0, "whole rows per block");
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    const int NC = DUAL ? 2 * N : N;
+    constexpr int RW = (DUAL ? 2 : 1) * BNC;  // floats per partial row
     const int tile = blockIdx.x / G::RB, rb = blockIdx.x % G::RB;
     const TileTable tt = tile_table<BMB, BM>(offsets, E, 2 * T, NT);
-    const int F = whole_tiles(tt.total, 1, true);
-    if (tile >= tt.total - F) return;  // uniform per block
+    const TailPlan tp = tail_plan(tt.total, kts, true);
+    const int ntail = tt.total - tp.F;
+    if (tp.f == 1 || tile >= ntail) return;  // uniform per block
     Tile tl;
-    tile_at<BNC>(tt, E, NT, F + tile, tl);
-    const int rl = rb * G::RPB + (int)threadIdx.x / G::Q, n = tl.n0 + ((int)threadIdx.x % G::Q) * 4;
+    tile_at<BNC>(tt, E, NT, tp.F + tile, tl);
+    const int rl = rb * G::RPB + (int)threadIdx.x / G::Q, cq = ((int)threadIdx.x % G::Q) * 4;
+    const int n = tl.n0 + cq;
     if (rl >= tl.rows || n >= N) return;
-    const size_t half = (size_t)2 * T * NC;
-    const float *src = part + (size_t)(tl.row0 + rl) * NC + n;
-    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(src), a1 = *reinterpret_cast<const f32x4 *>(src + half);
-    f32x4 b0 = {0.0f, 0.0f, 0.0f, 0.0f}, b1 = b0;
-    if (DUAL) {
-        b0 = *reinterpret_cast<const f32x4 *>(src + N);
-        b1 = *reinterpret_cast<const f32x4 *>(src + half + N);
-    }
-    float u[4], v[4];
+    const size_t pstride = (size_t)ntail * BM * RW;
+    const float *src = part + ((size_t)tile * BM + rl) * RW + cq;
+    float u[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p = 0; p < tp.f; ++p) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(src + p * pstride);
+        f32x4 b2 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (DUAL) b2 = *reinterpret_cast<const f32x4 *>(src + p * pstride + BNC);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        u[c] = (0.0f + a0[c]) + a1[c];
-        v[c] = (0.0f + b0[c]) + b1[c];
+        for (int c = 0; c < 4; ++c) {
+            u[c] += a[c];
+            v[c] += b2[c];
+        }
     }
     store_epilogue<EPI, 4>(C + (size_t)(tl.row0 + rl) * N + n, u, v, bias, tl.e, N, n);
 }
@@ -874,15 +898,14 @@ GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up) {
             if (us < best_cost - 1e-9) best_cost = us, best = {mid, BMB, (int)BNC, (int)S, false};
         }
     }
-    // First layer, no K split: when the expected tiles fill whole rounds of one
-    // workgroup per CU plus a last round of at most half the CUs, that round's
-    // tiles run as two K halves (the kernel decides from the actual tile count;
-    // the halves' sums go through the partials and a small reduce).
-    if (up && best.S == 1) {
+    // No K split: when the expected tiles fill whole rounds of one workgroup per
+    // CU plus a last round of at most half the CUs, that round's tiles run as
+    // K parts (tail_plan; the kernel decides from the actual tile count, the
+    // parts' sums go through the partials and a small reduce).
+    if (best.S == 1) {
         const long NT = (N + best.BNC - 1) / best.BNC;
         const long tiles = std::max<long>(std::min<long>(s.E, A), (A + BMB - 1) / BMB) * NT;
-        const long tail = tiles % 256;
-        best.tail = KT >= 8 && tiles > 256 && tail > 0 && 2 * tail <= 256;  // halves of >= 4 k-tiles
+        best.tail = tiles <= (1L << 30) && tail_plan((int)tiles, (int)KT, true).f > 1;
     }
     return best;
 }
@@ -896,8 +919,12 @@ hipError_t launch_shape(bool gather, const colibri_moe_shape_t &s, const void *A
     constexpr int BNC = EPI == EPI_SWIGLU ? BN / 2 : BN;
     const int A = 2 * s.T;
     const int NT = (N + BNC - 1) / BNC;
-    const int mtiles = (A + BMB - 1) / BMB + std::min(s.E, A);  // bound on the row tiles of all experts
-    const dim3 grid(mtiles * NT * (tail ? 2 : S));
+    // bound on the row tiles of all experts: sum over live experts of ceil(rows / H),
+    // H = BM for the pair tiling (BMB = 256), else BMB
+    constexpr int H = BMB == 256 ? BM : BMB;
+    const int mtiles = (int)std::min<long>(A, ((long)A + (long)(H - 1) * std::min(s.E, A)) / H);
+    // a tail split adds fewer than kCus blocks (f * tail <= kCus)
+    const dim3 grid(S > 1 ? mtiles * NT * S : mtiles * NT + (tail ? kCus : 0));
     constexpr int threads = (2 * 4 + BLD) * kWave;
     const CombineFold cf = fold ? *fold : CombineFold{};
     if (gather)
@@ -911,7 +938,7 @@ hipError_t launch_shape(bool gather, const colibri_moe_shape_t &s, const void *A
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && tail) {
         constexpr int blocks = TailReduceGrid<BMB, BM, BNC>::blocks;
-        tail_reduce_kernel<BMB, BM, BNC, EPI><<<blocks, 256, 0, st>>>(part, s.T, offsets, s.E, NT,
+        tail_reduce_kernel<BMB, BM, BNC, EPI><<<blocks, 256, 0, st>>>(part, s.T, offsets, s.E, NT, K / kBK,
                                                                       (const uint16_t *)bias, (uint16_t *)C, N);
         e = hipGetLastError();
     }
@@ -950,10 +977,11 @@ int gemm_splits(const colibri_moe_shape_t &s, bool up) {
 size_t gemm_scratch_bytes(const colibri_moe_shape_t &s, bool up) {
     if (s.dtype != COLIBRI_BF16 || s.T <= 0) return 0;
     const GemmPlan p = gemm_plan(s, up);
-    const int S = p.tail ? 2 : p.S;
-    if (S <= 1) return 0;
     const bool dual = up && s.act == COLIBRI_ACT_SWIGLU;
-    return align256((size_t)S * 2 * s.T * (size_t)(up ? s.h : s.d) * (dual ? 2 : 1) * 4);
+    if (p.tail)  // fewer than kCus tail tiles' parts: [part][tail tile][BM][(dual ? 2 : 1) BNC]
+        return align256((size_t)kCus * (p.mid ? 192 : 320) * (size_t)p.BNC * (dual ? 2 : 1) * 4);
+    if (p.S <= 1) return 0;
+    return align256((size_t)p.S * 2 * s.T * (size_t)(up ? s.h : s.d) * (dual ? 2 : 1) * 4);
 }
 
 hipError_t launch_gemm_up(const colibri_moe_shape_t &s, const void *x_rows, const int32_t *sorted_assign,

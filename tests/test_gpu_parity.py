@@ -277,11 +277,14 @@ def test_ffn_ragged_columns_and_presorted_rows(dt):
         G.assert_close(y, y_ref, dt, f"y_sorted gather={gather}", scale=sc[0])
 
 
-# first layers whose tiles fill a round of one workgroup per CU plus a last
-# round of at most half the CUs (17 or 33 column tiles per expert): that round's
-# tiles run as two K halves and a small kernel adds the halves; "skew" routes
-# every token to experts 0 and 1, so the kernel finds too few tiles to split
+# first layers whose tiles fill whole rounds of one workgroup per CU plus a
+# last round of at most half the CUs: that round's tiles run as f K parts and a
+# small kernel adds the parts.  f = 2 (272 and 528 tiles), f = 3 (328 tiles:
+# 72 in the last round), f = 4 (808 tiles: 40 in the last round); "skew"
+# routes every token to experts 0 and 1, so the kernel finds too few tiles to
+# split
 TAIL_CASES = [(80, 16, 512, 2176, "swiglu", None), (100, 8, 512, 8448, "gelu", None),
+              (100, 8, 768, 5248, "swiglu", None), (100, 8, 1024, 12928, "swiglu", None),
               (400, 16, 512, 2176, "swiglu", "skew")]
 
 
