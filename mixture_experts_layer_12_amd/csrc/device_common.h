@@ -72,10 +72,34 @@ __device__ __forceinline__ float silu_bf16out(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
+// GELU for results stored in bf16: erf from Hastings' rational approximation
+// (Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26; absolute
+// error at most 1.5e-7), with 1 + erf(z / sqrt 2) formed as q or 2 - q from
+// q = erfc(|z| / sqrt 2), so negative z loses nothing to cancellation; one
+// v_rcp_f32 and one v_exp_f32, about half the instructions of the library
+// erff and far below the 2^-9 rounding step of the bf16 store.
+__device__ __forceinline__ float gelu_bf16out(float z) {
+    constexpr double kInvSqrt2 = 0.70710678118654752;
+    constexpr float p = (float)(0.3275911 * kInvSqrt2);  // t = 1 / (1 + p x), x = |z| / sqrt 2
+    constexpr float a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f, a4 = -1.453152027f,
+                    a5 = 1.061405429f;
+    constexpr float c = -0.72134752044448170f;  // exp(-x^2) = 2^(c z^2), c = -log2(e) / 2
+    const float t = __builtin_amdgcn_rcpf(fmaf(p, fabsf(z), 1.0f));
+    const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+    const float q = poly * __builtin_amdgcn_exp2f(c * z * z);  // erfc(|z| / sqrt 2)
+    return 0.5f * z * (z >= 0.0f ? 2.0f - q : q);
+}
+
 template <int ACT>
 __device__ __forceinline__ float apply_act(float z) {
     if (ACT == ACT_RELU) return z > 0.0f ? z : 0.0f;
     return gelu_erf(z);
+}
+// the same for results stored in bf16
+template <int ACT>
+__device__ __forceinline__ float apply_act_bf16out(float z) {
+    if (ACT == ACT_RELU) return z > 0.0f ? z : 0.0f;
+    return gelu_bf16out(z);
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -14,8 +14,8 @@ template <int EPI>
 __device__ __forceinline__ float epi_value(float u, float v, const uint16_t *__restrict__ bias, int e, int N, int n) {
     if (EPI == EPI_SWIGLU) return silu_bf16out(u) * v;
     const float b = bias ? bf16_to_f32(bias[(size_t)e * N + n]) : 0.0f;
-    if (EPI == EPI_ACT_RELU) return apply_act<ACT_RELU>(u + b);
-    if (EPI == EPI_ACT_GELU) return apply_act<ACT_GELU>(u + b);
+    if (EPI == EPI_ACT_RELU) return apply_act_bf16out<ACT_RELU>(u + b);
+    if (EPI == EPI_ACT_GELU) return apply_act_bf16out<ACT_GELU>(u + b);
     return u + b;
 }
 

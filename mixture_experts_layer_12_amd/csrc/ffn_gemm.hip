@@ -785,8 +785,8 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
                 const int rl = wrow + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 float v;
                 if (EPI == EPI_SWIGLU) v = silu_bf16out(acc[0][i][j][r]) * acc[NB - 1][i][j][r];
-                else if (EPI == EPI_ACT_RELU) v = apply_act<ACT_RELU>(acc[0][i][j][r] + bv);
-                else if (EPI == EPI_ACT_GELU) v = apply_act<ACT_GELU>(acc[0][i][j][r] + bv);
+                else if (EPI == EPI_ACT_RELU) v = apply_act_bf16out<ACT_RELU>(acc[0][i][j][r] + bv);
+                else if (EPI == EPI_ACT_GELU) v = apply_act_bf16out<ACT_GELU>(acc[0][i][j][r] + bv);
                 else v = acc[0][i][j][r] + bv;
                 Cs[rl * BNC + cl] = (uint16_t)f32_to_bf16_bits(v);
             }
