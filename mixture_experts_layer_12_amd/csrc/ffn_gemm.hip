@@ -183,11 +183,23 @@ __device__ __forceinline__ bool locate_tile(const int32_t *__restrict__ offsets,
     int base = 0, cnt = S == 1 ? tp.F : total, SS = S, bb = b;
     const bool tail = S == 1 && b >= tp.F;
     if (tail) base = tp.F, cnt = total - tp.F, SS = tp.f, bb = b - tp.F;  // F is a multiple of 8
-    // keep consecutive logical indices on one XCD: block b runs on XCD b % 8;
-    // the index is split-major, so one XCD works on one K range of neighbouring tiles
+    // Block b runs on XCD b % 8.  Whole rounds of kCus blocks: XCD x takes the
+    // chunks x, x + 8, x + 16, ... of kCusPerXcd consecutive logical indices,
+    // so neighbouring tiles (a group sharing weight panels and token rows) run
+    // side by side on one XCD while every XCD gets chunks of every expert (one
+    // contiguous range per XCD gave each XCD one expert of the Mixtral-shaped
+    // prefill, and the XCD with the most rows set the kernel's time); the
+    // last, partial round is cut into 8 contiguous ranges.  The index is
+    // split-major, so a chunk is one K range of neighbouring tiles.
     const int xcd = bb % kXcds, i = bb / kXcds;
-    const int q = cnt * SS / kXcds, r = cnt * SS % kXcds;
-    const int LS = xcd * q + min(xcd, r) + i;
+    const int n = cnt * SS, nfull = n / kCus;
+    int LS;
+    if (i < nfull * kCusPerXcd) {
+        LS = (i / kCusPerXcd) * kCus + xcd * kCusPerXcd + i % kCusPerXcd;
+    } else {
+        const int rem = n - nfull * kCus, i2 = i - nfull * kCusPerXcd;
+        LS = nfull * kCus + xcd * (rem / kXcds) + min(xcd, rem % kXcds) + i2;
+    }
     t.split = LS / cnt;
     t.S = SS;
     t.tpos = tail ? LS - t.split * cnt : -1;
