@@ -23,15 +23,41 @@
 namespace colibri {
 namespace {
 
+// A thread takes kCombineUnroll vectors, gridDim * blockDim apart, per pass
+// and issues the loads of all of them before any arithmetic, so each thread
+// keeps several rows' loads in flight (one vector per thread left the kernel
+// bound by the latency of its dependent index and row loads).
+constexpr int kCombineUnroll = 4;
+
 template <typename TE>
 __global__ __launch_bounds__(256) void combine_kernel(const TE *__restrict__ y, const int32_t *__restrict__ pos,
                                                       const float *__restrict__ gate, TE *out, int T, int d,
                                                       const TE *shared, const TE *residual, SharedPartials sp) {
-    constexpr int VEC = 16 / sizeof(TE);
+    constexpr int VEC = 16 / sizeof(TE), U = kCombineUnroll;
     const int vpr = d / VEC;  // vectors per row
     const size_t total = (size_t)T * vpr;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x)
-        combine_rows_vec<TE>(y, pos, gate, out, T, d, shared, residual, sp, (int)(i / vpr), (int)(i % vpr) * VEC);
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    if (sp.part) {  // the shared row is formed from its partials inside the finish: one vector at a time
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride)
+            combine_rows_vec<TE>(y, pos, gate, out, T, d, shared, residual, sp, (int)(i / vpr), (int)(i % vpr) * VEC);
+        return;
+    }
+    for (size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < total; i0 += U * stride) {
+        RowsVec r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = i0 + u * stride;
+            if (i < total)
+                rows_vec_load<TE>(r[u], y, pos, gate, T, d, shared, residual, (int)(i / vpr), (int)(i % vpr) * VEC);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = i0 + u * stride;
+            if (i < total)
+                rows_vec_finish<TE>(r[u], shared != nullptr, residual != nullptr, out, sp, d, (int)(i / vpr),
+                                    (int)(i % vpr) * VEC);
+        }
+    }
 }
 
 // Same combine, but each expert row Y[p] is first formed from the second
@@ -173,7 +199,8 @@ hipError_t launch_combine(const colibri_moe_shape_t &s, const void *y_sorted, co
                           const void *residual, SharedPartials sp) {
     const int vec = s.dtype == COLIBRI_F32 ? 4 : 8;
     const size_t total = (size_t)s.T * (s.d / vec);
-    const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
+    const size_t per_block = sp.part ? 256 : 256 * kCombineUnroll;  // vectors a block takes per pass
+    const int blocks = (int)std::min<size_t>((total + per_block - 1) / per_block, 8192);
     if (s.dtype == COLIBRI_F32)
         combine_kernel<float><<<blocks, 256, 0, st>>>((const float *)y_sorted, assign_pos, topk_gate, (float *)out,
                                                       s.T, s.d, (const float *)shared, (const float *)residual,
