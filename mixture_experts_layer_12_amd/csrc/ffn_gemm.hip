@@ -820,14 +820,17 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
 // into part[part][tail tile][tile row][tile column] (SwiGLU: W3 products at
 // + BNC); the parts are added in order (0 + part 0 + part 1 + ..., as the
 // split reduce does), the epilogue applied and the bf16 tile stored.  Block
-// b: tail tile b / RB, tile rows [(b % RB) RPB, +RPB); one thread per 4
-// columns of one row.
+// b: tail tile b / RB, tile rows [(b % RB) RPB PR, +RPB PR); a thread takes 4
+// columns of PR rows RPB apart, with the PR rows' loads of a part in flight
+// together.  The grid covers the largest possible tail; without a tail every
+// block leaves at once, so few blocks keep that case cheap.
 template <int BMB, int BM, int BNC>
 struct TailReduceGrid {
-    static constexpr int Q = BNC / 4;                  // 4-column groups per tile row
-    static constexpr int RPB = 256 / Q;                // tile rows per block
-    static constexpr int RB = (BM + RPB - 1) / RPB;    // blocks per tile
-    static constexpr int blocks = kCus * RB;           // fewer than kCus tail tiles
+    static constexpr int Q = BNC / 4;                       // 4-column groups per tile row
+    static constexpr int RPB = 256 / Q;                     // tile rows per pass of a block
+    static constexpr int PR = 4;                            // passes (rows per thread)
+    static constexpr int RB = (BM + RPB * PR - 1) / (RPB * PR);  // blocks per tile
+    static constexpr int blocks = kCus * RB;                // fewer than kCus tail tiles
 };
 template <int BMB, int BM, int BNC, int EPI>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(const float *__restrict__ part, int T,
@@ -835,9 +838,10 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float *__restric
                                                           const uint16_t *__restrict__ bias, uint16_t *__restrict__ C,
                                                           int N) {
     using G = TailReduceGrid<BMB, BM, BNC>;
-    static_assert(256 % G::Q == 0, "whole rows per block");
+    static_assert(256 % G::Q == 0, "whole rows per pass");
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr int RW = (DUAL ? 2 : 1) * BNC;  // floats per partial row
+    constexpr int PR = G::PR;
     const int tile = blockIdx.x / G::RB, rb = blockIdx.x % G::RB;
     const TileTable tt = tile_table<BMB, BM>(offsets, E, 2 * T, NT);
     const TailPlan tp = tail_plan(tt.total, kts, true);
@@ -845,23 +849,37 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float *__restric
     if (tp.f == 1 || tile >= ntail) return;  // uniform per block
     Tile tl;
     tile_at<BNC>(tt, E, NT, tp.F + tile, tl);
-    const int rl = rb * G::RPB + (int)threadIdx.x / G::Q, cq = ((int)threadIdx.x % G::Q) * 4;
+    const int r0 = rb * G::RPB * PR + (int)threadIdx.x / G::Q, cq = ((int)threadIdx.x % G::Q) * 4;
     const int n = tl.n0 + cq;
-    if (rl >= tl.rows || n >= N) return;
+    if (r0 >= tl.rows || n >= N) return;
     const size_t pstride = (size_t)ntail * BM * RW;
-    const float *src = part + ((size_t)tile * BM + rl) * RW + cq;
-    float u[4] = {0.0f, 0.0f, 0.0f, 0.0f}, v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p = 0; p < tp.f; ++p) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(src + p * pstride);
-        f32x4 b2 = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (DUAL) b2 = *reinterpret_cast<const f32x4 *>(src + p * pstride + BNC);
+    const float *src = part + ((size_t)tile * BM + r0) * RW + cq;
+    float u[PR][4], v[PR][4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            u[c] += a[c];
-            v[c] += b2[c];
+    for (int k = 0; k < PR; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) u[k][c] = v[k][c] = 0.0f;
+    for (int p = 0; p < tp.f; ++p) {
+        f32x4 a[PR], b2[PR];
+#pragma unroll
+        for (int k = 0; k < PR; ++k) {  // rows past the tile read its row r0 (in bounds) and are not stored
+            const float *q = src + p * pstride + (r0 + k * G::RPB < tl.rows ? (size_t)k * G::RPB * RW : 0);
+            a[k] = *reinterpret_cast<const f32x4 *>(q);
+            b2[k] = DUAL ? *reinterpret_cast<const f32x4 *>(q + BNC) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
+#pragma unroll
+        for (int k = 0; k < PR; ++k)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                u[k][c] += a[k][c];
+                v[k][c] += b2[k][c];
+            }
     }
-    store_epilogue<EPI, 4>(C + (size_t)(tl.row0 + rl) * N + n, u, v, bias, tl.e, N, n);
+#pragma unroll
+    for (int k = 0; k < PR; ++k) {
+        const int rl = r0 + k * G::RPB;
+        if (rl < tl.rows) store_epilogue<EPI, 4>(C + (size_t)(tl.row0 + rl) * N + n, u[k], v[k], bias, tl.e, N, n);
+    }
 }
 
 // Tile shapes, BK = 64, one workgroup per CU:
@@ -914,10 +932,16 @@ GemmPlan gemm_plan(const colibri_moe_shape_t &s, bool up) {
     // CU plus a last round of at most half the CUs, that round's tiles run as
     // K parts (tail_plan; the kernel decides from the actual tile count, the
     // parts' sums go through the partials and a small reduce).
+    // A first layer of a prefill-sized batch (at least 4096 rows) always allows
+    // the split: a skewed routing cuts the experts into other row tiles than
+    // the even spread the estimate assumes (a Zipf-skewed 16-expert layer at
+    // T = 8192: 1140 tiles, where 1280 were expected), and the kernel finds
+    // the actual tail itself.
     if (best.S == 1) {
         const long NT = (N + best.BNC - 1) / best.BNC;
         const long tiles = std::max<long>(std::min<long>(s.E, A), (A + BMB - 1) / BMB) * NT;
-        best.tail = tiles <= (1L << 30) && tail_plan((int)tiles, (int)KT, true).f > 1;
+        best.tail = tiles <= (1L << 30) &&
+                    (tail_plan((int)tiles, (int)KT, true).f > 1 || (up && !mid && A >= 4096 && KT >= 8));
     }
     return best;
 }
