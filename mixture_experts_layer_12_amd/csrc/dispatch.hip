@@ -96,9 +96,17 @@ __global__ __launch_bounds__(kScanParts *kWave) void dispatch_scan_kernel(const 
     const int part = threadIdx.x / kWave;
     const int L = ceil_div(nchunks, kScanParts);
     const int c0 = min(nchunks, part * L), c1 = min(nchunks, c0 + L);
+    // up to kScanRegs chunk counts per thread are loaded once, all in flight
+    // (one after another the loads left the scan bound by their latency)
+    constexpr int kScanRegs = 32;
+    int v[kScanRegs];
+#pragma unroll
+    for (int q = 0; q < kScanRegs; ++q) v[q] = (e < E && c0 + q < c1) ? hist[(size_t)(c0 + q) * E + e] : 0;
     int sum = 0;
+#pragma unroll
+    for (int q = 0; q < kScanRegs; ++q) sum += v[q];
     if (e < E)
-        for (int c = c0; c < c1; ++c) sum += hist[(size_t)c * E + e];
+        for (int c = c0 + kScanRegs; c < c1; ++c) sum += hist[(size_t)c * E + e];
     psum[part][e] = sum;
     __syncthreads();
     if (part == 0) {
@@ -125,7 +133,12 @@ __global__ __launch_bounds__(kScanParts *kWave) void dispatch_scan_kernel(const 
     __syncthreads();
     if (e < E) {
         int run = pbase[part][e];
-        for (int c = c0; c < c1; ++c) {
+#pragma unroll
+        for (int q = 0; q < kScanRegs; ++q) {
+            if (c0 + q < c1) base[(size_t)(c0 + q) * E + e] = run;
+            run += v[q];
+        }
+        for (int c = c0 + kScanRegs; c < c1; ++c) {
             base[(size_t)c * E + e] = run;
             run += hist[(size_t)c * E + e];
         }
