@@ -323,6 +323,44 @@ def test_ffn_tail_split_full_size():
     G.assert_bf16_close(G.host(y)[pos], y_ref, "tail split, full size")
 
 
+def _random_ffn_cases(n=10, seed=2026):
+    """Seeded random grouped-GEMM shapes (T > 64, so the tiled GEMM path runs):
+    E in [2, 64], d and h multiples of 64, all three activations, uniform or
+    Zipf-skewed routing; tile counts land anywhere relative to the CU rounds,
+    so whole rounds, remainders and tail splits all occur.  The oracle's work
+    (2T rows of the full FFN) stays below about 4e9 multiply-adds per case."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(rng.integers(65, 2500))
+        E = int(rng.integers(2, 65))
+        d = 64 * int(rng.integers(1, 17))
+        h = 64 * int(rng.integers(1, 25))
+        act = ("relu", "gelu", "swiglu")[len(out) % 3]
+        skew = bool(rng.integers(0, 2))
+        if 2 * T * d * h * (3 if act == "swiglu" else 2) > 4e9:
+            continue
+        out.append((T, E, d, h, act, skew))
+    return out
+
+
+RANDOM_FFN_CASES = _random_ffn_cases()
+
+
+@pytest.mark.parametrize("T,E,d,h,act,skew", RANDOM_FFN_CASES,
+                         ids=[f"T{c[0]}-E{c[1]}-d{c[2]}-h{c[3]}-{c[4]}" + ("-zipf" if c[5] else "") for c in RANDOM_FFN_CASES])
+def test_ffn_random_shapes(T, E, d, h, act, skew):
+    """The grouped GEMM path on seeded random shapes against the oracle, every row."""
+    p = None
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        p = p / p.sum()
+    w, idx = small_ffn_case(act, gen.BF16, T=T, E=E, d=d, h=h, skew=p, seed=T + E + d + h)
+    for gather in (True, False):
+        y, y_ref = run_ffn(w, idx, act, gen.BF16, E=E, gather=gather)
+        G.assert_bf16_close(y, y_ref, f"random shape T={T} E={E} d={d} h={h} {act} gather={gather}")
+
+
 DECODE_CASES = [(1, 8, 256, 384, "swiglu"), (1, 2, 128, 320, "gelu"), (5, 8, 192, 256, "relu"),
                 (16, 4, 256, 320, "swiglu"), (33, 8, 128, 192, "gelu"), (64, 8, 256, 256, "swiglu"),
                 (64, 64, 64, 128, "relu"), (2, 16, 1024, 512, "swiglu")]
