@@ -597,17 +597,28 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
             f.a[i] = *(const lds_bf16x8 *)(L + a_row[i] + (((2 * ks + (lane >> 5)) ^ a_swz[i]) << 4));
         }
     };
-    auto mma = [&](const Frags &f, auto lv) {
+    // MFMAs of one k-step; copies [c0, c1) of k-tile ck into stage cs, if any,
+    // are placed after them one by one (copy c0 + m after MFMA m)
+    auto mma = [&](const Frags &f, auto lv, int c0 = 0, int c1 = 0, int cs = 0, int ck = 0) {
         constexpr int LV = decltype(lv)::value;
         const int nl = LV >= 0 ? LV : live_sm;
+        const int ck0 = ck * BK;
+        const uint16_t *cbk = b_base + (size_t)ck0 * N;
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
             if (i >= nl) break;  // uniform per wave
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int j = 0; j < SJ; ++j)
+                for (int j = 0; j < SJ; ++j) {
                     acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[b][j], acc[b][i][j], 0, 0, 0);
+                    if (LV >= 0 && c0 + (i * NB + b) * SJ + j < c1) copy_one(c0 + (i * NB + b) * SJ + j, cs, ck0, cbk);
+                }
+        }
+        if (LV >= 0) {
+            for (int m = c0 + (LV > 0 ? LV : 0) * NB * SJ; m < c1; ++m) copy_one(m, cs, ck0, cbk);
+        } else {
+            for (int m = c0; m < c1; ++m) copy_one(m, cs, ck0, cbk);
         }
         // Schedule the k-step as one MFMA, then one LDS read (of the next k-step's
         // operands, read before this step in the source), alternating for as long
@@ -626,14 +637,14 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
         }
     };
 
-    // The tile's last k-step with the copies of k-tile kt into stage s placed
-    // between its MFMAs (copy m after MFMA m): right after the barrier both waves
-    // of a SIMD issue their copies at the same time, and issued in one run they
-    // would leave the matrix unit idle meanwhile.
-    auto mma_issue = [&](const Frags &f, auto lv, int s, int kt) {
+    // The tile's last k-step with the copies [M0, M1) of k-tile kt into stage s
+    // placed between its MFMAs (copy M0 + m after MFMA m): right after the barrier
+    // both waves of a SIMD issue their copies at the same time, and issued in one
+    // run they would leave the matrix unit idle meanwhile.
+    auto mma_issue = [&](const Frags &f, auto lv, int s, int kt, auto m0, auto m1) {
         constexpr int LV = decltype(lv)::value;
         static_assert(LV >= 0, "compile-time live count");
-        constexpr int DPW_ = A_PW + B_PW;
+        constexpr int M0 = decltype(m0)::value, DPW_ = decltype(m1)::value;
         const int k0 = kt * BK;
         const uint16_t *bk = b_base + (size_t)k0 * N;
 #pragma unroll
@@ -643,19 +654,27 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
 #pragma unroll
                 for (int j = 0; j < SJ; ++j) {
                     acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[b][j], acc[b][i][j], 0, 0, 0);
-                    const int m = (i * NB + b) * SJ + j;  // a constant once the loops are unrolled
+                    const int m = M0 + (i * NB + b) * SJ + j;  // a constant once the loops are unrolled
                     if (m < DPW_) copy_one(m, s, k0, bk);
                 }
 #pragma unroll
-        for (int m = LV * NB * SJ; m < DPW_; ++m) copy_one(m, s, k0, bk);
+        for (int m = M0 + LV * NB * SJ; m < DPW_; ++m) copy_one(m, s, k0, bk);
     };
 
-    // ---- main loop over a ring of STAGES LDS stages.  The operands of k-step ks+1 are
+    // ---- main loop over a ring of two LDS stages.  The operands of k-step ks+1 are
     // read while k-step ks is multiplied; the workgroup barrier sits before the last
     // k-step of a tile, so the next tile's first reads overlap that step's MFMAs.
     // After the barrier every wave has finished reading tile kt (the barrier waits for
-    // outstanding LDS reads), so tile kt + STAGES is copied into its stage.  Copies past
-    // the last k-tile re-read it, so every wait covers the same number of copies.
+    // outstanding LDS reads), so tile kt + 2 is copied into its stage in two groups:
+    // its weight (B) copies between the MFMAs of tile kt's last k-step, its A copies
+    // between those of the first k-step of tile kt + 1.  Issued in one run, all
+    // copies of a wave queue behind each other in the memory pipeline while both
+    // waves of a SIMD wait to issue their next MFMA; in two runs the B copies, whose
+    // weights come from HBM, keep the longest lead (measured on the Mixtral-shaped
+    // prefill, A/B in one process: second layer 845 / 841 -> 807 / 806 us, first
+    // layer 1659 / 1645 -> 1661 / 1630 us; the Zipf-skewed layer 567 / 552 -> 551 /
+    // 547 and 311 / 305 -> 300 / 301 us).  Copies past the last k-tile re-read it.
+    static_assert(SPEC || STAGES == 2, "the split copy groups assume a ring of two stages");
     constexpr int KS = BK / 16;
     constexpr int DPW = A_PW + B_PW;
     // this block's K range: k-tiles [kt0, kt0 + KT) of the K / BK
@@ -675,18 +694,23 @@ __global__ __launch_bounds__((WM * WN + BLD) * kWave, WPE) void ffn_gemm_kernel(
         __syncthreads();                    // ... everyone's
         read_frags(0, A_BYTES, 0, f[0], lv);
         for (int kt = 0; kt < KT; ++kt) {
-            const int s = kt % STAGES;
+            const int s = kt & 1;
             const int so = s * STAGE_BYTES;
 #pragma unroll
             for (int ks = 0; ks + 1 < KS; ++ks) {
                 read_frags(so, so + A_BYTES, ks + 1, f[(ks + 1) & 1], lv);
-                mma(f[ks & 1], lv);
+                if (ks == 0 && kt > 0)
+                    mma(f[0], lv, 0, A_PW, s ^ 1, ktile(kt + 1));  // A copies of k-tile kt+1
+                else
+                    mma(f[ks & 1], lv);
             }
-            wait_vmcnt<(STAGES - 2) * DPW>();  // k-tile kt+1 has landed (this wave's copies)
-            __syncthreads();                    // ... everyone's; and k-tile kt is fully read
-            const int sn = ((kt + 1) % STAGES) * STAGE_BYTES;
+            wait_vmcnt<0>();  // k-tile kt+1 has landed (this wave's copies)
+            __syncthreads();  // ... everyone's; and k-tile kt is fully read
+            const int sn = (s ^ 1) * STAGE_BYTES;
             if (kt + 1 < KT) read_frags(sn, sn + A_BYTES, 0, f[0], lv);
-            mma_issue(f[(KS - 1) & 1], lv, s, ktile(kt + STAGES));  // refills stage s
+            // B copies of k-tile kt+2 into stage s
+            mma_issue(f[(KS - 1) & 1], lv, s, ktile(kt + 2), std::integral_constant<int, A_PW>{},
+                      std::integral_constant<int, DPW>{});
         }
     };
     // ---- SPEC: compute waves.  A stage kt & 1, B stage kt % BST.  Barrier P publishes
