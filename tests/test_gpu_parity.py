@@ -323,6 +323,21 @@ def test_ffn_tail_split_full_size():
     G.assert_bf16_close(G.host(y)[pos], y_ref, "tail split, full size")
 
 
+SHORT_K_CASES = [(256, 2, 64, 128, "swiglu"), (256, 2, 128, 64, "gelu"), (300, 2, 192, 320, "relu"),
+                 (256, 3, 64, 64, "swiglu")]
+
+
+@pytest.mark.parametrize("T,E,d,h,act", SHORT_K_CASES,
+                         ids=[f"T{c[0]}-E{c[1]}-d{c[2]}-h{c[3]}-{c[4]}" for c in SHORT_K_CASES])
+def test_ffn_big_tiles_short_k(T, E, d, h, act):
+    """The large-tile GEMM with K of 1, 2, 3 or 5 k-tiles of 64: the copies of the k-tiles past
+    the last one (which re-read it) and the first k-tiles' copies issued before the loop."""
+    w, idx = small_ffn_case(act, gen.BF16, T=T, E=E, d=d, h=h, seed=T + d + h)
+    for gather in (True, False):
+        y, y_ref = run_ffn(w, idx, act, gen.BF16, E=E, gather=gather)
+        G.assert_bf16_close(y, y_ref, f"short K d={d} h={h} gather={gather}")
+
+
 def _random_ffn_cases(n=10, seed=2026):
     """Seeded random grouped-GEMM shapes (T > 64, so the tiled GEMM path runs):
     E in [2, 64], d and h multiples of 64, all three activations, uniform or
