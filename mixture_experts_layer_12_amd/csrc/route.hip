@@ -39,7 +39,12 @@ namespace {
 constexpr int kRouteSmallT = COLIBRI_ROUTE_SMALL_T;
 constexpr int kRouteMaxW = 16;   // waves sharing one token group (split of the k-steps)
 constexpr int kFusedWaves = 16;  // waves of the fused route + dispatch workgroup
-constexpr int kFusedGroups = 2;  // token groups up to which routing and dispatch are fused
+constexpr int kFusedGroups = 2;  // token groups up to which fp32 routing and dispatch are fused
+// bf16 (MFMA router): one 16-token tile.  At 17..32 tokens the two launches,
+// whose router spreads each tile's k-steps over more waves, were faster
+// (Mixtral-shaped T = 24 / 32: 449.1 -> 447.1, 452.4 -> 449.7 us per layer;
+// 8-expert T = 32: 94.0 -> 93.1 us).
+constexpr int kFusedGroupsMfma = 1;
 
 template <int EP> constexpr int route_tw() { return EP == 2 ? 32 : 16; }  // tokens per group (a multiple of 64 / EP)
 
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(mfma_maxw<EP>() * kWave) void route_mfma_kernel(
     mfma_select<EP>(red, W, w, b_r, T, E, t0, topk_idx, topk_gate, logits, nullptr, gate_mode);
 }
 
-// Routing and dispatch in one workgroup of 16 waves for at most kFusedGroups
+// Routing and dispatch in one workgroup of 16 waves for at most kFusedGroupsMfma
 // tiles of 16 tokens; W waves per tile as in route_mfma_kernel, so the logits
 // are identical.
 template <int EP>
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(kFusedWaves *kWave) void route_dispatch_mfma_kernel
     constexpr int MW = mfma_maxw<EP>();
     __shared__ __align__(16) uint16_t wblk[MW][32 * EP];
     __shared__ float red[MW][16][EP];
-    __shared__ int32_t sidx[2 * kFusedGroups * 16];
+    __shared__ int32_t sidx[2 * kFusedGroupsMfma * 16];
     __shared__ DispatchShared<kFusedWaves> dsh;
     const int w = threadIdx.x / kWave;
     const int gi = w / W, wib = w % W;
@@ -509,7 +514,7 @@ __global__ __launch_bounds__(kFusedWaves *kWave) void route_dispatch_mfma_kernel
 
 // Waves per 16-token tile of the MFMA router: a power of two up to
 // mfma_maxw<EP>, each wave keeping at least 4 k-steps of 32 rows, G W <=
-// kMfmaMaxWaves in all; with at most kFusedGroups tiles also G W <= the fused
+// kMfmaMaxWaves in all; with at most kFusedGroupsMfma tiles also G W <= the fused
 // kernel's wave slots, min(kFusedWaves, mfma_maxw<EP>) (it uses the same W, so
 // both paths form every logit identically).
 #ifndef COLIBRI_MFMA_MAX_WAVES
@@ -522,7 +527,7 @@ inline int mfma_waves(int T, int d, int EP) {
     const int maxw = EP == 64 ? mfma_maxw<64>() : mfma_maxw<32>();
     int W = 1;
     const int fused = kFusedWaves < maxw ? kFusedWaves : maxw;
-    while (W < maxw && nks >= 8 * W && G * W * 2 <= kMfmaMaxWaves && (G > kFusedGroups || G * W * 2 <= fused))
+    while (W < maxw && nks >= 8 * W && G * W * 2 <= kMfmaMaxWaves && (G > kFusedGroupsMfma || G * W * 2 <= fused))
         W *= 2;
     return W;
 }
@@ -680,10 +685,12 @@ hipError_t launch_route(const colibri_moe_shape_t &s, const void *x, const void 
     return launch_t<uint16_t>(s, x, w_r, b_r, topk_idx, topk_gate, logits, gate_mode, st);
 }
 
-// at most kFusedGroups token groups (T <= 32; fp32 with E <= 2: T <= 64)
+// bf16: one 16-token tile (T <= 16); fp32: at most kFusedGroups token groups
+// (T <= 32; with E <= 2: T <= 64)
 bool route_dispatch_fusable(const colibri_moe_shape_t &s) {
     if (s.T <= 0) return false;
-    const int TW = (s.dtype == COLIBRI_F32 && s.E <= 2) ? 32 : 16;
+    if (s.dtype != COLIBRI_F32) return ceil_div(s.T, 16) <= kFusedGroupsMfma;
+    const int TW = s.E <= 2 ? 32 : 16;
     return ceil_div(s.T, TW) <= kFusedGroups;
 }
 

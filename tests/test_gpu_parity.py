@@ -600,7 +600,7 @@ def test_layer_parity(key, T, which):
     # routing over all tokens
     lg_ref = oracle.logits(layer.x, w["w_r"], w["b_r"])
     diff, ties = G.assert_selection(r["idx"], lg_ref, f"{key}/T={T}")
-    # the layer's own dispatch (the fused route + dispatch kernel up to 32 tokens) is
+    # the layer's own dispatch (the fused route + dispatch kernel up to 16 tokens) is
     # exactly the oracle's dispatch of the indices it chose
     d_ref = oracle.dispatch(r["idx"], E)
     for k in ("counts", "offsets", "sorted_assign", "assign_pos"):
@@ -722,7 +722,7 @@ ROUTER_SHAPES = [(24, 64, 1), (24, 320, 17), (40, 320, 33), (63, 192, 200), (48,
 def test_router_odd_shapes_and_fused_path(E, d, T):
     """The bf16 router at expert counts that leave part of a 16-expert column
     tile empty, k-step counts that do not fill the waves evenly, and token
-    counts around the 16-token tiles; up to 32 tokens the layer routes with
+    counts around the 16-token tiles; up to 16 tokens the layer routes with
     the fused route + dispatch kernel, which must choose exactly what the route
     entry point chooses."""
     rng = np.random.default_rng(E * 1000 + d + T)
@@ -744,7 +744,7 @@ def test_router_odd_shapes_and_fused_path(E, d, T):
     G.assert_selection(idx_h, lg_ref, "router odd shapes")
     g_ref = oracle.gates(lg_ref, idx_h)
     G.assert_fp32_close(gate_h, g_ref, G.gates_scale(S_lg, idx_h, g_ref, lg_ref), "gates")
-    # the whole layer (fused routing at T <= 32) picks the same experts and gates
+    # the whole layer (fused routing at T <= 16) picks the same experts and gates
     w1 = G.dev(gen.f32_to_bf16_bits((rng.standard_normal((E, d, 64)) / np.sqrt(d)).astype(np.float32)))
     w2 = G.dev(gen.f32_to_bf16_bits((rng.standard_normal((E, 64, d)) / 8).astype(np.float32)))
     ws_bytes = moe.workspace_size(sh)
