@@ -30,7 +30,10 @@
 //     transposes run in registers;
 //   * pipeline: a ring of two LDS stages; the operands of k-step ks+1 are
 //     read from LDS while k-step ks is multiplied, and the one workgroup
-//     barrier per k-tile sits before the tile's last k-step;
+//     barrier per k-tile sits before the tile's last k-step; the copies of a
+//     k-tile are issued two k-steps apart (weights right after the barrier
+//     that frees their stage, A rows one k-step later), each placed between
+//     MFMAs;
 //   * epilogue: bias + ReLU/GELU, silu(u)*v (the W1 and W3 tiles of a column
 //     block live in the same wave and lane), or bias only; the bf16 tile is
 //     staged through LDS and written back with 16-byte row stores;
