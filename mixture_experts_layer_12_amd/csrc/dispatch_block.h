@@ -40,11 +40,56 @@ __device__ __forceinline__ void dispatch_block(IdxAt idx_at, int A, int E, int32
                                                int32_t *__restrict__ assign_pos, DispatchShared<NW> &sh) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    if (A <= kWave) {
+        // one chunk: wave 0 alone, in registers, with no barrier (decode batches)
+        if (w != 0) return;
+        int e = (lane < A) ? idx_at(lane) : -1;
+        if (e < 0 || e >= E) e = -1;
+        int cnt = 0;  // lane x: assignments of expert x
+        uint64_t rem = __ballot(e >= 0);
+        while (rem) {
+            const int leader = __ffsll((unsigned long long)rem) - 1;
+            const int ee = __shfl(e, leader);
+            const uint64_t m = __ballot(e == ee);
+            if (lane == ee) cnt = __popcll(m);
+            rem &= ~m;
+        }
+        const int tot = (lane < E) ? cnt : 0;
+        int incl = tot;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int o = __shfl_up(incl, s);
+            if (lane >= s) incl += o;
+        }
+        const int excl = incl - tot;
+        if (lane < E) {
+            counts[lane] = tot;
+            offsets[lane] = excl;
+        }
+        if (lane == E - 1) offsets[E] = incl;
+        const int total_valid = __shfl(incl, E - 1);
+        int pos = -1;
+        rem = __ballot(e >= 0);
+        while (rem) {
+            const int leader = __ffsll((unsigned long long)rem) - 1;
+            const int ee = __shfl(e, leader);
+            const uint64_t m = __ballot(e == ee);
+            const int base = __shfl(excl, ee);
+            if (e == ee) pos = base + __popcll(m & lt_mask);
+            rem &= ~m;
+        }
+        if (lane < A) {
+            assign_pos[lane] = pos;
+            if (pos >= 0) sorted_assign[pos] = lane;
+            if (lane >= total_valid) sorted_assign[lane] = -1;
+        }
+        return;
+    }
     const int nchunks = ceil_div(A, kWave);
     const int per = ceil_div(nchunks, NW);
     const int c_begin = min(nchunks, w * per);
     const int c_end = min(nchunks, c_begin + per);
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 
     // pass 1: lane e accumulates this wave's count of expert e
     int my_cnt = 0;
