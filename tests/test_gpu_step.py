@@ -78,6 +78,7 @@ STEP_CASES = [
     ("e8", 1, 4, "pair", False, True),
     ("e8", 64, 3, "softmax", False, True),
     ("e8", 512, 2, "pair", False, False),
+    ("e8", 1024, 2, "pair", False, True),  # large-tile GEMMs, the second split in K
     ("shared15", 1, 3, "softmax", True, True),
     ("shared15", 64, 3, "softmax", True, True),
     ("mixtral_decode", 4, 2, "pair", False, True),
