@@ -708,6 +708,15 @@ def main():
         del EL
         rings.clear()
         torch.cuda.empty_cache()
+        # tiny fp32 layer: launch-latency bound (its 0.27 MB of weights stay in cache), so one weight copy
+        tcfg = gen.CONFIGS["tiny"]
+        rec["tiny"], TL = decode_batches(g, gen, moe, tcfg, Weights(g, gen, tcfg, 0.0), (32,), args.decode_iters)
+        rec["tiny"]["T=32"].pop("mfma_frac", None)
+        rec["tiny"]["T=32"].pop("hbm_frac", None)
+        rec["tiny"]["workload"] = (f"{tcfg.title}: E={tcfg.E}, d={tcfg.d}, h={tcfg.h}, {tcfg.act} + biases, fp32 "
+                                   "(launch-latency bound; one weight copy)")
+        del TL
+        torch.cuda.empty_cache()
         if not args.no_variants:
             rec["variants"] = time_variants(g, gen, moe, args.rotate_gb)
             torch.cuda.empty_cache()
