@@ -105,14 +105,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
 
     const int ty = tid / 16, tx = tid % 16;
     float acc[NB][4][4] = {};
+    // the next k-tile's operands are loaded into registers while the current
+    // one is multiplied, so each k-tile does not wait a full load latency
+    f32x4 av, bv[NB];
+    auto load = [&](int k0) {
+        av = a_ptr ? *reinterpret_cast<const f32x4 *>(a_ptr + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) bv[b] = *reinterpret_cast<const f32x4 *>(b_ptr[b] + (size_t)k0 * N);
+    };
+    load(0);
     for (int k0 = 0; k0 < K; k0 += BK) {
-        f32x4 av = a_ptr ? *reinterpret_cast<const f32x4 *>(a_ptr + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < 4; ++q) As[aq * 4 + q][ar] = av[q];
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            *reinterpret_cast<f32x4 *>(&Bs[b][br][bq * 4]) = *reinterpret_cast<const f32x4 *>(b_ptr[b] + (size_t)k0 * N);
+        for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4 *>(&Bs[b][br][bq * 4]) = bv[b];
         __syncthreads();
+        if (k0 + BK < K) load(k0 + BK);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
             const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&As[k][ty * 4]);
